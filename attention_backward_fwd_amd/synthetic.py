@@ -1,0 +1,67 @@
+"""Seeded synthetic inputs for attention forward/backward.
+
+This module only draws random numbers and names the workload shapes; it holds
+none of the attention arithmetic.  Both the fp64 oracle (through the tests) and
+the GPU path consume what it produces, so the two sides always see identical
+bf16 inputs.
+
+Recipe: a CPU ``torch.Generator`` seeded with ``seed`` draws standard-normal
+fp32 tensors in [batch, seq, heads, dim] order Q, K, V, dO; Q and K are then
+multiplied by ``qk_mult`` (1.5 gives sharper softmax rows); finally every
+tensor is rounded to bf16 (round-to-nearest-even).
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    heads_q: int
+    heads_kv: int
+    seqlen: int
+    head_dim: int
+    causal: tuple  # the causal settings the workload is run with
+    qk_mult: float = 1.0
+    paths: tuple = ("atomic", "split")
+
+    @property
+    def groups(self) -> int:
+        return self.heads_q // self.heads_kv
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+
+# The five seeded synthetic workloads (sizes only).
+WORKLOADS = {
+    "mha_s128_d64": Workload("mha_s128_d64", 1, 2, 2, 128, 64, (False,)),
+    "mha_causal_b8_h32_s1024_d64": Workload("mha_causal_b8_h32_s1024_d64", 8, 32, 32, 1024, 64, (True,), paths=("atomic",)),
+    "gqa4_causal_b8_h32_s2048_d128": Workload("gqa4_causal_b8_h32_s2048_d128", 8, 32, 8, 2048, 128, (True,)),
+    "mha_causal_b4_h32_s4096_d128": Workload("mha_causal_b4_h32_s4096_d128", 4, 32, 32, 4096, 128, (True,)),
+    "gqa8_b1_h64_s8192_d128": Workload("gqa8_b1_h64_s8192_d128", 1, 64, 8, 8192, 128, (False, True), qk_mult=1.5),
+}
+
+
+def make_inputs(batch, seqlen, heads_q, heads_kv, head_dim, seed=0, qk_mult=1.0):
+    """Return dict q, k, v, do of bf16 CPU tensors in BSHD layout."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    q = torch.randn((batch, seqlen, heads_q, head_dim), generator=g, dtype=torch.float32)
+    k = torch.randn((batch, seqlen, heads_kv, head_dim), generator=g, dtype=torch.float32)
+    v = torch.randn((batch, seqlen, heads_kv, head_dim), generator=g, dtype=torch.float32)
+    do = torch.randn((batch, seqlen, heads_q, head_dim), generator=g, dtype=torch.float32)
+    if qk_mult != 1.0:
+        q = q * qk_mult
+        k = k * qk_mult
+    return {n: t.to(torch.bfloat16) for n, t in (("q", q), ("k", k), ("v", v), ("do", do))}
+
+
+def workload_inputs(w: Workload, seed=0):
+    return make_inputs(w.batch, w.seqlen, w.heads_q, w.heads_kv, w.head_dim, seed=seed, qk_mult=w.qk_mult)
