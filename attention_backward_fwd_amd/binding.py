@@ -1,0 +1,180 @@
+"""Thin ctypes binding of libmi355_attn.so.
+
+The functions carry the C ABI's names and do argument marshalling only:
+tensor pointers, shapes and the current HIP stream go to the library, every
+step of the computation runs in its kernels.  torch supplies device memory
+and streams.  There is no fallback: a missing library raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmi355_attn.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "mi355_attn.h")
+
+ATTN_OK = 0
+
+
+class attn_shape(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("seqlen", ctypes.c_int32),
+        ("heads_q", ctypes.c_int32),
+        ("groups", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def library():
+    """Load the shared library once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m attention_backward_fwd_amd.build` "
+                "(there is no fallback implementation)")
+        lib = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        lib.attn_strerror.restype = ctypes.c_char_p
+        lib.attn_strerror.argtypes = [ctypes.c_int]
+        lib.attn_fwd.restype = ctypes.c_int
+        lib.attn_fwd.argtypes = [P, P, P, P, P, attn_shape, ctypes.c_float, ctypes.c_int, P]
+        lib.attn_bwd_preprocess.restype = ctypes.c_int
+        lib.attn_bwd_preprocess.argtypes = [P, P, P, P, attn_shape, P]
+        lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.attn_bwd_workspace_bytes.argtypes = [attn_shape, ctypes.c_int, ctypes.c_int]
+        lib.attn_bwd.restype = ctypes.c_int
+        lib.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, attn_shape, ctypes.c_float,
+                                 ctypes.c_int, ctypes.c_int, P]
+        lib.attn_bwd_postprocess.restype = ctypes.c_int
+        lib.attn_bwd_postprocess.argtypes = [P, P, ctypes.c_size_t, P, P, P, attn_shape, P]
+        _lib = lib
+    return _lib
+
+
+def header_functions():
+    """Names of the functions include/mi355_attn.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status, where):
+        msg = library().attn_strerror(status).decode()
+        super().__init__(f"{where}: status {status}: {msg}")
+        self.status = status
+
+
+def _check(status, where):
+    if status != ATTN_OK:
+        raise AttnError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def make_shape(batch, seqlen, heads_q, groups, head_dim):
+    return attn_shape(batch, seqlen, heads_q, groups, head_dim)
+
+
+def shape_of(q, k):
+    """attn_shape from BSHD q [B,S,Hq,D] and k [B,S,Hkv,D]."""
+    b, s, hq, d = q.shape
+    hkv = k.shape[2]
+    if hkv < 1 or hq % hkv:
+        raise ValueError("heads_q must be a multiple of heads_kv")
+    return attn_shape(b, s, hq, hq // hkv, d)
+
+
+# ------------------------------------------------------------ the C ABI calls
+
+def attn_fwd(q, k, v, o, lse, shape, softmax_scale, causal, stream=None):
+    _check(library().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), shape, float(softmax_scale),
+                              int(causal), _stream(stream)), "attn_fwd")
+
+
+def attn_bwd_preprocess(o, dout, delta, dq_accum, shape, stream=None):
+    _check(library().attn_bwd_preprocess(_ptr(o), _ptr(dout), _ptr(delta), _ptr(dq_accum), shape,
+                                         _stream(stream)), "attn_bwd_preprocess")
+
+
+def attn_bwd_workspace_bytes(shape, causal, use_atomic):
+    return int(library().attn_bwd_workspace_bytes(shape, int(causal), int(use_atomic)))
+
+
+def attn_bwd(q, k, v, dout, lse, delta, dq_accum, dk, dv, workspace, shape, softmax_scale, causal,
+             use_atomic, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq_accum),
+                              _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, shape, float(softmax_scale),
+                              int(causal), int(use_atomic), _stream(stream)), "attn_bwd")
+
+
+def attn_bwd_postprocess(dq_accum, workspace, dq, dk, dv, shape, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().attn_bwd_postprocess(_ptr(dq_accum), _ptr(workspace), ws_bytes, _ptr(dq), _ptr(dk),
+                                          _ptr(dv), shape, _stream(stream)), "attn_bwd_postprocess")
+
+
+# ------------------------------------------------------------ conveniences
+
+def _require_gpu_inputs(*ts):
+    for t in ts:
+        if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError("inputs must be contiguous bf16 tensors on the GPU")
+
+
+def forward(q, k, v, causal, scale, stream=None):
+    """O, LSE = attention(q, k, v); allocates the outputs with torch."""
+    _require_gpu_inputs(q, k, v)
+    shape = shape_of(q, k)
+    o = torch.empty_like(q)
+    lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=q.device)
+    attn_fwd(q, k, v, o, lse, shape, scale, causal, stream)
+    return o, lse
+
+
+class BwdBuffers:
+    """Outputs and scratch of one backward problem, allocated once."""
+
+    def __init__(self, q, k, causal, use_atomic):
+        self.shape = shape_of(q, k)
+        dev = q.device
+        b, s, hq, d = q.shape
+        self.delta = torch.empty((b, hq, s), dtype=torch.float32, device=dev)
+        self.dq_accum = torch.empty(q.shape, dtype=torch.float32, device=dev)
+        self.dq = torch.empty_like(q)
+        self.dk = torch.empty_like(k)
+        self.dv = torch.empty_like(k)
+        nbytes = attn_bwd_workspace_bytes(self.shape, causal, use_atomic)
+        self.workspace = torch.empty(max(nbytes, 0) // 4, dtype=torch.float32, device=dev) if nbytes else None
+
+
+def backward(q, k, v, o, lse, do, causal, scale, use_atomic=True, buffers=None, stream=None):
+    """dQ, dK, dV via preprocess -> bwd (-> sum) -> postprocess."""
+    _require_gpu_inputs(q, k, v, o, do)
+    bb = buffers or BwdBuffers(q, k, causal, use_atomic)
+    sh = bb.shape
+    attn_bwd_preprocess(o, do, bb.delta, bb.dq_accum if use_atomic else None, sh, stream)
+    attn_bwd(q, k, v, do, lse, bb.delta, bb.dq_accum, bb.dk, bb.dv, bb.workspace, sh, scale, causal, use_atomic,
+             stream)
+    attn_bwd_postprocess(bb.dq_accum, bb.workspace, bb.dq, bb.dk, bb.dv, sh, stream)
+    return bb.dq, bb.dk, bb.dv

@@ -1,0 +1,151 @@
+// Bandwidth-bound steps around the attention backward on gfx950:
+//   preprocess   Delta = rowsum(dO o O) (+ zero the fp32 dQ accumulator)
+//   dq_sum       split path: dQ = sum of the per-key-block partials, in
+//                ascending block order
+//   postprocess  dQ fp32 -> bf16; grouped-query dK/dV partial reduction
+// These are the flashattn_bwd_preprocess / flashattn_bwd_postprocess steps of
+// the TileLang #940 examples and the "sum" half of its split+sum template.
+// All moves are 16-byte vector loads/stores along contiguous rows.
+#include "common.h"
+#include "kernels.h"
+
+namespace mi355 {
+
+namespace {
+
+// One row (b, s, h) per D/8 lanes, 8 elements per lane.  Rows are numbered
+// (b, h, s) with s fastest so that Delta, stored [B][Hq][S], is written with
+// consecutive addresses by neighbouring row groups.
+template <int D>
+__global__ __launch_bounds__(256) void preprocess_kernel(const uint16_t* __restrict__ o,
+                                                         const uint16_t* __restrict__ dout,
+                                                         float* __restrict__ delta,
+                                                         float* __restrict__ dq_accum, int B, int S,
+                                                         int Hq) {
+  constexpr int TPR = D / 8;  // lanes per row
+  const long long rows = (long long)B * Hq * S;
+  const int sub = threadIdx.x % TPR;
+  const long long stride = (long long)gridDim.x * (256 / TPR);
+  for (long long row = (long long)blockIdx.x * (256 / TPR) + threadIdx.x / TPR; row < rows; row += stride) {
+    const int s = (int)(row % S);
+    const long long bh = row / S;
+    const int h = (int)(bh % Hq), b = (int)(bh / Hq);
+    const size_t off = ((size_t)((long long)b * S + s) * Hq + h) * D + 8 * sub;
+    const u32x4 ov = *reinterpret_cast<const u32x4*>(o + off);
+    const u32x4 dv = *reinterpret_cast<const u32x4*>(dout + off);
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      acc = fmaf(__uint_as_float(ov[i] << 16), __uint_as_float(dv[i] << 16), acc);
+      acc = fmaf(__uint_as_float(ov[i] & 0xffff0000u), __uint_as_float(dv[i] & 0xffff0000u), acc);
+    }
+#pragma unroll
+    for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+    if (sub == 0) delta[row] = acc;
+    if (dq_accum) {
+      f32x4* z = reinterpret_cast<f32x4*>(dq_accum + off);
+      z[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      z[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+}
+
+// dq_accum[b,s,h,:] = sum_{j=0..J(s)} part[j][b,s,h,:], ascending j, where
+// J(s) is the last key block (causal: the block holding key s).
+__global__ __launch_bounds__(256) void dq_sum_kernel(const float* __restrict__ part,
+                                                     float* __restrict__ dq, long long n4, int S,
+                                                     int HqD, int n_nblk, int causal) {
+  const size_t slot = (size_t)n4 * 4;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long long)gridDim.x * 256) {
+    const long long e = i * 4;
+    const int s = (int)((e / HqD) % S);
+    const int last = causal ? s / kBwdBlockN : n_nblk - 1;
+    const float* src = part + e;
+    f32x4 acc = *reinterpret_cast<const f32x4*>(src);
+    for (int j = 1; j <= last; j++) acc += *reinterpret_cast<const f32x4*>(src + (size_t)j * slot);
+    *reinterpret_cast<f32x4*>(dq + e) = acc;
+  }
+}
+
+__device__ __forceinline__ u32x4 cvt8(f32x4 a, f32x4 b) {
+  return u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+               pack_bf16x2(b[2], b[3])};
+}
+
+// Part 1 (chunks [0, nq8)): dq = bf16(dq_accum), 8 elements per chunk.
+// Part 2 (chunks [nq8, nq8 + nkv8), grouped queries only): dk/dv chunk of
+// (b, s, kv) = bf16(sum_r partial[b, s, kv*G + r]), ascending r.
+__global__ __launch_bounds__(256) void postprocess_kernel(const float* __restrict__ dq_accum,
+                                                          const float* __restrict__ dk_part,
+                                                          const float* __restrict__ dv_part,
+                                                          uint16_t* __restrict__ dq, uint16_t* __restrict__ dk,
+                                                          uint16_t* __restrict__ dv, long long nq8,
+                                                          long long nkv8, int G, int D) {
+  const long long total = nq8 + nkv8;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long long)gridDim.x * 256) {
+    if (i < nq8) {
+      const f32x4* src = reinterpret_cast<const f32x4*>(dq_accum + i * 8);
+      *reinterpret_cast<u32x4*>(dq + i * 8) = cvt8(src[0], src[1]);
+    } else {
+      const long long c = i - nq8;          // chunk of the [B,S,Hkv,D] output
+      const int dchunks = D / 8;
+      const long long rowkv = c / dchunks;  // (b, s, kv) flattened
+      const int d0 = (int)(c % dchunks) * 8;
+      const size_t base = (size_t)rowkv * G * D + d0;  // partial row (b, s, kv*G) at d0
+      f32x4 k0 = {0, 0, 0, 0}, k1 = {0, 0, 0, 0}, v0 = {0, 0, 0, 0}, v1 = {0, 0, 0, 0};
+      for (int r = 0; r < G; r++) {
+        const f32x4* pk = reinterpret_cast<const f32x4*>(dk_part + base + (size_t)r * D);
+        const f32x4* pv = reinterpret_cast<const f32x4*>(dv_part + base + (size_t)r * D);
+        k0 += pk[0];
+        k1 += pk[1];
+        v0 += pv[0];
+        v1 += pv[1];
+      }
+      *reinterpret_cast<u32x4*>(dk + c * 8) = cvt8(k0, k1);
+      *reinterpret_cast<u32x4*>(dv + c * 8) = cvt8(v0, v1);
+    }
+  }
+}
+
+unsigned grid_for(long long work, long long per_block) {
+  long long g = (work + per_block - 1) / per_block;
+  const long long cap = 256LL * 64;  // enough resident workgroups for the whole chip
+  if (g > cap) g = cap;
+  if (g < 1) g = 1;
+  return (unsigned)g;
+}
+
+}  // namespace
+
+hipError_t launch_preprocess(const uint16_t* o, const uint16_t* dout, float* delta, float* dq_accum,
+                             int B, int S, int Hq, int D, hipStream_t stream) {
+  const long long rows = (long long)B * Hq * S;
+  if (D == 64)
+    hipLaunchKernelGGL(preprocess_kernel<64>, dim3(grid_for(rows, 32)), dim3(256), 0, stream, o, dout, delta,
+                       dq_accum, B, S, Hq);
+  else
+    hipLaunchKernelGGL(preprocess_kernel<128>, dim3(grid_for(rows, 16)), dim3(256), 0, stream, o, dout, delta,
+                       dq_accum, B, S, Hq);
+  return hipGetLastError();
+}
+
+hipError_t launch_dq_sum(const float* dq_part, float* dq_accum, int B, int S, int Hq, int D, int causal,
+                         hipStream_t stream) {
+  const long long n4 = (long long)B * S * Hq * D / 4;
+  const int n_nblk = (S + kBwdBlockN - 1) / kBwdBlockN;
+  hipLaunchKernelGGL(dq_sum_kernel, dim3(grid_for(n4, 256)), dim3(256), 0, stream, dq_part, dq_accum, n4, S,
+                     Hq * D, n_nblk, causal);
+  return hipGetLastError();
+}
+
+hipError_t launch_postprocess(const float* dq_accum, const float* dk_part, const float* dv_part, uint16_t* dq,
+                              uint16_t* dk, uint16_t* dv, int B, int S, int Hq, int G, int D,
+                              hipStream_t stream) {
+  const long long nq8 = (long long)B * S * Hq * D / 8;
+  const long long nkv8 = G > 1 ? (long long)B * S * (Hq / G) * D / 8 : 0;
+  hipLaunchKernelGGL(postprocess_kernel, dim3(grid_for(nq8 + nkv8, 256)), dim3(256), 0, stream, dq_accum,
+                     dk_part, dv_part, dq, dk, dv, nq8, nkv8, G, D);
+  return hipGetLastError();
+}
+
+}  // namespace mi355

@@ -1,0 +1,224 @@
+// Forward of exact softmax attention on gfx950: O = softmax(scale Q K^T) V and
+// the per-row log-sum-exp.
+//
+// The FlashAttention forward (flashattn_fwd in the TileLang #940 examples)
+// streams key/value blocks past a resident query block with an online
+// softmax.  This kernel does the same with the products transposed, so that
+// every query row lives in one lane:
+//
+//   S^T (keys x queries) = K (keys x D) * Q^T        A = K from LDS, B = Q in registers
+//   O^T (D x queries)   += V^T (D x keys) * P^T      A = V via transposing LDS reads,
+//                                                     B = P^T straight from S^T's registers
+//
+// In the 32x32 MFMA result layout a lane holds one column (here: one query)
+// and 16 rows (keys), so the running row max and row sum are in-lane
+// reductions plus a single exchange between the two wavefront halves, and the
+// rescale factor of the online softmax is a per-lane scalar.
+//
+// Workgroup: 4 waves x 32 queries = 128 queries; key/value tiles of 64 rows,
+// double-staged through registers into LDS.  Scores stay fp32; P is rounded
+// to bf16 only as an MFMA operand; O is written as bf16 (RNE) and LSE as fp32
+// natural log including the scale.
+#include "common.h"
+#include "kernels.h"
+
+namespace mi355 {
+
+namespace {
+
+constexpr int kFwdBM = 128;
+constexpr int kFwdBN = 64;
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
+  constexpr int BM = kFwdBM, BN = kFwdBN;
+  constexpr int KP = D + 8;    // sK pitch in elements (16-byte row reads)
+  constexpr int VP = D + 16;   // sV pitch in elements (transposing reads)
+  constexpr int NKS = D / 16;  // MFMA k-steps over the head dimension
+  constexpr int NDT = D / 32;  // 32-row tiles of O^T
+  constexpr int CH = D / 8;    // 16-byte chunks per row
+  constexpr int LDI = BN * CH / 256;
+
+  __shared__ __attribute__((aligned(16))) uint16_t sK[BN * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[BN * VP];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int hi = lane >> 5, l32 = lane & 31, L = lane & 15, Gp = (lane >> 4) & 1;
+  const int S = p.S, Hq = p.Hq, G = p.G, Hkv = p.Hkv;
+  const int n_mblk = (S + BM - 1) / BM;
+
+  // Tile order: each XCD gets a contiguous range of (batch, KV head) groups;
+  // inside it, query blocks run heaviest-first under causal masking.
+  const int nwg = gridDim.x, NG = p.B * Hkv;
+  int t = blockIdx.x, x = 0, NGx = NG;
+  if (NG % 8 == 0) {
+    t = xcd_remap(blockIdx.x, nwg);
+    const int per = nwg / 8;
+    x = t / per;
+    t -= x * per;
+    NGx = NG / 8;
+  }
+  const int r = t % G;
+  t /= G;
+  const int grp = x * NGx + t % NGx;
+  const int mbo = t / NGx;
+  const int b = grp / Hkv, kvh = grp % Hkv, h = kvh * G + r;
+  const int mb = CAUSAL ? (n_mblk - 1 - mbo) : mbo;
+
+  const size_t qrs = (size_t)Hq * D, kvrs = (size_t)Hkv * D;
+  const uint16_t* Qb = p.q + ((size_t)b * S * Hq + h) * D;
+  const uint16_t* Kb = p.k + ((size_t)b * S * Hkv + kvh) * D;
+  const uint16_t* Vb = p.v + ((size_t)b * S * Hkv + kvh) * D;
+
+  const int q0 = mb * BM + 32 * w;  // first query of this wave
+  const int qi = q0 + l32;          // this lane's query
+
+  bf16x8 qf[NKS];
+  if (qi < S) {
+    const uint16_t* qr = Qb + (size_t)qi * qrs + 8 * hi;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ks++) qf[ks] = *reinterpret_cast<const bf16x8*>(qr + 16 * ks);
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ks++) qf[ks] = bf16x8{};
+  }
+
+  const int n_end = CAUSAL ? min(S, mb * BM + BM) : S;
+  const int n_tiles = (n_end + BN - 1) / BN;
+  const float c = p.scale * kLog2e;
+
+  u32x4 kr[LDI], vr[LDI];
+  auto gload = [&](int n0) {
+#pragma unroll
+    for (int i = 0; i < LDI; i++) {
+      const int idx = tid + 256 * i, row = idx / CH, col = (idx % CH) * 8, key = n0 + row;
+      if (key < S) {
+        kr[i] = *reinterpret_cast<const u32x4*>(Kb + (size_t)key * kvrs + col);
+        vr[i] = *reinterpret_cast<const u32x4*>(Vb + (size_t)key * kvrs + col);
+      } else {
+        kr[i] = u32x4{0, 0, 0, 0};
+        vr[i] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+
+  f32x16 oacc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; dt++) oacc[dt] = f32x16{};
+  float m_i = -INFINITY, l_i = 0.f;
+
+  gload(0);
+  for (int it = 0; it < n_tiles; it++) {
+    const int n0 = it * BN;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < LDI; i++) {
+      const int idx = tid + 256 * i, row = idx / CH, col = (idx % CH) * 8;
+      *reinterpret_cast<u32x4*>(&sK[row * KP + col]) = kr[i];
+      *reinterpret_cast<u32x4*>(&sV[row * VP + col]) = vr[i];
+    }
+    __syncthreads();
+    if (it + 1 < n_tiles) gload(n0 + BN);
+
+    // A wave whose queries all precede the tile has nothing to do in it.
+    if (CAUSAL && n0 > q0 + 31) continue;
+
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ks++) {
+#pragma unroll
+      for (int mt = 0; mt < 2; mt++) {
+        const bf16x8 a = lds_read_b128(&sK[(32 * mt + l32) * KP + 16 * ks + 8 * hi]);
+        s[mt] = mfma32(a, qf[ks], s[mt]);
+      }
+    }
+
+    const bool need_mask = (n0 + BN > S) || (CAUSAL && n0 + BN - 1 > q0);
+    if (need_mask) {
+#pragma unroll
+      for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+          const int key = n0 + 32 * mt + 8 * (j >> 2) + 4 * hi + (j & 3);
+          if (key >= S || (CAUSAL && key > qi)) s[mt][j] = -INFINITY;
+        }
+    }
+
+    float mx = s[0][0];
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+      for (int j = 0; j < 16; j++) mx = fmaxf(mx, s[mt][j]);
+    mx = xhalf_max(mx);
+    const float m_new = fmaxf(m_i, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float mc = m_use * c;
+    const float alpha = __builtin_amdgcn_exp2f(m_i * c - mc);
+    float rs = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+      for (int j = 0; j < 16; j++) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(s[mt][j], c, -mc));
+        s[mt][j] = e;
+        rs += e;
+      }
+    l_i = fmaf(l_i, alpha, rs);
+    m_i = m_new;
+#pragma unroll
+    for (int dt = 0; dt < NDT; dt++) oacc[dt] *= alpha;
+
+    // P^T as the B operand: k-step kk covers keys 16kk.. of the tile, in the
+    // order the S^T result layout holds them.
+    bf16x8 pb[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; kk++) {
+      const int mt = kk >> 1, o8 = 8 * (kk & 1);
+      pb[kk] = pack8(s[mt][o8 + 0], s[mt][o8 + 1], s[mt][o8 + 2], s[mt][o8 + 3], s[mt][o8 + 4],
+                     s[mt][o8 + 5], s[mt][o8 + 6], s[mt][o8 + 7]);
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; dt++) {
+      const int col = 32 * dt + 16 * Gp + 4 * (L & 3);
+#pragma unroll
+      for (int kk = 0; kk < 4; kk++) {
+        const int row = 16 * kk + 4 * hi + (L >> 2);
+        const bf16x8 a = lds_read_tr8(&sV[row * VP + col], &sV[(row + 8) * VP + col]);
+        oacc[dt] = mfma32(a, pb[kk], oacc[dt]);
+      }
+    }
+  }
+
+  const float l_tot = xhalf_sum(l_i);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (qi < S) {
+    uint16_t* orow = p.o + ((size_t)(b * S + qi) * Hq + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; dt++)
+#pragma unroll
+      for (int jg = 0; jg < 4; jg++) {
+        const int d = 32 * dt + 8 * jg + 4 * hi;
+        u32x2 v2 = {pack_bf16x2(oacc[dt][4 * jg] * inv, oacc[dt][4 * jg + 1] * inv),
+                    pack_bf16x2(oacc[dt][4 * jg + 2] * inv, oacc[dt][4 * jg + 3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + d) = v2;
+      }
+    if (hi == 0) p.lse[(size_t)(b * Hq + h) * S + qi] = m_i * p.scale + __builtin_amdgcn_logf(l_tot) * kLn2;
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
+  const int n_mblk = (p.S + kFwdBM - 1) / kFwdBM;
+  const long long nwg = (long long)p.B * p.Hq * n_mblk;
+  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL>), dim3((unsigned)nwg), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
+  if (p.D == 64) return p.causal ? launch_fwd_t<64, true>(p, stream) : launch_fwd_t<64, false>(p, stream);
+  return p.causal ? launch_fwd_t<128, true>(p, stream) : launch_fwd_t<128, false>(p, stream);
+}
+
+}  // namespace mi355

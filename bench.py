@@ -1,0 +1,197 @@
+"""Throughput of the fused attention forward + backward on one MI355X.
+
+One step = the whole hot path on one batch of seeded synthetic input already
+resident in HBM: attn_fwd, attn_bwd_preprocess, attn_bwd (plus the dQ sum on
+the split path) and attn_bwd_postprocess, all through the C ABI.
+
+Prints one JSON line.  ``value`` is fwd+bwd TFLOP/s with the FLOP count
+4*B*Hq*S^2*D (forward) + 10*B*Hq*S^2*D (backward), halved under causal
+masking.  ``roofline`` covers the dominant kernel (the backward kernel),
+timed with HIP events on the stream it runs on; ``cpu_baseline`` times the
+fp64 oracle on the host cores on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+METRIC = "attention fwd+bwd TFLOP/s (bf16, causal) and % of MI355X bf16 MFMA peak"
+DEFAULT_WORKLOAD = "mha_causal_b4_h32_s4096_d128"
+
+
+def flops(w, causal):
+    f = w.batch * w.heads_q * w.seqlen * w.seqlen * w.head_dim
+    div = 2 if causal else 1
+    return 4 * f / div, 10 * f / div
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "attention_backward_fwd_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload, path):
+    """HBM bytes per bwd launch from the committed counter summary, if it still
+    describes the current kernel sources; else None."""
+    fn = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(fn) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(f"{workload}/{path}")
+    if not entry or entry.get("source_hash") != kernel_source_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def cpu_baseline(w, causal, budget_s):
+    """The fp64 oracle on host cores, one KV group at a time until the budget is used."""
+    import numpy as np
+    import torch
+
+    from attention_backward_fwd_amd.synthetic import make_inputs
+    from oracle import attention as orc
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
+    except Exception:  # threadpoolctl missing: numpy BLAS default
+        cores = os.cpu_count() or 1
+    g = w.groups
+    groups_done, t_total = 0, 0.0
+    seed = 0
+    while t_total < budget_s and groups_done < w.batch * (w.heads_q // g):
+        # one (batch, KV head) group: g query heads and their KV head, full length
+        inp = make_inputs(1, w.seqlen, g, 1, w.head_dim, seed=seed + groups_done, qk_mult=w.qk_mult)
+        f = {n: t.to(torch.float64).numpy() for n, t in inp.items()}
+        t0 = time.perf_counter()
+        orc.attention_fwd(f["q"], f["k"], f["v"], w.scale, causal, g)
+        orc.attention_bwd(f["q"], f["k"], f["v"], f["do"], w.scale, causal, g)
+        t_total += time.perf_counter() - t0
+        groups_done += 1
+    fwd_f, bwd_f = flops(w, causal)
+    frac = groups_done * g / (w.batch * w.heads_q)
+    tflops = (fwd_f + bwd_f) * frac / t_total / 1e12
+    return {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{groups_done} of {w.batch * (w.heads_q // g)} (batch, KV-head) groups at full length "
+                      f"({groups_done * g} query heads), fwd+bwd in fp64, {t_total:.1f} s; "
+                      f"FLOPs counted with the same causal-halved formula"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--causal", type=int, default=None, help="override the workload's causal setting")
+    ap.add_argument("--use-atomic", type=int, default=1, choices=(0, 1))
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the problem shards over (batch, KV head) with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from attention_backward_fwd_amd import binding as bd
+    from attention_backward_fwd_amd.synthetic import WORKLOADS, workload_inputs
+
+    w = WORKLOADS[args.workload]
+    causal = w.causal[-1] if args.causal is None else bool(args.causal)
+    use_atomic = args.use_atomic
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = {n: t.to(dev) for n, t in workload_inputs(w).items()}
+    q, k, v, do = inp["q"], inp["k"], inp["v"], inp["do"]
+    sh = bd.shape_of(q, k)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.batch, w.heads_q, w.seqlen), dtype=torch.float32, device=dev)
+    bb = bd.BwdBuffers(q, k, causal, use_atomic)
+    stream = torch.cuda.current_stream()
+
+    ev = {n: [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)] for n in ("fwd", "bwd")}
+
+    def step(i=None):
+        if i is not None:
+            ev["fwd"][2 * i].record(stream)
+        bd.attn_fwd(q, k, v, o, lse, sh, w.scale, causal, stream)
+        if i is not None:
+            ev["fwd"][2 * i + 1].record(stream)
+        bd.attn_bwd_preprocess(o, do, bb.delta, bb.dq_accum if use_atomic else None, sh, stream)
+        if i is not None:
+            ev["bwd"][2 * i].record(stream)
+        bd.attn_bwd(q, k, v, do, lse, bb.delta, bb.dq_accum, bb.dk, bb.dv, bb.workspace, sh, w.scale, causal,
+                    use_atomic, stream)
+        if i is not None:
+            ev["bwd"][2 * i + 1].record(stream)
+        bd.attn_bwd_postprocess(bb.dq_accum, bb.workspace, bb.dq, bb.dk, bb.dv, sh, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    fwd_f, bwd_f = flops(w, causal)
+    ms_per_step = elapsed / args.steps * 1e3
+    value = (fwd_f + bwd_f) * args.steps / elapsed / 1e12
+    fwd_ms = sum(ev["fwd"][2 * i].elapsed_time(ev["fwd"][2 * i + 1]) for i in range(args.steps)) / args.steps
+    bwd_ms = sum(ev["bwd"][2 * i].elapsed_time(ev["bwd"][2 * i + 1]) for i in range(args.steps)) / args.steps
+    bwd_tflops = bwd_f / (bwd_ms * 1e-3) / 1e12
+    path = "atomic" if use_atomic else "split"
+    kernel = "bwd_kernel" if use_atomic else "bwd_kernel + dq_sum_kernel"
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "heads_q": w.heads_q, "heads_kv": w.heads_kv,
+                   "seq_len": w.seqlen, "head_dim": w.head_dim, "causal": causal, "dq_path": path,
+                   "parallelism": "none (1 GPU)"},
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 3),
+        "fwd_kernel_ms": round(fwd_ms, 4),
+        "fwd_tflops": round(fwd_f / (fwd_ms * 1e-3) / 1e12, 3),
+        "bwd_kernel_ms": round(bwd_ms, 4),
+        "roofline": {"kernel": kernel, "bound": "mfma", "achieved": round(bwd_tflops, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": recorded_traffic(w.name, path)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, causal, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

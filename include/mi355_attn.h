@@ -1,0 +1,139 @@
+/*
+ * mi355_attn.h - C ABI of the MI355X (gfx950) fused exact-softmax attention
+ * forward and backward library, libmi355_attn.so.
+ *
+ * The operation and its decomposition follow the FlashAttention backward
+ * examples of the TileLang pull request "[Example] Introduce split+sum
+ * template, and optimize atomic_add performance for bwd examples"
+ * (tile-ai/tilelang #940): a forward kernel, a backward preprocess, a
+ * backward kernel whose dQ is accumulated either with fp32 atomic adds or
+ * through a split-then-sum scheme (the `use_atomic` switch of its sequence
+ * diagram), and a backward postprocess.
+ *
+ * Definitions (per batch b and query head h, with kv = h / groups):
+ *   S = scale * Q_h K_kv^T,  S_ij = -inf for j > i when causal,
+ *   P = softmax(S) row-wise,  O_h = P V_kv,  LSE_i = ln sum_j exp(S_ij),
+ *   Delta_i = sum_d dO_id O_id,  dS = P o (dP - Delta), dP = dO V_kv^T,
+ *   dV_kv = sum_h P^T dO_h,  dK_kv = scale * sum_h dS^T Q_h,
+ *   dQ_h = scale * dS K_kv.
+ *
+ * Conventions shared by every call
+ *   - Tensors are dense row-major device buffers.  Q, O, dO, dQ are
+ *     [batch, seqlen, heads_q, head_dim] (BSHD); K, V, dK, dV are
+ *     [batch, seqlen, heads_q/groups, head_dim]; LSE and Delta are
+ *     [batch, heads_q, seqlen] fp32.  bf16 tensors hold raw bf16 bit patterns
+ *     (uint16_t).  dq_accum is fp32 BSHD like dQ.
+ *   - Every pointer is device memory allocated and owned by the caller; it
+ *     must be 16-byte aligned.  The library allocates nothing, frees
+ *     nothing, never synchronises and keeps no pointer after a call returns.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream);
+ *     the caller keeps every buffer alive until the stream has completed it.
+ *   - Return value: ATTN_OK (0) or a negative ATTN_ERR_* code.  All argument
+ *     checks run on the host before anything is enqueued, so a call that
+ *     fails a check has launched nothing.  ATTN_ERR_HIP reports a launch
+ *     failure seen through hipGetLastError after enqueueing.
+ */
+#ifndef MI355_ATTN_H
+#define MI355_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct attn_shape {
+  int32_t batch;    /* B >= 1 */
+  int32_t seqlen;   /* S >= 1; queries and keys have the same length */
+  int32_t heads_q;  /* Hq >= 1 query heads */
+  int32_t groups;   /* g >= 1 query heads per KV head; Hq % g == 0, Hkv = Hq / g */
+  int32_t head_dim; /* D, 64 or 128 */
+} attn_shape;
+
+enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL_PTR = -1,  /* a required pointer is NULL */
+  ATTN_ERR_BAD_SHAPE = -2, /* a size < 1, or heads_q not a multiple of groups */
+  ATTN_ERR_HEAD_DIM = -3,  /* head_dim not 64 or 128 */
+  ATTN_ERR_ALIGN = -4,     /* a tensor base is not 16-byte aligned */
+  ATTN_ERR_RANGE = -5,     /* a tensor has >= 2^31 elements, or scale is not finite and > 0 */
+  ATTN_ERR_WORKSPACE = -6, /* workspace NULL or smaller than attn_bwd_workspace_bytes() */
+  ATTN_ERR_HIP = -7,       /* the HIP runtime reported a launch error */
+  ATTN_ERR_FLAG = -8       /* causal or use_atomic is not 0 or 1 */
+};
+
+/* Static message for a status code (never NULL). */
+const char* attn_strerror(int status);
+
+/*
+ * Forward: O = softmax(scale * Q K^T [causal]) V and the per-row LSE.
+ * (TileLang #940, sequence diagram: attention(Q, K, V, causal, groups, ...)
+ * runs flashattn_fwd, which returns O; its backward needs the row
+ * normaliser, exported here as LSE.)
+ *   q [B,S,Hq,D] bf16, k/v [B,S,Hkv,D] bf16 (inputs)
+ *   o [B,S,Hq,D] bf16, lse [B,Hq,S] fp32 natural-log, scale included (outputs)
+ *   softmax_scale: finite, > 0 (usually 1/sqrt(D)); causal: 0 or 1.
+ * Every element of o and lse is written.
+ */
+int attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
+             attn_shape shape, float softmax_scale, int causal, void* stream);
+
+/*
+ * Backward preprocess: Delta_i = sum_d dO_id * O_id in fp32 (the
+ * flashattn_bwd_preprocess step of the TileLang #940 examples).
+ *   o, dout [B,S,Hq,D] bf16 (inputs); delta [B,Hq,S] fp32 (output).
+ *   dq_accum: NULL, or an fp32 [B,S,Hq,D] buffer that is set to zero here,
+ *   as the fp32 atomic dQ accumulator of attn_bwd(use_atomic=1) requires.
+ */
+int attn_bwd_preprocess(const uint16_t* o, const uint16_t* dout, float* delta, float* dq_accum,
+                        attn_shape shape, void* stream);
+
+/*
+ * Bytes of device workspace attn_bwd and attn_bwd_postprocess need for this
+ * problem (0 when none is needed).  Layout, for reference only:
+ *   groups > 1: fp32 per-query-head dK and dV partials, [B,S,Hq,D] each;
+ *   use_atomic == 0: fp32 per-KV-block dQ partials, [n_kv_blocks,B,S,Hq,D].
+ * Returns 0 for an invalid shape.
+ */
+size_t attn_bwd_workspace_bytes(attn_shape shape, int causal, int use_atomic);
+
+/*
+ * Backward: dQ, dK, dV from Q, K, V, dO and the forward's LSE plus the
+ * preprocess's Delta (the flashattn_bwd_atomic_add / flashattn_bwd_split
+ * pair of the TileLang #940 examples, chosen by use_atomic as its
+ * sequence diagram does).
+ *   use_atomic = 1: dQ (scaled, fp32) is added with fp32 atomics into
+ *     dq_accum, which must hold zeros on entry (attn_bwd_preprocess zeroes
+ *     it).  Bits of dq_accum may differ run to run (summation order).
+ *   use_atomic = 0: each KV block stores its dQ contribution into its own
+ *     workspace slot; a second kernel sums the slots in ascending block order
+ *     into dq_accum (fully overwritten).  Bitwise deterministic.
+ *   groups == 1: dk, dv [B,S,Hkv,D] bf16 are written here.
+ *   groups  > 1: per-query-head fp32 dK/dV partials go to the workspace and
+ *     attn_bwd_postprocess reduces them; dk and dv are not touched (may be NULL).
+ *   workspace/workspace_bytes: at least attn_bwd_workspace_bytes(shape,
+ *     causal, use_atomic) bytes; may be NULL when that is 0.
+ */
+int attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
+             const float* lse, const float* delta, float* dq_accum, uint16_t* dk, uint16_t* dv,
+             void* workspace, size_t workspace_bytes, attn_shape shape, float softmax_scale,
+             int causal, int use_atomic, void* stream);
+
+/*
+ * Backward postprocess (flashattn_bwd_postprocess of the TileLang #940
+ * examples): dq = bf16(dq_accum) with round-to-nearest-even; for groups > 1
+ * also dk/dv[b,s,kv,:] = bf16(sum over r < groups, ascending, of the
+ * workspace partials of query head kv*groups + r).
+ *   dq_accum fp32 [B,S,Hq,D] (input); dq [B,S,Hq,D] bf16 (output);
+ *   dk, dv [B,S,Hkv,D] bf16 (outputs, required only when groups > 1);
+ *   workspace: the buffer attn_bwd used (required only when groups > 1).
+ */
+int attn_bwd_postprocess(const float* dq_accum, const void* workspace, size_t workspace_bytes,
+                         uint16_t* dq, uint16_t* dk, uint16_t* dv, attn_shape shape, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI355_ATTN_H */

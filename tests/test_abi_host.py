@@ -1,0 +1,141 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+Every call here fails an argument check, which the library performs on the
+host before any HIP call, so nothing is launched.  Fake device addresses are
+never dereferenced.
+"""
+
+import ctypes
+import math
+
+import pytest
+
+from attention_backward_fwd_amd import binding as bd
+
+P = ctypes.c_void_p
+A = P(0x10000)      # 16-byte aligned fake device address
+MIS = P(0x10008)    # misaligned
+
+
+def lib():
+    return bd.library()
+
+
+def shp(b=2, s=300, hq=8, g=2, d=128):
+    return bd.attn_shape(b, s, hq, g, d)
+
+
+def test_library_exports_every_header_symbol():
+    names = bd.header_functions()
+    assert names == sorted(["attn_fwd", "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_bwd",
+                            "attn_bwd_postprocess", "attn_strerror"])
+    for n in names:
+        assert hasattr(lib(), n), n
+
+
+def test_strerror_covers_every_code():
+    msgs = {lib().attn_strerror(c).decode() for c in range(0, -9, -1)}
+    assert len(msgs) == 9
+    assert lib().attn_strerror(-99).decode() == "unknown status"
+
+
+@pytest.mark.parametrize("g", [1, 4])
+@pytest.mark.parametrize("s", [1, 128, 129, 4096])
+def test_workspace_bytes(g, s):
+    sh = shp(b=2, s=s, hq=8, g=g, d=64)
+    nq = 2 * s * 8 * 64
+    nblk = math.ceil(s / 128)
+    gqa = 2 * nq * 4 if g > 1 else 0
+    for causal in (0, 1):
+        assert lib().attn_bwd_workspace_bytes(sh, causal, 1) == gqa
+        assert lib().attn_bwd_workspace_bytes(sh, causal, 0) == gqa + nblk * nq * 4
+
+
+def test_workspace_bytes_invalid_is_zero():
+    assert lib().attn_bwd_workspace_bytes(shp(hq=6, g=4), 0, 0) == 0
+    assert lib().attn_bwd_workspace_bytes(shp(d=96), 0, 0) == 0
+    assert lib().attn_bwd_workspace_bytes(shp(), 2, 0) == 0
+
+
+def fwd(**kw):
+    args = dict(q=A, k=A, v=A, o=A, lse=A, shape=shp(), scale=0.1, causal=1, stream=None)
+    args.update(kw)
+    return lib().attn_fwd(args["q"], args["k"], args["v"], args["o"], args["lse"], args["shape"],
+                          args["scale"], args["causal"], args["stream"])
+
+
+def pre(**kw):
+    args = dict(o=A, do=A, delta=A, dq=A, shape=shp(), stream=None)
+    args.update(kw)
+    return lib().attn_bwd_preprocess(args["o"], args["do"], args["delta"], args["dq"], args["shape"], args["stream"])
+
+
+def bwd(**kw):
+    args = dict(q=A, k=A, v=A, do=A, lse=A, delta=A, dq=A, dk=A, dv=A, ws=A, wsb=1 << 40, shape=shp(), scale=0.1,
+                causal=1, atomic=1, stream=None)
+    args.update(kw)
+    return lib().attn_bwd(args["q"], args["k"], args["v"], args["do"], args["lse"], args["delta"], args["dq"],
+                          args["dk"], args["dv"], args["ws"], args["wsb"], args["shape"], args["scale"],
+                          args["causal"], args["atomic"], args["stream"])
+
+
+def post(**kw):
+    args = dict(dq_accum=A, ws=A, wsb=1 << 40, dq=A, dk=A, dv=A, shape=shp(), stream=None)
+    args.update(kw)
+    return lib().attn_bwd_postprocess(args["dq_accum"], args["ws"], args["wsb"], args["dq"], args["dk"], args["dv"],
+                                      args["shape"], args["stream"])
+
+
+E = {"null": -1, "shape": -2, "hd": -3, "align": -4, "range": -5, "ws": -6, "flag": -8}
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"q": None}, "null"), ({"lse": None}, "null"),
+    ({"shape": shp(b=0)}, "shape"), ({"shape": shp(s=0)}, "shape"), ({"shape": shp(hq=6, g=4)}, "shape"),
+    ({"shape": shp(g=0)}, "shape"), ({"shape": shp(d=96)}, "hd"), ({"shape": shp(d=256)}, "hd"),
+    ({"shape": shp(b=64, s=8192, hq=64, g=1, d=128)}, "range"),
+    ({"scale": 0.0}, "range"), ({"scale": -1.0}, "range"), ({"scale": float("nan")}, "range"),
+    ({"scale": float("inf")}, "range"), ({"causal": 2}, "flag"), ({"o": MIS}, "align"), ({"lse": MIS}, "align"),
+])
+def test_fwd_errors(kw, code):
+    assert fwd(**kw) == E[code]
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"o": None}, "null"), ({"delta": None}, "null"), ({"shape": shp(hq=7, g=2)}, "shape"),
+    ({"shape": shp(d=32)}, "hd"), ({"dq": MIS}, "align"), ({"do": MIS}, "align"),
+])
+def test_preprocess_errors(kw, code):
+    assert pre(**kw) == E[code]
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"dq": None}, "null"), ({"lse": None}, "null"),
+    ({"shape": shp(g=1), "dk": None}, "null"),
+    ({"shape": shp(hq=0)}, "shape"), ({"shape": shp(d=80)}, "hd"),
+    ({"atomic": 3}, "flag"), ({"causal": -1}, "flag"),
+    ({"scale": float("-inf")}, "range"),
+    ({"ws": None}, "ws"), ({"wsb": 1024}, "ws"),
+    ({"atomic": 0, "shape": shp(g=1), "ws": None}, "ws"),
+    ({"delta": MIS}, "align"), ({"ws": MIS}, "align"),
+])
+def test_bwd_errors(kw, code):
+    assert bwd(**kw) == E[code]
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"dq": None}, "null"), ({"dk": None}, "null"), ({"ws": None}, "ws"), ({"wsb": 16}, "ws"),
+    ({"shape": shp(s=-3)}, "shape"), ({"dq_accum": MIS}, "align"),
+])
+def test_postprocess_errors(kw, code):
+    assert post(**kw) == E[code]
+
+
+def test_python_shape_helpers():
+    import torch
+    q = torch.empty((2, 17, 8, 64))
+    k = torch.empty((2, 17, 2, 64))
+    sh = bd.shape_of(q, k)
+    assert (sh.batch, sh.seqlen, sh.heads_q, sh.groups, sh.head_dim) == (2, 17, 8, 4, 64)
+    with pytest.raises(ValueError):
+        bd.shape_of(q, torch.empty((2, 17, 3, 64)))
