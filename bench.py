@@ -103,6 +103,9 @@ def main():
     ap.add_argument("--use-atomic", type=int, default=1, choices=(0, 1))
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, run a plain fp32 copy kernel over MIB MiB "
+                         "(reference for scaling the HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -115,6 +118,16 @@ def main():
 
     from attention_backward_fwd_amd import binding as bd
     from attention_backward_fwd_amd.synthetic import WORKLOADS, workload_inputs
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        a = torch.randn(n, device="cuda:0")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.mul(a, 1.0, out=b)  # one elementwise kernel: reads n*4 bytes, writes n*4 bytes
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "launches": 3}))
+        return
 
     w = WORKLOADS[args.workload]
     causal = w.causal[-1] if args.causal is None else bool(args.causal)
