@@ -75,6 +75,81 @@ __device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, 
   return __builtin_bit_cast(bf16x8, u);
 }
 
+// ---------------------------------------------------------------- LDS tiles
+// A tile holds R rows of D bf16 values, unpadded (so that the LDS-DMA loads,
+// which place lane i's 16 bytes at base + 16*i, can fill it), with the
+// 16-byte slot index of row r XORed by swz<D>(r).  The swizzle is chosen so
+// that both access patterns of the kernels are free of bank conflicts:
+//   * 16-byte row reads (MFMA A operands): 16 consecutive rows, same slot;
+//   * transposing 8-byte reads: 4 consecutive rows (first one a multiple of
+//     4) x 4 consecutive slots.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);  // 16 slots per 256-byte row
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);              // 8 slots per 128-byte row
+}
+
+// Element offset of (row, col) in a swizzled tile; col is a multiple of 4.
+template <int D>
+__device__ __forceinline__ int swz_off(int row, int col) {
+  return row * D + ((((col >> 3) ^ swz<D>(row))) << 3) + (col & 7);
+}
+
+// Because the swizzle is an XOR on the slot index, moving the column by a
+// multiple of 8 elements whose bits do not overlap the starting slot turns
+// into an XOR of the element offset: swz_off(r, c + 8k) == swz_off(r, c) ^ 8k
+// when (c >> 3) & k == 0.  Row moves by multiples of 16 keep swz() unchanged
+// and are plain additions.  The kernels build one offset per lane and derive
+// the rest this way.
+__device__ __forceinline__ int xslot(int off, int k8) { return off ^ k8; }
+
+// Keep the compiler from hoisting values derived from v out of a loop: v
+// becomes opaque at this point (scalar / per-lane variants).
+template <typename T>
+__device__ __forceinline__ T opaque(T v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
+template <typename T>
+__device__ __forceinline__ T opaque_v(T v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+__device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(void* p) {
+  return (__attribute__((address_space(3))) void*)(p);
+}
+
+// Asynchronous global -> LDS copy of rows [row0, row0 + R) of a row-major
+// bf16 matrix with row stride rs elements into a swizzled tile.  Rows at or
+// past `nrows` read row nrows - 1 instead (callers mask them); every source
+// address is therefore inside the matrix.  Each wave instruction moves 1 KB;
+// the 4 waves of the workgroup split the tile.  Completion: vmcnt.
+template <int D, int R>
+__device__ __forceinline__ void tile_load_async(const uint16_t* g, size_t rs, int row0, int nrows,
+                                                uint16_t* tile, int w, int lane) {
+  constexpr int CPR = D / 8;       // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;    // rows per wave instruction
+  constexpr int NI = R / RPI;      // wave instructions per tile
+  static_assert(NI % 4 == 0, "tile must split evenly over 4 waves");
+  const int rl = lane / CPR, slot = lane % CPR;
+#pragma unroll
+  for (int j = w; j < NI; j += 4) {
+    const int r = j * RPI + rl;
+    const int gr = min(row0 + r, nrows - 1);
+    const uint16_t* src = g + (size_t)gr * rs + ((slot ^ swz<D>(r)) << 3);
+    __builtin_amdgcn_global_load_lds(src, lds_ptr(tile + j * 512), 16, 0, 0);
+  }
+}
+
+// Wait until every vector-memory operation of this wave (including LDS-DMA
+// writes) has completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 // Workgroups are handed to the 8 XCDs round-robin (id % 8).  This maps the
 // hardware id to a logical id so that consecutive logical ids run on the same
 // XCD and share its L2.  Identity when the grid is not a multiple of 8.

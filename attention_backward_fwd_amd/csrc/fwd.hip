@@ -16,7 +16,8 @@
 // rescale factor of the online softmax is a per-lane scalar.
 //
 // Workgroup: 4 waves x 32 queries = 128 queries; key/value tiles of 64 rows,
-// double-staged through registers into LDS.  Scores stay fp32; P is rounded
+// double-buffered in LDS and filled by LDS-DMA loads one tile ahead (one
+// workgroup barrier per tile).  Scores stay fp32; P is rounded
 // to bf16 only as an MFMA operand; O is written as bf16 (RNE) and LSE as fp32
 // natural log including the scale.
 #include "common.h"
@@ -29,26 +30,35 @@ namespace {
 constexpr int kFwdBM = 128;
 constexpr int kFwdBN = 64;
 
+// The online softmax keeps a per-row reference maximum m and accumulates
+// l = sum exp(s - m) and O = sum exp(s - m) v.  Any reference gives the same
+// O / l, so m is only raised when a new score exceeds it by more than
+// 2^kRescaleLog2 in exp2 units; until then every exponent stays below that
+// bound (fp32 accumulators and bf16 P are unaffected) and the O rescale is
+// skipped for the whole wavefront.
+constexpr float kRescaleLog2 = 8.f;
+
+// Two waves per SIMD: this also keeps the kernel within 256 VGPRs, so the
+// MFMA accumulators live in VGPRs next to the softmax arithmetic.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void fwd_kernel(FwdParams p) {
   constexpr int BM = kFwdBM, BN = kFwdBN;
-  constexpr int KP = D + 8;    // sK pitch in elements (16-byte row reads)
-  constexpr int VP = D + 16;   // sV pitch in elements (transposing reads)
   constexpr int NKS = D / 16;  // MFMA k-steps over the head dimension
   constexpr int NDT = D / 32;  // 32-row tiles of O^T
-  constexpr int CH = D / 8;    // 16-byte chunks per row
-  constexpr int LDI = BN * CH / 256;
+  constexpr int TK = BN * D;   // elements of one K or V tile
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[BN * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[BN * VP];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2 * TK];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2 * TK];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hi = lane >> 5, l32 = lane & 31, L = lane & 15, Gp = (lane >> 4) & 1;
   const int S = p.S, Hq = p.Hq, G = p.G, Hkv = p.Hkv;
   const int n_mblk = (S + BM - 1) / BM;
 
-  // Tile order: each XCD gets a contiguous range of (batch, KV head) groups;
-  // inside it, query blocks run heaviest-first under causal masking.
+  // Tile order: each XCD gets a contiguous range of (batch, KV head) groups
+  // and works through them one at a time, so a group's K/V stay in its L2;
+  // inside a group, query blocks run heaviest-first under causal masking,
+  // with the group's query heads side by side.
   const int nwg = gridDim.x, NG = p.B * Hkv;
   int t = blockIdx.x, x = 0, NGx = NG;
   if (NG % 8 == 0) {
@@ -58,10 +68,10 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
     t -= x * per;
     NGx = NG / 8;
   }
+  const int per_group = n_mblk * G;
+  const int grp = x * NGx + t / per_group;
+  const int mbo = (t % per_group) / G;
   const int r = t % G;
-  t /= G;
-  const int grp = x * NGx + t % NGx;
-  const int mbo = t / NGx;
   const int b = grp / Hkv, kvh = grp % Hkv, h = kvh * G + r;
   const int mb = CAUSAL ? (n_mblk - 1 - mbo) : mbo;
 
@@ -72,6 +82,11 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
 
   const int q0 = mb * BM + 32 * w;  // first query of this wave
   const int qi = q0 + l32;          // this lane's query
+  const int n_end = CAUSAL ? min(S, mb * BM + BM) : S;
+  const int n_tiles = (n_end + BN - 1) / BN;
+
+  tile_load_async<D, BN>(Kb, kvrs, 0, S, sK, w, lane);
+  tile_load_async<D, BN>(Vb, kvrs, 0, S, sV, w, lane);
 
   bf16x8 qf[NKS];
   if (qi < S) {
@@ -83,76 +98,63 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
     for (int ks = 0; ks < NKS; ks++) qf[ks] = bf16x8{};
   }
 
-  const int n_end = CAUSAL ? min(S, mb * BM + BM) : S;
-  const int n_tiles = (n_end + BN - 1) / BN;
+  // Per-lane LDS element offsets (16-byte row reads of K; transposing reads
+  // of V); the loop derives the rest with XORs and 16-row additions.
+  const int offA0 = swz_off<D>(l32, 8 * hi);
+  const int tcol = 16 * Gp + 4 * (L & 3);
+  const int offV00 = swz_off<D>(4 * hi + (L >> 2), tcol);
+  const int offV10 = swz_off<D>(4 * hi + (L >> 2) + 8, tcol);
+
   const float c = p.scale * kLog2e;
-
-  u32x4 kr[LDI], vr[LDI];
-  auto gload = [&](int n0) {
-#pragma unroll
-    for (int i = 0; i < LDI; i++) {
-      const int idx = tid + 256 * i, row = idx / CH, col = (idx % CH) * 8, key = n0 + row;
-      if (key < S) {
-        kr[i] = *reinterpret_cast<const u32x4*>(Kb + (size_t)key * kvrs + col);
-        vr[i] = *reinterpret_cast<const u32x4*>(Vb + (size_t)key * kvrs + col);
-      } else {
-        kr[i] = u32x4{0, 0, 0, 0};
-        vr[i] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-
   f32x16 oacc[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; dt++) oacc[dt] = f32x16{};
   float m_i = -INFINITY, l_i = 0.f;
 
-  gload(0);
   for (int it = 0; it < n_tiles; it++) {
+    const int buf = it & 1;
     const int n0 = it * BN;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < LDI; i++) {
-      const int idx = tid + 256 * i, row = idx / CH, col = (idx % CH) * 8;
-      *reinterpret_cast<u32x4*>(&sK[row * KP + col]) = kr[i];
-      *reinterpret_cast<u32x4*>(&sV[row * VP + col]) = vr[i];
+    wait_vmem();
+    __syncthreads();  // tile it resident; every wave is done with tile it-1
+    if (it + 1 < n_tiles) {
+      tile_load_async<D, BN>(Kb, kvrs, n0 + BN, S, sK + (buf ^ 1) * TK, w, lane);
+      tile_load_async<D, BN>(Vb, kvrs, n0 + BN, S, sV + (buf ^ 1) * TK, w, lane);
     }
-    __syncthreads();
-    if (it + 1 < n_tiles) gload(n0 + BN);
-
     // A wave whose queries all precede the tile has nothing to do in it.
     if (CAUSAL && n0 > q0 + 31) continue;
+    const uint16_t* cK = sK + buf * TK;
+    const uint16_t* cV = sV + buf * TK;
+    const int offA = opaque_v(offA0), offV0 = opaque_v(offV00), offV1 = opaque_v(offV10);
 
+    // S^T (64 keys x 32 queries): element j of s[mt] is key
+    // n0 + 32mt + 8(j/4) + 4hi + j%4, query qi.
     f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int ks = 0; ks < NKS; ks++) {
+    for (int ks = 0; ks < NKS; ks++)
 #pragma unroll
-      for (int mt = 0; mt < 2; mt++) {
-        const bf16x8 a = lds_read_b128(&sK[(32 * mt + l32) * KP + 16 * ks + 8 * hi]);
-        s[mt] = mfma32(a, qf[ks], s[mt]);
-      }
-    }
+      for (int mt = 0; mt < 2; mt++)
+        s[mt] = mfma32(lds_read_b128(cK + xslot(offA, 16 * ks) + 32 * mt * D), qf[ks], s[mt]);
 
-    const bool need_mask = (n0 + BN > S) || (CAUSAL && n0 + BN - 1 > q0);
-    if (need_mask) {
+    // Edge tiles (past the end, or crossing the causal diagonal): a key at
+    // tile offset k is visible iff k <= lim.
+    if ((n0 + BN > S) || (CAUSAL && n0 + BN - 1 > q0)) {
+      const int lim = (CAUSAL ? min(S - 1, qi) : S - 1) - n0 - 4 * hi;
 #pragma unroll
       for (int mt = 0; mt < 2; mt++)
 #pragma unroll
-        for (int j = 0; j < 16; j++) {
-          const int key = n0 + 32 * mt + 8 * (j >> 2) + 4 * hi + (j & 3);
-          if (key >= S || (CAUSAL && key > qi)) s[mt][j] = -INFINITY;
-        }
+        for (int j = 0; j < 16; j++)
+          if (32 * mt + 8 * (j >> 2) + (j & 3) > lim) s[mt][j] = -INFINITY;
     }
-
-    float mx = s[0][0];
+    float mx = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < 2; mt++)
 #pragma unroll
       for (int j = 0; j < 16; j++) mx = fmaxf(mx, s[mt][j]);
     mx = xhalf_max(mx);
-    const float m_new = fmaxf(m_i, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float mc = m_use * c;
+    const float m_cand = fmaxf(m_i, mx);
+    const bool upd = (m_cand - m_i) * c > kRescaleLog2;  // true on the first visible tile
+    const float m_new = upd ? m_cand : m_i;
+    const float mc = (m_new == -INFINITY ? 0.f : m_new) * c;
     const float alpha = __builtin_amdgcn_exp2f(m_i * c - mc);
     float rs = 0.f;
 #pragma unroll
@@ -165,8 +167,10 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
       }
     l_i = fmaf(l_i, alpha, rs);
     m_i = m_new;
+    if (__builtin_amdgcn_ballot_w64(upd) != 0) {
 #pragma unroll
-    for (int dt = 0; dt < NDT; dt++) oacc[dt] *= alpha;
+      for (int dt = 0; dt < NDT; dt++) oacc[dt] *= alpha;
+    }
 
     // P^T as the B operand: k-step kk covers keys 16kk.. of the tile, in the
     // order the S^T result layout holds them.
@@ -177,16 +181,14 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
       pb[kk] = pack8(s[mt][o8 + 0], s[mt][o8 + 1], s[mt][o8 + 2], s[mt][o8 + 3], s[mt][o8 + 4],
                      s[mt][o8 + 5], s[mt][o8 + 6], s[mt][o8 + 7]);
     }
+    // O^T += V^T P^T with V^T read by transposing LDS reads.
 #pragma unroll
-    for (int dt = 0; dt < NDT; dt++) {
-      const int col = 32 * dt + 16 * Gp + 4 * (L & 3);
+    for (int kk = 0; kk < 4; kk++)
 #pragma unroll
-      for (int kk = 0; kk < 4; kk++) {
-        const int row = 16 * kk + 4 * hi + (L >> 2);
-        const bf16x8 a = lds_read_tr8(&sV[row * VP + col], &sV[(row + 8) * VP + col]);
+      for (int dt = 0; dt < NDT; dt++) {
+        const bf16x8 a = lds_read_tr8(cV + xslot(offV0, 32 * dt) + 16 * kk * D, cV + xslot(offV1, 32 * dt) + 16 * kk * D);
         oacc[dt] = mfma32(a, pb[kk], oacc[dt]);
       }
-    }
   }
 
   const float l_tot = xhalf_sum(l_i);
