@@ -18,6 +18,8 @@ int check_shape(const attn_shape& s) {
   if (s.head_dim != 64 && s.head_dim != 128) return ATTN_ERR_HEAD_DIM;
   const long long nq = (long long)s.batch * s.seqlen * s.heads_q * s.head_dim;
   if (nq >= (1LL << 31)) return ATTN_ERR_RANGE;
+  // Kernels address up to 128 rows of one head with 32-bit byte offsets.
+  if ((long long)s.heads_q * s.head_dim > (1LL << 22)) return ATTN_ERR_RANGE;
   return ATTN_OK;
 }
 
@@ -46,7 +48,9 @@ const char* attn_strerror(int status) {
     case ATTN_ERR_BAD_SHAPE: return "invalid shape: sizes must be >= 1 and heads_q a multiple of groups";
     case ATTN_ERR_HEAD_DIM: return "head_dim must be 64 or 128";
     case ATTN_ERR_ALIGN: return "tensor base pointers must be 16-byte aligned";
-    case ATTN_ERR_RANGE: return "out of range: a tensor has >= 2^31 elements or softmax_scale is not finite and > 0";
+    case ATTN_ERR_RANGE:
+      return "out of range: a tensor has >= 2^31 elements, heads_q * head_dim > 2^22, or softmax_scale is not "
+             "finite and > 0";
     case ATTN_ERR_WORKSPACE: return "workspace is NULL or smaller than attn_bwd_workspace_bytes()";
     case ATTN_ERR_HIP: return "HIP runtime reported a launch error";
     case ATTN_ERR_FLAG: return "causal and use_atomic must be 0 or 1";
@@ -135,6 +139,7 @@ int attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint
   p.Hkv = shape.heads_q / shape.groups;
   p.D = shape.head_dim;
   p.scale = softmax_scale;
+  p.log2_scale = log2f(softmax_scale);
   p.causal = causal;
   p.use_atomic = use_atomic;
   hipStream_t s = (hipStream_t)stream;

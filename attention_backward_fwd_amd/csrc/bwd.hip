@@ -44,27 +44,39 @@ namespace mi355 {
 
 namespace {
 
-constexpr int kBN = kBwdBlockN;  // keys per workgroup (4 waves x 32)
+constexpr int kBN = kBwdBlockN;  // keys per workgroup
 constexpr int kBM = 64;          // queries per step
+constexpr int kNW = 8;           // waves per workgroup: 4 key quarters x 2 query halves
 
+// Two waves per SIMD: the kernel must fit 256 VGPRs, which also keeps every
+// MFMA accumulator in VGPRs.
 template <int D, bool CAUSAL, bool ATOMIC, bool PARTIAL>
-__global__ __launch_bounds__(256) void bwd_kernel(BwdParams p) {
-  constexpr int BN = kBN, BM = kBM;
+__global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) void bwd_kernel(BwdParams p) {
+  constexpr int BN = kBN, BM = kBM, NW = kNW;
   constexpr int TQ = BM * D;  // elements of one Q or dO block
   constexpr int NKS = D / 16, NDT = D / 32;
-  // dQ tile split over the 4 waves: D=128 -> one 32-wide d tile and both
-  // 32-row query tiles per wave; D=64 -> one 32x32 tile per wave.
-  constexpr int DQ_MT = (D == 128) ? 2 : 1;
 
+  // Separate LDS objects, so that the compiler can tell the block being
+  // loaded (LDS-DMA in flight) from the block being read and does not wait
+  // for the former before reading the latter.  After the loop the K and V
+  // blocks hold the dK/dV hand-over between the query halves.
   __shared__ __attribute__((aligned(16))) uint16_t sK[BN * D];
   __shared__ __attribute__((aligned(16))) uint16_t sV[BN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[2 * TQ];
-  __shared__ __attribute__((aligned(16))) uint16_t sdO[2 * TQ];
+  __shared__ __attribute__((aligned(16))) uint16_t sQ0[TQ];
+  __shared__ __attribute__((aligned(16))) uint16_t sQ1[TQ];
+  __shared__ __attribute__((aligned(16))) uint16_t sdO0[TQ];
+  __shared__ __attribute__((aligned(16))) uint16_t sdO1[TQ];
   __shared__ __attribute__((aligned(16))) uint16_t sdSt[BN * BM];  // dS'^T [key][query], swizzled
-  __shared__ __attribute__((aligned(16))) float sL[2 * BM];
-  __shared__ __attribute__((aligned(16))) float sDl[2 * BM];
+  // Raw LSE and Delta rows of the query block (LDS-DMA, one per buffer).
+  __shared__ __attribute__((aligned(16))) float sL0[BM];
+  __shared__ __attribute__((aligned(16))) float sL1[BM];
+  __shared__ __attribute__((aligned(16))) float sD0[BM];
+  __shared__ __attribute__((aligned(16))) float sD1[BM];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (scalar)
+  const int kw = w & 3;   // this wave's keys: 32kw .. 32kw+31 of the block
+  const int qh = w >> 2;  // this wave's queries: 32qh .. 32qh+31 of each query block
   const int hi = lane >> 5, l32 = lane & 31, L = lane & 15, Gp = (lane >> 4) & 1;
   const int S = p.S, Hq = p.Hq, G = p.G, Hkv = p.Hkv;
   const int n_nblk = (S + BN - 1) / BN;
@@ -98,40 +110,28 @@ __global__ __launch_bounds__(256) void bwd_kernel(BwdParams p) {
   const float* dl_b = p.delta + (size_t)(b * Hq + h) * S;
 
   const float c = p.scale * kLog2e;
-  const float lsc = __builtin_amdgcn_logf(p.scale);  // log2(scale)
+  const float lsc = p.log2_scale;
   const int m_begin = CAUSAL ? n0 : 0;               // n0 is a multiple of BM
   const int n_steps = (S - m_begin + BM - 1) / BM;
 
-  float lr = 0.f, dlr = 0.f;
-  auto load_rows = [&](int m0) {
-    if (tid < BM) {
-      const int q = m0 + tid;
-      // Rows past the end get +inf, so P = 0 there without a mask.
-      lr = q < S ? fmaf(lse_b[q], kLog2e, -lsc) : INFINITY;
-      dlr = q < S ? dl_b[q] : 0.f;
-    }
+  // LSE and Delta of a query block land in LDS as raw fp32 rows (waves 0
+  // and 1 each issue one 4-byte LDS-DMA load); rows past the end repeat the
+  // last row and are masked below.
+  auto load_rows = [&](int m0, float* l_dst, float* d_dst) {
+    if (w == 0) row_load_async(lse_b + m0, S - m0, l_dst, lane);
+    if (w == 1) row_load_async(dl_b + m0, S - m0, d_dst, lane);
   };
   // Key/value block (resident for the whole sweep) and the first Q/dO block.
-  tile_load_async<D, BN>(Kb, kvrs, n0, S, sK, w, lane);
-  tile_load_async<D, BN>(Vb, kvrs, n0, S, sV, w, lane);
-  tile_load_async<D, BM>(Qb, qrs, m_begin, S, sQ, w, lane);
-  tile_load_async<D, BM>(dOb, qrs, m_begin, S, sdO, w, lane);
-  load_rows(m_begin);
+  tile_load_async<D, BN, NW>(Kb, kvrs, n0, S, sK, w, lane);
+  tile_load_async<D, BN, NW>(Vb, kvrs, n0, S, sV, w, lane);
+  tile_load_async<D, BM, NW>(Qb, qrs, m_begin, S, sQ0, w, lane);
+  tile_load_async<D, BM, NW>(dOb, qrs, m_begin, S, sdO0, w, lane);
+  load_rows(m_begin, sL0, sD0);
 
-  // Per-lane LDS element offsets; the loops derive the rest with XORs of
-  // column moves and additions of 16-row moves (see xslot()).
-  const int offR0 = swz_off<D>(l32, 8 * hi);         // 16-byte row reads, row l32
-  const int offKV0 = offR0 + 32 * w * D;              //   ... row 32w + l32 (this wave's keys)
-  const int tcol = 16 * Gp + 4 * (L & 3);
-  const int offT00 = swz_off<D>(4 * hi + (L >> 2), tcol);      // transposing reads of Q / dO
-  const int offT10 = swz_off<D>(4 * hi + (L >> 2) + 8, tcol);
-  const int dq_nt = (D == 128) ? w : (w & 1);
-  const int dq_mt0 = (D == 128) ? 0 : (w >> 1);
-  const int offK00 = swz_off<D>(8 * hi + (L >> 2), 32 * dq_nt + tcol);  // transposing reads of K
-  const int offK10 = swz_off<D>(8 * hi + (L >> 2) + 4, 32 * dq_nt + tcol);
-  const int offS00 = swz_off<BM>(8 * hi + (L >> 2), tcol);     // transposing reads of dS'^T
-  const int offS10 = swz_off<BM>(8 * hi + (L >> 2) + 4, tcol);
-  const int offW0 = swz_off<BM>(32 * w + l32, 4 * hi);         // 8-byte writes of dS'^T
+  // dQ tile of this wave: queries 32*dq_mt.., d 32*dq_nt.. (D=64 uses waves 0-3).
+  const int dq_mt = (D == 128) ? qh : (w >> 1);
+  const int dq_nt = (D == 128) ? kw : (w & 1);
+  const bool dq_wave = (D == 128) || (w < 4);
 
   f32x16 dk[NDT], dv[NDT];
 #pragma unroll
@@ -139,160 +139,206 @@ __global__ __launch_bounds__(256) void bwd_kernel(BwdParams p) {
     dk[dt] = f32x16{};
     dv[dt] = f32x16{};
   }
-  const int key_l = n0 + 32 * w + l32;
+  const int key_l = n0 + 32 * kw + l32;
   const int dq_d = 32 * dq_nt + l32;
   const uint32_t row_bytes = (uint32_t)(Hq * D) * 4u;
   const uint32_t dq_voff = (uint32_t)(4 * hi) * row_bytes + (uint32_t)dq_d * 4u;
   const size_t nq = (size_t)p.B * S * Hq * D;
 
-  for (int st = 0; st < n_steps; st++) {
-    const int buf = st & 1;
+  // One query block; BUF selects the LDS buffers it reads (the other pair
+  // receives the next block meanwhile).
+  auto step = [&](auto buf_tag, int st) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    uint16_t* cQ = BUF ? sQ1 : sQ0;
+    uint16_t* cdO = BUF ? sdO1 : sdO0;
+    uint16_t* nQ = BUF ? sQ0 : sQ1;
+    uint16_t* ndO = BUF ? sdO0 : sdO1;
+    const float* cL = BUF ? sL1 : sL0;
+    const float* cDl = BUF ? sD1 : sD0;
+    float* nL = BUF ? sL0 : sL1;
+    float* nD = BUF ? sD0 : sD1;
     const int m0 = m_begin + st * BM;
-    if (tid < BM) {
-      sL[buf * BM + tid] = lr;
-      sDl[buf * BM + tid] = dlr;
-    }
-    wait_vmem();
-    __syncthreads();  // block st resident; every wave is done with step st-1
+    // Block st resident.  After the first step, the 16 dQ atomics/stores a
+    // dQ wave issued at the end of step st-1 came after those loads and may
+    // stay in flight.
+    if (dq_wave && st > 0)
+      wait_vmem_but<16>();
+    else
+      wait_vmem();
+    lds_barrier();  // block st resident; every wave is done with step st-1
     if (st + 1 < n_steps) {
-      tile_load_async<D, BM>(Qb, qrs, m0 + BM, S, sQ + (buf ^ 1) * TQ, w, lane);
-      tile_load_async<D, BM>(dOb, qrs, m0 + BM, S, sdO + (buf ^ 1) * TQ, w, lane);
-      load_rows(m0 + BM);
+      tile_load_async<D, BM, NW>(Qb, qrs, m0 + BM, S, nQ, w, lane);
+      tile_load_async<D, BM, NW>(dOb, qrs, m0 + BM, S, ndO, w, lane);
+      load_rows(m0 + BM, nL, nD);
     }
-    const uint16_t* cQ = sQ + buf * TQ;
-    const uint16_t* cdO = sdO + buf * TQ;
-    const float* cL = sL + buf * BM;
-    const float* cDl = sDl + buf * BM;
-    // Recompute the LDS addresses every step (one XOR each) rather than
-    // keeping dozens of them live across the loop.
-    const int offR = opaque_v(offR0), offKV = opaque_v(offKV0), offT0 = opaque_v(offT00),
-              offT1 = opaque_v(offT10), offK0 = opaque_v(offK00), offK1 = opaque_v(offK10),
-              offS0 = opaque_v(offS00), offS1 = opaque_v(offS10), offW = opaque_v(offW0);
+    // Per-lane LDS element offsets, recomputed from the lane id every step
+    // rather than kept live across the loop; the loops below derive the rest
+    // with XORs of column moves and additions of 16-row moves (see xslot()).
+    const int ln = opaque_v(lane);
+    const int lhi = ln >> 5, ll32 = ln & 31, lL = ln & 15, tcol = 16 * ((ln >> 4) & 1) + 4 * (lL & 3);
+    const int offR = swz_off<D>(ll32, 8 * lhi);                    // 16-byte row reads, row l32
+    const int offT0 = swz_off<D>(4 * lhi + (lL >> 2), tcol);        // transposing reads of Q / dO
+    const int offT1 = swz_off<D>(4 * lhi + (lL >> 2) + 8, tcol);
 
-    // Two 32-query halves in turn: S, dP, softmax, dS'^T to LDS and the
-    // dV/dK updates of the first half are independent of the second half's
-    // products, so the scheduler can overlap them.
-    const bool need_mask = (n0 + BN > S) || (CAUSAL && m0 < n0 + BN);
+    // S = Q K^T and dP = dO V^T for this wave's 32 queries x 32 keys.
+    f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-    for (int mt = 0; mt < 2; mt++) {
-      // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys.
-      f32x16 s = f32x16{}, dp = f32x16{};
+    for (int ks = 0; ks < NKS; ks++) {
+      const int oq = xslot(offR, 16 * ks) + 32 * qh * D;
+      const int ok = xslot(offR, 16 * ks) + 32 * kw * D;
+      s = mfma32(lds_read_b128(cQ + oq), lds_read_b128(sK + ok), s);
+      dp = mfma32(lds_read_b128(cdO + oq), lds_read_b128(sV + ok), dp);
+      // Bound how far ahead the scheduler hoists operand reads (each one
+      // holds 4 VGPRs until its MFMA issues).
+      if (ks & 1) __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // P' = scale P and dS' = scale dS.  Element j of lane l is query
+    // 32qh + 8(j/4) + 4hi + j%4 of the block, key 32kw + l32.
+    const bool need_mask = (n0 + BN > S) || (m0 + BM > S) || (CAUSAL && m0 < n0 + BN);
+    // This lane's key is hidden from block queries below qlim (all of them
+    // for keys past the end, the earlier ones under causal masking) and from
+    // queries at or past qend (rows past the end of the sequence).
+    const int qlim = key_l >= S ? BM : (CAUSAL ? key_l - m0 : -1);
+    const int qend = S - m0;
+    uint32_t pp[8], dd[8];
 #pragma unroll
-      for (int ks = 0; ks < NKS; ks++) {
-        const int o = xslot(offR, 16 * ks) + 32 * mt * D;
-        s = mfma32(lds_read_b128(cQ + o), lds_read_b128(sK + xslot(offKV, 16 * ks)), s);
-        dp = mfma32(lds_read_b128(cdO + o), lds_read_b128(sV + xslot(offKV, 16 * ks)), dp);
+    for (int jg = 0; jg < 4; jg++) {
+      const int qo = 32 * qh + 8 * jg + 4 * hi;
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(cL + qo) * kLog2e - lsc;
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(cDl + qo);
+      float pv[4], dv4[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; jj++) {
+        const int j = 4 * jg + jj;
+        float e = __builtin_amdgcn_exp2f(fmaf(s[j], c, -l4[jj]));
+        if (need_mask && (qo + jj < qlim || qo + jj >= qend)) e = 0.f;
+        pv[jj] = e;
+        dv4[jj] = e * (dp[j] - d4[jj]);
       }
-      // P' = scale P and dS' = scale dS.  Element j of lane l is query
-      // 32mt + 8(j/4) + 4hi + j%4 of the block, key 32w + l32.
-      uint32_t pp[8], dd[8];
-#pragma unroll
-      for (int jg = 0; jg < 4; jg++) {
-        const int qo = 32 * mt + 8 * jg + 4 * hi;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(cL + qo);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(cDl + qo);
-        float pv[4], dv4[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; jj++) {
-          const int j = 4 * jg + jj;
-          float e = __builtin_amdgcn_exp2f(fmaf(s[j], c, -l4[jj]));
-          const int q = m0 + qo + jj;
-          e = (need_mask && (key_l >= S || (CAUSAL && key_l > q))) ? 0.f : e;
-          pv[jj] = e;
-          dv4[jj] = e * (dp[j] - d4[jj]);
-        }
-        pp[2 * jg] = pack_bf16x2(pv[0], pv[1]);
-        pp[2 * jg + 1] = pack_bf16x2(pv[2], pv[3]);
-        dd[2 * jg] = pack_bf16x2(dv4[0], dv4[1]);
-        dd[2 * jg + 1] = pack_bf16x2(dv4[2], dv4[3]);
-      }
-      // dS'^T to LDS as [key][query] (a 64-wide swizzled tile): four
-      // consecutive queries per 8-byte write.
+      pp[2 * jg] = pack_bf16x2(pv[0], pv[1]);
+      pp[2 * jg + 1] = pack_bf16x2(pv[2], pv[3]);
+      dd[2 * jg] = pack_bf16x2(dv4[0], dv4[1]);
+      dd[2 * jg + 1] = pack_bf16x2(dv4[2], dv4[3]);
+    }
+    // dS'^T to LDS as [key][query] (a 64-wide swizzled tile): four
+    // consecutive queries per 8-byte write.
+    {
+      const int offW = swz_off<BM>(32 * kw + ll32, 32 * qh + 4 * lhi);
 #pragma unroll
       for (int jg = 0; jg < 4; jg++)
-        *reinterpret_cast<u32x2*>(sdSt + xslot(offW, 8 * jg + 32 * mt)) = u32x2{dd[2 * jg], dd[2 * jg + 1]};
-      // dV += P'^T dO and dK += dS'^T Q; the B operands are columns of dO
-      // and Q, fetched with transposing LDS reads in the query order of pp/dd.
+        lds_store_b64_asm(sdSt + xslot(offW, 8 * jg), u32x2{dd[2 * jg], dd[2 * jg + 1]});
+    }
+    // dV += P'^T dO and dK += dS'^T Q over this wave's 32 queries; the B
+    // operands are columns of dO and Q, fetched with transposing LDS reads
+    // in the query order of pp/dd.
 #pragma unroll
-      for (int k2 = 0; k2 < 2; k2++) {
-        const int kq = 2 * mt + k2, o4 = 4 * k2;
-        const bf16x8 pa = __builtin_bit_cast(bf16x8, u32x4{pp[o4], pp[o4 + 1], pp[o4 + 2], pp[o4 + 3]});
-        const bf16x8 da = __builtin_bit_cast(bf16x8, u32x4{dd[o4], dd[o4 + 1], dd[o4 + 2], dd[o4 + 3]});
+    for (int k2 = 0; k2 < 2; k2++) {
+      const int kq = 2 * qh + k2, o4 = 4 * k2;
+      const bf16x8 pa = __builtin_bit_cast(bf16x8, u32x4{pp[o4], pp[o4 + 1], pp[o4 + 2], pp[o4 + 3]});
+      const bf16x8 da = __builtin_bit_cast(bf16x8, u32x4{dd[o4], dd[o4 + 1], dd[o4 + 2], dd[o4 + 3]});
 #pragma unroll
-        for (int dt = 0; dt < NDT; dt++) {
-          const int o1 = xslot(offT0, 32 * dt) + 16 * kq * D, o2 = xslot(offT1, 32 * dt) + 16 * kq * D;
-          dv[dt] = mfma32(pa, lds_read_tr8(cdO + o1, cdO + o2), dv[dt]);
-          dk[dt] = mfma32(da, lds_read_tr8(cQ + o1, cQ + o2), dk[dt]);
-        }
+      for (int dt = 0; dt < NDT; dt++) {
+        const int o1 = xslot(offT0, 32 * dt) + 16 * kq * D, o2 = xslot(offT1, 32 * dt) + 16 * kq * D;
+        dv[dt] = mfma32(pa, lds_read_tr8(cdO + o1, cdO + o2), dv[dt]);
+        dk[dt] = mfma32(da, lds_read_tr8(cQ + o1, cQ + o2), dk[dt]);
+        if (dt & 1) __builtin_amdgcn_sched_barrier(0);
       }
     }
-    __syncthreads();  // dS'^T complete in LDS
+    lds_barrier();  // dS'^T complete in LDS
 
-    // dQ' (64 x D) = dS' (64 x 128 keys) K (128 keys x D).
-    f32x16 dq[DQ_MT];
+    // dQ' (64 x D) = dS' (64 x 128 keys) K (128 keys x D), one 32x32 tile
+    // per wave.
+    if (dq_wave) {
+      const int offK0 = swz_off<D>(8 * lhi + (lL >> 2), 32 * dq_nt + tcol);      // transposing reads of K
+      const int offK1 = swz_off<D>(8 * lhi + (lL >> 2) + 4, 32 * dq_nt + tcol);
+      const int offS0 = swz_off<BM>(8 * lhi + (lL >> 2), 32 * dq_mt + tcol);     // ... of dS'^T
+      const int offS1 = swz_off<BM>(8 * lhi + (lL >> 2) + 4, 32 * dq_mt + tcol);
+      f32x16 dq = f32x16{};
 #pragma unroll
-    for (int i = 0; i < DQ_MT; i++) dq[i] = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < BN / 16; kk++) {
-      const bf16x8 bk = lds_read_tr8(sK + offK0 + 16 * kk * D, sK + offK1 + 16 * kk * D);
-#pragma unroll
-      for (int i = 0; i < DQ_MT; i++) {
-        const int m8 = 32 * (dq_mt0 + i);
-        const bf16x8 as = lds_read_tr8(sdSt + xslot(offS0, m8) + 16 * kk * BM, sdSt + xslot(offS1, m8) + 16 * kk * BM);
-        dq[i] = mfma32(as, bk, dq[i]);
+      for (int kk = 0; kk < BN / 16; kk++) {
+        const bf16x8 bk = lds_read_tr8(sK + offK0 + 16 * kk * D, sK + offK1 + 16 * kk * D);
+        const bf16x8 as = lds_read_tr8(sdSt + offS0 + 16 * kk * BM, sdSt + offS1 + 16 * kk * BM);
+        dq = mfma32(as, bk, dq);
+        if (kk & 1) __builtin_amdgcn_sched_barrier(0);
       }
-    }
-    // Element j of dq[i] is query 32(dq_mt0+i) + 8(j/4) + 4hi + j%4, d = dq_d.
-    const size_t blk_off = ((size_t)(b * S + m0) * Hq + h) * D;
-    float* dst_base = ATOMIC ? p.dq_accum + blk_off : p.dq_part + (size_t)jb * nq + blk_off;
-    if (m0 + BM <= S) {
-      // Whole block in range: row offsets are wave-uniform (scalar) operands.
-      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(dst_base, (uint32_t)BM * row_bytes);
-      const uint32_t rb = opaque(row_bytes);
-#pragma unroll
-      for (int i = 0; i < DQ_MT; i++)
+      // Element j of dq is query 32dq_mt + 8(j/4) + 4hi + j%4, d = dq_d.
+      const size_t blk_off = ((size_t)(b * S + m0) * Hq + h) * D;
+      float* dst_base = ATOMIC ? p.dq_accum + blk_off : p.dq_part + (size_t)jb * nq + blk_off;
+      if (m0 + BM <= S) {
+        // Whole block in range: row offsets are wave-uniform (scalar) operands.
+        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(dst_base, (uint32_t)BM * row_bytes);
+        const uint32_t rb = opaque(row_bytes);
 #pragma unroll
         for (int j = 0; j < 16; j++) {
-          const uint32_t so = (uint32_t)(32 * (dq_mt0 + i) + 8 * (j >> 2) + (j & 3)) * rb;
+          const uint32_t so = (uint32_t)(32 * dq_mt + 8 * (j >> 2) + (j & 3)) * rb;
           if (ATOMIC)
-            __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(dq[i][j], rs, dq_voff, so, 0);
+            __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(dq[j], rs, dq_voff, so, 0);
           else
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dq[i][j]), rs, dq_voff, so, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dq[j]), rs, dq_voff, so, 0);
         }
-    } else {
-#pragma unroll
-      for (int i = 0; i < DQ_MT; i++)
+      } else {
+        // Last, partial block (addresses derived here, not kept live).
+        const int lt = opaque_v(lane);
+        const int thi = lt >> 5, td = 32 * dq_nt + (lt & 31);
 #pragma unroll
         for (int j = 0; j < 16; j++) {
-          const int qr = 32 * (dq_mt0 + i) + 8 * (j >> 2) + 4 * hi + (j & 3);
+          const int qr = 32 * dq_mt + 8 * (j >> 2) + 4 * thi + (j & 3);
           if (m0 + qr < S) {
-            float* a = dst_base + (size_t)qr * Hq * D + dq_d;
+            float* a = dst_base + (size_t)qr * Hq * D + td;
             if (ATOMIC)
-              unsafeAtomicAdd(a, dq[i][j]);
+              unsafeAtomicAdd(a, dq[j]);
             else
-              *a = dq[i][j];
+              *a = dq[j];
           }
         }
+      }
     }
+  };
+
+  for (int st = 0; st < n_steps; st += 2) {
+    step(std::integral_constant<int, 0>{}, st);
+    if (st + 1 < n_steps) step(std::integral_constant<int, 1>{}, st + 1);
   }
 
-  // Epilogue: element j of lane l is key 32w + 8(j/4) + 4hi + j%4, d = 32dt + l32.
+  // The two query halves hold partial dK/dV of the same keys: the second
+  // half hands its accumulators over through LDS (key quarters 0-1 in the K
+  // block, 2-3 in the V block, free after the loop) in the MFMA result
+  // layout, and the first half adds and stores.  Element j of lane l is key
+  // 32kw + 8(j/4) + 4hi + j%4, d = 32dt + l32.
+  static_assert(2 * NDT * 16 * 64 * sizeof(float) <= BN * D * sizeof(uint16_t), "hand-over space");
+  float* xch = reinterpret_cast<float*>(kw < 2 ? sK : sV) + (kw & 1) * (NDT * 16 * 64);
   const float inv_scale = 1.f / p.scale;
+  const int le = opaque_v(lane);  // output addresses derived here, not kept live
+  const int ehi = le >> 5, el32 = le & 31;
 #pragma unroll
-  for (int dt = 0; dt < NDT; dt++) {
-    const int d = 32 * dt + l32;
+  for (int tensor = 0; tensor < 2; tensor++) {
+    lds_barrier();
+    if (qh == 1) {
 #pragma unroll
-    for (int j = 0; j < 16; j++) {
-      const int key = n0 + 32 * w + 8 * (j >> 2) + 4 * hi + (j & 3);
-      if (key < S) {
-        if (PARTIAL) {
-          const size_t off = ((size_t)(b * S + key) * Hq + h) * D + d;
-          p.dk_part[off] = dk[dt][j];
-          p.dv_part[off] = dv[dt][j] * inv_scale;
-        } else {
-          const size_t off = ((size_t)(b * S + key) * Hkv + kvh) * D + d;
-          p.dk[off] = to_bf16(dk[dt][j]);
-          p.dv[off] = to_bf16(dv[dt][j] * inv_scale);
+      for (int dt = 0; dt < NDT; dt++)
+#pragma unroll
+        for (int j = 0; j < 16; j++) xch[(dt * 16 + j) * 64 + le] = tensor == 0 ? dk[dt][j] : dv[dt][j];
+    }
+    lds_barrier();
+    if (qh == 0) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; dt++) {
+        const int d = 32 * dt + el32;
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+          const float v = (tensor == 0 ? dk[dt][j] : dv[dt][j]) + xch[(dt * 16 + j) * 64 + le];
+          const float out = tensor == 0 ? v : v * inv_scale;
+          const int key = n0 + 32 * kw + 8 * (j >> 2) + 4 * ehi + (j & 3);
+          if (key < S) {
+            if (PARTIAL) {
+              const size_t off = ((size_t)(b * S + key) * Hq + h) * D + d;
+              (tensor == 0 ? p.dk_part : p.dv_part)[off] = out;
+            } else {
+              const size_t off = ((size_t)(b * S + key) * Hkv + kvh) * D + d;
+              (tensor == 0 ? p.dk : p.dv)[off] = to_bf16(out);
+            }
+          }
         }
       }
     }
@@ -303,7 +349,7 @@ template <int D, bool CAUSAL, bool ATOMIC, bool PARTIAL>
 hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   const int n_nblk = (p.S + kBN - 1) / kBN;
   const long long nwg = (long long)p.B * p.Hq * n_nblk;
-  hipLaunchKernelGGL((bwd_kernel<D, CAUSAL, ATOMIC, PARTIAL>), dim3((unsigned)nwg), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((bwd_kernel<D, CAUSAL, ATOMIC, PARTIAL>), dim3((unsigned)nwg), dim3(kNW * 64), 0, stream, p);
   return hipGetLastError();
 }
 

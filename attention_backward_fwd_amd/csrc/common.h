@@ -124,27 +124,64 @@ __device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(void*
 // bf16 matrix with row stride rs elements into a swizzled tile.  Rows at or
 // past `nrows` read row nrows - 1 instead (callers mask them); every source
 // address is therefore inside the matrix.  Each wave instruction moves 1 KB;
-// the 4 waves of the workgroup split the tile.  Completion: vmcnt.
-template <int D, int R>
+// the NW waves of the workgroup split the tile.  Completion: vmcnt.
+template <int D, int R, int NW = 4>
 __device__ __forceinline__ void tile_load_async(const uint16_t* g, size_t rs, int row0, int nrows,
                                                 uint16_t* tile, int w, int lane) {
   constexpr int CPR = D / 8;       // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;    // rows per wave instruction
   constexpr int NI = R / RPI;      // wave instructions per tile
-  static_assert(NI % 4 == 0, "tile must split evenly over 4 waves");
+  static_assert(NI % NW == 0, "tile must split evenly over the waves");
   const int rl = lane / CPR, slot = lane % CPR;
+  const uint16_t* base = g + (size_t)row0 * rs;  // wave-uniform
+  const int last = nrows - 1 - row0;
 #pragma unroll
-  for (int j = w; j < NI; j += 4) {
+  for (int j = w; j < NI; j += NW) {
     const int r = j * RPI + rl;
-    const int gr = min(row0 + r, nrows - 1);
-    const uint16_t* src = g + (size_t)gr * rs + ((slot ^ swz<D>(r)) << 3);
-    __builtin_amdgcn_global_load_lds(src, lds_ptr(tile + j * 512), 16, 0, 0);
+    // 32-bit per-lane byte offset from the uniform row base.
+    const uint32_t off = ((uint32_t)min(r, last) * (uint32_t)rs + (uint32_t)((slot ^ swz<D>(r)) << 3)) * 2u;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(base) + off, lds_ptr(tile + j * 512), 16, 0, 0);
   }
+}
+
+// Workgroup barrier for LDS hand-offs only.  Waves of these kernels exchange
+// data through LDS alone, so a wave only has to finish its own LDS
+// instructions (lgkmcnt) before the barrier; in particular it does not wait
+// for its outstanding global loads, LDS-DMA loads, stores or atomics (an
+// LDS-scoped fence would, because LDS-DMA writes count as LDS writes).  The
+// LDS-DMA loads are waited for explicitly (wait_vmem / wait_vmem_but) where
+// their data is needed.  The "memory" clobber keeps the compiler from moving
+// memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// 8-byte LDS store issued as inline assembly.  The compiler's LDS-DMA
+// tracking does not see it, so it is not held back behind LDS-DMA loads in
+// flight to other buffers.  Ordering with lds_barrier() (also volatile asm)
+// is preserved; the compiler's own lgkmcnt waits only become stricter.
+__device__ __forceinline__ void lds_store_b64_asm(uint16_t* p, u32x2 v) {
+  const uint32_t addr = (uint32_t)(uintptr_t)lds_ptr(p);
+  asm volatile("ds_write_b64 %0, %1" ::"v"(addr), "v"(v));
+}
+
+// Asynchronous global -> LDS copy of n <= 64 consecutive fp32 values (one per
+// lane, lanes >= n read the last one again) to lds[0 .. 63].
+__device__ __forceinline__ void row_load_async(const float* g, int n, float* lds, int lane) {
+  __builtin_amdgcn_global_load_lds(g + min(lane, n - 1), lds_ptr(lds), 4, 0, 0);
 }
 
 // Wait until every vector-memory operation of this wave (including LDS-DMA
 // writes) has completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Wait until at most N vector-memory operations of this wave are still in
+// flight.  The counter retires operations in issue order, so this waits for
+// everything except the N most recent ones (e.g. fire-and-forget atomics
+// issued after the loads that must be complete).
+template <int N>
+__device__ __forceinline__ void wait_vmem_but() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);

@@ -20,6 +20,8 @@
 // workgroup barrier per tile).  Scores stay fp32; P is rounded
 // to bf16 only as an MFMA operand; O is written as bf16 (RNE) and LSE as fp32
 // natural log including the scale.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -47,10 +49,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
   constexpr int NDT = D / 32;  // 32-row tiles of O^T
   constexpr int TK = BN * D;   // elements of one K or V tile
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2 * TK];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2 * TK];
+  // Separate LDS objects for the two buffers, so that the compiler can tell
+  // the tile being loaded (LDS-DMA in flight) from the tile being read.
+  __shared__ __attribute__((aligned(16))) uint16_t sK0[TK];
+  __shared__ __attribute__((aligned(16))) uint16_t sK1[TK];
+  __shared__ __attribute__((aligned(16))) uint16_t sV0[TK];
+  __shared__ __attribute__((aligned(16))) uint16_t sV1[TK];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (scalar)
   const int hi = lane >> 5, l32 = lane & 31, L = lane & 15, Gp = (lane >> 4) & 1;
   const int S = p.S, Hq = p.Hq, G = p.G, Hkv = p.Hkv;
   const int n_mblk = (S + BM - 1) / BM;
@@ -85,8 +92,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
   const int n_end = CAUSAL ? min(S, mb * BM + BM) : S;
   const int n_tiles = (n_end + BN - 1) / BN;
 
-  tile_load_async<D, BN>(Kb, kvrs, 0, S, sK, w, lane);
-  tile_load_async<D, BN>(Vb, kvrs, 0, S, sV, w, lane);
+  tile_load_async<D, BN>(Kb, kvrs, 0, S, sK0, w, lane);
+  tile_load_async<D, BN>(Vb, kvrs, 0, S, sV0, w, lane);
 
   bf16x8 qf[NKS];
   if (qi < S) {
@@ -111,19 +118,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
   for (int dt = 0; dt < NDT; dt++) oacc[dt] = f32x16{};
   float m_i = -INFINITY, l_i = 0.f;
 
-  for (int it = 0; it < n_tiles; it++) {
-    const int buf = it & 1;
+  // One key/value tile; BUF selects the LDS buffers it reads (the other
+  // pair receives the next tile meanwhile).
+  auto tile = [&](auto buf_tag, int it) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    const uint16_t* cK = BUF ? sK1 : sK0;
+    const uint16_t* cV = BUF ? sV1 : sV0;
+    uint16_t* nK = BUF ? sK0 : sK1;
+    uint16_t* nV = BUF ? sV0 : sV1;
     const int n0 = it * BN;
     wait_vmem();
-    __syncthreads();  // tile it resident; every wave is done with tile it-1
+    lds_barrier();  // tile it resident; every wave is done with tile it-1
     if (it + 1 < n_tiles) {
-      tile_load_async<D, BN>(Kb, kvrs, n0 + BN, S, sK + (buf ^ 1) * TK, w, lane);
-      tile_load_async<D, BN>(Vb, kvrs, n0 + BN, S, sV + (buf ^ 1) * TK, w, lane);
+      tile_load_async<D, BN>(Kb, kvrs, n0 + BN, S, nK, w, lane);
+      tile_load_async<D, BN>(Vb, kvrs, n0 + BN, S, nV, w, lane);
     }
     // A wave whose queries all precede the tile has nothing to do in it.
-    if (CAUSAL && n0 > q0 + 31) continue;
-    const uint16_t* cK = sK + buf * TK;
-    const uint16_t* cV = sV + buf * TK;
+    if (CAUSAL && n0 > q0 + 31) return;
     const int offA = opaque_v(offA0), offV0 = opaque_v(offV00), offV1 = opaque_v(offV10);
 
     // S^T (64 keys x 32 queries): element j of s[mt] is key
@@ -189,6 +200,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
         const bf16x8 a = lds_read_tr8(cV + xslot(offV0, 32 * dt) + 16 * kk * D, cV + xslot(offV1, 32 * dt) + 16 * kk * D);
         oacc[dt] = mfma32(a, pb[kk], oacc[dt]);
       }
+  };
+  for (int it = 0; it < n_tiles; it += 2) {
+    tile(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < n_tiles) tile(std::integral_constant<int, 1>{}, it + 1);
   }
 
   const float l_tot = xhalf_sum(l_i);

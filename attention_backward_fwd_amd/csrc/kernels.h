@@ -37,6 +37,7 @@ struct BwdParams {
   float* dv_part;
   int B, S, Hq, G, Hkv, D;
   float scale;
+  float log2_scale;  // log2(scale), computed on the host
   int causal, use_atomic;
 };
 

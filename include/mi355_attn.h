@@ -57,7 +57,8 @@ enum {
   ATTN_ERR_BAD_SHAPE = -2, /* a size < 1, or heads_q not a multiple of groups */
   ATTN_ERR_HEAD_DIM = -3,  /* head_dim not 64 or 128 */
   ATTN_ERR_ALIGN = -4,     /* a tensor base is not 16-byte aligned */
-  ATTN_ERR_RANGE = -5,     /* a tensor has >= 2^31 elements, or scale is not finite and > 0 */
+  ATTN_ERR_RANGE = -5,     /* a tensor has >= 2^31 elements, heads_q * head_dim > 2^22,
+                              or softmax_scale is not finite and > 0 */
   ATTN_ERR_WORKSPACE = -6, /* workspace NULL or smaller than attn_bwd_workspace_bytes() */
   ATTN_ERR_HIP = -7,       /* the HIP runtime reported a launch error */
   ATTN_ERR_FLAG = -8       /* causal or use_atomic is not 0 or 1 */

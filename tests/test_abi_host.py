@@ -94,6 +94,7 @@ E = {"null": -1, "shape": -2, "hd": -3, "align": -4, "range": -5, "ws": -6, "fla
     ({"shape": shp(b=0)}, "shape"), ({"shape": shp(s=0)}, "shape"), ({"shape": shp(hq=6, g=4)}, "shape"),
     ({"shape": shp(g=0)}, "shape"), ({"shape": shp(d=96)}, "hd"), ({"shape": shp(d=256)}, "hd"),
     ({"shape": shp(b=64, s=8192, hq=64, g=1, d=128)}, "range"),
+    ({"shape": shp(b=1, s=2, hq=65536, g=1, d=128)}, "range"),
     ({"scale": 0.0}, "range"), ({"scale": -1.0}, "range"), ({"scale": float("nan")}, "range"),
     ({"scale": float("inf")}, "range"), ({"causal": 2}, "flag"), ({"o": MIS}, "align"), ({"lse": MIS}, "align"),
 ])
