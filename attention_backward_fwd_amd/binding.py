@@ -160,7 +160,7 @@ class BwdBuffers:
         dev = q.device
         b, s, hq, d = q.shape
         self.delta = torch.empty((b, hq, s), dtype=torch.float32, device=dev)
-        self.dq_accum = torch.empty(q.shape, dtype=torch.float32, device=dev)
+        self.dq_accum = torch.empty((b, hq, s, d), dtype=torch.float32, device=dev)  # head-major
         self.dq = torch.empty_like(q)
         self.dk = torch.empty_like(k)
         self.dv = torch.empty_like(k)

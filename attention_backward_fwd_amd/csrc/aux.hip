@@ -2,7 +2,8 @@
 //   preprocess   Delta = rowsum(dO o O) (+ zero the fp32 dQ accumulator)
 //   dq_sum       split path: dQ = sum of the per-key-block partials, in
 //                ascending block order
-//   postprocess  dQ fp32 -> bf16; grouped-query dK/dV partial reduction
+//   postprocess  dQ fp32 -> bf16 (head-major accumulator to BSHD);
+//                grouped-query dK/dV partial reduction
 // These are the flashattn_bwd_preprocess / flashattn_bwd_postprocess steps of
 // the TileLang #940 examples and the "sum" half of its split+sum template.
 // All moves are 16-byte vector loads/stores along contiguous rows.
@@ -42,23 +43,24 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const uint16_t* __restr
 #pragma unroll
     for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
     if (sub == 0) delta[row] = acc;
-    if (dq_accum) {
-      f32x4* z = reinterpret_cast<f32x4*>(dq_accum + off);
+    if (dq_accum) {  // head-major [B][Hq][S][D]: row `row` starts at row * D
+      f32x4* z = reinterpret_cast<f32x4*>(dq_accum + (size_t)row * D + 8 * sub);
       z[0] = f32x4{0.f, 0.f, 0.f, 0.f};
       z[1] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
 }
 
-// dq_accum[b,s,h,:] = sum_{j=0..J(s)} part[j][b,s,h,:], ascending j, where
-// J(s) is the last key block (causal: the block holding key s).
+// dq_accum[b,h,s,:] = sum_{j=0..J(s)} part[j][b,h,s,:], ascending j, where
+// J(s) is the last key block (causal: the block holding key s).  Both are
+// head-major fp32 [B][Hq][S][D].
 __global__ __launch_bounds__(256) void dq_sum_kernel(const float* __restrict__ part,
                                                      float* __restrict__ dq, long long n4, int S,
-                                                     int HqD, int n_nblk, int causal) {
+                                                     int D, int n_nblk, int causal) {
   const size_t slot = (size_t)n4 * 4;
   for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long long)gridDim.x * 256) {
     const long long e = i * 4;
-    const int s = (int)((e / HqD) % S);
+    const int s = (int)((e / D) % S);
     const int last = causal ? s / kBwdBlockN : n_nblk - 1;
     const float* src = part + e;
     f32x4 acc = *reinterpret_cast<const f32x4*>(src);
@@ -72,7 +74,8 @@ __device__ __forceinline__ u32x4 cvt8(f32x4 a, f32x4 b) {
                pack_bf16x2(b[2], b[3])};
 }
 
-// Part 1 (chunks [0, nq8)): dq = bf16(dq_accum), 8 elements per chunk.
+// Part 1 (chunks [0, nq8)): dq[b,s,h,:] = bf16(dq_accum[b,h,s,:]), 8 elements
+// per chunk (chunks numbered in the BSHD output order).
 // Part 2 (chunks [nq8, nq8 + nkv8), grouped queries only): dk/dv chunk of
 // (b, s, kv) = bf16(sum_r partial[b, s, kv*G + r]), ascending r.
 __global__ __launch_bounds__(256) void postprocess_kernel(const float* __restrict__ dq_accum,
@@ -80,15 +83,21 @@ __global__ __launch_bounds__(256) void postprocess_kernel(const float* __restric
                                                           const float* __restrict__ dv_part,
                                                           uint16_t* __restrict__ dq, uint16_t* __restrict__ dk,
                                                           uint16_t* __restrict__ dv, long long nq8,
-                                                          long long nkv8, int G, int D) {
+                                                          long long nkv8, int G, int D, int S, int Hq) {
   const long long total = nq8 + nkv8;
+  const int dchunks = D / 8;
   for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long long)gridDim.x * 256) {
     if (i < nq8) {
-      const f32x4* src = reinterpret_cast<const f32x4*>(dq_accum + i * 8);
+      const long long row = i / dchunks;  // (b, s, h) of the output
+      const int d0 = (int)(i % dchunks) * 8;
+      const int h = (int)(row % Hq);
+      const long long bs = row / Hq;
+      const int s = (int)(bs % S);
+      const long long b = bs / S;
+      const f32x4* src = reinterpret_cast<const f32x4*>(dq_accum + ((b * Hq + h) * S + s) * D + d0);
       *reinterpret_cast<u32x4*>(dq + i * 8) = cvt8(src[0], src[1]);
     } else {
       const long long c = i - nq8;          // chunk of the [B,S,Hkv,D] output
-      const int dchunks = D / 8;
       const long long rowkv = c / dchunks;  // (b, s, kv) flattened
       const int d0 = (int)(c % dchunks) * 8;
       const size_t base = (size_t)rowkv * G * D + d0;  // partial row (b, s, kv*G) at d0
@@ -133,8 +142,8 @@ hipError_t launch_dq_sum(const float* dq_part, float* dq_accum, int B, int S, in
                          hipStream_t stream) {
   const long long n4 = (long long)B * S * Hq * D / 4;
   const int n_nblk = (S + kBwdBlockN - 1) / kBwdBlockN;
-  hipLaunchKernelGGL(dq_sum_kernel, dim3(grid_for(n4, 256)), dim3(256), 0, stream, dq_part, dq_accum, n4, S,
-                     Hq * D, n_nblk, causal);
+  hipLaunchKernelGGL(dq_sum_kernel, dim3(grid_for(n4, 256)), dim3(256), 0, stream, dq_part, dq_accum, n4, S, D,
+                     n_nblk, causal);
   return hipGetLastError();
 }
 
@@ -144,7 +153,7 @@ hipError_t launch_postprocess(const float* dq_accum, const float* dk_part, const
   const long long nq8 = (long long)B * S * Hq * D / 8;
   const long long nkv8 = G > 1 ? (long long)B * S * (Hq / G) * D / 8 : 0;
   hipLaunchKernelGGL(postprocess_kernel, dim3(grid_for(nq8 + nkv8, 256)), dim3(256), 0, stream, dq_accum,
-                     dk_part, dv_part, dq, dk, dv, nq8, nkv8, G, D);
+                     dk_part, dv_part, dq, dk, dv, nq8, nkv8, G, D, S, Hq);
   return hipGetLastError();
 }
 

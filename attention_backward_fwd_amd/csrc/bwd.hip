@@ -141,9 +141,33 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
   }
   const int key_l = n0 + 32 * kw + l32;
   const int dq_d = 32 * dq_nt + l32;
-  const uint32_t row_bytes = (uint32_t)(Hq * D) * 4u;
+  // dQ accumulator and partials are head-major ([.., B, Hq, S, D]): the rows
+  // of one query block are one contiguous run.
+  const uint32_t row_bytes = (uint32_t)D * 4u;
   const uint32_t dq_voff = (uint32_t)(4 * hi) * row_bytes + (uint32_t)dq_d * 4u;
   const size_t nq = (size_t)p.B * S * Hq * D;
+
+  // dQ of a full query block leaves the workgroup during the *next* step,
+  // spread over its S/dP products, so that the 16 atomics/stores per wave
+  // overlap compute instead of arriving in one burst.  dq_prev holds it.
+  f32x16 dq_prev = f32x16{};
+  auto dq_rsrc = [&](int m0) {
+    const size_t blk_off = ((size_t)(b * Hq + h) * S + m0) * D;
+    float* dst_base = ATOMIC ? p.dq_accum + blk_off : p.dq_part + (size_t)jb * nq + blk_off;
+    return buffer_rsrc(dst_base, (uint32_t)BM * row_bytes);
+  };
+  // Rows j0 .. j0+3 of a dQ tile (element j: row 32dq_mt + 8(j/4) + 4hi + j%4).
+  auto dq_emit4 = [&](const __amdgpu_buffer_rsrc_t& rs, const f32x16& v, int j0) {
+    const uint32_t rb = opaque(row_bytes);
+#pragma unroll
+    for (int j = j0; j < j0 + 4; j++) {
+      const uint32_t so = (uint32_t)(32 * dq_mt + 8 * (j >> 2) + (j & 3)) * rb;
+      if (ATOMIC)
+        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v[j], rs, dq_voff, so, 0);
+      else
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[j]), rs, dq_voff, so, 0);
+    }
+  };
 
   // One query block; BUF selects the LDS buffers it reads (the other pair
   // receives the next block meanwhile).
@@ -158,10 +182,10 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     float* nL = BUF ? sL0 : sL1;
     float* nD = BUF ? sD0 : sD1;
     const int m0 = m_begin + st * BM;
-    // Block st resident.  After the first step, the 16 dQ atomics/stores a
-    // dQ wave issued at the end of step st-1 came after those loads and may
-    // stay in flight.
-    if (dq_wave && st > 0)
+    // Block st resident.  From step 2 on, the 16 deferred dQ atomics/stores
+    // a dQ wave issued during step st-1 came after those loads and may stay
+    // in flight.
+    if (dq_wave && st > 1)
       wait_vmem_but<16>();
     else
       wait_vmem();
@@ -181,6 +205,9 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     const int offT1 = swz_off<D>(4 * lhi + (lL >> 2) + 8, tcol);
 
     // S = Q K^T and dP = dO V^T for this wave's 32 queries x 32 keys.
+    // The previous block's dQ goes out meanwhile (16 rows, 4 per 2 k-steps).
+    const bool emit = dq_wave && st > 0;
+    const __amdgpu_buffer_rsrc_t prs = dq_rsrc(max(m0 - BM, 0));
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < NKS; ks++) {
@@ -188,10 +215,15 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
       const int ok = xslot(offR, 16 * ks) + 32 * kw * D;
       s = mfma32(lds_read_b128(cQ + oq), lds_read_b128(sK + ok), s);
       dp = mfma32(lds_read_b128(cdO + oq), lds_read_b128(sV + ok), dp);
-      // Bound how far ahead the scheduler hoists operand reads (each one
-      // holds 4 VGPRs until its MFMA issues).
-      if (ks & 1) __builtin_amdgcn_sched_barrier(0);
+      if (ks & 1) {
+        if (emit && (ks >> 1) < 4) dq_emit4(prs, dq_prev, 4 * (ks >> 1));
+        // Bound how far ahead the scheduler hoists operand reads (each one
+        // holds 4 VGPRs until its MFMA issues).
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
+    if (NKS < 8 && emit)  // D = 64: four k-steps carried half of the rows
+      for (int j0 = 4 * (NKS / 2); j0 < 16; j0 += 4) dq_emit4(prs, dq_prev, j0);
 
     // P' = scale P and dS' = scale dS.  Element j of lane l is query
     // 32qh + 8(j/4) + 4hi + j%4 of the block, key 32kw + l32.
@@ -263,29 +295,20 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
         if (kk & 1) __builtin_amdgcn_sched_barrier(0);
       }
       // Element j of dq is query 32dq_mt + 8(j/4) + 4hi + j%4, d = dq_d.
-      const size_t blk_off = ((size_t)(b * S + m0) * Hq + h) * D;
-      float* dst_base = ATOMIC ? p.dq_accum + blk_off : p.dq_part + (size_t)jb * nq + blk_off;
       if (m0 + BM <= S) {
-        // Whole block in range: row offsets are wave-uniform (scalar) operands.
-        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(dst_base, (uint32_t)BM * row_bytes);
-        const uint32_t rb = opaque(row_bytes);
-#pragma unroll
-        for (int j = 0; j < 16; j++) {
-          const uint32_t so = (uint32_t)(32 * dq_mt + 8 * (j >> 2) + (j & 3)) * rb;
-          if (ATOMIC)
-            __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(dq[j], rs, dq_voff, so, 0);
-          else
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dq[j]), rs, dq_voff, so, 0);
-        }
+        dq_prev = dq;  // written during the next step, or after the loop
       } else {
-        // Last, partial block (addresses derived here, not kept live).
+        // Last, partial block: written now, row by row (addresses derived
+        // here, not kept live).
+        const size_t blk_off = ((size_t)(b * Hq + h) * S + m0) * D;
+        float* dst_base = ATOMIC ? p.dq_accum + blk_off : p.dq_part + (size_t)jb * nq + blk_off;
         const int lt = opaque_v(lane);
         const int thi = lt >> 5, td = 32 * dq_nt + (lt & 31);
 #pragma unroll
         for (int j = 0; j < 16; j++) {
           const int qr = 32 * dq_mt + 8 * (j >> 2) + 4 * thi + (j & 3);
           if (m0 + qr < S) {
-            float* a = dst_base + (size_t)qr * Hq * D + td;
+            float* a = dst_base + (size_t)qr * D + td;
             if (ATOMIC)
               unsafeAtomicAdd(a, dq[j]);
             else
@@ -299,6 +322,13 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
   for (int st = 0; st < n_steps; st += 2) {
     step(std::integral_constant<int, 0>{}, st);
     if (st + 1 < n_steps) step(std::integral_constant<int, 1>{}, st + 1);
+  }
+  // The last block's dQ, if it was a full block, is still held.
+  const int m_last = m_begin + (n_steps - 1) * BM;
+  if (dq_wave && m_last + BM <= S) {
+    const __amdgpu_buffer_rsrc_t rs = dq_rsrc(m_last);
+#pragma unroll
+    for (int j0 = 0; j0 < 16; j0 += 4) dq_emit4(rs, dq_prev, j0);
   }
 
   // The two query halves hold partial dK/dV of the same keys: the second

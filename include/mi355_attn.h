@@ -22,7 +22,8 @@
  *     [batch, seqlen, heads_q, head_dim] (BSHD); K, V, dK, dV are
  *     [batch, seqlen, heads_q/groups, head_dim]; LSE and Delta are
  *     [batch, heads_q, seqlen] fp32.  bf16 tensors hold raw bf16 bit patterns
- *     (uint16_t).  dq_accum is fp32 BSHD like dQ.
+ *     (uint16_t).  dq_accum, the fp32 dQ accumulator handed from attn_bwd to
+ *     attn_bwd_postprocess, is head-major: [batch, heads_q, seqlen, head_dim].
  *   - Every pointer is device memory allocated and owned by the caller; it
  *     must be 16-byte aligned.  The library allocates nothing, frees
  *     nothing, never synchronises and keeps no pointer after a call returns.
@@ -84,7 +85,7 @@ int attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* 
  * Backward preprocess: Delta_i = sum_d dO_id * O_id in fp32 (the
  * flashattn_bwd_preprocess step of the TileLang #940 examples).
  *   o, dout [B,S,Hq,D] bf16 (inputs); delta [B,Hq,S] fp32 (output).
- *   dq_accum: NULL, or an fp32 [B,S,Hq,D] buffer that is set to zero here,
+ *   dq_accum: NULL, or an fp32 [B,Hq,S,D] buffer that is set to zero here,
  *   as the fp32 atomic dQ accumulator of attn_bwd(use_atomic=1) requires.
  */
 int attn_bwd_preprocess(const uint16_t* o, const uint16_t* dout, float* delta, float* dq_accum,
@@ -94,7 +95,7 @@ int attn_bwd_preprocess(const uint16_t* o, const uint16_t* dout, float* delta, f
  * Bytes of device workspace attn_bwd and attn_bwd_postprocess need for this
  * problem (0 when none is needed).  Layout, for reference only:
  *   groups > 1: fp32 per-query-head dK and dV partials, [B,S,Hq,D] each;
- *   use_atomic == 0: fp32 per-KV-block dQ partials, [n_kv_blocks,B,S,Hq,D].
+ *   use_atomic == 0: fp32 per-KV-block dQ partials, [n_kv_blocks,B,Hq,S,D].
  * Returns 0 for an invalid shape.
  */
 size_t attn_bwd_workspace_bytes(attn_shape shape, int causal, int use_atomic);
@@ -126,7 +127,7 @@ int attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint
  * examples): dq = bf16(dq_accum) with round-to-nearest-even; for groups > 1
  * also dk/dv[b,s,kv,:] = bf16(sum over r < groups, ascending, of the
  * workspace partials of query head kv*groups + r).
- *   dq_accum fp32 [B,S,Hq,D] (input); dq [B,S,Hq,D] bf16 (output);
+ *   dq_accum fp32 [B,Hq,S,D] (input); dq [B,S,Hq,D] bf16 (output);
  *   dk, dv [B,S,Hkv,D] bf16 (outputs, required only when groups > 1);
  *   workspace: the buffer attn_bwd used (required only when groups > 1).
  */
