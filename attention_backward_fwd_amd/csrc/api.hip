@@ -18,7 +18,7 @@ int check_shape(const attn_shape& s) {
   if (s.head_dim != 64 && s.head_dim != 128) return ATTN_ERR_HEAD_DIM;
   const long long nq = (long long)s.batch * s.seqlen * s.heads_q * s.head_dim;
   if (nq >= (1LL << 31)) return ATTN_ERR_RANGE;
-  // Kernels address up to 128 rows of one head with 32-bit byte offsets.
+  // Kernels address up to 256 rows of one head with 32-bit byte offsets.
   if ((long long)s.heads_q * s.head_dim > (1LL << 22)) return ATTN_ERR_RANGE;
   return ATTN_OK;
 }

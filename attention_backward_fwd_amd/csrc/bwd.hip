@@ -2,12 +2,13 @@
 //
 // Decomposition as in the FlashAttention backward examples of TileLang #940
 // (flashattn_bwd_atomic_add / flashattn_bwd_split): one workgroup owns a block
-// of 128 keys of one (batch, query head), keeps its dK/dV accumulators on
+// of 256 keys of one (batch, query head), keeps its dK/dV accumulators on
 // chip for the whole sweep and walks the query blocks that see those keys.
-// Per 64-query block the five tile contractions run on the matrix cores:
+// Each of the 8 waves owns 32 of the keys.  Per 32-query block the five tile
+// contractions run on the matrix cores:
 //
 //   S  = Q K^T            A = Q (LDS, row reads)      B = K (LDS, row reads)
-//   dP = dO V^T           A = dO (LDS, row reads)     B = V (LDS, row reads)
+//   dP = dO V^T           A = dO (LDS, row reads)     B = V (registers)
 //   dV += P^T dO          A = P^T (registers)         B = dO (LDS, transposing reads)
 //   dK += dS^T Q          A = dS^T (registers)        B = Q (LDS, transposing reads)
 //   dQ  = dS K            A = dS (LDS, transposing)   B = K (LDS, transposing reads)
@@ -16,7 +17,16 @@
 // 32x32 MFMA result layout puts one key in each lane and 16 query rows in its
 // registers; that is already the A-operand layout of P^T and dS^T for the dV
 // and dK products, so those never leave registers.  dQ needs dS with queries
-// in lanes, so dS^T goes through LDS.
+// in lanes, so dS^T goes through LDS; dQ (32 queries x D) is split over the
+// waves as 16x16 tiles.
+//
+// Why 256 keys: every key block adds its dQ contribution once per query
+// block, so the dQ traffic leaving the workgroups (fp32 atomics, or the split
+// path's partials) is inversely proportional to the key-block height, and
+// the fp32 atomic rate of the memory system, not the matrix cores, bounds a
+// 128-key version.  The dK/dV accumulators of 256 keys fill half of the
+// register file; V lives in registers (it is only ever a B operand of dP),
+// which leaves LDS for K, double-buffered Q/dO blocks and dS^T.
 //
 // The softmax scale is folded into the exponent: the kernel forms
 // P' = scale * P = exp2(S*scale*log2e - (LSE*log2e - log2(scale))), so that
@@ -45,8 +55,21 @@ namespace mi355 {
 namespace {
 
 constexpr int kBN = kBwdBlockN;  // keys per workgroup
-constexpr int kBM = 64;          // queries per step
-constexpr int kNW = 8;           // waves per workgroup: 4 key quarters x 2 query halves
+constexpr int kBM = 32;          // queries per step
+constexpr int kNW = 8;           // waves per workgroup, 32 keys each
+static_assert(kBN == 32 * kNW, "one 32-key slice per wave");
+
+// dS'^T tile [256 keys][32 queries] bf16, 64-byte rows.  The 8-byte chunk
+// index of row r is XORed with fS(r) (bits 3, 2, 4 of r to chunk bits 2, 1,
+// 0), which keeps both of its access patterns free of bank conflicts: the
+// writes (32 consecutive keys, one chunk) and the transposing reads of the
+// dQ product (keys 8g + e, g < 4, e < 4, four consecutive chunks).
+__device__ __forceinline__ int dst_f(int row) {
+  return (((row >> 3) & 1) << 2) | (((row >> 2) & 1) << 1) | ((row >> 4) & 1);
+}
+__device__ __forceinline__ int dst_off(int row, int col) {
+  return row * kBM + ((((col >> 2) ^ dst_f(row)) << 2) | (col & 3));
+}
 
 // Two waves per SIMD: the kernel must fit 256 VGPRs, which also keeps every
 // MFMA accumulator in VGPRs.
@@ -55,29 +78,29 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
   constexpr int BN = kBN, BM = kBM, NW = kNW;
   constexpr int TQ = BM * D;  // elements of one Q or dO block
   constexpr int NKS = D / 16, NDT = D / 32;
+  // dQ tiles (16 queries x 16 d) per wave: D = 128 has 16 tiles (wave w
+  // takes d columns 16w.. for both query halves), D = 64 has 8 (one each).
+  constexpr int NQT = D / 64;
 
   // Separate LDS objects, so that the compiler can tell the block being
   // loaded (LDS-DMA in flight) from the block being read and does not wait
-  // for the former before reading the latter.  After the loop the K and V
-  // blocks hold the dK/dV hand-over between the query halves.
+  // for the former before reading the latter.
   __shared__ __attribute__((aligned(16))) uint16_t sK[BN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[BN * D];
   __shared__ __attribute__((aligned(16))) uint16_t sQ0[TQ];
   __shared__ __attribute__((aligned(16))) uint16_t sQ1[TQ];
   __shared__ __attribute__((aligned(16))) uint16_t sdO0[TQ];
   __shared__ __attribute__((aligned(16))) uint16_t sdO1[TQ];
-  __shared__ __attribute__((aligned(16))) uint16_t sdSt[BN * BM];  // dS'^T [key][query], swizzled
-  // Raw LSE and Delta rows of the query block (LDS-DMA, one per buffer).
-  __shared__ __attribute__((aligned(16))) float sL0[BM];
-  __shared__ __attribute__((aligned(16))) float sL1[BM];
-  __shared__ __attribute__((aligned(16))) float sD0[BM];
-  __shared__ __attribute__((aligned(16))) float sD1[BM];
+  __shared__ __attribute__((aligned(16))) uint16_t sdSt[BN * BM];  // dS'^T [key][query], dst_off()
+  // Raw LSE and Delta rows of the query block (LDS-DMA, one per buffer; the
+  // 64-lane load also fills the 32 entries past the block, unused).
+  __shared__ __attribute__((aligned(16))) float sL0[64];
+  __shared__ __attribute__((aligned(16))) float sL1[64];
+  __shared__ __attribute__((aligned(16))) float sD0[64];
+  __shared__ __attribute__((aligned(16))) float sD1[64];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (scalar)
-  const int kw = w & 3;   // this wave's keys: 32kw .. 32kw+31 of the block
-  const int qh = w >> 2;  // this wave's queries: 32qh .. 32qh+31 of each query block
-  const int hi = lane >> 5, l32 = lane & 31, L = lane & 15, Gp = (lane >> 4) & 1;
+  const int hi = lane >> 5, l32 = lane & 31;
   const int S = p.S, Hq = p.Hq, G = p.G, Hkv = p.Hkv;
   const int n_nblk = (S + BN - 1) / BN;
 
@@ -111,7 +134,7 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
 
   const float c = p.scale * kLog2e;
   const float lsc = p.log2_scale;
-  const int m_begin = CAUSAL ? n0 : 0;               // n0 is a multiple of BM
+  const int m_begin = CAUSAL ? n0 : 0;  // n0 is a multiple of BM
   const int n_steps = (S - m_begin + BM - 1) / BM;
 
   // LSE and Delta of a query block land in LDS as raw fp32 rows (waves 0
@@ -121,17 +144,24 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     if (w == 0) row_load_async(lse_b + m0, S - m0, l_dst, lane);
     if (w == 1) row_load_async(dl_b + m0, S - m0, d_dst, lane);
   };
-  // Key/value block (resident for the whole sweep) and the first Q/dO block.
+  // Key block (resident for the whole sweep) and the first Q/dO block.
   tile_load_async<D, BN, NW>(Kb, kvrs, n0, S, sK, w, lane);
-  tile_load_async<D, BN, NW>(Vb, kvrs, n0, S, sV, w, lane);
   tile_load_async<D, BM, NW>(Qb, qrs, m_begin, S, sQ0, w, lane);
   tile_load_async<D, BM, NW>(dOb, qrs, m_begin, S, sdO0, w, lane);
   load_rows(m_begin, sL0, sD0);
-
-  // dQ tile of this wave: queries 32*dq_mt.., d 32*dq_nt.. (D=64 uses waves 0-3).
-  const int dq_mt = (D == 128) ? qh : (w >> 1);
-  const int dq_nt = (D == 128) ? kw : (w & 1);
-  const bool dq_wave = (D == 128) || (w < 4);
+  // This wave's keys: n0 + 32w + l32.  Its V rows are the B operand of dP
+  // (lane l: V[key][16ks + 8hi .. +7]) and stay in registers; keys past the
+  // end read the last row (their P is masked to zero).  The first step
+  // waits for every load anyway; waiting here, before the loop, lets the
+  // compiler see that V is ready inside it.
+  const int key_l = n0 + 32 * w + l32;
+  bf16x8 vb[NKS];
+  {
+    const uint16_t* vrow = Vb + (size_t)min(key_l, S - 1) * kvrs + 8 * hi;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ks++) vb[ks] = *reinterpret_cast<const bf16x8*>(vrow + 16 * ks);
+  }
+  wait_vmem();
 
   f32x16 dk[NDT], dv[NDT];
 #pragma unroll
@@ -139,34 +169,38 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     dk[dt] = f32x16{};
     dv[dt] = f32x16{};
   }
-  const int key_l = n0 + 32 * kw + l32;
-  const int dq_d = 32 * dq_nt + l32;
+
+  // dQ tiles of this wave: d columns 16dq_dt .., query tiles dq_qt0 ...
+  const int dq_dt = (D == 128) ? w : (w & 3);
+  const int dq_qt0 = (D == 128) ? 0 : (w >> 2);
   // dQ accumulator and partials are head-major ([.., B, Hq, S, D]): the rows
-  // of one query block are one contiguous run.
+  // of one query block are one contiguous run.  16x16 result element j of
+  // lane l is query 16qt + 4(l/16) + j, d 16dq_dt + l%16.
   const uint32_t row_bytes = (uint32_t)D * 4u;
-  const uint32_t dq_voff = (uint32_t)(4 * hi) * row_bytes + (uint32_t)dq_d * 4u;
+  const uint32_t dq_voff = (uint32_t)(4 * (lane >> 4)) * row_bytes + (uint32_t)(16 * dq_dt + (lane & 15)) * 4u;
   const size_t nq = (size_t)p.B * S * Hq * D;
+  constexpr int NEMIT = 4 * NQT;  // atomics / stores per wave per block
 
   // dQ of a full query block leaves the workgroup during the *next* step,
-  // spread over its S/dP products, so that the 16 atomics/stores per wave
-  // overlap compute instead of arriving in one burst.  dq_prev holds it.
-  f32x16 dq_prev = f32x16{};
+  // spread over its S/dP products, so that the atomics/stores overlap
+  // compute instead of arriving in one burst.  dq_prev holds it.
+  f32x4 dq_prev[NQT];
+#pragma unroll
+  for (int i = 0; i < NQT; i++) dq_prev[i] = f32x4{};
   auto dq_rsrc = [&](int m0) {
     const size_t blk_off = ((size_t)(b * Hq + h) * S + m0) * D;
     float* dst_base = ATOMIC ? p.dq_accum + blk_off : p.dq_part + (size_t)jb * nq + blk_off;
     return buffer_rsrc(dst_base, (uint32_t)BM * row_bytes);
   };
-  // Rows j0 .. j0+3 of a dQ tile (element j: row 32dq_mt + 8(j/4) + 4hi + j%4).
-  auto dq_emit4 = [&](const __amdgpu_buffer_rsrc_t& rs, const f32x16& v, int j0) {
+  // Emission e (0 .. NEMIT-1): element e % 4 of tile e / 4.
+  auto dq_emit = [&](const __amdgpu_buffer_rsrc_t& rs, int e) {
     const uint32_t rb = opaque(row_bytes);
-#pragma unroll
-    for (int j = j0; j < j0 + 4; j++) {
-      const uint32_t so = (uint32_t)(32 * dq_mt + 8 * (j >> 2) + (j & 3)) * rb;
-      if (ATOMIC)
-        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v[j], rs, dq_voff, so, 0);
-      else
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[j]), rs, dq_voff, so, 0);
-    }
+    const int i = e >> 2, j = e & 3;
+    const uint32_t so = (uint32_t)(16 * (dq_qt0 + i) + j) * rb;
+    if (ATOMIC)
+      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(dq_prev[i][j], rs, dq_voff, so, 0);
+    else
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dq_prev[i][j]), rs, dq_voff, so, 0);
   };
 
   // One query block; BUF selects the LDS buffers it reads (the other pair
@@ -182,11 +216,10 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     float* nL = BUF ? sL0 : sL1;
     float* nD = BUF ? sD0 : sD1;
     const int m0 = m_begin + st * BM;
-    // Block st resident.  From step 2 on, the 16 deferred dQ atomics/stores
-    // a dQ wave issued during step st-1 came after those loads and may stay
-    // in flight.
-    if (dq_wave && st > 1)
-      wait_vmem_but<16>();
+    // Block st resident.  From step 2 on, the deferred dQ atomics/stores
+    // issued during step st-1 came after those loads and may stay in flight.
+    if (st > 1)
+      wait_vmem_but<NEMIT>();
     else
       wait_vmem();
     lds_barrier();  // block st resident; every wave is done with step st-1
@@ -200,121 +233,143 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     // with XORs of column moves and additions of 16-row moves (see xslot()).
     const int ln = opaque_v(lane);
     const int lhi = ln >> 5, ll32 = ln & 31, lL = ln & 15, tcol = 16 * ((ln >> 4) & 1) + 4 * (lL & 3);
-    const int offR = swz_off<D>(ll32, 8 * lhi);                    // 16-byte row reads, row l32
-    const int offT0 = swz_off<D>(4 * lhi + (lL >> 2), tcol);        // transposing reads of Q / dO
+    const int offR = swz_off<D>(ll32, 8 * lhi);                // 16-byte row reads, row l32
+    const int offT0 = swz_off<D>(4 * lhi + (lL >> 2), tcol);    // transposing reads of Q / dO
     const int offT1 = swz_off<D>(4 * lhi + (lL >> 2) + 8, tcol);
 
-    // S = Q K^T and dP = dO V^T for this wave's 32 queries x 32 keys.
-    // The previous block's dQ goes out meanwhile (16 rows, 4 per 2 k-steps).
-    const bool emit = dq_wave && st > 0;
+    // Keys n0 .. n0+n_vis-1 exist and see some query of this block.  A wave
+    // whose 32 keys lie past that has P = 0 throughout: it skips the four
+    // products, writes zeros as its rows of dS'^T and only takes part in dQ
+    // and the barriers.
+    const int n_vis = CAUSAL ? min(min(BN, S - n0), m0 + BM - n0) : min(BN, S - n0);
+    const bool active = 32 * w < n_vis;
+    const bool emit = st > 0;
     const __amdgpu_buffer_rsrc_t prs = dq_rsrc(max(m0 - BM, 0));
-    f32x16 s = f32x16{}, dp = f32x16{};
+    if (active) {
+      // S = Q K^T and dP = dO V^T for the block's 32 queries x this wave's
+      // 32 keys.  The previous block's dQ goes out meanwhile.
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < NKS; ks++) {
-      const int oq = xslot(offR, 16 * ks) + 32 * qh * D;
-      const int ok = xslot(offR, 16 * ks) + 32 * kw * D;
-      s = mfma32(lds_read_b128(cQ + oq), lds_read_b128(sK + ok), s);
-      dp = mfma32(lds_read_b128(cdO + oq), lds_read_b128(sV + ok), dp);
-      if (ks & 1) {
-        if (emit && (ks >> 1) < 4) dq_emit4(prs, dq_prev, 4 * (ks >> 1));
-        // Bound how far ahead the scheduler hoists operand reads (each one
-        // holds 4 VGPRs until its MFMA issues).
-        __builtin_amdgcn_sched_barrier(0);
+      for (int ks = 0; ks < NKS; ks++) {
+        const int oq = xslot(offR, 16 * ks);
+        s = mfma32(lds_read_b128(cQ + oq), lds_read_b128(sK + oq + 32 * w * D), s);
+        dp = mfma32(lds_read_b128(cdO + oq), vb[ks], dp);
+        if (emit)
+          for (int e = ks * NEMIT / NKS; e < (ks + 1) * NEMIT / NKS; e++) dq_emit(prs, e);
+        if (ks & 1) __builtin_amdgcn_sched_barrier(0);
       }
-    }
-    if (NKS < 8 && emit)  // D = 64: four k-steps carried half of the rows
-      for (int j0 = 4 * (NKS / 2); j0 < 16; j0 += 4) dq_emit4(prs, dq_prev, j0);
 
-    // P' = scale P and dS' = scale dS.  Element j of lane l is query
-    // 32qh + 8(j/4) + 4hi + j%4 of the block, key 32kw + l32.
-    const bool need_mask = (n0 + BN > S) || (m0 + BM > S) || (CAUSAL && m0 < n0 + BN);
-    // This lane's key is hidden from block queries below qlim (all of them
-    // for keys past the end, the earlier ones under causal masking) and from
-    // queries at or past qend (rows past the end of the sequence).
-    const int qlim = key_l >= S ? BM : (CAUSAL ? key_l - m0 : -1);
-    const int qend = S - m0;
-    uint32_t pp[8], dd[8];
+      // P' = scale P and dS' = scale dS.  Element j of lane l is query
+      // 8(j/4) + 4hi + j%4 of the block, key 32w + l32.
+      const bool need_mask = (n0 + BN > S) || (m0 + BM > S) || (CAUSAL && m0 < n0 + BN);
+      // This lane's key is hidden from block queries below qlim (all of
+      // them for keys past the end, the earlier ones under causal masking)
+      // and from queries at or past qend (rows past the end of the sequence).
+      // Both limits are taken relative to 4hi, so that the per-element
+      // query index becomes a constant.
+      const int key_e = n0 + 32 * w + ll32;
+      const int qlim = (key_e >= S ? BM : (CAUSAL ? key_e - m0 : -1)) - 4 * lhi;
+      const int qend = S - m0 - 4 * lhi;
+      const float* lrow = cL + 4 * lhi;
+      const float* drow = cDl + 4 * lhi;
+      uint32_t pp[8], dd[8];
 #pragma unroll
-    for (int jg = 0; jg < 4; jg++) {
-      const int qo = 32 * qh + 8 * jg + 4 * hi;
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(cL + qo) * kLog2e - lsc;
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(cDl + qo);
-      float pv[4], dv4[4];
+      for (int jg = 0; jg < 4; jg++) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lrow + 8 * jg) * kLog2e - lsc;
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(drow + 8 * jg);
+        float pv[4], dv4[4];
 #pragma unroll
-      for (int jj = 0; jj < 4; jj++) {
-        const int j = 4 * jg + jj;
-        float e = __builtin_amdgcn_exp2f(fmaf(s[j], c, -l4[jj]));
-        if (need_mask && (qo + jj < qlim || qo + jj >= qend)) e = 0.f;
-        pv[jj] = e;
-        dv4[jj] = e * (dp[j] - d4[jj]);
+        for (int jj = 0; jj < 4; jj++) {
+          const int j = 4 * jg + jj;
+          float e = __builtin_amdgcn_exp2f(fmaf(s[j], c, -l4[jj]));
+          if (need_mask && (8 * jg + jj < qlim || 8 * jg + jj >= qend)) e = 0.f;
+          pv[jj] = e;
+          dv4[jj] = e * (dp[j] - d4[jj]);
+        }
+        pp[2 * jg] = pack_bf16x2(pv[0], pv[1]);
+        pp[2 * jg + 1] = pack_bf16x2(pv[2], pv[3]);
+        dd[2 * jg] = pack_bf16x2(dv4[0], dv4[1]);
+        dd[2 * jg + 1] = pack_bf16x2(dv4[2], dv4[3]);
       }
-      pp[2 * jg] = pack_bf16x2(pv[0], pv[1]);
-      pp[2 * jg + 1] = pack_bf16x2(pv[2], pv[3]);
-      dd[2 * jg] = pack_bf16x2(dv4[0], dv4[1]);
-      dd[2 * jg + 1] = pack_bf16x2(dv4[2], dv4[3]);
-    }
-    // dS'^T to LDS as [key][query] (a 64-wide swizzled tile): four
-    // consecutive queries per 8-byte write.
-    {
-      const int offW = swz_off<BM>(32 * kw + ll32, 32 * qh + 4 * lhi);
+      // dS'^T to LDS as [key][query]: four consecutive queries per 8-byte
+      // write.
+      {
+        const int offW = dst_off(32 * w + ll32, 4 * lhi);
 #pragma unroll
-      for (int jg = 0; jg < 4; jg++)
-        lds_store_b64_asm(sdSt + xslot(offW, 8 * jg), u32x2{dd[2 * jg], dd[2 * jg + 1]});
-    }
-    // dV += P'^T dO and dK += dS'^T Q over this wave's 32 queries; the B
-    // operands are columns of dO and Q, fetched with transposing LDS reads
-    // in the query order of pp/dd.
-#pragma unroll
-    for (int k2 = 0; k2 < 2; k2++) {
-      const int kq = 2 * qh + k2, o4 = 4 * k2;
-      const bf16x8 pa = __builtin_bit_cast(bf16x8, u32x4{pp[o4], pp[o4 + 1], pp[o4 + 2], pp[o4 + 3]});
-      const bf16x8 da = __builtin_bit_cast(bf16x8, u32x4{dd[o4], dd[o4 + 1], dd[o4 + 2], dd[o4 + 3]});
-#pragma unroll
-      for (int dt = 0; dt < NDT; dt++) {
-        const int o1 = xslot(offT0, 32 * dt) + 16 * kq * D, o2 = xslot(offT1, 32 * dt) + 16 * kq * D;
-        dv[dt] = mfma32(pa, lds_read_tr8(cdO + o1, cdO + o2), dv[dt]);
-        dk[dt] = mfma32(da, lds_read_tr8(cQ + o1, cQ + o2), dk[dt]);
-        if (dt & 1) __builtin_amdgcn_sched_barrier(0);
+        for (int jg = 0; jg < 4; jg++)
+          lds_store_b64_asm(sdSt + xslot(offW, 8 * jg), u32x2{dd[2 * jg], dd[2 * jg + 1]});
       }
+      // dV += P'^T dO and dK += dS'^T Q over the block's 32 queries; the B
+      // operands are columns of dO and Q, fetched with transposing LDS reads
+      // in the query order of pp/dd.
+#pragma unroll
+      for (int k2 = 0; k2 < 2; k2++) {
+        const int o4 = 4 * k2;
+        const bf16x8 pa = __builtin_bit_cast(bf16x8, u32x4{pp[o4], pp[o4 + 1], pp[o4 + 2], pp[o4 + 3]});
+        const bf16x8 da = __builtin_bit_cast(bf16x8, u32x4{dd[o4], dd[o4 + 1], dd[o4 + 2], dd[o4 + 3]});
+#pragma unroll
+        for (int dt = 0; dt < NDT; dt++) {
+          const int o1 = xslot(offT0, 32 * dt) + 16 * k2 * D, o2 = xslot(offT1, 32 * dt) + 16 * k2 * D;
+          dv[dt] = mfma32(pa, lds_read_tr8(cdO + o1, cdO + o2), dv[dt]);
+          dk[dt] = mfma32(da, lds_read_tr8(cQ + o1, cQ + o2), dk[dt]);
+          if (dt & 1) __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    } else {
+      // Zero rows of dS'^T, so that the dQ product can run over all keys.
+      const int offW = dst_off(32 * w + ll32, 4 * lhi);
+#pragma unroll
+      for (int jg = 0; jg < 4; jg++) lds_store_b64_asm(sdSt + xslot(offW, 8 * jg), u32x2{0u, 0u});
+      if (emit)
+#pragma unroll
+        for (int e = 0; e < NEMIT; e++) dq_emit(prs, e);
     }
     lds_barrier();  // dS'^T complete in LDS
 
-    // dQ' (64 x D) = dS' (64 x 128 keys) K (128 keys x D), one 32x32 tile
-    // per wave.
-    if (dq_wave) {
-      const int offK0 = swz_off<D>(8 * lhi + (lL >> 2), 32 * dq_nt + tcol);      // transposing reads of K
-      const int offK1 = swz_off<D>(8 * lhi + (lL >> 2) + 4, 32 * dq_nt + tcol);
-      const int offS0 = swz_off<BM>(8 * lhi + (lL >> 2), 32 * dq_mt + tcol);     // ... of dS'^T
-      const int offS1 = swz_off<BM>(8 * lhi + (lL >> 2) + 4, 32 * dq_mt + tcol);
-      f32x16 dq = f32x16{};
+    // dQ' (32 x D) = dS' (32 x 256 keys) K (256 keys x D) as 16x16 tiles.
+    {
+      const int lg = lL >> 2, lc = lL & 3, lg4 = ln >> 4;  // e, c, group of the 16x16 layout
+      const int offK0 = swz_off<D>(8 * lg4 + lg, 16 * dq_dt + 4 * lc);        // transposing reads of K
+      const int offK1 = swz_off<D>(8 * lg4 + lg + 4, 16 * dq_dt + 4 * lc);
+      const int offS0 = dst_off(8 * lg4 + lg, 16 * dq_qt0 + 4 * lc);          // ... of dS'^T
+      const int offS1 = dst_off(8 * lg4 + lg + 4, 16 * dq_qt0 + 4 * lc);
+      f32x4 dq[NQT];
 #pragma unroll
-      for (int kk = 0; kk < BN / 16; kk++) {
-        const bf16x8 bk = lds_read_tr8(sK + offK0 + 16 * kk * D, sK + offK1 + 16 * kk * D);
-        const bf16x8 as = lds_read_tr8(sdSt + offS0 + 16 * kk * BM, sdSt + offS1 + 16 * kk * BM);
-        dq = mfma32(as, bk, dq);
+      for (int i = 0; i < NQT; i++) dq[i] = f32x4{};
+#pragma unroll
+      for (int kk = 0; kk < BN / 32; kk++) {
+        const bf16x8 bk = lds_read_tr8(sK + offK0 + 32 * kk * D, sK + offK1 + 32 * kk * D);
+#pragma unroll
+        for (int i = 0; i < NQT; i++) {
+          const bf16x8 as = lds_read_tr8(sdSt + xslot(offS0, 16 * i) + 32 * kk * BM,
+                                         sdSt + xslot(offS1, 16 * i) + 32 * kk * BM);
+          dq[i] = mfma16(as, bk, dq[i]);
+        }
         if (kk & 1) __builtin_amdgcn_sched_barrier(0);
       }
-      // Element j of dq is query 32dq_mt + 8(j/4) + 4hi + j%4, d = dq_d.
       if (m0 + BM <= S) {
-        dq_prev = dq;  // written during the next step, or after the loop
+#pragma unroll
+        for (int i = 0; i < NQT; i++) dq_prev[i] = dq[i];  // written during the next step, or after the loop
       } else {
         // Last, partial block: written now, row by row (addresses derived
         // here, not kept live).
         const size_t blk_off = ((size_t)(b * Hq + h) * S + m0) * D;
         float* dst_base = ATOMIC ? p.dq_accum + blk_off : p.dq_part + (size_t)jb * nq + blk_off;
         const int lt = opaque_v(lane);
-        const int thi = lt >> 5, td = 32 * dq_nt + (lt & 31);
+        const int tg = lt >> 4, td = 16 * dq_dt + (lt & 15);
 #pragma unroll
-        for (int j = 0; j < 16; j++) {
-          const int qr = 32 * dq_mt + 8 * (j >> 2) + 4 * thi + (j & 3);
-          if (m0 + qr < S) {
-            float* a = dst_base + (size_t)qr * D + td;
-            if (ATOMIC)
-              unsafeAtomicAdd(a, dq[j]);
-            else
-              *a = dq[j];
+        for (int i = 0; i < NQT; i++)
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            const int qr = 16 * (dq_qt0 + i) + 4 * tg + j;
+            if (m0 + qr < S) {
+              float* a = dst_base + (size_t)qr * D + td;
+              if (ATOMIC)
+                unsafeAtomicAdd(a, dq[i][j]);
+              else
+                *a = dq[i][j];
+            }
           }
-        }
       }
     }
   };
@@ -325,50 +380,32 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
   }
   // The last block's dQ, if it was a full block, is still held.
   const int m_last = m_begin + (n_steps - 1) * BM;
-  if (dq_wave && m_last + BM <= S) {
+  if (m_last + BM <= S) {
     const __amdgpu_buffer_rsrc_t rs = dq_rsrc(m_last);
 #pragma unroll
-    for (int j0 = 0; j0 < 16; j0 += 4) dq_emit4(rs, dq_prev, j0);
+    for (int e = 0; e < NEMIT; e++) dq_emit(rs, e);
   }
 
-  // The two query halves hold partial dK/dV of the same keys: the second
-  // half hands its accumulators over through LDS (key quarters 0-1 in the K
-  // block, 2-3 in the V block, free after the loop) in the MFMA result
-  // layout, and the first half adds and stores.  Element j of lane l is key
-  // 32kw + 8(j/4) + 4hi + j%4, d = 32dt + l32.
-  static_assert(2 * NDT * 16 * 64 * sizeof(float) <= BN * D * sizeof(uint16_t), "hand-over space");
-  float* xch = reinterpret_cast<float*>(kw < 2 ? sK : sV) + (kw & 1) * (NDT * 16 * 64);
+  // Each wave holds the complete dK/dV of its 32 keys.  Element j of lane l
+  // of tile dt is key 32w + 8(j/4) + 4hi + j%4, d = 32dt + l32.
   const float inv_scale = 1.f / p.scale;
   const int le = opaque_v(lane);  // output addresses derived here, not kept live
   const int ehi = le >> 5, el32 = le & 31;
 #pragma unroll
-  for (int tensor = 0; tensor < 2; tensor++) {
-    lds_barrier();
-    if (qh == 1) {
+  for (int dt = 0; dt < NDT; dt++) {
+    const int d = 32 * dt + el32;
 #pragma unroll
-      for (int dt = 0; dt < NDT; dt++)
-#pragma unroll
-        for (int j = 0; j < 16; j++) xch[(dt * 16 + j) * 64 + le] = tensor == 0 ? dk[dt][j] : dv[dt][j];
-    }
-    lds_barrier();
-    if (qh == 0) {
-#pragma unroll
-      for (int dt = 0; dt < NDT; dt++) {
-        const int d = 32 * dt + el32;
-#pragma unroll
-        for (int j = 0; j < 16; j++) {
-          const float v = (tensor == 0 ? dk[dt][j] : dv[dt][j]) + xch[(dt * 16 + j) * 64 + le];
-          const float out = tensor == 0 ? v : v * inv_scale;
-          const int key = n0 + 32 * kw + 8 * (j >> 2) + 4 * ehi + (j & 3);
-          if (key < S) {
-            if (PARTIAL) {
-              const size_t off = ((size_t)(b * S + key) * Hq + h) * D + d;
-              (tensor == 0 ? p.dk_part : p.dv_part)[off] = out;
-            } else {
-              const size_t off = ((size_t)(b * S + key) * Hkv + kvh) * D + d;
-              (tensor == 0 ? p.dk : p.dv)[off] = to_bf16(out);
-            }
-          }
+    for (int j = 0; j < 16; j++) {
+      const int key = n0 + 32 * w + 8 * (j >> 2) + 4 * ehi + (j & 3);
+      if (key < S) {
+        if (PARTIAL) {
+          const size_t off = ((size_t)(b * S + key) * Hq + h) * D + d;
+          p.dk_part[off] = dk[dt][j];
+          p.dv_part[off] = dv[dt][j] * inv_scale;
+        } else {
+          const size_t off = ((size_t)(b * S + key) * Hkv + kvh) * D + d;
+          p.dk[off] = to_bf16(dk[dt][j]);
+          p.dv[off] = to_bf16(dv[dt][j] * inv_scale);
         }
       }
     }

@@ -18,6 +18,13 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// D = A(16x32) * B(32x16) + C, bf16 in, fp32 accumulate.  Lane l (r = l % 16,
+// g = l / 16) supplies A[r][8g .. 8g+7] and B[8g .. 8g+7][r]; result element j
+// of lane l is C[4g + j][r].
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 // D = A(32x16) * B(16x32) + C on the matrix cores, bf16 in, fp32 accumulate.
 // Lane l (r = l % 32, g = l / 32) supplies A[r][8g .. 8g+7] and B[8g .. 8g+7][r];
 // result element j of lane l is C[8*(j/4) + 4*g + j%4][r].
@@ -124,14 +131,15 @@ __device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(void*
 // bf16 matrix with row stride rs elements into a swizzled tile.  Rows at or
 // past `nrows` read row nrows - 1 instead (callers mask them); every source
 // address is therefore inside the matrix.  Each wave instruction moves 1 KB;
-// the NW waves of the workgroup split the tile.  Completion: vmcnt.
+// the NW waves of the workgroup split the tile (waves w >= R*D/512 issue
+// nothing when the tile is smaller than NW KB).  Completion: vmcnt.
 template <int D, int R, int NW = 4>
 __device__ __forceinline__ void tile_load_async(const uint16_t* g, size_t rs, int row0, int nrows,
                                                 uint16_t* tile, int w, int lane) {
   constexpr int CPR = D / 8;       // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;    // rows per wave instruction
   constexpr int NI = R / RPI;      // wave instructions per tile
-  static_assert(NI % NW == 0, "tile must split evenly over the waves");
+  static_assert(NI % NW == 0 || NI < NW, "tile must split evenly over the waves");
   const int rl = lane / CPR, slot = lane % CPR;
   const uint16_t* base = g + (size_t)row0 * rs;  // wave-uniform
   const int last = nrows - 1 - row0;

@@ -9,7 +9,7 @@ namespace mi355 {
 
 // Key-block height of the backward kernel; the split dQ path keeps one fp32
 // dQ partial per block of this many keys.
-constexpr int kBwdBlockN = 128;
+constexpr int kBwdBlockN = 256;
 
 struct FwdParams {
   const uint16_t* q;

@@ -95,7 +95,8 @@ int attn_bwd_preprocess(const uint16_t* o, const uint16_t* dout, float* delta, f
  * Bytes of device workspace attn_bwd and attn_bwd_postprocess need for this
  * problem (0 when none is needed).  Layout, for reference only:
  *   groups > 1: fp32 per-query-head dK and dV partials, [B,S,Hq,D] each;
- *   use_atomic == 0: fp32 per-KV-block dQ partials, [n_kv_blocks,B,Hq,S,D].
+ *   use_atomic == 0: fp32 per-KV-block dQ partials, [n_kv_blocks,B,Hq,S,D],
+ *     n_kv_blocks = ceil(S / 256) (the backward kernel's key-block height).
  * Returns 0 for an invalid shape.
  */
 size_t attn_bwd_workspace_bytes(attn_shape shape, int causal, int use_atomic);
