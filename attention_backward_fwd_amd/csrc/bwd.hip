@@ -84,19 +84,23 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
 
   // Separate LDS objects, so that the compiler can tell the block being
   // loaded (LDS-DMA in flight) from the block being read and does not wait
-  // for the former before reading the latter.
+  // for the former before reading the latter.  The compiler places objects
+  // of larger alignment first: the query-block tiles, dS'^T and the rows go
+  // below 64 KB, where their addresses fit the LDS instructions' offset
+  // field, and the K block above them.  The 1 KB alignment also lets the
+  // swizzles be applied as XORs on whole LDS addresses.
   __shared__ __attribute__((aligned(16))) uint16_t sK[BN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sQ0[TQ];
-  __shared__ __attribute__((aligned(16))) uint16_t sQ1[TQ];
-  __shared__ __attribute__((aligned(16))) uint16_t sdO0[TQ];
-  __shared__ __attribute__((aligned(16))) uint16_t sdO1[TQ];
-  __shared__ __attribute__((aligned(16))) uint16_t sdSt[BN * BM];  // dS'^T [key][query], dst_off()
+  __shared__ __attribute__((aligned(1024))) uint16_t sQ0[TQ];
+  __shared__ __attribute__((aligned(1024))) uint16_t sQ1[TQ];
+  __shared__ __attribute__((aligned(1024))) uint16_t sdO0[TQ];
+  __shared__ __attribute__((aligned(1024))) uint16_t sdO1[TQ];
+  __shared__ __attribute__((aligned(1024))) uint16_t sdSt[BN * BM];  // dS'^T [key][query], dst_off()
   // Raw LSE and Delta rows of the query block (LDS-DMA, one per buffer; the
   // 64-lane load also fills the 32 entries past the block, unused).
-  __shared__ __attribute__((aligned(16))) float sL0[64];
-  __shared__ __attribute__((aligned(16))) float sL1[64];
-  __shared__ __attribute__((aligned(16))) float sD0[64];
-  __shared__ __attribute__((aligned(16))) float sD1[64];
+  __shared__ __attribute__((aligned(1024))) float sL0[64];
+  __shared__ __attribute__((aligned(1024))) float sL1[64];
+  __shared__ __attribute__((aligned(1024))) float sD0[64];
+  __shared__ __attribute__((aligned(1024))) float sD1[64];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (scalar)
@@ -181,26 +185,20 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
   const size_t nq = (size_t)p.B * S * Hq * D;
   constexpr int NEMIT = 4 * NQT;  // atomics / stores per wave per block
 
-  // dQ of a full query block leaves the workgroup during the *next* step,
-  // spread over its S/dP products, so that the atomics/stores overlap
-  // compute instead of arriving in one burst.  dq_prev holds it.
-  f32x4 dq_prev[NQT];
-#pragma unroll
-  for (int i = 0; i < NQT; i++) dq_prev[i] = f32x4{};
   auto dq_rsrc = [&](int m0) {
     const size_t blk_off = ((size_t)(b * Hq + h) * S + m0) * D;
     float* dst_base = ATOMIC ? p.dq_accum + blk_off : p.dq_part + (size_t)jb * nq + blk_off;
     return buffer_rsrc(dst_base, (uint32_t)BM * row_bytes);
   };
-  // Emission e (0 .. NEMIT-1): element e % 4 of tile e / 4.
-  auto dq_emit = [&](const __amdgpu_buffer_rsrc_t& rs, int e) {
+  // Element e % 4 of dQ tile e / 4 (e < NEMIT) to the block's rows.
+  auto dq_emit = [&](const __amdgpu_buffer_rsrc_t& rs, const f32x4* v, int e) {
     const uint32_t rb = opaque(row_bytes);
     const int i = e >> 2, j = e & 3;
     const uint32_t so = (uint32_t)(16 * (dq_qt0 + i) + j) * rb;
     if (ATOMIC)
-      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(dq_prev[i][j], rs, dq_voff, so, 0);
+      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v[i][j], rs, dq_voff, so, 0);
     else
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dq_prev[i][j]), rs, dq_voff, so, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[i][j]), rs, dq_voff, so, 0);
   };
 
   // One query block; BUF selects the LDS buffers it reads (the other pair
@@ -216,9 +214,9 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     float* nL = BUF ? sL0 : sL1;
     float* nD = BUF ? sD0 : sD1;
     const int m0 = m_begin + st * BM;
-    // Block st resident.  From step 2 on, the deferred dQ atomics/stores
-    // issued during step st-1 came after those loads and may stay in flight.
-    if (st > 1)
+    // Block st resident.  The dQ atomics/stores that ended step st-1 came
+    // after those loads and may stay in flight.
+    if (st > 0)
       wait_vmem_but<NEMIT>();
     else
       wait_vmem();
@@ -228,14 +226,14 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
       tile_load_async<D, BM, NW>(dOb, qrs, m0 + BM, S, ndO, w, lane);
       load_rows(m0 + BM, nL, nD);
     }
-    // Per-lane LDS element offsets, recomputed from the lane id every step
+    // Per-lane LDS byte offsets, recomputed from the lane id every step
     // rather than kept live across the loop; the loops below derive the rest
     // with XORs of column moves and additions of 16-row moves (see xslot()).
     const int ln = opaque_v(lane);
     const int lhi = ln >> 5, ll32 = ln & 31, lL = ln & 15, tcol = 16 * ((ln >> 4) & 1) + 4 * (lL & 3);
-    const int offR = swz_off<D>(ll32, 8 * lhi);                // 16-byte row reads, row l32
-    const int offT0 = swz_off<D>(4 * lhi + (lL >> 2), tcol);    // transposing reads of Q / dO
-    const int offT1 = swz_off<D>(4 * lhi + (lL >> 2) + 8, tcol);
+    const uint32_t offR = 2 * swz_off<D>(ll32, 8 * lhi);                // 16-byte row reads, row l32
+    const uint32_t offT0 = 2 * swz_off<D>(4 * lhi + (lL >> 2), tcol);    // transposing reads of Q / dO
+    const uint32_t offT1 = 2 * swz_off<D>(4 * lhi + (lL >> 2) + 8, tcol);
 
     // Keys n0 .. n0+n_vis-1 exist and see some query of this block.  A wave
     // whose 32 keys lie past that has P = 0 throughout: it skips the four
@@ -243,113 +241,152 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     // and the barriers.
     const int n_vis = CAUSAL ? min(min(BN, S - n0), m0 + BM - n0) : min(BN, S - n0);
     const bool active = 32 * w < n_vis;
-    const bool emit = st > 0;
-    const __amdgpu_buffer_rsrc_t prs = dq_rsrc(max(m0 - BM, 0));
     if (active) {
       // S = Q K^T and dP = dO V^T for the block's 32 queries x this wave's
-      // 32 keys.  The previous block's dQ goes out meanwhile.
+      // 32 keys.  Operands are read one k-step ahead of the products that
+      // use them.
       f32x16 s = f32x16{}, dp = f32x16{};
+      {
+        const uint16_t* kw_base = sK + 32 * w * D;
+        bf16x8 aq = lds_b128_at(cQ, offR), bk = lds_b128_at(kw_base, offR), ad = lds_b128_at(cdO, offR);
 #pragma unroll
-      for (int ks = 0; ks < NKS; ks++) {
-        const int oq = xslot(offR, 16 * ks);
-        s = mfma32(lds_read_b128(cQ + oq), lds_read_b128(sK + oq + 32 * w * D), s);
-        dp = mfma32(lds_read_b128(cdO + oq), vb[ks], dp);
-        if (emit)
-          for (int e = ks * NEMIT / NKS; e < (ks + 1) * NEMIT / NKS; e++) dq_emit(prs, e);
-        if (ks & 1) __builtin_amdgcn_sched_barrier(0);
+        for (int ks = 0; ks < NKS; ks++) {
+          bf16x8 aq1 = aq, bk1 = bk, ad1 = ad;
+          if (ks + 1 < NKS) {
+            const uint32_t oq = offR ^ (32u * (ks + 1));
+            aq1 = lds_b128_at(cQ, oq);
+            bk1 = lds_b128_at(kw_base, oq);
+            ad1 = lds_b128_at(cdO, oq);
+          }
+          s = mfma32(aq, bk, s);
+          dp = mfma32(ad, vb[ks], dp);
+          aq = aq1;
+          bk = bk1;
+          ad = ad1;
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
 
       // P' = scale P and dS' = scale dS.  Element j of lane l is query
       // 8(j/4) + 4hi + j%4 of the block, key 32w + l32.
-      const bool need_mask = (n0 + BN > S) || (m0 + BM > S) || (CAUSAL && m0 < n0 + BN);
-      // This lane's key is hidden from block queries below qlim (all of
-      // them for keys past the end, the earlier ones under causal masking)
-      // and from queries at or past qend (rows past the end of the sequence).
-      // Both limits are taken relative to 4hi, so that the per-element
-      // query index becomes a constant.
-      const int key_e = n0 + 32 * w + ll32;
-      const int qlim = (key_e >= S ? BM : (CAUSAL ? key_e - m0 : -1)) - 4 * lhi;
-      const int qend = S - m0 - 4 * lhi;
-      const float* lrow = cL + 4 * lhi;
-      const float* drow = cDl + 4 * lhi;
+      const uint32_t orow = 16 * lhi;  // byte offset of query 4hi in the LSE / Delta rows
       uint32_t pp[8], dd[8];
+      auto softmax_grad = [&](auto mask_tag, int qlim, int qend) {
+        constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
-      for (int jg = 0; jg < 4; jg++) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lrow + 8 * jg) * kLog2e - lsc;
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(drow + 8 * jg);
-        float pv[4], dv4[4];
+        for (int jg = 0; jg < 4; jg++) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(reinterpret_cast<const char*>(cL) + orow + 32 * jg) *
+                               kLog2e - lsc;
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(reinterpret_cast<const char*>(cDl) + orow + 32 * jg);
+          float pv[4], dv4[4];
 #pragma unroll
-        for (int jj = 0; jj < 4; jj++) {
-          const int j = 4 * jg + jj;
-          float e = __builtin_amdgcn_exp2f(fmaf(s[j], c, -l4[jj]));
-          if (need_mask && (8 * jg + jj < qlim || 8 * jg + jj >= qend)) e = 0.f;
-          pv[jj] = e;
-          dv4[jj] = e * (dp[j] - d4[jj]);
+          for (int jj = 0; jj < 4; jj++) {
+            const int j = 4 * jg + jj;
+            float e = __builtin_amdgcn_exp2f(fmaf(s[j], c, -l4[jj]));
+            if (MASK && (8 * jg + jj < qlim || 8 * jg + jj >= qend)) e = 0.f;
+            pv[jj] = e;
+            dv4[jj] = e * (dp[j] - d4[jj]);
+          }
+          pp[2 * jg] = pack_bf16x2(pv[0], pv[1]);
+          pp[2 * jg + 1] = pack_bf16x2(pv[2], pv[3]);
+          dd[2 * jg] = pack_bf16x2(dv4[0], dv4[1]);
+          dd[2 * jg + 1] = pack_bf16x2(dv4[2], dv4[3]);
         }
-        pp[2 * jg] = pack_bf16x2(pv[0], pv[1]);
-        pp[2 * jg + 1] = pack_bf16x2(pv[2], pv[3]);
-        dd[2 * jg] = pack_bf16x2(dv4[0], dv4[1]);
-        dd[2 * jg + 1] = pack_bf16x2(dv4[2], dv4[3]);
+      };
+      // Blocks on the causal diagonal or at either end of the sequence are
+      // masked.  This lane's key is hidden from block queries below qlim (all
+      // of them for keys past the end, the earlier ones under causal masking)
+      // and from queries at or past qend (rows past the end of the sequence);
+      // both limits are taken relative to 4hi, so that the per-element query
+      // index is a constant.
+      if ((n0 + BN > S) || (m0 + BM > S) || (CAUSAL && m0 < n0 + BN)) {
+        const int key_e = n0 + 32 * w + ll32;
+        const int qlim = (key_e >= S ? BM : (CAUSAL ? key_e - m0 : -1)) - 4 * lhi;
+        softmax_grad(std::true_type{}, qlim, S - m0 - 4 * lhi);
+      } else {
+        softmax_grad(std::false_type{}, 0, 0);
       }
       // dS'^T to LDS as [key][query]: four consecutive queries per 8-byte
       // write.
       {
-        const int offW = dst_off(32 * w + ll32, 4 * lhi);
+        const uint32_t aW = lds_addr(sdSt) + 2 * dst_off(32 * w + ll32, 4 * lhi);
 #pragma unroll
-        for (int jg = 0; jg < 4; jg++)
-          lds_store_b64_asm(sdSt + xslot(offW, 8 * jg), u32x2{dd[2 * jg], dd[2 * jg + 1]});
+        for (int jg = 0; jg < 4; jg++) lds_store_b64_addr(aW ^ (16u * jg), u32x2{dd[2 * jg], dd[2 * jg + 1]});
       }
       // dV += P'^T dO and dK += dS'^T Q over the block's 32 queries; the B
-      // operands are columns of dO and Q, fetched with transposing LDS reads
-      // in the query order of pp/dd.
+      // operands are columns of dO and Q, fetched (one product ahead) with
+      // transposing LDS reads in the query order of pp/dd.
+      {
+        auto tr_off = [&](int it, int which) {  // it = k2 * NDT + dt
+          const int k2 = it / NDT, dt = it % NDT;
+          return ((which ? offT1 : offT0) ^ (64u * dt)) + 32u * k2 * D;
+        };
+        bf16x8 bo = lds_tr8_at(cdO, tr_off(0, 0), tr_off(0, 1));
+        bf16x8 bq = lds_tr8_at(cQ, tr_off(0, 0), tr_off(0, 1));
 #pragma unroll
-      for (int k2 = 0; k2 < 2; k2++) {
-        const int o4 = 4 * k2;
-        const bf16x8 pa = __builtin_bit_cast(bf16x8, u32x4{pp[o4], pp[o4 + 1], pp[o4 + 2], pp[o4 + 3]});
-        const bf16x8 da = __builtin_bit_cast(bf16x8, u32x4{dd[o4], dd[o4 + 1], dd[o4 + 2], dd[o4 + 3]});
-#pragma unroll
-        for (int dt = 0; dt < NDT; dt++) {
-          const int o1 = xslot(offT0, 32 * dt) + 16 * k2 * D, o2 = xslot(offT1, 32 * dt) + 16 * k2 * D;
-          dv[dt] = mfma32(pa, lds_read_tr8(cdO + o1, cdO + o2), dv[dt]);
-          dk[dt] = mfma32(da, lds_read_tr8(cQ + o1, cQ + o2), dk[dt]);
-          if (dt & 1) __builtin_amdgcn_sched_barrier(0);
+        for (int it = 0; it < 2 * NDT; it++) {
+          bf16x8 bo1 = bo, bq1 = bq;
+          if (it + 1 < 2 * NDT) {
+            bo1 = lds_tr8_at(cdO, tr_off(it + 1, 0), tr_off(it + 1, 1));
+            bq1 = lds_tr8_at(cQ, tr_off(it + 1, 0), tr_off(it + 1, 1));
+          }
+          const int o4 = 4 * (it / NDT), dt = it % NDT;
+          const bf16x8 pa = __builtin_bit_cast(bf16x8, u32x4{pp[o4], pp[o4 + 1], pp[o4 + 2], pp[o4 + 3]});
+          const bf16x8 da = __builtin_bit_cast(bf16x8, u32x4{dd[o4], dd[o4 + 1], dd[o4 + 2], dd[o4 + 3]});
+          dv[dt] = mfma32(pa, bo, dv[dt]);
+          dk[dt] = mfma32(da, bq, dk[dt]);
+          bo = bo1;
+          bq = bq1;
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     } else {
       // Zero rows of dS'^T, so that the dQ product can run over all keys.
-      const int offW = dst_off(32 * w + ll32, 4 * lhi);
+      const uint32_t aW = lds_addr(sdSt) + 2 * dst_off(32 * w + ll32, 4 * lhi);
 #pragma unroll
-      for (int jg = 0; jg < 4; jg++) lds_store_b64_asm(sdSt + xslot(offW, 8 * jg), u32x2{0u, 0u});
-      if (emit)
-#pragma unroll
-        for (int e = 0; e < NEMIT; e++) dq_emit(prs, e);
+      for (int jg = 0; jg < 4; jg++) lds_store_b64_addr(aW ^ (16u * jg), u32x2{0u, 0u});
     }
     lds_barrier();  // dS'^T complete in LDS
 
     // dQ' (32 x D) = dS' (32 x 256 keys) K (256 keys x D) as 16x16 tiles.
     {
       const int lg = lL >> 2, lc = lL & 3, lg4 = ln >> 4;  // e, c, group of the 16x16 layout
-      const int offK0 = swz_off<D>(8 * lg4 + lg, 16 * dq_dt + 4 * lc);        // transposing reads of K
-      const int offK1 = swz_off<D>(8 * lg4 + lg + 4, 16 * dq_dt + 4 * lc);
-      const int offS0 = dst_off(8 * lg4 + lg, 16 * dq_qt0 + 4 * lc);          // ... of dS'^T
-      const int offS1 = dst_off(8 * lg4 + lg + 4, 16 * dq_qt0 + 4 * lc);
+      const uint32_t offK0 = 2 * swz_off<D>(8 * lg4 + lg, 16 * dq_dt + 4 * lc);  // transposing reads of K
+      const uint32_t offK1 = 2 * swz_off<D>(8 * lg4 + lg + 4, 16 * dq_dt + 4 * lc);
+      const uint32_t offS0 = 2 * dst_off(8 * lg4 + lg, 16 * dq_qt0 + 4 * lc);    // ... of dS'^T
+      const uint32_t offS1 = 2 * dst_off(8 * lg4 + lg + 4, 16 * dq_qt0 + 4 * lc);
       f32x4 dq[NQT];
 #pragma unroll
       for (int i = 0; i < NQT; i++) dq[i] = f32x4{};
+      // Operands are read one key slice ahead of the products.
+      auto rd_k = [&](int kk) { return lds_tr8_at(sK, offK0 + 64u * kk * D, offK1 + 64u * kk * D); };
+      auto rd_s = [&](int kk, int i) {
+        return lds_tr8_at(sdSt, (offS0 ^ (32u * i)) + 64u * kk * BM, (offS1 ^ (32u * i)) + 64u * kk * BM);
+      };
+      bf16x8 bk = rd_k(0), as[NQT];
+#pragma unroll
+      for (int i = 0; i < NQT; i++) as[i] = rd_s(0, i);
 #pragma unroll
       for (int kk = 0; kk < BN / 32; kk++) {
-        const bf16x8 bk = lds_read_tr8(sK + offK0 + 32 * kk * D, sK + offK1 + 32 * kk * D);
+        bf16x8 bk1 = bk, as1[NQT];
 #pragma unroll
-        for (int i = 0; i < NQT; i++) {
-          const bf16x8 as = lds_read_tr8(sdSt + xslot(offS0, 16 * i) + 32 * kk * BM,
-                                         sdSt + xslot(offS1, 16 * i) + 32 * kk * BM);
-          dq[i] = mfma16(as, bk, dq[i]);
+        for (int i = 0; i < NQT; i++) as1[i] = as[i];
+        if (kk + 1 < BN / 32) {
+          bk1 = rd_k(kk + 1);
+#pragma unroll
+          for (int i = 0; i < NQT; i++) as1[i] = rd_s(kk + 1, i);
         }
-        if (kk & 1) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NQT; i++) dq[i] = mfma16(as[i], bk, dq[i]);
+        bk = bk1;
+#pragma unroll
+        for (int i = 0; i < NQT; i++) as[i] = as1[i];
+        __builtin_amdgcn_sched_barrier(0);
       }
       if (m0 + BM <= S) {
+        const __amdgpu_buffer_rsrc_t rs = dq_rsrc(m0);
 #pragma unroll
-        for (int i = 0; i < NQT; i++) dq_prev[i] = dq[i];  // written during the next step, or after the loop
+        for (int e = 0; e < NEMIT; e++) dq_emit(rs, dq, e);
       } else {
         // Last, partial block: written now, row by row (addresses derived
         // here, not kept live).
@@ -378,14 +415,6 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     step(std::integral_constant<int, 0>{}, st);
     if (st + 1 < n_steps) step(std::integral_constant<int, 1>{}, st + 1);
   }
-  // The last block's dQ, if it was a full block, is still held.
-  const int m_last = m_begin + (n_steps - 1) * BM;
-  if (m_last + BM <= S) {
-    const __amdgpu_buffer_rsrc_t rs = dq_rsrc(m_last);
-#pragma unroll
-    for (int e = 0; e < NEMIT; e++) dq_emit(rs, e);
-  }
-
   // Each wave holds the complete dK/dV of its 32 keys.  Element j of lane l
   // of tile dt is key 32w + 8(j/4) + 4hi + j%4, d = 32dt + l32.
   const float inv_scale = 1.f / p.scale;

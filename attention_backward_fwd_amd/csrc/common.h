@@ -53,6 +53,18 @@ __device__ __forceinline__ bf16x8 lds_read_b128(const uint16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
 
+// The same reads at a byte offset from an LDS array.  The array's address is
+// a constant, which the compiler folds into the instruction's 16-bit offset
+// field when it fits, so that reads of different arrays at the same offset
+// share one address register.
+__device__ __forceinline__ bf16x8 lds_b128_at(const void* base, uint32_t boff) {
+  return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(base) + boff);
+}
+__device__ __forceinline__ bf16x8 lds_tr8_at(const void* base, uint32_t b0, uint32_t b1) {
+  const char* c = reinterpret_cast<const char*>(base);
+  return lds_read_tr8(reinterpret_cast<const uint16_t*>(c + b0), reinterpret_cast<const uint16_t*>(c + b1));
+}
+
 // Combine a per-lane value with the one held 32 lanes away (the other half of
 // the wavefront).  permlane32_swap(x, x) returns {own, other} in the lower half
 // and {other, own} in the upper half, so any symmetric operation of the pair
@@ -170,6 +182,13 @@ __device__ __forceinline__ void lds_store_b64_asm(uint16_t* p, u32x2 v) {
   const uint32_t addr = (uint32_t)(uintptr_t)lds_ptr(p);
   asm volatile("ds_write_b64 %0, %1" ::"v"(addr), "v"(v));
 }
+// Same, at an LDS byte address.
+__device__ __forceinline__ void lds_store_b64_addr(uint32_t addr, u32x2 v) {
+  asm volatile("ds_write_b64 %0, %1" ::"v"(addr), "v"(v));
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)lds_ptr(const_cast<void*>(p));
+}
 
 // Asynchronous global -> LDS copy of n <= 64 consecutive fp32 values (one per
 // lane, lanes >= n read the last one again) to lds[0 .. 63].
@@ -191,8 +210,16 @@ __device__ __forceinline__ void wait_vmem_but() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
+// Buffer resource for a wave-uniform base address.  The address goes
+// through readfirstlane so that the descriptor is known to be uniform and
+// lives in scalar registers (a descriptor the compiler believes divergent
+// turns every buffer instruction into a loop over distinct values).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* p = (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
 // Workgroups are handed to the 8 XCDs round-robin (id % 8).  This maps the
