@@ -94,7 +94,10 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
   __shared__ __attribute__((aligned(1024))) uint16_t sQ1[TQ];
   __shared__ __attribute__((aligned(1024))) uint16_t sdO0[TQ];
   __shared__ __attribute__((aligned(1024))) uint16_t sdO1[TQ];
-  __shared__ __attribute__((aligned(1024))) uint16_t sdSt[BN * BM];  // dS'^T [key][query], dst_off()
+  // dS'^T [key][query] (dst_off()), one per step parity: block i's tile is
+  // written in step i and read by the dQ product in step i + 1.
+  __shared__ __attribute__((aligned(1024))) uint16_t sdSt0[BN * BM];
+  __shared__ __attribute__((aligned(1024))) uint16_t sdSt1[BN * BM];
   // Raw LSE and Delta rows of the query block (LDS-DMA, one per buffer; the
   // 64-lane load also fills the 32 entries past the block, unused).
   __shared__ __attribute__((aligned(1024))) float sL0[64];
@@ -121,11 +124,14 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     t -= x * per;
     NGx = NG / 8;
   }
+  // (Integer division runs on the vector unit; readfirstlane returns the
+  // results to scalar registers, where everything derived from them stays.)
   const int per_group = n_nblk * G;
   const int grp = x * NGx + t / per_group;
-  const int jb = (t % per_group) / G;
+  const int jb = __builtin_amdgcn_readfirstlane((t % per_group) / G);
   const int r = t % G;
-  const int b = grp / Hkv, kvh = grp % Hkv, h = kvh * G + r;
+  const int b = __builtin_amdgcn_readfirstlane(grp / Hkv), kvh = __builtin_amdgcn_readfirstlane(grp % Hkv);
+  const int h = __builtin_amdgcn_readfirstlane(kvh * G + r);
   const int n0 = jb * BN;
 
   const size_t qrs = (size_t)Hq * D, kvrs = (size_t)Hkv * D;
@@ -201,8 +207,76 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[i][j]), rs, dq_voff, so, 0);
   };
 
+  // dQ' (32 x D) = dS' (32 x 256 keys) K (256 keys x D) of one block as
+  // 16x16 tiles, from the dS'^T tile `sdSt`.  Operands are read one key
+  // slice ahead of the products.
+  auto dq_block = [&](const uint16_t* sdSt, f32x4* dq) {
+    const int ln = opaque_v(lane);
+    const int lL = ln & 15, lg = lL >> 2, lc = lL & 3, lg4 = ln >> 4;  // e, c, group of the 16x16 layout
+    const uint32_t offK0 = 2 * swz_off<D>(8 * lg4 + lg, 16 * dq_dt + 4 * lc);  // transposing reads of K
+    const uint32_t offK1 = 2 * swz_off<D>(8 * lg4 + lg + 4, 16 * dq_dt + 4 * lc);
+    const uint32_t offS0 = 2 * dst_off(8 * lg4 + lg, 16 * dq_qt0 + 4 * lc);    // ... of dS'^T
+    const uint32_t offS1 = 2 * dst_off(8 * lg4 + lg + 4, 16 * dq_qt0 + 4 * lc);
+#pragma unroll
+    for (int i = 0; i < NQT; i++) dq[i] = f32x4{};
+    auto rd_k = [&](int kk) { return lds_tr8_at(sK, offK0 + 64u * kk * D, offK1 + 64u * kk * D); };
+    auto rd_s = [&](int kk, int i) {
+      return lds_tr8_at(sdSt, (offS0 ^ (32u * i)) + 64u * kk * BM, (offS1 ^ (32u * i)) + 64u * kk * BM);
+    };
+    bf16x8 bk = rd_k(0), as[NQT];
+#pragma unroll
+    for (int i = 0; i < NQT; i++) as[i] = rd_s(0, i);
+#pragma unroll
+    for (int kk = 0; kk < BN / 32; kk++) {
+      bf16x8 bk1 = bk, as1[NQT];
+#pragma unroll
+      for (int i = 0; i < NQT; i++) as1[i] = as[i];
+      if (kk + 1 < BN / 32) {
+        bk1 = rd_k(kk + 1);
+#pragma unroll
+        for (int i = 0; i < NQT; i++) as1[i] = rd_s(kk + 1, i);
+      }
+#pragma unroll
+      for (int i = 0; i < NQT; i++) dq[i] = mfma16(as[i], bk, dq[i]);
+      bk = bk1;
+#pragma unroll
+      for (int i = 0; i < NQT; i++) as[i] = as1[i];
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // dQ of the block at m0 leaves the workgroup: a full block as buffer
+  // atomics/stores, the last, partial one row by row (addresses derived
+  // here, not kept live).
+  auto dq_store = [&](int m0, const f32x4* dq) {
+    if (m0 + BM <= S) {
+      const __amdgpu_buffer_rsrc_t rs = dq_rsrc(m0);
+#pragma unroll
+      for (int e = 0; e < NEMIT; e++) dq_emit(rs, dq, e);
+    } else {
+      const size_t blk_off = ((size_t)(b * Hq + h) * S + m0) * D;
+      float* dst_base = ATOMIC ? p.dq_accum + blk_off : p.dq_part + (size_t)jb * nq + blk_off;
+      const int lt = opaque_v(lane);
+      const int tg = lt >> 4, td = 16 * dq_dt + (lt & 15);
+#pragma unroll
+      for (int i = 0; i < NQT; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const int qr = 16 * (dq_qt0 + i) + 4 * tg + j;
+          if (m0 + qr < S) {
+            float* a = dst_base + (size_t)qr * D + td;
+            if (ATOMIC)
+              unsafeAtomicAdd(a, dq[i][j]);
+            else
+              *a = dq[i][j];
+          }
+        }
+    }
+  };
+
   // One query block; BUF selects the LDS buffers it reads (the other pair
-  // receives the next block meanwhile).
+  // receives the next block meanwhile) and the dS'^T tile it writes.  It
+  // also computes and writes the dQ of the previous block from the other
+  // dS'^T tile, completed by the barrier that starts this step.
   auto step = [&](auto buf_tag, int st) {
     constexpr int BUF = decltype(buf_tag)::value;
     uint16_t* cQ = BUF ? sQ1 : sQ0;
@@ -213,19 +287,25 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     const float* cDl = BUF ? sD1 : sD0;
     float* nL = BUF ? sL0 : sL1;
     float* nD = BUF ? sD0 : sD1;
+    uint16_t* wS = BUF ? sdSt1 : sdSt0;        // this block's dS'^T
+    const uint16_t* pS = BUF ? sdSt0 : sdSt1;  // the previous block's
     const int m0 = m_begin + st * BM;
-    // Block st resident.  The dQ atomics/stores that ended step st-1 came
-    // after those loads and may stay in flight.
-    if (st > 0)
+    // Block st resident.  From step 2 on, the dQ atomics/stores that ended
+    // step st-1 (those of block st-2) came after those loads and may stay in
+    // flight; step 0 wrote no dQ, so step 1 waits for everything.
+    if (st > 1)
       wait_vmem_but<NEMIT>();
     else
       wait_vmem();
-    lds_barrier();  // block st resident; every wave is done with step st-1
+    lds_barrier();  // block st resident, dS'^T of block st-1 complete; every wave is done with step st-1
     if (st + 1 < n_steps) {
       tile_load_async<D, BM, NW>(Qb, qrs, m0 + BM, S, nQ, w, lane);
       tile_load_async<D, BM, NW>(dOb, qrs, m0 + BM, S, ndO, w, lane);
       load_rows(m0 + BM, nL, nD);
     }
+    // These loads stay ahead of this step's dQ atomics/stores in the
+    // instruction stream: the next step's wait counts on that order.
+    asm volatile("" ::: "memory");
     // Per-lane LDS byte offsets, recomputed from the lane id every step
     // rather than kept live across the loop; the loops below derive the rest
     // with XORs of column moves and additions of 16-row moves (see xslot()).
@@ -241,6 +321,7 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     // and the barriers.
     const int n_vis = CAUSAL ? min(min(BN, S - n0), m0 + BM - n0) : min(BN, S - n0);
     const bool active = 32 * w < n_vis;
+    f32x4 dq[NQT];
     if (active) {
       // S = Q K^T and dP = dO V^T for the block's 32 queries x this wave's
       // 32 keys.  Operands are read one k-step ahead of the products that
@@ -266,6 +347,7 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      if (st > 0) dq_block(pS, dq);
 
       // P' = scale P and dS' = scale dS.  Element j of lane l is query
       // 8(j/4) + 4hi + j%4 of the block, key 32w + l32.
@@ -309,7 +391,7 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
       // dS'^T to LDS as [key][query]: four consecutive queries per 8-byte
       // write.
       {
-        const uint32_t aW = lds_addr(sdSt) + 2 * dst_off(32 * w + ll32, 4 * lhi);
+        const uint32_t aW = lds_addr(wS) + 2 * dst_off(32 * w + ll32, 4 * lhi);
 #pragma unroll
         for (int jg = 0; jg < 4; jg++) lds_store_b64_addr(aW ^ (16u * jg), u32x2{dd[2 * jg], dd[2 * jg + 1]});
       }
@@ -341,79 +423,25 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
         }
       }
     } else {
+      if (st > 0) dq_block(pS, dq);
       // Zero rows of dS'^T, so that the dQ product can run over all keys.
-      const uint32_t aW = lds_addr(sdSt) + 2 * dst_off(32 * w + ll32, 4 * lhi);
+      const uint32_t aW = lds_addr(wS) + 2 * dst_off(32 * w + ll32, 4 * lhi);
 #pragma unroll
       for (int jg = 0; jg < 4; jg++) lds_store_b64_addr(aW ^ (16u * jg), u32x2{0u, 0u});
     }
-    lds_barrier();  // dS'^T complete in LDS
-
-    // dQ' (32 x D) = dS' (32 x 256 keys) K (256 keys x D) as 16x16 tiles.
-    {
-      const int lg = lL >> 2, lc = lL & 3, lg4 = ln >> 4;  // e, c, group of the 16x16 layout
-      const uint32_t offK0 = 2 * swz_off<D>(8 * lg4 + lg, 16 * dq_dt + 4 * lc);  // transposing reads of K
-      const uint32_t offK1 = 2 * swz_off<D>(8 * lg4 + lg + 4, 16 * dq_dt + 4 * lc);
-      const uint32_t offS0 = 2 * dst_off(8 * lg4 + lg, 16 * dq_qt0 + 4 * lc);    // ... of dS'^T
-      const uint32_t offS1 = 2 * dst_off(8 * lg4 + lg + 4, 16 * dq_qt0 + 4 * lc);
-      f32x4 dq[NQT];
-#pragma unroll
-      for (int i = 0; i < NQT; i++) dq[i] = f32x4{};
-      // Operands are read one key slice ahead of the products.
-      auto rd_k = [&](int kk) { return lds_tr8_at(sK, offK0 + 64u * kk * D, offK1 + 64u * kk * D); };
-      auto rd_s = [&](int kk, int i) {
-        return lds_tr8_at(sdSt, (offS0 ^ (32u * i)) + 64u * kk * BM, (offS1 ^ (32u * i)) + 64u * kk * BM);
-      };
-      bf16x8 bk = rd_k(0), as[NQT];
-#pragma unroll
-      for (int i = 0; i < NQT; i++) as[i] = rd_s(0, i);
-#pragma unroll
-      for (int kk = 0; kk < BN / 32; kk++) {
-        bf16x8 bk1 = bk, as1[NQT];
-#pragma unroll
-        for (int i = 0; i < NQT; i++) as1[i] = as[i];
-        if (kk + 1 < BN / 32) {
-          bk1 = rd_k(kk + 1);
-#pragma unroll
-          for (int i = 0; i < NQT; i++) as1[i] = rd_s(kk + 1, i);
-        }
-#pragma unroll
-        for (int i = 0; i < NQT; i++) dq[i] = mfma16(as[i], bk, dq[i]);
-        bk = bk1;
-#pragma unroll
-        for (int i = 0; i < NQT; i++) as[i] = as1[i];
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (m0 + BM <= S) {
-        const __amdgpu_buffer_rsrc_t rs = dq_rsrc(m0);
-#pragma unroll
-        for (int e = 0; e < NEMIT; e++) dq_emit(rs, dq, e);
-      } else {
-        // Last, partial block: written now, row by row (addresses derived
-        // here, not kept live).
-        const size_t blk_off = ((size_t)(b * Hq + h) * S + m0) * D;
-        float* dst_base = ATOMIC ? p.dq_accum + blk_off : p.dq_part + (size_t)jb * nq + blk_off;
-        const int lt = opaque_v(lane);
-        const int tg = lt >> 4, td = 16 * dq_dt + (lt & 15);
-#pragma unroll
-        for (int i = 0; i < NQT; i++)
-#pragma unroll
-          for (int j = 0; j < 4; j++) {
-            const int qr = 16 * (dq_qt0 + i) + 4 * tg + j;
-            if (m0 + qr < S) {
-              float* a = dst_base + (size_t)qr * D + td;
-              if (ATOMIC)
-                unsafeAtomicAdd(a, dq[i][j]);
-              else
-                *a = dq[i][j];
-            }
-          }
-      }
-    }
+    if (st > 0) dq_store(m0 - BM, dq);
   };
 
   for (int st = 0; st < n_steps; st += 2) {
     step(std::integral_constant<int, 0>{}, st);
     if (st + 1 < n_steps) step(std::integral_constant<int, 1>{}, st + 1);
+  }
+  // dQ of the last block.
+  {
+    lds_barrier();  // its dS'^T complete
+    f32x4 dq[NQT];
+    dq_block(((n_steps - 1) & 1) ? sdSt1 : sdSt0, dq);
+    dq_store(m_begin + (n_steps - 1) * BM, dq);
   }
   // Each wave holds the complete dK/dV of its 32 keys.  Element j of lane l
   // of tile dt is key 32w + 8(j/4) + 4hi + j%4, d = 32dt + l32.

@@ -71,6 +71,19 @@ def test_multi_block_gqa(d, causal):
         _compare(f"gqa4 s520 d{d} causal={causal} atomic={use_atomic}", gpu, ref)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_long_sweep(d, causal):
+    """Five key blocks (the last one ragged) and up to 35 query blocks per
+    sweep, one query head per KV head (bf16 dK/dV written by the kernel)."""
+    inp = make_inputs(1, 1100, 2, 2, d, seed=1100 + d)
+    scale = 1.0 / math.sqrt(d)
+    ref = _oracle(inp, causal, scale, 1)
+    for use_atomic in (1, 0):
+        gpu = run_path(to_dev(inp), causal, scale, use_atomic)
+        _compare(f"s1100 d{d} causal={causal} atomic={use_atomic}", gpu, ref)
+
+
 def test_group_of_eight_odd_length():
     inp = make_inputs(1, 333, 16, 2, 128, seed=5, qk_mult=1.5)
     scale = 1.0 / math.sqrt(128)
