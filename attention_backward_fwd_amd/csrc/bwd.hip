@@ -180,27 +180,37 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     dv[dt] = f32x16{};
   }
 
-  // dQ tiles of this wave: d columns 16dq_dt .., query tiles dq_qt0 ...
+  // dQ tiles.  D = 128: waves 0-3 each compute 32 queries x d columns
+  // 32w .. 32w+31 as one 32x32 tile (one such wave per SIMD, so the matrix
+  // work per SIMD stays even; each dS'^T and K element is read by fewer
+  // waves than with 16x16 tiles).  D = 64: every wave computes one 16x16
+  // tile, d columns 16dq_dt .., queries 16dq_qt0 ...
+  constexpr bool DQ32 = (D == 128);
+  constexpr int DQF4 = DQ32 ? 4 : NQT;  // f32x4 registers of dQ per lane
+  const bool dq_wave = DQ32 ? (w < 4) : true;
   const int dq_dt = (D == 128) ? w : (w & 3);
   const int dq_qt0 = (D == 128) ? 0 : (w >> 2);
   // dQ accumulator and partials are head-major ([.., B, Hq, S, D]): the rows
   // of one query block are one contiguous run.  16x16 result element j of
   // lane l is query 16qt + 4(l/16) + j, d 16dq_dt + l%16.
   const uint32_t row_bytes = (uint32_t)D * 4u;
-  const uint32_t dq_voff = (uint32_t)(4 * (lane >> 4)) * row_bytes + (uint32_t)(16 * dq_dt + (lane & 15)) * 4u;
+  const uint32_t dq_voff = DQ32 ? (uint32_t)(4 * (lane >> 5)) * row_bytes + (uint32_t)(32 * w + (lane & 31)) * 4u
+                                : (uint32_t)(4 * (lane >> 4)) * row_bytes + (uint32_t)(16 * dq_dt + (lane & 15)) * 4u;
   const size_t nq = (size_t)p.B * S * Hq * D;
-  constexpr int NEMIT = 4 * NQT;  // atomics / stores per wave per block
+  constexpr int NEMIT = 4 * DQF4;  // atomics / stores per dQ wave per block
 
   auto dq_rsrc = [&](int m0) {
     const size_t blk_off = ((size_t)(b * Hq + h) * S + m0) * D;
     float* dst_base = ATOMIC ? p.dq_accum + blk_off : p.dq_part + (size_t)jb * nq + blk_off;
     return buffer_rsrc(dst_base, (uint32_t)BM * row_bytes);
   };
-  // Element e % 4 of dQ tile e / 4 (e < NEMIT) to the block's rows.
+  // Element e % 4 of register e / 4 (e < NEMIT) to the block's rows: row
+  // 8(e/4) + 4(l/32) + e%4 of the 32x32 tile, or 16(dq_qt0 + e/4) + 4(l/16)
+  // + e%4 of the 16x16 tiles.
   auto dq_emit = [&](const __amdgpu_buffer_rsrc_t& rs, const f32x4* v, int e) {
     const uint32_t rb = opaque(row_bytes);
     const int i = e >> 2, j = e & 3;
-    const uint32_t so = (uint32_t)(16 * (dq_qt0 + i) + j) * rb;
+    const uint32_t so = (uint32_t)(DQ32 ? 8 * i + j : 16 * (dq_qt0 + i) + j) * rb;
     if (ATOMIC)
       __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v[i][j], rs, dq_voff, so, 0);
     else
@@ -210,7 +220,43 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
   // dQ' (32 x D) = dS' (32 x 256 keys) K (256 keys x D) of one block as
   // 16x16 tiles, from the dS'^T tile `sdSt`.  Operands are read one key
   // slice ahead of the products.
+  auto dq_block32 = [&](const uint16_t* sdSt, f32x4* dq) {
+    // 32x32x16 products over 16 slices of 16 keys; transposing reads of
+    // dS'^T (rows = keys) and K, in the layout of the dV/dK B operands.
+    const int ln = opaque_v(lane);
+    const int lhi = ln >> 5, lL = ln & 15, tcol = 16 * ((ln >> 4) & 1) + 4 * (lL & 3);
+    const uint32_t offK0 = 2 * swz_off<D>(8 * lhi + (lL >> 2), 32 * w + tcol);
+    const uint32_t offK1 = 2 * swz_off<D>(8 * lhi + (lL >> 2) + 4, 32 * w + tcol);
+    const uint32_t offS0 = 2 * dst_off(8 * lhi + (lL >> 2), tcol);
+    const uint32_t offS1 = 2 * dst_off(8 * lhi + (lL >> 2) + 4, tcol);
+    // A 16-row step flips bit 4 of the dS'^T row, which enters its swizzle
+    // (dst_f): odd slices XOR the element offset with 4 (8 bytes).  The K
+    // swizzle only sees the low 4 row bits.
+    auto rd = [&](int kk, bf16x8& a, bf16x8& bk) {
+      const uint32_t fx = 8u * (kk & 1);
+      a = lds_tr8_at(sdSt, (offS0 ^ fx) + 32u * kk * BM, (offS1 ^ fx) + 32u * kk * BM);
+      bk = lds_tr8_at(sK, offK0 + 32u * kk * D, offK1 + 32u * kk * D);
+    };
+    f32x16 acc = f32x16{};
+    bf16x8 a, bk;
+    rd(0, a, bk);
+#pragma unroll
+    for (int kk = 0; kk < BN / 16; kk++) {
+      bf16x8 a1 = a, bk1 = bk;
+      if (kk + 1 < BN / 16) rd(kk + 1, a1, bk1);
+      acc = mfma32(a, bk, acc);
+      a = a1;
+      bk = bk1;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) dq[i] = f32x4{acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]};
+  };
   auto dq_block = [&](const uint16_t* sdSt, f32x4* dq) {
+    if constexpr (DQ32) {
+      if (dq_wave) dq_block32(sdSt, dq);
+      return;
+    }
     const int ln = opaque_v(lane);
     const int lL = ln & 15, lg = lL >> 2, lc = lL & 3, lg4 = ln >> 4;  // e, c, group of the 16x16 layout
     const uint32_t offK0 = 2 * swz_off<D>(8 * lg4 + lg, 16 * dq_dt + 4 * lc);  // transposing reads of K
@@ -248,6 +294,7 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
   // atomics/stores, the last, partial one row by row (addresses derived
   // here, not kept live).
   auto dq_store = [&](int m0, const f32x4* dq) {
+    if (!dq_wave) return;
     if (m0 + BM <= S) {
       const __amdgpu_buffer_rsrc_t rs = dq_rsrc(m0);
 #pragma unroll
@@ -256,12 +303,13 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
       const size_t blk_off = ((size_t)(b * Hq + h) * S + m0) * D;
       float* dst_base = ATOMIC ? p.dq_accum + blk_off : p.dq_part + (size_t)jb * nq + blk_off;
       const int lt = opaque_v(lane);
-      const int tg = lt >> 4, td = 16 * dq_dt + (lt & 15);
+      const int tg = DQ32 ? lt >> 5 : lt >> 4;
+      const int td = DQ32 ? 32 * w + (lt & 31) : 16 * dq_dt + (lt & 15);
 #pragma unroll
-      for (int i = 0; i < NQT; i++)
+      for (int i = 0; i < DQF4; i++)
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-          const int qr = 16 * (dq_qt0 + i) + 4 * tg + j;
+          const int qr = DQ32 ? 8 * i + 4 * tg + j : 16 * (dq_qt0 + i) + 4 * tg + j;
           if (m0 + qr < S) {
             float* a = dst_base + (size_t)qr * D + td;
             if (ATOMIC)
@@ -293,7 +341,7 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     // Block st resident.  From step 2 on, the dQ atomics/stores that ended
     // step st-1 (those of block st-2) came after those loads and may stay in
     // flight; step 0 wrote no dQ, so step 1 waits for everything.
-    if (st > 1)
+    if (st > 1 && dq_wave)
       wait_vmem_but<NEMIT>();
     else
       wait_vmem();
@@ -321,7 +369,7 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     // and the barriers.
     const int n_vis = CAUSAL ? min(min(BN, S - n0), m0 + BM - n0) : min(BN, S - n0);
     const bool active = 32 * w < n_vis;
-    f32x4 dq[NQT];
+    f32x4 dq[DQF4];
     if (active) {
       // S = Q K^T and dP = dO V^T for the block's 32 queries x this wave's
       // 32 keys.  Operands are read one k-step ahead of the products that
@@ -439,7 +487,7 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
   // dQ of the last block.
   {
     lds_barrier();  // its dS'^T complete
-    f32x4 dq[NQT];
+    f32x4 dq[DQF4];
     dq_block(((n_steps - 1) & 1) ? sdSt1 : sdSt0, dq);
     dq_store(m_begin + (n_steps - 1) * BM, dq);
   }
