@@ -139,12 +139,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
 
     // S^T (64 keys x 32 queries): element j of s[mt] is key
     // n0 + 32mt + 8(j/4) + 4hi + j%4, query qi.
+    // Operands are read one k-step ahead of the products that use them.
     f32x16 s[2] = {f32x16{}, f32x16{}};
+    bf16x8 k0 = lds_read_b128(cK + offA), k1 = lds_read_b128(cK + offA + 32 * D);
 #pragma unroll
-    for (int ks = 0; ks < NKS; ks++)
-#pragma unroll
-      for (int mt = 0; mt < 2; mt++)
-        s[mt] = mfma32(lds_read_b128(cK + xslot(offA, 16 * ks) + 32 * mt * D), qf[ks], s[mt]);
+    for (int ks = 0; ks < NKS; ks++) {
+      bf16x8 n0v = k0, n1v = k1;
+      if (ks + 1 < NKS) {
+        n0v = lds_read_b128(cK + xslot(offA, 16 * (ks + 1)));
+        n1v = lds_read_b128(cK + xslot(offA, 16 * (ks + 1)) + 32 * D);
+      }
+      s[0] = mfma32(k0, qf[ks], s[0]);
+      s[1] = mfma32(k1, qf[ks], s[1]);
+      k0 = n0v;
+      k1 = n1v;
+      __builtin_amdgcn_sched_barrier(0);
+    }
 
     // Edge tiles (past the end, or crossing the causal diagonal): a key at
     // tile offset k is visible iff k <= lim.
@@ -192,14 +202,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
       pb[kk] = pack8(s[mt][o8 + 0], s[mt][o8 + 1], s[mt][o8 + 2], s[mt][o8 + 3], s[mt][o8 + 4],
                      s[mt][o8 + 5], s[mt][o8 + 6], s[mt][o8 + 7]);
     }
-    // O^T += V^T P^T with V^T read by transposing LDS reads.
+    // O^T += V^T P^T with V^T read by transposing LDS reads, one product
+    // ahead.
+    auto rd = [&](int it) {
+      const int kk = it / NDT, dt = it % NDT;
+      return lds_read_tr8(cV + xslot(offV0, 32 * dt) + 16 * kk * D, cV + xslot(offV1, 32 * dt) + 16 * kk * D);
+    };
+    bf16x8 a = rd(0);
 #pragma unroll
-    for (int kk = 0; kk < 4; kk++)
-#pragma unroll
-      for (int dt = 0; dt < NDT; dt++) {
-        const bf16x8 a = lds_read_tr8(cV + xslot(offV0, 32 * dt) + 16 * kk * D, cV + xslot(offV1, 32 * dt) + 16 * kk * D);
-        oacc[dt] = mfma32(a, pb[kk], oacc[dt]);
-      }
+    for (int it = 0; it < 4 * NDT; it++) {
+      bf16x8 a1 = a;
+      if (it + 1 < 4 * NDT) a1 = rd(it + 1);
+      oacc[it % NDT] = mfma32(a, pb[it / NDT], oacc[it % NDT]);
+      a = a1;
+    }
   };
   for (int it = 0; it < n_tiles; it += 2) {
     tile(std::integral_constant<int, 0>{}, it);

@@ -35,10 +35,15 @@ def flops(w, causal):
     return 4 * f / div, 10 * f / div
 
 
+BWD_SOURCES = ("bwd.hip", "common.h", "kernels.h")  # what the backward kernel is built from
+
+
 def kernel_source_hash():
+    """Hash of the backward kernel's sources: recorded counters stay valid
+    until one of these files changes."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "attention_backward_fwd_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in BWD_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
