@@ -57,6 +57,8 @@ def library():
                                  ctypes.c_int, ctypes.c_int, P]
         lib.attn_bwd_postprocess.restype = ctypes.c_int
         lib.attn_bwd_postprocess.argtypes = [P, P, ctypes.c_size_t, P, P, P, attn_shape, P]
+        lib.attn_merge.restype = ctypes.c_int
+        lib.attn_merge.argtypes = [P, P, ctypes.c_int, P, P, attn_shape, P]
         _lib = lib
     return _lib
 
@@ -134,6 +136,11 @@ def attn_bwd_postprocess(dq_accum, workspace, dq, dk, dv, shape, stream=None):
                                           _ptr(dv), shape, _stream(stream)), "attn_bwd_postprocess")
 
 
+def attn_merge(o_parts, lse_parts, n_parts, o, lse, shape, stream=None):
+    _check(library().attn_merge(_ptr(o_parts), _ptr(lse_parts), int(n_parts), _ptr(o), _ptr(lse), shape,
+                                _stream(stream)), "attn_merge")
+
+
 # ------------------------------------------------------------ conveniences
 
 def _require_gpu_inputs(*ts):
@@ -178,3 +185,19 @@ def backward(q, k, v, o, lse, do, causal, scale, use_atomic=True, buffers=None, 
              stream)
     attn_bwd_postprocess(bb.dq_accum, bb.workspace, bb.dq, bb.dk, bb.dv, sh, stream)
     return bb.dq, bb.dk, bb.dv
+
+
+def merge(o_parts, lse_parts, stream=None):
+    """O, LSE merged over the parts: o_parts [P,B,S,Hq,D] bf16, lse_parts
+    [P,B,Hq,S] fp32 (contiguous, on the GPU)."""
+    _require_gpu_inputs(o_parts)
+    if not lse_parts.is_cuda or lse_parts.dtype != torch.float32 or not lse_parts.is_contiguous():
+        raise ValueError("lse_parts must be a contiguous fp32 GPU tensor")
+    n, b, s, hq, d = o_parts.shape
+    if lse_parts.shape != (n, b, hq, s):
+        raise ValueError("lse_parts must be [P, B, Hq, S] matching o_parts")
+    shape = attn_shape(b, s, hq, 1, d)
+    o = torch.empty((b, s, hq, d), dtype=torch.bfloat16, device=o_parts.device)
+    lse = torch.empty((b, hq, s), dtype=torch.float32, device=o_parts.device)
+    attn_merge(o_parts, lse_parts, n, o, lse, shape, stream)
+    return o, lse

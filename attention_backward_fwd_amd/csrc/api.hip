@@ -168,4 +168,15 @@ int attn_bwd_postprocess(const float* dq_accum, const void* workspace, size_t wo
                                        shape.groups, shape.head_dim, (hipStream_t)stream));
 }
 
+int attn_merge(const uint16_t* o_parts, const float* lse_parts, int n_parts, uint16_t* o, float* lse,
+               attn_shape shape, void* stream) {
+  if (!o_parts || !lse_parts || !o || !lse) return ATTN_ERR_NULL_PTR;
+  if (n_parts < 1) return ATTN_ERR_BAD_SHAPE;
+  const int st = check_shape(shape);
+  if (st) return st;
+  if (!aligned16(o_parts) || !aligned16(lse_parts) || !aligned16(o) || !aligned16(lse)) return ATTN_ERR_ALIGN;
+  return hip_status(launch_merge(o_parts, lse_parts, n_parts, o, lse, shape.batch, shape.seqlen, shape.heads_q,
+                                 shape.head_dim, (hipStream_t)stream));
+}
+
 }  // extern "C"

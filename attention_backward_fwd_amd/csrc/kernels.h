@@ -51,4 +51,7 @@ hipError_t launch_postprocess(const float* dq_accum, const float* dk_part, const
                               uint16_t* dq, uint16_t* dk, uint16_t* dv, int B, int S, int Hq, int G,
                               int D, hipStream_t stream);
 
+hipError_t launch_merge(const uint16_t* o_parts, const float* lse_parts, int n_parts, uint16_t* o, float* lse,
+                        int B, int S, int Hq, int D, hipStream_t stream);
+
 }  // namespace mi355

@@ -24,6 +24,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 METRIC = "attention fwd+bwd TFLOP/s (bf16, causal) and % of MI355X bf16 MFMA peak"
 DEFAULT_WORKLOAD = "mha_causal_b4_h32_s4096_d128"
@@ -98,6 +99,41 @@ def cpu_baseline(w, causal, budget_s):
                       f"FLOPs counted with the same causal-halved formula"}
 
 
+def bench_merge(args, w, bd, torch):
+    """attn_merge of P synthetic partials shaped like the workload's O/LSE:
+    one JSON line with GB/s against the HBM peak (bytes = every part's O
+    and LSE read once, O and LSE written once)."""
+    n = args.merge_parts
+    g = torch.Generator(device="cuda:0").manual_seed(7)
+    o_p = torch.randn((n, w.batch, w.seqlen, w.heads_q, w.head_dim), device="cuda:0", generator=g).to(torch.bfloat16)
+    l_p = torch.randn((n, w.batch, w.heads_q, w.seqlen), device="cuda:0", generator=g)
+    shape = bd.make_shape(w.batch, w.seqlen, w.heads_q, 1, w.head_dim)
+    o = torch.empty(o_p.shape[1:], dtype=torch.bfloat16, device="cuda:0")
+    lse = torch.empty(l_p.shape[1:], dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        bd.attn_merge(o_p, l_p, n, o, lse, shape, stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        ev[2 * i].record(stream)
+        bd.attn_merge(o_p, l_p, n, o, lse, shape, stream)
+        ev[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)) / args.steps
+    nq = w.batch * w.seqlen * w.heads_q * w.head_dim
+    rows = w.batch * w.heads_q * w.seqlen
+    nbytes = n * (2 * nq + 4 * rows) + 2 * nq + 4 * rows
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({"metric": "attn_merge HBM throughput", "value": round(gbs, 1), "unit": "GB/s",
+                      "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+                      "higher_is_better": True, "dtype": "bf16 O, fp32 LSE", "data": "synthetic",
+                      "config": {"workload": w.name, "parts": n},
+                      "roofline": {"kernel": "merge_kernel", "bound": "hbm", "achieved": round(gbs, 1),
+                                   "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                   "traffic": None}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -111,6 +147,9 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run a plain fp32 copy kernel over MIB MiB "
                          "(reference for scaling the HBM byte counters)")
+    ap.add_argument("--merge-parts", type=int, default=0, metavar="P",
+                    help="instead of the fwd+bwd step, time attn_merge of P partial (O, LSE) results "
+                         "of the workload's query shape (the context-parallel merge; HBM-bound)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -135,6 +174,9 @@ def main():
         return
 
     w = WORKLOADS[args.workload]
+    if args.merge_parts:
+        bench_merge(args, w, bd, torch)
+        return
     causal = w.causal[-1] if args.causal is None else bool(args.causal)
     use_atomic = args.use_atomic
     dev = torch.device("cuda:0")

@@ -135,6 +135,29 @@ int attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint
 int attn_bwd_postprocess(const float* dq_accum, const void* workspace, size_t workspace_bytes,
                          uint16_t* dq, uint16_t* dk, uint16_t* dv, attn_shape shape, void* stream);
 
+/*
+ * Merge of partial results over disjoint key chunks: for every query row,
+ *   LSE = ln sum_k exp(LSE_k),   O = sum_k exp(LSE_k - LSE) O_k   (fp32).
+ * This is the step context-parallel (ring) attention needs once a query
+ * chunk has met every key chunk it can see; the Megatron-LM pull request
+ * "TileLang implementation of the fused DSA operations" (NVIDIA Megatron-LM
+ * #5049, description, "Packed THD and CP behavior") routes such cases
+ * through its common path.  With chunks of equal length every (query chunk,
+ * key chunk) pair is an ordinary attn_fwd call (causal for the diagonal
+ * pair), and attn_bwd of each pair with the merged LSE and the Delta of the
+ * merged O yields that pair's gradient terms.
+ *   o_parts  [n_parts][B,S,Hq,D] bf16, contiguous (each part an attn_fwd O)
+ *   lse_parts [n_parts][B,Hq,S] fp32 natural log (each part an attn_fwd LSE)
+ *   o [B,S,Hq,D] bf16, lse [B,Hq,S] fp32 (outputs; every element written)
+ *   n_parts >= 1 (else ATTN_ERR_BAD_SHAPE); shape.groups is not used but
+ *   must be valid.
+ * Rows whose LSE_k is -inf (no visible key in that part) get weight 0 (their
+ * O_k must still be finite, as attn_fwd's zeros are); a row that is -inf in
+ * every part gets O = 0 and LSE = -inf.
+ */
+int attn_merge(const uint16_t* o_parts, const float* lse_parts, int n_parts, uint16_t* o, float* lse,
+               attn_shape shape, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,7 @@ def shp(b=2, s=300, hq=8, g=2, d=128):
 def test_library_exports_every_header_symbol():
     names = bd.header_functions()
     assert names == sorted(["attn_fwd", "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_bwd",
-                            "attn_bwd_postprocess", "attn_strerror"])
+                            "attn_bwd_postprocess", "attn_merge", "attn_strerror"])
     for n in names:
         assert hasattr(lib(), n), n
 
@@ -130,6 +130,21 @@ def test_bwd_errors(kw, code):
 ])
 def test_postprocess_errors(kw, code):
     assert post(**kw) == E[code]
+
+
+def merge(**kw):
+    args = dict(op=A, lp=A, n=3, o=A, lse=A, shape=shp(), stream=None)
+    args.update(kw)
+    return lib().attn_merge(args["op"], args["lp"], args["n"], args["o"], args["lse"], args["shape"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"op": None}, "null"), ({"lse": None}, "null"), ({"n": 0}, "shape"), ({"n": -2}, "shape"),
+    ({"shape": shp(s=0)}, "shape"), ({"shape": shp(d=96)}, "hd"), ({"shape": shp(b=64, s=8192, hq=64, g=1)}, "range"),
+    ({"o": MIS}, "align"), ({"lp": MIS}, "align"),
+])
+def test_merge_errors(kw, code):
+    assert merge(**kw) == E[code]
 
 
 def test_python_shape_helpers():
