@@ -69,6 +69,70 @@ __global__ __launch_bounds__(256) void dq_sum_kernel(const float* __restrict__ p
   }
 }
 
+// Packed sequences: the sequence holding row t, found by bisection over the
+// clamped sequence starts (non-decreasing when cu_seqlens is), with its first
+// row and its length cut to S rows; -1 for rows outside every such range
+// (capacity padding, or rows of a sequence past S).
+__device__ __forceinline__ int seq_of_row(const int* cu, int n_seqs, int T, int S, int t, int& start, int& len) {
+  if (n_seqs < 1) return -1;
+  const int first = min(max(cu[0], 0), T);
+  if (t < first || t >= min(max(cu[n_seqs], first), T)) return -1;
+  int lo = 0, hi = n_seqs - 1;  // largest b with start_b <= t
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (min(max(cu[mid], 0), T) <= t) lo = mid; else hi = mid - 1;
+  }
+  const SeqRows r = seq_rows(cu, T, lo, S);
+  start = r.base;
+  len = r.len;
+  return t >= r.base && t < r.base + r.len ? lo : -1;
+}
+
+// Packed sequences, split path: dq_accum[h, t, :] = sum over the key blocks
+// j = 0 .. J of row t's own sequence (J: the block holding t's position under
+// causal masking, else the sequence's last block) of part[j][h, t, :], in
+// ascending j; 0 for rows outside every sequence.  Rows are [Hq][T].
+__global__ __launch_bounds__(256) void dq_sum_varlen_kernel(const float* __restrict__ part,
+                                                            float* __restrict__ dq, const int* __restrict__ cu,
+                                                            int n_seqs, int T, int S, long long n4, int D,
+                                                            int causal) {
+  const size_t slot = (size_t)n4 * 4;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long long)gridDim.x * 256) {
+    const long long e = i * 4;
+    const int t = (int)((e / D) % T);
+    int start = 0, len = 0;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (seq_of_row(cu, n_seqs, T, S, t, start, len) >= 0) {
+      const int last = causal ? (t - start) / kBwdBlockN : (len - 1) / kBwdBlockN;
+      const float* src = part + e;
+      for (int j = 0; j <= last; j++) acc += *reinterpret_cast<const f32x4*>(src + (size_t)j * slot);
+    }
+    *reinterpret_cast<f32x4*>(dq + e) = acc;
+  }
+}
+
+// Rows of packed tensors outside every sequence (see seq_of_row): the rows of
+// [T][heads][D] tensors x0 and x1 (bf16, or fp32 when `fp32`; either may be
+// null) set to 0, and those rows of an [Hq][T] LSE (may be null) set to
+// lse_value.  One row per workgroup and step; rows inside a sequence are
+// left untouched.
+__global__ __launch_bounds__(256) void pad_fill_kernel(void* __restrict__ x0, void* __restrict__ x1, int fp32,
+                                                       int heads, float* __restrict__ lse, int Hq, float lse_value,
+                                                       const int* __restrict__ cu, int n_seqs, int T, int S, int D) {
+  const int per_row = heads * D / (fp32 ? 4 : 8);  // 16-byte chunks per row
+  for (int t = blockIdx.x; t < T; t += gridDim.x) {
+    int start, len;
+    if (seq_of_row(cu, n_seqs, T, S, t, start, len) >= 0) continue;
+    const size_t row = (size_t)t * per_row;
+    for (int c = threadIdx.x; c < per_row; c += 256) {
+      if (x0) reinterpret_cast<u32x4*>(x0)[row + c] = u32x4{0u, 0u, 0u, 0u};
+      if (x1) reinterpret_cast<u32x4*>(x1)[row + c] = u32x4{0u, 0u, 0u, 0u};
+    }
+    if (lse)
+      for (int h = threadIdx.x; h < Hq; h += 256) lse[(size_t)h * T + t] = lse_value;
+  }
+}
+
 __device__ __forceinline__ u32x4 cvt8(f32x4 a, f32x4 b) {
   return u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
                pack_bf16x2(b[2], b[3])};
@@ -144,6 +208,22 @@ hipError_t launch_dq_sum(const float* dq_part, float* dq_accum, int B, int S, in
   const int n_nblk = (S + kBwdBlockN - 1) / kBwdBlockN;
   hipLaunchKernelGGL(dq_sum_kernel, dim3(grid_for(n4, 256)), dim3(256), 0, stream, dq_part, dq_accum, n4, S, D,
                      n_nblk, causal);
+  return hipGetLastError();
+}
+
+hipError_t launch_dq_sum_varlen(const float* dq_part, float* dq_accum, const int* cu, int n_seqs, int T, int S,
+                                int Hq, int D, int causal, hipStream_t stream) {
+  const long long n4 = (long long)T * Hq * D / 4;
+  hipLaunchKernelGGL(dq_sum_varlen_kernel, dim3(grid_for(n4, 256)), dim3(256), 0, stream, dq_part, dq_accum, cu,
+                     n_seqs, T, S, n4, D, causal);
+  return hipGetLastError();
+}
+
+hipError_t launch_pad_fill(void* x0, void* x1, int fp32, int heads, float* lse, int Hq, float lse_value,
+                           const int* cu, int n_seqs, int T, int S, int D, hipStream_t stream) {
+  const int g = T < 256 * 64 ? T : 256 * 64;
+  hipLaunchKernelGGL(pad_fill_kernel, dim3(g), dim3(256), 0, stream, x0, x1, fp32, heads, lse, Hq, lse_value, cu,
+                     n_seqs, T, S, D);
   return hipGetLastError();
 }
 

@@ -108,8 +108,8 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (scalar)
   const int hi = lane >> 5, l32 = lane & 31;
-  const int S = p.S, Hq = p.Hq, G = p.G, Hkv = p.Hkv;
-  const int n_nblk = (S + BN - 1) / BN;
+  const int Hq = p.Hq, G = p.G, Hkv = p.Hkv;
+  const int n_nblk = (p.S + BN - 1) / BN;
 
   // Tile order: each XCD gets a contiguous range of (batch, KV head) groups
   // and works through them one at a time (their Q/dO rows stay in its L2);
@@ -133,14 +133,21 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
   const int b = __builtin_amdgcn_readfirstlane(grp / Hkv), kvh = __builtin_amdgcn_readfirstlane(grp % Hkv);
   const int h = __builtin_amdgcn_readfirstlane(kvh * G + r);
   const int n0 = jb * BN;
+  // This sequence's rows (packed sequences: its own length; key blocks past
+  // it have nothing to do).
+  const SeqRows sr = seq_rows(p.cu, p.T, b, p.S);
+  const int S = __builtin_amdgcn_readfirstlane(sr.len), row0 = __builtin_amdgcn_readfirstlane(sr.base);
+  if (n0 >= S) return;
+  // Row-indexed tensors: [B][Hq][S], or [Hq][T] for packed sequences.
+  const size_t hrow0 = p.cu ? (size_t)h * p.T + row0 : (size_t)(b * Hq + h) * S;
 
   const size_t qrs = (size_t)Hq * D, kvrs = (size_t)Hkv * D;
-  const uint16_t* Qb = p.q + ((size_t)b * S * Hq + h) * D;
-  const uint16_t* dOb = p.dout + ((size_t)b * S * Hq + h) * D;
-  const uint16_t* Kb = p.k + ((size_t)b * S * Hkv + kvh) * D;
-  const uint16_t* Vb = p.v + ((size_t)b * S * Hkv + kvh) * D;
-  const float* lse_b = p.lse + (size_t)(b * Hq + h) * S;
-  const float* dl_b = p.delta + (size_t)(b * Hq + h) * S;
+  const uint16_t* Qb = p.q + ((size_t)row0 * Hq + h) * D;
+  const uint16_t* dOb = p.dout + ((size_t)row0 * Hq + h) * D;
+  const uint16_t* Kb = p.k + ((size_t)row0 * Hkv + kvh) * D;
+  const uint16_t* Vb = p.v + ((size_t)row0 * Hkv + kvh) * D;
+  const float* lse_b = p.lse + hrow0;
+  const float* dl_b = p.delta + hrow0;
 
   const float c = p.scale * kLog2e;
   const float lsc = p.log2_scale;
@@ -196,11 +203,11 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
   const uint32_t row_bytes = (uint32_t)D * 4u;
   const uint32_t dq_voff = DQ32 ? (uint32_t)(4 * (lane >> 5)) * row_bytes + (uint32_t)(32 * w + (lane & 31)) * 4u
                                 : (uint32_t)(4 * (lane >> 4)) * row_bytes + (uint32_t)(16 * dq_dt + (lane & 15)) * 4u;
-  const size_t nq = (size_t)p.B * S * Hq * D;
+  const size_t nq = (size_t)(p.cu ? p.T : p.B * p.S) * Hq * D;  // elements of one split partial slot
   constexpr int NEMIT = 4 * DQF4;  // atomics / stores per dQ wave per block
 
   auto dq_rsrc = [&](int m0) {
-    const size_t blk_off = ((size_t)(b * Hq + h) * S + m0) * D;
+    const size_t blk_off = (hrow0 + m0) * D;
     float* dst_base = ATOMIC ? p.dq_accum + blk_off : p.dq_part + (size_t)jb * nq + blk_off;
     return buffer_rsrc(dst_base, (uint32_t)BM * row_bytes);
   };
@@ -300,7 +307,7 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
       for (int e = 0; e < NEMIT; e++) dq_emit(rs, dq, e);
     } else {
-      const size_t blk_off = ((size_t)(b * Hq + h) * S + m0) * D;
+      const size_t blk_off = (hrow0 + m0) * D;
       float* dst_base = ATOMIC ? p.dq_accum + blk_off : p.dq_part + (size_t)jb * nq + blk_off;
       const int lt = opaque_v(lane);
       const int tg = DQ32 ? lt >> 5 : lt >> 4;
@@ -504,11 +511,11 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
       const int key = n0 + 32 * w + 8 * (j >> 2) + 4 * ehi + (j & 3);
       if (key < S) {
         if (PARTIAL) {
-          const size_t off = ((size_t)(b * S + key) * Hq + h) * D + d;
+          const size_t off = ((size_t)(row0 + key) * Hq + h) * D + d;
           p.dk_part[off] = dk[dt][j];
           p.dv_part[off] = dv[dt][j] * inv_scale;
         } else {
-          const size_t off = ((size_t)(b * S + key) * Hkv + kvh) * D + d;
+          const size_t off = ((size_t)(row0 + key) * Hkv + kvh) * D + d;
           p.dk[off] = to_bf16(dk[dt][j]);
           p.dv[off] = to_bf16(dv[dt][j] * inv_scale);
         }

@@ -59,8 +59,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (scalar)
   const int hi = lane >> 5, l32 = lane & 31, L = lane & 15, Gp = (lane >> 4) & 1;
-  const int S = p.S, Hq = p.Hq, G = p.G, Hkv = p.Hkv;
-  const int n_mblk = (S + BM - 1) / BM;
+  const int Hq = p.Hq, G = p.G, Hkv = p.Hkv;
+  const int n_mblk = (p.S + BM - 1) / BM;
 
   // Tile order: each XCD gets a contiguous range of (batch, KV head) groups
   // and works through them one at a time, so a group's K/V stay in its L2;
@@ -79,13 +79,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
   const int grp = x * NGx + t / per_group;
   const int mbo = (t % per_group) / G;
   const int r = t % G;
-  const int b = grp / Hkv, kvh = grp % Hkv, h = kvh * G + r;
-  const int mb = CAUSAL ? (n_mblk - 1 - mbo) : mbo;
+  const int b = __builtin_amdgcn_readfirstlane(grp / Hkv), kvh = __builtin_amdgcn_readfirstlane(grp % Hkv);
+  const int h = __builtin_amdgcn_readfirstlane(kvh * G + r);
+  // This sequence's rows (packed sequences: its own length; blocks past it
+  // have nothing to do).  Causal blocks still run heaviest-first.
+  const SeqRows sr = seq_rows(p.cu, p.T, b, p.S);
+  const int S = __builtin_amdgcn_readfirstlane(sr.len), row0 = __builtin_amdgcn_readfirstlane(sr.base);
+  const int n_mblk_b = (S + BM - 1) / BM;
+  const int mb = CAUSAL ? (n_mblk_b - 1 - mbo) : mbo;
+  if (mb < 0 || mb >= n_mblk_b) return;
 
   const size_t qrs = (size_t)Hq * D, kvrs = (size_t)Hkv * D;
-  const uint16_t* Qb = p.q + ((size_t)b * S * Hq + h) * D;
-  const uint16_t* Kb = p.k + ((size_t)b * S * Hkv + kvh) * D;
-  const uint16_t* Vb = p.v + ((size_t)b * S * Hkv + kvh) * D;
+  const uint16_t* Qb = p.q + ((size_t)row0 * Hq + h) * D;
+  const uint16_t* Kb = p.k + ((size_t)row0 * Hkv + kvh) * D;
+  const uint16_t* Vb = p.v + ((size_t)row0 * Hkv + kvh) * D;
 
   const int q0 = mb * BM + 32 * w;  // first query of this wave
   const int qi = q0 + l32;          // this lane's query
@@ -225,7 +232,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
   const float l_tot = xhalf_sum(l_i);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qi < S) {
-    uint16_t* orow = p.o + ((size_t)(b * S + qi) * Hq + h) * D;
+    uint16_t* orow = p.o + ((size_t)(row0 + qi) * Hq + h) * D;
 #pragma unroll
     for (int dt = 0; dt < NDT; dt++)
 #pragma unroll
@@ -235,7 +242,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
                     pack_bf16x2(oacc[dt][4 * jg + 2] * inv, oacc[dt][4 * jg + 3] * inv)};
         *reinterpret_cast<u32x2*>(orow + d) = v2;
       }
-    if (hi == 0) p.lse[(size_t)(b * Hq + h) * S + qi] = m_i * p.scale + __builtin_amdgcn_logf(l_tot) * kLn2;
+    // LSE rows: [B][Hq][S], or [Hq][T] for packed sequences.
+    const size_t lrow = p.cu ? (size_t)h * p.T + row0 : (size_t)(b * Hq + h) * S;
+    if (hi == 0) p.lse[lrow + qi] = m_i * p.scale + __builtin_amdgcn_logf(l_tot) * kLn2;
   }
 }
 

@@ -11,12 +11,30 @@ namespace mi355 {
 // dQ partial per block of this many keys.
 constexpr int kBwdBlockN = 256;
 
+// Packed variable-length sequences: when `cu` is set, "batch" b is sequence
+// b of the packed rows, its rows cu[b] .. cu[b+1]-1 (clamped to [0, T] and
+// cut to S rows), S is the bound of the sequence lengths that sizes the grid,
+// and the
+// row-indexed tensors (LSE, Delta, dQ accumulator and partials) are
+// head-major over all T rows.  Otherwise sequence b is rows b*S .. b*S+S-1.
+struct SeqRows {
+  int base, len;  // first row and length of one sequence
+};
+__device__ __forceinline__ SeqRows seq_rows(const int* cu, int T, int b, int S) {
+  if (!cu) return SeqRows{b * S, S};
+  const int a = min(max(cu[b], 0), T);
+  const int e = min(max(cu[b + 1], a), T);
+  return SeqRows{a, min(e - a, S)};
+}
+
 struct FwdParams {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
   uint16_t* o;
   float* lse;
+  const int* cu;  // packed sequences, or nullptr
+  int T;          // rows of the packed tensors (with cu)
   int B, S, Hq, G, Hkv, D;
   float scale;
   int causal;
@@ -35,6 +53,8 @@ struct BwdParams {
   uint16_t* dv;
   float* dk_part;   // groups > 1: per-query-head partials, [B][S][Hq][D] fp32
   float* dv_part;
+  const int* cu;    // packed sequences, or nullptr
+  int T;            // rows of the packed tensors (with cu)
   int B, S, Hq, G, Hkv, D;
   float scale;
   float log2_scale;  // log2(scale), computed on the host
@@ -47,6 +67,15 @@ hipError_t launch_preprocess(const uint16_t* o, const uint16_t* dout, float* del
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
 hipError_t launch_dq_sum(const float* dq_part, float* dq_accum, int B, int S, int Hq, int D,
                          int causal, hipStream_t stream);
+// Packed sequences: rows of dq_accum are [Hq][T]; sums the key blocks of each
+// row's own sequence, writes 0 to rows outside every sequence.
+hipError_t launch_dq_sum_varlen(const float* dq_part, float* dq_accum, const int* cu, int n_seqs, int T, int S,
+                                int Hq, int D, int causal, hipStream_t stream);
+// Rows outside every sequence (capacity padding, and rows of a sequence past
+// S) of up to two [T][heads][D] tensors (bf16, or fp32 when `fp32`) set to 0,
+// and those rows of an [Hq][T] LSE set to lse_value; null tensors skipped.
+hipError_t launch_pad_fill(void* x0, void* x1, int fp32, int heads, float* lse, int Hq, float lse_value,
+                           const int* cu, int n_seqs, int T, int S, int D, hipStream_t stream);
 hipError_t launch_postprocess(const float* dq_accum, const float* dk_part, const float* dv_part,
                               uint16_t* dq, uint16_t* dk, uint16_t* dv, int B, int S, int Hq, int G,
                               int D, hipStream_t stream);

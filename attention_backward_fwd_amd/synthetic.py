@@ -9,6 +9,12 @@ Recipe: a CPU ``torch.Generator`` seeded with ``seed`` draws standard-normal
 fp32 tensors in [batch, seq, heads, dim] order Q, K, V, dO; Q and K are then
 multiplied by ``qk_mult`` (1.5 gives sharper softmax rows); finally every
 tensor is rounded to bf16 (round-to-nearest-even).
+
+Packed sequences: ``length_mix`` draws sequence lengths uniformly from
+[lo, hi] with its own seeded generator until the next one would overflow the
+token budget, and gives the last sequence the tokens left; ``cu_seqlens`` is
+the running sum of the lengths.  The packed tensors are ``make_inputs`` with
+batch 1 and seq = total rows (capacity), viewed as [T, heads, dim].
 """
 
 from __future__ import annotations
@@ -65,3 +71,39 @@ def make_inputs(batch, seqlen, heads_q, heads_kv, head_dim, seed=0, qk_mult=1.0)
 
 def workload_inputs(w: Workload, seed=0):
     return make_inputs(w.batch, w.seqlen, w.heads_q, w.heads_kv, w.head_dim, seed=seed, qk_mult=w.qk_mult)
+
+
+def length_mix(budget, lo, hi, seed=0):
+    """Seeded sequence lengths in [lo, hi] summing to ``budget`` (the last one
+    takes the remainder, so it may be shorter than ``lo``)."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    out, used = [], 0
+    while used < budget:
+        n = int(torch.randint(lo, hi + 1, (1,), generator=g))
+        n = min(n, budget - used)
+        out.append(n)
+        used += n
+    return out
+
+
+def cu_seqlens(lengths):
+    """int32 cumulative offsets [0, l0, l0+l1, ...] as a CPU tensor."""
+    cu = [0]
+    for n in lengths:
+        cu.append(cu[-1] + int(n))
+    return torch.tensor(cu, dtype=torch.int32)
+
+
+# Packed causal workload: 16384 tokens (the token count of four 4096-token
+# sequences) in a seeded mix of 256 .. 4096-token sequences, 32 heads of 128,
+# plus 512 rows of capacity padding.
+VARLEN_PACK = {"name": "varlen_causal_h32_t16384_d128", "tokens": 16384, "lo": 256, "hi": 4096, "pad": 512,
+               "heads_q": 32, "heads_kv": 32, "head_dim": 128, "seed": 7}
+
+
+def varlen_pack_inputs(spec=VARLEN_PACK, seed=0):
+    """(inputs dict of [T, H, D] bf16 tensors, lengths, cu_seqlens) of a pack."""
+    lengths = length_mix(spec["tokens"], spec["lo"], spec["hi"], spec["seed"])
+    t = spec["tokens"] + spec["pad"]
+    inp = make_inputs(1, t, spec["heads_q"], spec["heads_kv"], spec["head_dim"], seed=seed)
+    return {n: x[0] for n, x in inp.items()}, lengths, cu_seqlens(lengths)

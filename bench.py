@@ -134,6 +134,76 @@ def bench_merge(args, w, bd, torch):
                                    "traffic": None}}), flush=True)
 
 
+def bench_varlen(args, bd, torch):
+    """The whole step over the packed causal pack of sequences: attn_fwd_varlen,
+    the preprocess, attn_bwd_varlen (plus the dQ sum on the split path) and
+    the postprocess.  FLOPs are the per-sequence causal-halved counts summed
+    over the pack; padding rows count nothing."""
+    from attention_backward_fwd_amd.synthetic import VARLEN_PACK, varlen_pack_inputs
+
+    spec = VARLEN_PACK
+    inp, lengths, cu_cpu = varlen_pack_inputs(spec)
+    dev = torch.device("cuda:0")
+    d = {n: t.to(dev) for n, t in inp.items()}
+    cu = cu_cpu.to(dev)
+    q, k, v, do = d["q"], d["k"], d["v"], d["do"]
+    hq, dim = spec["heads_q"], spec["head_dim"]
+    scale = 1.0 / math.sqrt(dim)
+    use_atomic = args.use_atomic
+    m = max(lengths)
+    sh = bd.varlen_shape_of(q, k, len(lengths), m)
+    o = torch.empty_like(q)
+    lse = torch.empty((hq, q.shape[0]), dtype=torch.float32, device=dev)
+    bb = bd.VarlenBwdBuffers(q, k, len(lengths), m, True, use_atomic)
+    stream = torch.cuda.current_stream()
+    ev = {n: [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)] for n in ("fwd", "bwd")}
+
+    def step(i=None):
+        if i is not None:
+            ev["fwd"][2 * i].record(stream)
+        bd.attn_fwd_varlen(q, k, v, o, lse, cu, sh, scale, True, stream)
+        if i is not None:
+            ev["fwd"][2 * i + 1].record(stream)
+        bd.attn_bwd_preprocess(o, do, bb.delta, bb.dq_accum if use_atomic else None, bb.dense, stream)
+        if i is not None:
+            ev["bwd"][2 * i].record(stream)
+        bd.attn_bwd_varlen(q, k, v, do, lse, bb.delta, bb.dq_accum, bb.dk, bb.dv, bb.workspace, cu, sh, scale,
+                           True, use_atomic, stream)
+        if i is not None:
+            ev["bwd"][2 * i + 1].record(stream)
+        bd.attn_bwd_postprocess(bb.dq_accum, bb.workspace, bb.dq, bb.dk, bb.dv, bb.dense, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    per = sum(n * n for n in lengths) * hq * dim / 2  # causal
+    fwd_f, bwd_f = 4 * per, 10 * per
+    fwd_ms = sum(ev["fwd"][2 * i].elapsed_time(ev["fwd"][2 * i + 1]) for i in range(args.steps)) / args.steps
+    bwd_ms = sum(ev["bwd"][2 * i].elapsed_time(ev["bwd"][2 * i + 1]) for i in range(args.steps)) / args.steps
+    value = (fwd_f + bwd_f) * args.steps / elapsed / 1e12
+    bwd_tflops = bwd_f / (bwd_ms * 1e-3) / 1e12
+    path = "atomic" if use_atomic else "split"
+    print(json.dumps({
+        "metric": "packed-sequence attention fwd+bwd TFLOP/s (bf16, causal)", "value": round(value, 3),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": spec["name"], "lengths": lengths, "padding_rows": spec["pad"], "heads_q": hq,
+                   "heads_kv": spec["heads_kv"], "head_dim": dim, "causal": True, "dq_path": path},
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 3),
+        "fwd_kernel_ms": round(fwd_ms, 4), "fwd_tflops": round(fwd_f / (fwd_ms * 1e-3) / 1e12, 3),
+        "bwd_kernel_ms": round(bwd_ms, 4),
+        "roofline": {"kernel": "bwd_kernel (packed)" + ("" if use_atomic else " + dq_sum_varlen_kernel"),
+                     "bound": "mfma", "achieved": round(bwd_tflops, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -150,6 +220,9 @@ def main():
     ap.add_argument("--merge-parts", type=int, default=0, metavar="P",
                     help="instead of the fwd+bwd step, time attn_merge of P partial (O, LSE) results "
                          "of the workload's query shape (the context-parallel merge; HBM-bound)")
+    ap.add_argument("--varlen", action="store_true",
+                    help="instead of the dense step, time the step over the packed causal pack of "
+                         "variable-length sequences (16384 tokens, 32 heads of 128)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -173,6 +246,9 @@ def main():
         print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "launches": 3}))
         return
 
+    if args.varlen:
+        bench_varlen(args, bd, torch)
+        return
     w = WORKLOADS[args.workload]
     if args.merge_parts:
         bench_merge(args, w, bd, torch)

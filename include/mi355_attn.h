@@ -55,7 +55,7 @@ typedef struct attn_shape {
 enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL_PTR = -1,  /* a required pointer is NULL */
-  ATTN_ERR_BAD_SHAPE = -2, /* a size < 1, or heads_q not a multiple of groups */
+  ATTN_ERR_BAD_SHAPE = -2, /* a size out of range, or heads_q not a multiple of groups */
   ATTN_ERR_HEAD_DIM = -3,  /* head_dim not 64 or 128 */
   ATTN_ERR_ALIGN = -4,     /* a tensor base is not 16-byte aligned */
   ATTN_ERR_RANGE = -5,     /* a tensor has >= 2^31 elements, heads_q * head_dim > 2^22,
@@ -157,6 +157,75 @@ int attn_bwd_postprocess(const float* dq_accum, const void* workspace, size_t wo
  */
 int attn_merge(const uint16_t* o_parts, const float* lse_parts, int n_parts, uint16_t* o, float* lse,
                attn_shape shape, void* stream);
+
+/*
+ * Packed variable-length sequences ("THD" layout).  The T rows of all
+ * sequences are stored back to back and located by int32 cumulative offsets
+ * cu_seqlens[0 .. n_seqs], the way the cuDNN frontend pull request "CSA: add
+ * fused Compressor forward+backward CuTe-DSL kernels (ported from
+ * Megatron-LM)" (NVIDIA cudnn-frontend #427, description) passes packs, rows
+ * at or past cu_seqlens[n_seqs] being static token-capacity padding.
+ * Attention never crosses sequences: sequence b (rows cu_seqlens[b] ..
+ * cu_seqlens[b+1]-1) is ordinary attention over its own rows, causal in its
+ * own positions when `causal`.
+ *   q, o, dout, dq [T,Hq,D] bf16; k, v, dk, dv [T,Hkv,D] bf16;
+ *   lse, delta [Hq,T] fp32; dq_accum [Hq,T,D] fp32 (head-major over rows).
+ *   cu_seqlens: DEVICE memory, n_seqs + 1 int32, read by the kernels (so the
+ *     host cannot check it).  It must be non-decreasing with every length
+ *     <= max_seqlen; the kernels clamp every offset to [0, T] and cut a
+ *     sequence to its first max_seqlen rows, so no access leaves the tensors
+ *     whatever it holds, but rows past the cut count as padding and
+ *     overlapping sequences give unspecified results.
+ * Rows outside every sequence (padding, and rows past such a cut) get O = 0,
+ * LSE = -inf and dK = dV = 0 (dQ = 0 through dq_accum); their dout is never
+ * read by the backward kernel.
+ *
+ * The preprocess and postprocess are the dense calls with the shape
+ *   { batch = 1, seqlen = T, heads_q, groups, head_dim }:
+ * the packed tensors are exactly the batch-1 dense tensors of that shape, and
+ * the workspace of attn_bwd_varlen starts with the same dK/dV partials.
+ */
+typedef struct attn_varlen_shape {
+  int32_t n_seqs;     /* >= 0 sequences; cu_seqlens has n_seqs + 1 entries */
+  int32_t total;      /* T >= 0 rows of the packed tensors (capacity) */
+  int32_t max_seqlen; /* >= 0, bound of every sequence length (sizes the grid) */
+  int32_t heads_q;    /* Hq >= 1 */
+  int32_t groups;     /* g >= 1, Hq % g == 0 */
+  int32_t head_dim;   /* 64 or 128 */
+} attn_varlen_shape;
+
+/*
+ * Forward over packed sequences: O and LSE of every sequence as attn_fwd
+ * computes them, padding rows O = 0 and LSE = -inf.  Every element of o and
+ * lse is written.  A call with total == 0 (after the shape, flag and scale
+ * checks) enqueues nothing and may pass NULL pointers.
+ */
+int attn_fwd_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
+                    const int32_t* cu_seqlens, attn_varlen_shape shape, float softmax_scale, int causal,
+                    void* stream);
+
+/*
+ * Workspace bytes of attn_bwd_varlen (0 when none is needed):
+ *   groups > 1: fp32 dK and dV partials, [T,Hq,D] each;
+ *   use_atomic == 0: fp32 dQ partials, [ceil(max_seqlen / 256),Hq,T,D].
+ * Returns 0 for an invalid shape.
+ */
+size_t attn_bwd_varlen_workspace_bytes(attn_varlen_shape shape, int causal, int use_atomic);
+
+/*
+ * Backward over packed sequences, with attn_bwd's contract per sequence:
+ * dq_accum must be zero on entry when use_atomic = 1 (the dense preprocess
+ * zeroes it) and is fully overwritten when use_atomic = 0 (sums in ascending
+ * key-block order, bitwise deterministic); groups == 1 writes dk and dv,
+ * groups > 1 writes the workspace partials for attn_bwd_postprocess.
+ * Padding rows get zero dK/dV (or zero partials) and no dQ contribution.
+ * A call with total == 0 (after the shape, flag and scale checks) enqueues
+ * nothing and may pass NULL pointers.
+ */
+int attn_bwd_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
+                    const float* lse, const float* delta, float* dq_accum, uint16_t* dk, uint16_t* dv,
+                    void* workspace, size_t workspace_bytes, const int32_t* cu_seqlens,
+                    attn_varlen_shape shape, float softmax_scale, int causal, int use_atomic, void* stream);
 
 #ifdef __cplusplus
 }

@@ -28,7 +28,8 @@ def shp(b=2, s=300, hq=8, g=2, d=128):
 def test_library_exports_every_header_symbol():
     names = bd.header_functions()
     assert names == sorted(["attn_fwd", "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_bwd",
-                            "attn_bwd_postprocess", "attn_merge", "attn_strerror"])
+                            "attn_bwd_postprocess", "attn_merge", "attn_strerror", "attn_fwd_varlen",
+                            "attn_bwd_varlen_workspace_bytes", "attn_bwd_varlen"])
     for n in names:
         assert hasattr(lib(), n), n
 
@@ -155,3 +156,80 @@ def test_python_shape_helpers():
     assert (sh.batch, sh.seqlen, sh.heads_q, sh.groups, sh.head_dim) == (2, 17, 8, 4, 64)
     with pytest.raises(ValueError):
         bd.shape_of(q, torch.empty((2, 17, 3, 64)))
+
+
+# ------------------------------------------------------------ packed sequences
+
+def vshp(n=3, t=1000, m=400, hq=8, g=2, d=128):
+    return bd.attn_varlen_shape(n, t, m, hq, g, d)
+
+
+@pytest.mark.parametrize("g", [1, 4])
+@pytest.mark.parametrize("m", [0, 1, 256, 257, 4096])
+def test_varlen_workspace_bytes(g, m):
+    sh = vshp(n=5, t=3000, m=m, hq=8, g=g, d=64)
+    nq = 3000 * 8 * 64
+    gqa = 2 * nq * 4 if g > 1 else 0
+    for causal in (0, 1):
+        assert lib().attn_bwd_varlen_workspace_bytes(sh, causal, 1) == gqa
+        assert lib().attn_bwd_varlen_workspace_bytes(sh, causal, 0) == gqa + math.ceil(m / 256) * nq * 4
+    assert lib().attn_bwd_varlen_workspace_bytes(vshp(hq=6, g=4), 0, 0) == 0
+    assert lib().attn_bwd_varlen_workspace_bytes(vshp(), 0, 7) == 0
+
+
+def vfwd(**kw):
+    args = dict(q=A, k=A, v=A, o=A, lse=A, cu=A, shape=vshp(), scale=0.1, causal=1, stream=None)
+    args.update(kw)
+    return lib().attn_fwd_varlen(args["q"], args["k"], args["v"], args["o"], args["lse"], args["cu"],
+                                 args["shape"], args["scale"], args["causal"], args["stream"])
+
+
+def vbwd(**kw):
+    args = dict(q=A, k=A, v=A, do=A, lse=A, delta=A, dq=A, dk=A, dv=A, ws=A, wsb=1 << 40, cu=A, shape=vshp(),
+                scale=0.1, causal=1, atomic=1, stream=None)
+    args.update(kw)
+    return lib().attn_bwd_varlen(args["q"], args["k"], args["v"], args["do"], args["lse"], args["delta"],
+                                 args["dq"], args["dk"], args["dv"], args["ws"], args["wsb"], args["cu"],
+                                 args["shape"], args["scale"], args["causal"], args["atomic"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"q": None}, "null"), ({"cu": None}, "null"), ({"lse": None}, "null"),
+    ({"shape": vshp(n=-1)}, "shape"), ({"shape": vshp(t=-1)}, "shape"), ({"shape": vshp(m=-1)}, "shape"),
+    ({"shape": vshp(hq=0)}, "shape"), ({"shape": vshp(hq=6, g=4)}, "shape"), ({"shape": vshp(d=96)}, "hd"),
+    ({"shape": vshp(t=1 << 20, hq=64, g=1)}, "range"), ({"shape": vshp(hq=65536, g=1)}, "range"),
+    ({"shape": vshp(n=1 << 20, m=1 << 16, hq=64, g=1, t=1000)}, "range"),
+    ({"scale": 0.0}, "range"), ({"causal": 3}, "flag"), ({"o": MIS}, "align"), ({"v": MIS}, "align"),
+])
+def test_fwd_varlen_errors(kw, code):
+    assert vfwd(**kw) == E[code]
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"dq": None}, "null"), ({"cu": None}, "null"), ({"shape": vshp(g=1), "dv": None}, "null"),
+    ({"shape": vshp(hq=7, g=2)}, "shape"), ({"shape": vshp(d=32)}, "hd"),
+    ({"atomic": 2}, "flag"), ({"scale": float("nan")}, "range"),
+    ({"ws": None}, "ws"), ({"wsb": 64}, "ws"), ({"atomic": 0, "shape": vshp(g=1), "ws": None}, "ws"),
+    ({"delta": MIS}, "align"), ({"ws": MIS}, "align"),
+])
+def test_bwd_varlen_errors(kw, code):
+    assert vbwd(**kw) == E[code]
+
+
+def test_varlen_empty_pack_is_a_no_op():
+    """total == 0: every check still runs, then nothing is enqueued (NULL
+    pointers allowed), so this runs without a GPU."""
+    empty = vshp(n=2, t=0, m=5)
+    assert vfwd(q=None, k=None, v=None, o=None, lse=None, cu=None, shape=empty) == 0
+    assert vbwd(q=None, k=None, v=None, do=None, lse=None, delta=None, dq=None, dk=None, dv=None, ws=None,
+                cu=None, shape=empty) == 0
+    assert vfwd(q=None, shape=empty, causal=2) == E["flag"]
+    assert vbwd(q=None, shape=bd.attn_varlen_shape(2, 0, 5, 8, 2, 96)) == E["hd"]
+
+
+def test_varlen_shape_helper():
+    import torch
+    q = torch.empty((50, 8, 64))
+    k = torch.empty((50, 2, 64))
+    sh = bd.varlen_shape_of(q, k, 4, 20)
+    assert (sh.n_seqs, sh.total, sh.max_seqlen, sh.heads_q, sh.groups, sh.head_dim) == (4, 50, 20, 8, 4, 64)
