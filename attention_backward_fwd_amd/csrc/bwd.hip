@@ -111,23 +111,25 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
   const int Hq = p.Hq, G = p.G, Hkv = p.Hkv;
   const int n_nblk = (p.S + BN - 1) / BN;
 
-  // Tile order: each XCD gets a contiguous range of (batch, KV head) groups
-  // and works through them one at a time (their Q/dO rows stay in its L2);
-  // inside a group, key blocks run heaviest-first (block 0 sees every query
-  // under causal masking) with the group's query heads side by side.
+  // Tile order: every eighth (batch, KV head) group goes to the same XCD,
+  // which works through its groups one at a time (their Q/dO rows stay in
+  // its L2; interleaving keeps the XCDs evenly loaded when sequences differ
+  // in length); inside a group, key blocks run heaviest-first (block 0 sees
+  // every query under causal masking) with the group's query heads side by
+  // side.
   const int nwg = gridDim.x, NG = p.B * Hkv;
-  int t = blockIdx.x, x = 0, NGx = NG;
+  int t = blockIdx.x, x = 0, nx = 1;
   if (NG % 8 == 0) {
     t = xcd_remap(blockIdx.x, nwg);
     const int per = nwg / 8;
     x = t / per;
     t -= x * per;
-    NGx = NG / 8;
+    nx = 8;
   }
   // (Integer division runs on the vector unit; readfirstlane returns the
   // results to scalar registers, where everything derived from them stays.)
   const int per_group = n_nblk * G;
-  const int grp = x * NGx + t / per_group;
+  const int grp = (t / per_group) * nx + x;
   const int jb = __builtin_amdgcn_readfirstlane((t % per_group) / G);
   const int r = t % G;
   const int b = __builtin_amdgcn_readfirstlane(grp / Hkv), kvh = __builtin_amdgcn_readfirstlane(grp % Hkv);

@@ -62,21 +62,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
   const int Hq = p.Hq, G = p.G, Hkv = p.Hkv;
   const int n_mblk = (p.S + BM - 1) / BM;
 
-  // Tile order: each XCD gets a contiguous range of (batch, KV head) groups
-  // and works through them one at a time, so a group's K/V stay in its L2;
-  // inside a group, query blocks run heaviest-first under causal masking,
-  // with the group's query heads side by side.
+  // Tile order: every eighth (batch, KV head) group goes to the same XCD,
+  // which works through its groups one at a time, so a group's K/V stay in
+  // its L2 (interleaving keeps the XCDs evenly loaded when sequences differ
+  // in length); inside a group, query blocks run heaviest-first under causal
+  // masking, with the group's query heads side by side.
   const int nwg = gridDim.x, NG = p.B * Hkv;
-  int t = blockIdx.x, x = 0, NGx = NG;
+  int t = blockIdx.x, x = 0, nx = 1;
   if (NG % 8 == 0) {
     t = xcd_remap(blockIdx.x, nwg);
     const int per = nwg / 8;
     x = t / per;
     t -= x * per;
-    NGx = NG / 8;
+    nx = 8;
   }
   const int per_group = n_mblk * G;
-  const int grp = x * NGx + t / per_group;
+  const int grp = (t / per_group) * nx + x;
   const int mbo = (t % per_group) / G;
   const int r = t % G;
   const int b = __builtin_amdgcn_readfirstlane(grp / Hkv), kvh = __builtin_amdgcn_readfirstlane(grp % Hkv);
