@@ -34,8 +34,10 @@ class attn_shape(ctypes.Structure):
 class attn_varlen_shape(ctypes.Structure):
     _fields_ = [
         ("n_seqs", ctypes.c_int32),
-        ("total", ctypes.c_int32),
-        ("max_seqlen", ctypes.c_int32),
+        ("total_q", ctypes.c_int32),
+        ("total_k", ctypes.c_int32),
+        ("max_seqlen_q", ctypes.c_int32),
+        ("max_seqlen_k", ctypes.c_int32),
         ("heads_q", ctypes.c_int32),
         ("groups", ctypes.c_int32),
         ("head_dim", ctypes.c_int32),
@@ -71,12 +73,14 @@ def library():
         lib.attn_merge.restype = ctypes.c_int
         lib.attn_merge.argtypes = [P, P, ctypes.c_int, P, P, attn_shape, P]
         lib.attn_fwd_varlen.restype = ctypes.c_int
-        lib.attn_fwd_varlen.argtypes = [P, P, P, P, P, P, attn_varlen_shape, ctypes.c_float, ctypes.c_int, P]
+        lib.attn_fwd_varlen.argtypes = [P, P, P, P, P, P, P, attn_varlen_shape, ctypes.c_float, ctypes.c_int, P]
         lib.attn_bwd_varlen_workspace_bytes.restype = ctypes.c_size_t
         lib.attn_bwd_varlen_workspace_bytes.argtypes = [attn_varlen_shape, ctypes.c_int, ctypes.c_int]
         lib.attn_bwd_varlen.restype = ctypes.c_int
-        lib.attn_bwd_varlen.argtypes = [P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P, attn_varlen_shape,
+        lib.attn_bwd_varlen.argtypes = [P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P, P, attn_varlen_shape,
                                         ctypes.c_float, ctypes.c_int, ctypes.c_int, P]
+        lib.attn_bwd_varlen_postprocess.restype = ctypes.c_int
+        lib.attn_bwd_varlen_postprocess.argtypes = [P, P, ctypes.c_size_t, P, P, P, attn_varlen_shape, P]
         _lib = lib
     return _lib
 
@@ -159,22 +163,29 @@ def attn_merge(o_parts, lse_parts, n_parts, o, lse, shape, stream=None):
                                 _stream(stream)), "attn_merge")
 
 
-def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, shape, softmax_scale, causal, stream=None):
-    _check(library().attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens), shape,
-                                     float(softmax_scale), int(causal), _stream(stream)), "attn_fwd_varlen")
+def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, shape, softmax_scale, causal, stream=None):
+    _check(library().attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens_q),
+                                     _ptr(cu_seqlens_k), shape, float(softmax_scale), int(causal), _stream(stream)),
+           "attn_fwd_varlen")
 
 
 def attn_bwd_varlen_workspace_bytes(shape, causal, use_atomic):
     return int(library().attn_bwd_varlen_workspace_bytes(shape, int(causal), int(use_atomic)))
 
 
-def attn_bwd_varlen(q, k, v, dout, lse, delta, dq_accum, dk, dv, workspace, cu_seqlens, shape, softmax_scale,
-                    causal, use_atomic, stream=None):
+def attn_bwd_varlen(q, k, v, dout, lse, delta, dq_accum, dk, dv, workspace, cu_seqlens_q, cu_seqlens_k, shape,
+                    softmax_scale, causal, use_atomic, stream=None):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(library().attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(delta),
                                      _ptr(dq_accum), _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes,
-                                     _ptr(cu_seqlens), shape, float(softmax_scale), int(causal), int(use_atomic),
-                                     _stream(stream)), "attn_bwd_varlen")
+                                     _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), shape, float(softmax_scale),
+                                     int(causal), int(use_atomic), _stream(stream)), "attn_bwd_varlen")
+
+
+def attn_bwd_varlen_postprocess(dq_accum, workspace, dq, dk, dv, shape, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().attn_bwd_varlen_postprocess(_ptr(dq_accum), _ptr(workspace), ws_bytes, _ptr(dq), _ptr(dk),
+                                                 _ptr(dv), shape, _stream(stream)), "attn_bwd_varlen_postprocess")
 
 
 # ------------------------------------------------------------ conveniences
@@ -239,13 +250,14 @@ def merge(o_parts, lse_parts, stream=None):
     return o, lse
 
 
-def varlen_shape_of(q, k, n_seqs, max_seqlen):
-    """attn_varlen_shape from packed q [T,Hq,D] and k [T,Hkv,D]."""
-    t, hq, d = q.shape
-    hkv = k.shape[1]
+def varlen_shape_of(q, k, n_seqs, max_seqlen_q, max_seqlen_k=None):
+    """attn_varlen_shape from packed q [Tq,Hq,D] and k [Tk,Hkv,D]."""
+    tq, hq, d = q.shape
+    tk, hkv = k.shape[0], k.shape[1]
     if hkv < 1 or hq % hkv:
         raise ValueError("heads_q must be a multiple of heads_kv")
-    return attn_varlen_shape(n_seqs, t, max_seqlen, hq, hq // hkv, d)
+    mk = max_seqlen_q if max_seqlen_k is None else max_seqlen_k
+    return attn_varlen_shape(n_seqs, tq, tk, max_seqlen_q, mk, hq, hq // hkv, d)
 
 
 def _require_cu(cu):
@@ -253,28 +265,32 @@ def _require_cu(cu):
         raise ValueError("cu_seqlens must be a contiguous int32 tensor on the GPU")
 
 
-def forward_varlen(q, k, v, cu_seqlens, max_seqlen, causal, scale, stream=None):
-    """Packed sequences: O [T,Hq,D], LSE [Hq,T]; allocates the outputs."""
+def forward_varlen(q, k, v, cu_seqlens_q, max_seqlen_q, causal, scale, cu_seqlens_k=None, max_seqlen_k=None,
+                   stream=None):
+    """Packed sequences: O [Tq,Hq,D], LSE [Hq,Tq]; allocates the outputs.
+    Keys default to the query offsets and bound."""
     _require_gpu_inputs(q, k, v)
-    _require_cu(cu_seqlens)
-    shape = varlen_shape_of(q, k, cu_seqlens.numel() - 1, max_seqlen)
+    cu_k = cu_seqlens_q if cu_seqlens_k is None else cu_seqlens_k
+    _require_cu(cu_seqlens_q)
+    _require_cu(cu_k)
+    shape = varlen_shape_of(q, k, cu_seqlens_q.numel() - 1, max_seqlen_q, max_seqlen_k)
     o = torch.empty_like(q)
     lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
-    attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, shape, scale, causal, stream)
+    attn_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_k, shape, scale, causal, stream)
     return o, lse
 
 
 class VarlenBwdBuffers:
     """Outputs and scratch of one packed-sequence backward problem."""
 
-    def __init__(self, q, k, n_seqs, max_seqlen, causal, use_atomic):
-        self.shape = varlen_shape_of(q, k, n_seqs, max_seqlen)
-        t, hq, d = q.shape
+    def __init__(self, q, k, n_seqs, max_seqlen_q, causal, use_atomic, max_seqlen_k=None):
+        self.shape = varlen_shape_of(q, k, n_seqs, max_seqlen_q, max_seqlen_k)
+        tq, hq, d = q.shape
         dev = q.device
-        # The preprocess and postprocess see the packed tensors as one batch.
-        self.dense = attn_shape(1, t, hq, self.shape.groups, d)
-        self.delta = torch.empty((hq, t), dtype=torch.float32, device=dev)
-        self.dq_accum = torch.empty((hq, t, d), dtype=torch.float32, device=dev)
+        # The preprocess sees the packed query tensors as one batch.
+        self.dense = attn_shape(1, tq, hq, self.shape.groups, d)
+        self.delta = torch.empty((hq, tq), dtype=torch.float32, device=dev)
+        self.dq_accum = torch.empty((hq, tq, d), dtype=torch.float32, device=dev)
         self.dq = torch.empty_like(q)
         self.dk = torch.empty_like(k)
         self.dv = torch.empty_like(k)
@@ -282,16 +298,18 @@ class VarlenBwdBuffers:
         self.workspace = torch.empty(nbytes // 4, dtype=torch.float32, device=dev) if nbytes else None
 
 
-def backward_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen, causal, scale, use_atomic=True, buffers=None,
-                    stream=None):
+def backward_varlen(q, k, v, o, lse, do, cu_seqlens_q, max_seqlen_q, causal, scale, use_atomic=True,
+                    buffers=None, cu_seqlens_k=None, max_seqlen_k=None, stream=None):
     """Packed sequences: dQ, dK, dV via preprocess -> bwd (-> sum) -> postprocess."""
     _require_gpu_inputs(q, k, v, o, do)
-    _require_cu(cu_seqlens)
-    bb = buffers or VarlenBwdBuffers(q, k, cu_seqlens.numel() - 1, max_seqlen, causal, use_atomic)
-    if q.shape[0] == 0:
-        return bb.dq, bb.dk, bb.dv
-    attn_bwd_preprocess(o, do, bb.delta, bb.dq_accum if use_atomic else None, bb.dense, stream)
-    attn_bwd_varlen(q, k, v, do, lse, bb.delta, bb.dq_accum, bb.dk, bb.dv, bb.workspace, cu_seqlens, bb.shape,
-                    scale, causal, use_atomic, stream)
-    attn_bwd_postprocess(bb.dq_accum, bb.workspace, bb.dq, bb.dk, bb.dv, bb.dense, stream)
+    cu_k = cu_seqlens_q if cu_seqlens_k is None else cu_seqlens_k
+    _require_cu(cu_seqlens_q)
+    _require_cu(cu_k)
+    bb = buffers or VarlenBwdBuffers(q, k, cu_seqlens_q.numel() - 1, max_seqlen_q, causal, use_atomic,
+                                     max_seqlen_k)
+    if q.shape[0] > 0:
+        attn_bwd_preprocess(o, do, bb.delta, bb.dq_accum if use_atomic else None, bb.dense, stream)
+    attn_bwd_varlen(q, k, v, do, lse, bb.delta, bb.dq_accum, bb.dk, bb.dv, bb.workspace, cu_seqlens_q, cu_k,
+                    bb.shape, scale, causal, use_atomic, stream)
+    attn_bwd_varlen_postprocess(bb.dq_accum, bb.workspace, bb.dq, bb.dk, bb.dv, bb.shape, stream)
     return bb.dq, bb.dk, bb.dv

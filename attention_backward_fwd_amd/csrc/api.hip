@@ -37,24 +37,35 @@ size_t ws_split_bytes(const attn_shape& s, int use_atomic) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 
-// Packed sequences: the same limits as the dense batch-1 problem of T rows.
+// Packed sequences: the same limits as the dense batch-1 problems of Tq
+// query rows and Tk key rows.
 int check_varlen(const attn_varlen_shape& s) {
-  if (s.n_seqs < 0 || s.total < 0 || s.max_seqlen < 0 || s.heads_q < 1 || s.groups < 1) return ATTN_ERR_BAD_SHAPE;
+  if (s.n_seqs < 0 || s.total_q < 0 || s.total_k < 0 || s.max_seqlen_q < 0 || s.max_seqlen_k < 0 ||
+      s.heads_q < 1 || s.groups < 1)
+    return ATTN_ERR_BAD_SHAPE;
   if (s.heads_q % s.groups) return ATTN_ERR_BAD_SHAPE;
   if (s.head_dim != 64 && s.head_dim != 128) return ATTN_ERR_HEAD_DIM;
-  if ((long long)s.total * s.heads_q * s.head_dim >= (1LL << 31)) return ATTN_ERR_RANGE;
-  if ((long long)s.heads_q * s.head_dim > (1LL << 22)) return ATTN_ERR_RANGE;
-  // Grid: n_seqs * heads * ceil(max_seqlen / 32) workgroups must fit 32 bits.
-  if ((long long)s.n_seqs * s.heads_q * ((s.max_seqlen + 31) / 32) >= (1LL << 31)) return ATTN_ERR_RANGE;
+  const long long hd = (long long)s.heads_q * s.head_dim;
+  if ((long long)s.total_q * hd >= (1LL << 31) || (long long)s.total_k * hd >= (1LL << 31)) return ATTN_ERR_RANGE;
+  if (hd > (1LL << 22)) return ATTN_ERR_RANGE;
+  // Grids: n_seqs * heads * ceil(max_seqlen / 32) workgroups must fit 32 bits.
+  const long long blk = (long long)((s.max_seqlen_q > s.max_seqlen_k ? s.max_seqlen_q : s.max_seqlen_k) + 31) / 32;
+  if ((long long)s.n_seqs * s.heads_q * blk >= (1LL << 31)) return ATTN_ERR_RANGE;
   return ATTN_OK;
 }
 
-size_t elems_varlen(const attn_varlen_shape& s) { return (size_t)s.total * s.heads_q * s.head_dim; }
-size_t ws_varlen_gqa_bytes(const attn_varlen_shape& s) { return s.groups > 1 ? 2 * elems_varlen(s) * 4 : 0; }
-size_t ws_varlen_split_bytes(const attn_varlen_shape& s, int use_atomic) {
-  const int nblk = (s.max_seqlen + kBwdBlockN - 1) / kBwdBlockN;
-  return use_atomic ? 0 : (size_t)nblk * elems_varlen(s) * 4;
+// Varlen workspace: [dK partials | dV partials] ([Tk][Hq][D] fp32 each) when
+// groups > 1, then the split path's dQ partials ([n_kv_blocks][Hq][Tq][D]).
+size_t ws_varlen_gqa_bytes(const attn_varlen_shape& s) {
+  return s.groups > 1 ? 2 * (size_t)s.total_k * s.heads_q * s.head_dim * 4 : 0;
 }
+size_t ws_varlen_split_bytes(const attn_varlen_shape& s, int use_atomic) {
+  const int nblk = (s.max_seqlen_k + kBwdBlockN - 1) / kBwdBlockN;
+  return use_atomic ? 0 : (size_t)nblk * s.total_q * s.heads_q * s.head_dim * 4;
+}
+
+// Sequences with rows on both sides exist: the main kernels have work.
+bool varlen_any(const attn_varlen_shape& s) { return s.n_seqs > 0 && s.max_seqlen_q > 0 && s.max_seqlen_k > 0; }
 
 }  // namespace
 
@@ -100,7 +111,9 @@ int attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* 
   p.scale = softmax_scale;
   p.causal = causal;
   p.cu = nullptr;
-  p.T = 0;
+  p.cu_k = nullptr;
+  p.T = p.Tk = 0;
+  p.Sk = shape.seqlen;
   return hip_status(launch_fwd(p, (hipStream_t)stream));
 }
 
@@ -164,7 +177,9 @@ int attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint
   p.causal = causal;
   p.use_atomic = use_atomic;
   p.cu = nullptr;
-  p.T = 0;
+  p.cu_k = nullptr;
+  p.T = p.Tk = 0;
+  p.Sk = shape.seqlen;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = launch_bwd(p, s);
   if (e != hipSuccess) return ATTN_ERR_HIP;
@@ -188,7 +203,8 @@ int attn_bwd_postprocess(const float* dq_accum, const void* workspace, size_t wo
   return hip_status(launch_postprocess(dq_accum, gqa ? (const float*)ws : nullptr,
                                        gqa ? (const float*)(ws + nq_bytes) : nullptr, dq, gqa ? dk : nullptr,
                                        gqa ? dv : nullptr, shape.batch, shape.seqlen, shape.heads_q,
-                                       shape.groups, shape.head_dim, (hipStream_t)stream));
+                                       shape.groups, shape.head_dim, (long long)shape.batch * shape.seqlen,
+                                       (hipStream_t)stream));
 }
 
 int attn_merge(const uint16_t* o_parts, const float* lse_parts, int n_parts, uint16_t* o, float* lse,
@@ -203,27 +219,31 @@ int attn_merge(const uint16_t* o_parts, const float* lse_parts, int n_parts, uin
 }
 
 int attn_fwd_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
-                    const int32_t* cu_seqlens, attn_varlen_shape shape, float softmax_scale, int causal,
-                    void* stream) {
+                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, attn_varlen_shape shape,
+                    float softmax_scale, int causal, void* stream) {
   const int st = check_varlen(shape);
   if (st) return st;
   if (causal != 0 && causal != 1) return ATTN_ERR_FLAG;
   if (!good_scale(softmax_scale)) return ATTN_ERR_RANGE;
-  if (shape.total == 0) return ATTN_OK;  // no rows: nothing to do, pointers unused
-  if (!q || !k || !v || !o || !lse || !cu_seqlens) return ATTN_ERR_NULL_PTR;
+  if (shape.total_q == 0) return ATTN_OK;  // no query rows: nothing to do, pointers unused
+  if (!q || !o || !lse || !cu_seqlens_q || !cu_seqlens_k) return ATTN_ERR_NULL_PTR;
+  if (shape.total_k > 0 && (!k || !v)) return ATTN_ERR_NULL_PTR;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return ATTN_ERR_ALIGN;
   hipStream_t s = (hipStream_t)stream;
-  if (shape.n_seqs > 0 && shape.max_seqlen > 0) {
+  if (shape.total_k > 0 && varlen_any(shape)) {
     FwdParams p;
     p.q = q;
     p.k = k;
     p.v = v;
     p.o = o;
     p.lse = lse;
-    p.cu = cu_seqlens;
-    p.T = shape.total;
+    p.cu = cu_seqlens_q;
+    p.cu_k = cu_seqlens_k;
+    p.T = shape.total_q;
+    p.Tk = shape.total_k;
     p.B = shape.n_seqs;
-    p.S = shape.max_seqlen;
+    p.S = shape.max_seqlen_q;
+    p.Sk = shape.max_seqlen_k;
     p.Hq = shape.heads_q;
     p.G = shape.groups;
     p.Hkv = shape.heads_q / shape.groups;
@@ -232,9 +252,14 @@ int attn_fwd_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v, uin
     p.causal = causal;
     const hipError_t e = launch_fwd(p, s);
     if (e != hipSuccess) return ATTN_ERR_HIP;
+    // Rows inside a sequence are all written by the kernel (O = 0 and
+    // LSE = -inf where no key is visible); the rest is padding.
+    return hip_status(launch_pad_fill(o, nullptr, 0, shape.heads_q, lse, shape.heads_q, -INFINITY, cu_seqlens_q,
+                                      shape.n_seqs, shape.total_q, shape.max_seqlen_q, shape.head_dim, s));
   }
-  return hip_status(launch_pad_fill(o, nullptr, 0, shape.heads_q, lse, shape.heads_q, -INFINITY, cu_seqlens,
-                                    shape.n_seqs, shape.total, shape.max_seqlen, shape.head_dim, s));
+  // No key anywhere: every query row is empty.
+  return hip_status(launch_pad_fill(o, nullptr, 0, shape.heads_q, lse, shape.heads_q, -INFINITY, cu_seqlens_q, 0,
+                                    shape.total_q, 0, shape.head_dim, s));
 }
 
 size_t attn_bwd_varlen_workspace_bytes(attn_varlen_shape shape, int causal, int use_atomic) {
@@ -245,15 +270,18 @@ size_t attn_bwd_varlen_workspace_bytes(attn_varlen_shape shape, int causal, int 
 
 int attn_bwd_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
                     const float* lse, const float* delta, float* dq_accum, uint16_t* dk, uint16_t* dv,
-                    void* workspace, size_t workspace_bytes, const int32_t* cu_seqlens,
-                    attn_varlen_shape shape, float softmax_scale, int causal, int use_atomic, void* stream) {
+                    void* workspace, size_t workspace_bytes, const int32_t* cu_seqlens_q,
+                    const int32_t* cu_seqlens_k, attn_varlen_shape shape, float softmax_scale, int causal,
+                    int use_atomic, void* stream) {
   const int st = check_varlen(shape);
   if (st) return st;
   if ((causal != 0 && causal != 1) || (use_atomic != 0 && use_atomic != 1)) return ATTN_ERR_FLAG;
   if (!good_scale(softmax_scale)) return ATTN_ERR_RANGE;
-  if (shape.total == 0) return ATTN_OK;  // no rows: nothing to do, pointers unused
-  if (!q || !k || !v || !dout || !lse || !delta || !dq_accum || !cu_seqlens) return ATTN_ERR_NULL_PTR;
-  if (shape.groups == 1 && (!dk || !dv)) return ATTN_ERR_NULL_PTR;
+  if (shape.total_q == 0 && shape.total_k == 0) return ATTN_OK;  // no rows: nothing to do, pointers unused
+  if (!cu_seqlens_q || !cu_seqlens_k) return ATTN_ERR_NULL_PTR;
+  if (shape.total_q > 0 && (!q || !dout || !lse || !delta || !dq_accum)) return ATTN_ERR_NULL_PTR;
+  if (shape.total_k > 0 && (!k || !v)) return ATTN_ERR_NULL_PTR;
+  if (shape.total_k > 0 && shape.groups == 1 && (!dk || !dv)) return ATTN_ERR_NULL_PTR;
   const size_t need = ws_varlen_gqa_bytes(shape) + ws_varlen_split_bytes(shape, use_atomic);
   if (need && (!workspace || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(lse) ||
@@ -272,15 +300,18 @@ int attn_bwd_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v, con
   p.dk = dk;
   p.dv = dv;
   char* ws = (char*)workspace;
-  const size_t nq_bytes = elems_varlen(shape) * sizeof(float);
   const bool gqa = shape.groups > 1;
+  const size_t nkv_bytes = (size_t)shape.total_k * shape.heads_q * shape.head_dim * sizeof(float);
   p.dk_part = gqa ? (float*)ws : nullptr;
-  p.dv_part = gqa ? (float*)(ws + nq_bytes) : nullptr;
+  p.dv_part = gqa ? (float*)(ws + nkv_bytes) : nullptr;
   p.dq_part = use_atomic ? nullptr : (float*)(ws + ws_varlen_gqa_bytes(shape));
-  p.cu = cu_seqlens;
-  p.T = shape.total;
+  p.cu = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  p.T = shape.total_q;
+  p.Tk = shape.total_k;
   p.B = shape.n_seqs;
-  p.S = shape.max_seqlen;
+  p.S = shape.max_seqlen_q;
+  p.Sk = shape.max_seqlen_k;
   p.Hq = shape.heads_q;
   p.G = shape.groups;
   p.Hkv = shape.heads_q / shape.groups;
@@ -291,19 +322,44 @@ int attn_bwd_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v, con
   p.use_atomic = use_atomic;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
-  const bool any = shape.n_seqs > 0 && shape.max_seqlen > 0;
-  if (any) e = launch_bwd(p, s);
+  const bool run = shape.total_q > 0 && shape.total_k > 0 && varlen_any(shape);
+  if (run) e = launch_bwd(p, s);
   if (e != hipSuccess) return ATTN_ERR_HIP;
-  // Padding rows: zero dK/dV (the fp32 partials when groups > 1).
-  e = gqa ? launch_pad_fill(p.dk_part, p.dv_part, 1, shape.heads_q, nullptr, shape.heads_q, 0.f, cu_seqlens,
-                            shape.n_seqs, shape.total, shape.max_seqlen, shape.head_dim, s)
-          : launch_pad_fill(dk, dv, 0, p.Hkv, nullptr, shape.heads_q, 0.f, cu_seqlens, shape.n_seqs, shape.total,
-                            shape.max_seqlen, shape.head_dim, s);
-  if (e != hipSuccess) return ATTN_ERR_HIP;
-  if (!use_atomic)
-    e = launch_dq_sum_varlen(p.dq_part, dq_accum, cu_seqlens, shape.n_seqs, shape.total, shape.max_seqlen,
-                             shape.heads_q, shape.head_dim, causal, s);
+  // Key rows outside every sequence (all of them when the kernel had no
+  // work): zero dK/dV (the fp32 partials when groups > 1).
+  if (shape.total_k > 0) {
+    const int ns = run ? shape.n_seqs : 0;
+    e = gqa ? launch_pad_fill(p.dk_part, p.dv_part, 1, shape.heads_q, nullptr, shape.heads_q, 0.f, cu_seqlens_k,
+                              ns, shape.total_k, shape.max_seqlen_k, shape.head_dim, s)
+            : launch_pad_fill(dk, dv, 0, p.Hkv, nullptr, shape.heads_q, 0.f, cu_seqlens_k, ns, shape.total_k,
+                              shape.max_seqlen_k, shape.head_dim, s);
+    if (e != hipSuccess) return ATTN_ERR_HIP;
+  }
+  if (!use_atomic && shape.total_q > 0)
+    e = launch_dq_sum_varlen(p.dq_part, dq_accum, cu_seqlens_q, cu_seqlens_k, shape.n_seqs, shape.total_q,
+                             shape.total_k, shape.max_seqlen_q, shape.max_seqlen_k, shape.heads_q, shape.head_dim,
+                             causal, s);
   return hip_status(e);
+}
+
+int attn_bwd_varlen_postprocess(const float* dq_accum, const void* workspace, size_t workspace_bytes,
+                                uint16_t* dq, uint16_t* dk, uint16_t* dv, attn_varlen_shape shape,
+                                void* stream) {
+  const int st = check_varlen(shape);
+  if (st) return st;
+  const bool gqa = shape.groups > 1 && shape.total_k > 0;
+  if (shape.total_q == 0 && !gqa) return ATTN_OK;  // nothing to convert, pointers unused
+  if (shape.total_q > 0 && (!dq_accum || !dq)) return ATTN_ERR_NULL_PTR;
+  if (gqa && (!dk || !dv)) return ATTN_ERR_NULL_PTR;
+  if (gqa && (!workspace || workspace_bytes < ws_varlen_gqa_bytes(shape))) return ATTN_ERR_WORKSPACE;
+  if (!aligned16(dq_accum) || !aligned16(dq) || (gqa && (!aligned16(dk) || !aligned16(dv) || !aligned16(workspace))))
+    return ATTN_ERR_ALIGN;
+  const char* ws = (const char*)workspace;
+  const size_t nkv_bytes = (size_t)shape.total_k * shape.heads_q * shape.head_dim * sizeof(float);
+  return hip_status(launch_postprocess(dq_accum, gqa ? (const float*)ws : nullptr,
+                                       gqa ? (const float*)(ws + nkv_bytes) : nullptr, dq, gqa ? dk : nullptr,
+                                       gqa ? dv : nullptr, 1, shape.total_q, shape.heads_q, gqa ? shape.groups : 1,
+                                       shape.head_dim, shape.total_k, (hipStream_t)stream));
 }
 
 }  // extern "C"

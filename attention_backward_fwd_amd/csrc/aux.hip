@@ -89,12 +89,14 @@ __device__ __forceinline__ int seq_of_row(const int* cu, int n_seqs, int T, int 
 }
 
 // Packed sequences, split path: dq_accum[h, t, :] = sum over the key blocks
-// j = 0 .. J of row t's own sequence (J: the block holding t's position under
-// causal masking, else the sequence's last block) of part[j][h, t, :], in
-// ascending j; 0 for rows outside every sequence.  Rows are [Hq][T].
+// j = 0 .. J of row t's own sequence of part[j][h, t, :], in ascending j, J
+// being the block of the last key the row sees (under causal masking, key
+// position + lk - lq; else the sequence's last key); 0 for rows outside every
+// sequence and rows that see no key.  Rows are [Hq][T].
 __global__ __launch_bounds__(256) void dq_sum_varlen_kernel(const float* __restrict__ part,
                                                             float* __restrict__ dq, const int* __restrict__ cu,
-                                                            int n_seqs, int T, int S, long long n4, int D,
+                                                            const int* __restrict__ cu_k, int n_seqs, int T,
+                                                            int Tk, int S, int Sk, long long n4, int D,
                                                             int causal) {
   const size_t slot = (size_t)n4 * 4;
   for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long long)gridDim.x * 256) {
@@ -102,10 +104,13 @@ __global__ __launch_bounds__(256) void dq_sum_varlen_kernel(const float* __restr
     const int t = (int)((e / D) % T);
     int start = 0, len = 0;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (seq_of_row(cu, n_seqs, T, S, t, start, len) >= 0) {
-      const int last = causal ? (t - start) / kBwdBlockN : (len - 1) / kBwdBlockN;
+    const int b = seq_of_row(cu, n_seqs, T, S, t, start, len);
+    if (b >= 0) {
+      const int lk = seq_rows(cu_k, Tk, b, Sk).len;
+      const int last_key = causal ? min(t - start + lk - len, lk - 1) : lk - 1;
       const float* src = part + e;
-      for (int j = 0; j <= last; j++) acc += *reinterpret_cast<const f32x4*>(src + (size_t)j * slot);
+      if (last_key >= 0)
+        for (int j = 0; j <= last_key / kBwdBlockN; j++) acc += *reinterpret_cast<const f32x4*>(src + (size_t)j * slot);
     }
     *reinterpret_cast<f32x4*>(dq + e) = acc;
   }
@@ -211,11 +216,11 @@ hipError_t launch_dq_sum(const float* dq_part, float* dq_accum, int B, int S, in
   return hipGetLastError();
 }
 
-hipError_t launch_dq_sum_varlen(const float* dq_part, float* dq_accum, const int* cu, int n_seqs, int T, int S,
-                                int Hq, int D, int causal, hipStream_t stream) {
+hipError_t launch_dq_sum_varlen(const float* dq_part, float* dq_accum, const int* cu, const int* cu_k, int n_seqs,
+                                int T, int Tk, int S, int Sk, int Hq, int D, int causal, hipStream_t stream) {
   const long long n4 = (long long)T * Hq * D / 4;
   hipLaunchKernelGGL(dq_sum_varlen_kernel, dim3(grid_for(n4, 256)), dim3(256), 0, stream, dq_part, dq_accum, cu,
-                     n_seqs, T, S, n4, D, causal);
+                     cu_k, n_seqs, T, Tk, S, Sk, n4, D, causal);
   return hipGetLastError();
 }
 
@@ -229,9 +234,9 @@ hipError_t launch_pad_fill(void* x0, void* x1, int fp32, int heads, float* lse, 
 
 hipError_t launch_postprocess(const float* dq_accum, const float* dk_part, const float* dv_part, uint16_t* dq,
                               uint16_t* dk, uint16_t* dv, int B, int S, int Hq, int G, int D,
-                              hipStream_t stream) {
+                              long long kv_rows, hipStream_t stream) {
   const long long nq8 = (long long)B * S * Hq * D / 8;
-  const long long nkv8 = G > 1 ? (long long)B * S * (Hq / G) * D / 8 : 0;
+  const long long nkv8 = G > 1 ? kv_rows * (Hq / G) * D / 8 : 0;
   hipLaunchKernelGGL(postprocess_kernel, dim3(grid_for(nq8 + nkv8, 256)), dim3(256), 0, stream, dq_accum,
                      dk_part, dv_part, dq, dk, dv, nq8, nkv8, G, D, S, Hq);
   return hipGetLastError();

@@ -109,52 +109,59 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (scalar)
   const int hi = lane >> 5, l32 = lane & 31;
   const int Hq = p.Hq, G = p.G, Hkv = p.Hkv;
-  const int n_nblk = (p.S + BN - 1) / BN;
+  const int n_nblk = (p.Sk + BN - 1) / BN;
 
-  // Tile order: every eighth (batch, KV head) group goes to the same XCD,
-  // which works through its groups one at a time (their Q/dO rows stay in
-  // its L2; interleaving keeps the XCDs evenly loaded when sequences differ
-  // in length); inside a group, key blocks run heaviest-first (block 0 sees
-  // every query under causal masking) with the group's query heads side by
-  // side.
+  // Tile order: each XCD gets a contiguous range of (batch, KV head) groups
+  // (packed sequences: every eighth group, so that sequences of unequal
+  // length load the XCDs evenly) and works through them one at a time (their
+  // Q/dO rows stay in its L2); inside a group, key blocks run heaviest-first
+  // (block 0 sees every query under causal masking) with the group's query
+  // heads side by side.
   const int nwg = gridDim.x, NG = p.B * Hkv;
-  int t = blockIdx.x, x = 0, nx = 1;
+  int t = blockIdx.x, x = 0, nx = 1, NGx = NG;
   if (NG % 8 == 0) {
     t = xcd_remap(blockIdx.x, nwg);
     const int per = nwg / 8;
     x = t / per;
     t -= x * per;
     nx = 8;
+    NGx = NG / 8;
   }
   // (Integer division runs on the vector unit; readfirstlane returns the
   // results to scalar registers, where everything derived from them stays.)
   const int per_group = n_nblk * G;
-  const int grp = (t / per_group) * nx + x;
+  const int grp = p.cu ? (t / per_group) * nx + x : x * NGx + t / per_group;
   const int jb = __builtin_amdgcn_readfirstlane((t % per_group) / G);
   const int r = t % G;
   const int b = __builtin_amdgcn_readfirstlane(grp / Hkv), kvh = __builtin_amdgcn_readfirstlane(grp % Hkv);
   const int h = __builtin_amdgcn_readfirstlane(kvh * G + r);
   const int n0 = jb * BN;
-  // This sequence's rows (packed sequences: its own length; key blocks past
-  // it have nothing to do).
+  // This sequence's query and key rows (packed sequences: their own
+  // lengths; key blocks past the end have nothing to do).  Query i sees key
+  // j iff j <= i + off under causal masking.
   const SeqRows sr = seq_rows(p.cu, p.T, b, p.S);
+  const SeqRows sk = seq_rows(p.cu ? p.cu_k : nullptr, p.Tk, b, p.Sk);
   const int S = __builtin_amdgcn_readfirstlane(sr.len), row0 = __builtin_amdgcn_readfirstlane(sr.base);
-  if (n0 >= S) return;
+  const int Sk = __builtin_amdgcn_readfirstlane(sk.len), krow0 = __builtin_amdgcn_readfirstlane(sk.base);
+  const int off = Sk - S;
+  if (n0 >= Sk) return;
   // Row-indexed tensors: [B][Hq][S], or [Hq][T] for packed sequences.
   const size_t hrow0 = p.cu ? (size_t)h * p.T + row0 : (size_t)(b * Hq + h) * S;
 
   const size_t qrs = (size_t)Hq * D, kvrs = (size_t)Hkv * D;
   const uint16_t* Qb = p.q + ((size_t)row0 * Hq + h) * D;
   const uint16_t* dOb = p.dout + ((size_t)row0 * Hq + h) * D;
-  const uint16_t* Kb = p.k + ((size_t)row0 * Hkv + kvh) * D;
-  const uint16_t* Vb = p.v + ((size_t)row0 * Hkv + kvh) * D;
+  const uint16_t* Kb = p.k + ((size_t)krow0 * Hkv + kvh) * D;
+  const uint16_t* Vb = p.v + ((size_t)krow0 * Hkv + kvh) * D;
   const float* lse_b = p.lse + hrow0;
   const float* dl_b = p.delta + hrow0;
 
   const float c = p.scale * kLog2e;
   const float lsc = p.log2_scale;
-  const int m_begin = CAUSAL ? n0 : 0;  // n0 is a multiple of BM
-  const int n_steps = (S - m_begin + BM - 1) / BM;
+  // Query blocks that see a key of this block: from the one holding query
+  // n0 - off on (causal); none when that is past the end (dK = dV = 0).
+  const int m_begin = CAUSAL ? max(n0 - off, 0) / BM * BM : 0;
+  const int n_steps = S > m_begin ? (S - m_begin + BM - 1) / BM : 0;
 
   // LSE and Delta of a query block land in LDS as raw fp32 rows (waves 0
   // and 1 each issue one 4-byte LDS-DMA load); rows past the end repeat the
@@ -164,10 +171,12 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     if (w == 1) row_load_async(dl_b + m0, S - m0, d_dst, lane);
   };
   // Key block (resident for the whole sweep) and the first Q/dO block.
-  tile_load_async<D, BN, NW>(Kb, kvrs, n0, S, sK, w, lane);
-  tile_load_async<D, BM, NW>(Qb, qrs, m_begin, S, sQ0, w, lane);
-  tile_load_async<D, BM, NW>(dOb, qrs, m_begin, S, sdO0, w, lane);
-  load_rows(m_begin, sL0, sD0);
+  tile_load_async<D, BN, NW>(Kb, kvrs, n0, Sk, sK, w, lane);
+  if (n_steps > 0) {
+    tile_load_async<D, BM, NW>(Qb, qrs, m_begin, S, sQ0, w, lane);
+    tile_load_async<D, BM, NW>(dOb, qrs, m_begin, S, sdO0, w, lane);
+    load_rows(m_begin, sL0, sD0);
+  }
   // This wave's keys: n0 + 32w + l32.  Its V rows are the B operand of dP
   // (lane l: V[key][16ks + 8hi .. +7]) and stay in registers; keys past the
   // end read the last row (their P is masked to zero).  The first step
@@ -176,7 +185,7 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
   const int key_l = n0 + 32 * w + l32;
   bf16x8 vb[NKS];
   {
-    const uint16_t* vrow = Vb + (size_t)min(key_l, S - 1) * kvrs + 8 * hi;
+    const uint16_t* vrow = Vb + (size_t)min(key_l, Sk - 1) * kvrs + 8 * hi;
 #pragma unroll
     for (int ks = 0; ks < NKS; ks++) vb[ks] = *reinterpret_cast<const bf16x8*>(vrow + 16 * ks);
   }
@@ -376,7 +385,7 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     // whose 32 keys lie past that has P = 0 throughout: it skips the four
     // products, writes zeros as its rows of dS'^T and only takes part in dQ
     // and the barriers.
-    const int n_vis = CAUSAL ? min(min(BN, S - n0), m0 + BM - n0) : min(BN, S - n0);
+    const int n_vis = CAUSAL ? min(min(BN, Sk - n0), m0 + BM + off - n0) : min(BN, Sk - n0);
     const bool active = 32 * w < n_vis;
     f32x4 dq[DQF4];
     if (active) {
@@ -438,9 +447,9 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
       // and from queries at or past qend (rows past the end of the sequence);
       // both limits are taken relative to 4hi, so that the per-element query
       // index is a constant.
-      if ((n0 + BN > S) || (m0 + BM > S) || (CAUSAL && m0 < n0 + BN)) {
+      if ((n0 + BN > Sk) || (m0 + BM > S) || (CAUSAL && m0 + off < n0 + BN)) {
         const int key_e = n0 + 32 * w + ll32;
-        const int qlim = (key_e >= S ? BM : (CAUSAL ? key_e - m0 : -1)) - 4 * lhi;
+        const int qlim = (key_e >= Sk ? BM : (CAUSAL ? key_e - off - m0 : -1)) - 4 * lhi;
         softmax_grad(std::true_type{}, qlim, S - m0 - 4 * lhi);
       } else {
         softmax_grad(std::false_type{}, 0, 0);
@@ -494,7 +503,7 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     if (st + 1 < n_steps) step(std::integral_constant<int, 1>{}, st + 1);
   }
   // dQ of the last block.
-  {
+  if (n_steps > 0) {
     lds_barrier();  // its dS'^T complete
     f32x4 dq[DQF4];
     dq_block(((n_steps - 1) & 1) ? sdSt1 : sdSt0, dq);
@@ -511,15 +520,15 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
     for (int j = 0; j < 16; j++) {
       const int key = n0 + 32 * w + 8 * (j >> 2) + 4 * ehi + (j & 3);
-      if (key < S) {
+      if (key < Sk) {
         if (PARTIAL) {
-          const size_t off = ((size_t)(row0 + key) * Hq + h) * D + d;
-          p.dk_part[off] = dk[dt][j];
-          p.dv_part[off] = dv[dt][j] * inv_scale;
+          const size_t o = ((size_t)(krow0 + key) * Hq + h) * D + d;
+          p.dk_part[o] = dk[dt][j];
+          p.dv_part[o] = dv[dt][j] * inv_scale;
         } else {
-          const size_t off = ((size_t)(row0 + key) * Hkv + kvh) * D + d;
-          p.dk[off] = to_bf16(dk[dt][j]);
-          p.dv[off] = to_bf16(dv[dt][j] * inv_scale);
+          const size_t o = ((size_t)(krow0 + key) * Hkv + kvh) * D + d;
+          p.dk[o] = to_bf16(dk[dt][j]);
+          p.dv[o] = to_bf16(dv[dt][j] * inv_scale);
         }
       }
     }
@@ -528,7 +537,7 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
 
 template <int D, bool CAUSAL, bool ATOMIC, bool PARTIAL>
 hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
-  const int n_nblk = (p.S + kBN - 1) / kBN;
+  const int n_nblk = (p.Sk + kBN - 1) / kBN;
   const long long nwg = (long long)p.B * p.Hq * n_nblk;
   hipLaunchKernelGGL((bwd_kernel<D, CAUSAL, ATOMIC, PARTIAL>), dim3((unsigned)nwg), dim3(kNW * 64), 0, stream, p);
   return hipGetLastError();

@@ -62,46 +62,56 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
   const int Hq = p.Hq, G = p.G, Hkv = p.Hkv;
   const int n_mblk = (p.S + BM - 1) / BM;
 
-  // Tile order: every eighth (batch, KV head) group goes to the same XCD,
-  // which works through its groups one at a time, so a group's K/V stay in
-  // its L2 (interleaving keeps the XCDs evenly loaded when sequences differ
-  // in length); inside a group, query blocks run heaviest-first under causal
-  // masking, with the group's query heads side by side.
+  // Tile order: each XCD gets a contiguous range of (batch, KV head) groups
+  // (packed sequences: every eighth group, so that sequences of unequal
+  // length load the XCDs evenly) and works through them one at a time, so a
+  // group's K/V stay in its L2; inside a group, query blocks run
+  // heaviest-first under causal masking, with the group's query heads side by
+  // side.
   const int nwg = gridDim.x, NG = p.B * Hkv;
-  int t = blockIdx.x, x = 0, nx = 1;
+  int t = blockIdx.x, x = 0, nx = 1, NGx = NG;
   if (NG % 8 == 0) {
     t = xcd_remap(blockIdx.x, nwg);
     const int per = nwg / 8;
     x = t / per;
     t -= x * per;
     nx = 8;
+    NGx = NG / 8;
   }
   const int per_group = n_mblk * G;
-  const int grp = (t / per_group) * nx + x;
+  const int grp = p.cu ? (t / per_group) * nx + x : x * NGx + t / per_group;
   const int mbo = (t % per_group) / G;
   const int r = t % G;
   const int b = __builtin_amdgcn_readfirstlane(grp / Hkv), kvh = __builtin_amdgcn_readfirstlane(grp % Hkv);
   const int h = __builtin_amdgcn_readfirstlane(kvh * G + r);
-  // This sequence's rows (packed sequences: its own length; blocks past it
-  // have nothing to do).  Causal blocks still run heaviest-first.
+  // This sequence's query and key rows (packed sequences: their own
+  // lengths; query blocks past the end have nothing to do).  Causal blocks
+  // still run heaviest-first.  Query i sees key j iff j <= i + off.
   const SeqRows sr = seq_rows(p.cu, p.T, b, p.S);
+  const SeqRows sk = seq_rows(p.cu ? p.cu_k : nullptr, p.Tk, b, p.Sk);
   const int S = __builtin_amdgcn_readfirstlane(sr.len), row0 = __builtin_amdgcn_readfirstlane(sr.base);
+  const int Sk = __builtin_amdgcn_readfirstlane(sk.len), krow0 = __builtin_amdgcn_readfirstlane(sk.base);
+  const int off = Sk - S;
   const int n_mblk_b = (S + BM - 1) / BM;
   const int mb = CAUSAL ? (n_mblk_b - 1 - mbo) : mbo;
   if (mb < 0 || mb >= n_mblk_b) return;
 
   const size_t qrs = (size_t)Hq * D, kvrs = (size_t)Hkv * D;
   const uint16_t* Qb = p.q + ((size_t)row0 * Hq + h) * D;
-  const uint16_t* Kb = p.k + ((size_t)row0 * Hkv + kvh) * D;
-  const uint16_t* Vb = p.v + ((size_t)row0 * Hkv + kvh) * D;
+  const uint16_t* Kb = p.k + ((size_t)krow0 * Hkv + kvh) * D;
+  const uint16_t* Vb = p.v + ((size_t)krow0 * Hkv + kvh) * D;
 
   const int q0 = mb * BM + 32 * w;  // first query of this wave
   const int qi = q0 + l32;          // this lane's query
-  const int n_end = CAUSAL ? min(S, mb * BM + BM) : S;
+  // Keys the block's queries can see; none (n_tiles = 0) leaves O = 0 and
+  // LSE = -inf.
+  const int n_end = CAUSAL ? max(0, min(Sk, mb * BM + BM + off)) : Sk;
   const int n_tiles = (n_end + BN - 1) / BN;
 
-  tile_load_async<D, BN>(Kb, kvrs, 0, S, sK0, w, lane);
-  tile_load_async<D, BN>(Vb, kvrs, 0, S, sV0, w, lane);
+  if (n_tiles > 0) {
+    tile_load_async<D, BN>(Kb, kvrs, 0, Sk, sK0, w, lane);
+    tile_load_async<D, BN>(Vb, kvrs, 0, Sk, sV0, w, lane);
+  }
 
   bf16x8 qf[NKS];
   if (qi < S) {
@@ -138,11 +148,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     wait_vmem();
     lds_barrier();  // tile it resident; every wave is done with tile it-1
     if (it + 1 < n_tiles) {
-      tile_load_async<D, BN>(Kb, kvrs, n0 + BN, S, nK, w, lane);
-      tile_load_async<D, BN>(Vb, kvrs, n0 + BN, S, nV, w, lane);
+      tile_load_async<D, BN>(Kb, kvrs, n0 + BN, Sk, nK, w, lane);
+      tile_load_async<D, BN>(Vb, kvrs, n0 + BN, Sk, nV, w, lane);
     }
     // A wave whose queries all precede the tile has nothing to do in it.
-    if (CAUSAL && n0 > q0 + 31) return;
+    if (CAUSAL && n0 > q0 + 31 + off) return;
     const int offA = opaque_v(offA0), offV0 = opaque_v(offV00), offV1 = opaque_v(offV10);
 
     // S^T (64 keys x 32 queries): element j of s[mt] is key
@@ -166,8 +176,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
 
     // Edge tiles (past the end, or crossing the causal diagonal): a key at
     // tile offset k is visible iff k <= lim.
-    if ((n0 + BN > S) || (CAUSAL && n0 + BN - 1 > q0)) {
-      const int lim = (CAUSAL ? min(S - 1, qi) : S - 1) - n0 - 4 * hi;
+    if ((n0 + BN > Sk) || (CAUSAL && n0 + BN - 1 > q0 + off)) {
+      const int lim = (CAUSAL ? min(Sk - 1, qi + off) : Sk - 1) - n0 - 4 * hi;
 #pragma unroll
       for (int mt = 0; mt < 2; mt++)
 #pragma unroll

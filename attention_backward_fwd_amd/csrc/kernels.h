@@ -12,11 +12,13 @@ namespace mi355 {
 constexpr int kBwdBlockN = 256;
 
 // Packed variable-length sequences: when `cu` is set, "batch" b is sequence
-// b of the packed rows, its rows cu[b] .. cu[b+1]-1 (clamped to [0, T] and
-// cut to S rows), S is the bound of the sequence lengths that sizes the grid,
-// and the
+// b of the packed rows: queries cu[b] .. cu[b+1]-1 of T query rows and keys
+// cu_k[b] .. cu_k[b+1]-1 of Tk key rows (each range clamped to its tensor and
+// cut to S, resp. Sk, rows: the bounds that size the grid), and the
 // row-indexed tensors (LSE, Delta, dQ accumulator and partials) are
-// head-major over all T rows.  Otherwise sequence b is rows b*S .. b*S+S-1.
+// head-major over all T query rows.  Otherwise sequence b is rows
+// b*S .. b*S+S-1 of both (Sk == S, Tk unused).  Under causal masking query i
+// of a sequence with lq queries and lk keys sees key j iff j <= i + lk - lq.
 struct SeqRows {
   int base, len;  // first row and length of one sequence
 };
@@ -33,9 +35,10 @@ struct FwdParams {
   const uint16_t* v;
   uint16_t* o;
   float* lse;
-  const int* cu;  // packed sequences, or nullptr
-  int T;          // rows of the packed tensors (with cu)
-  int B, S, Hq, G, Hkv, D;
+  const int* cu;    // packed sequences: query offsets, or nullptr
+  const int* cu_k;  // packed sequences: key offsets
+  int T, Tk;        // query / key rows of the packed tensors (with cu)
+  int B, S, Sk, Hq, G, Hkv, D;
   float scale;
   int causal;
 };
@@ -51,11 +54,12 @@ struct BwdParams {
   float* dq_part;   // split path: [n_kv_blocks][B][S][Hq][D] fp32
   uint16_t* dk;     // groups == 1 outputs, [B][S][Hkv][D] bf16
   uint16_t* dv;
-  float* dk_part;   // groups > 1: per-query-head partials, [B][S][Hq][D] fp32
+  float* dk_part;   // groups > 1: per-query-head partials, [B][Sk][Hq][D] fp32
   float* dv_part;
-  const int* cu;    // packed sequences, or nullptr
-  int T;            // rows of the packed tensors (with cu)
-  int B, S, Hq, G, Hkv, D;
+  const int* cu;    // packed sequences: query offsets, or nullptr
+  const int* cu_k;  // packed sequences: key offsets
+  int T, Tk;        // query / key rows of the packed tensors (with cu)
+  int B, S, Sk, Hq, G, Hkv, D;
   float scale;
   float log2_scale;  // log2(scale), computed on the host
   int causal, use_atomic;
@@ -67,18 +71,21 @@ hipError_t launch_preprocess(const uint16_t* o, const uint16_t* dout, float* del
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
 hipError_t launch_dq_sum(const float* dq_part, float* dq_accum, int B, int S, int Hq, int D,
                          int causal, hipStream_t stream);
-// Packed sequences: rows of dq_accum are [Hq][T]; sums the key blocks of each
-// row's own sequence, writes 0 to rows outside every sequence.
-hipError_t launch_dq_sum_varlen(const float* dq_part, float* dq_accum, const int* cu, int n_seqs, int T, int S,
-                                int Hq, int D, int causal, hipStream_t stream);
+// Packed sequences: rows of dq_accum are [Hq][T]; sums the key blocks each
+// row sees of its own sequence, writes 0 to rows outside every sequence and
+// to rows that see no key.
+hipError_t launch_dq_sum_varlen(const float* dq_part, float* dq_accum, const int* cu, const int* cu_k, int n_seqs,
+                                int T, int Tk, int S, int Sk, int Hq, int D, int causal, hipStream_t stream);
 // Rows outside every sequence (capacity padding, and rows of a sequence past
 // S) of up to two [T][heads][D] tensors (bf16, or fp32 when `fp32`) set to 0,
 // and those rows of an [Hq][T] LSE set to lse_value; null tensors skipped.
 hipError_t launch_pad_fill(void* x0, void* x1, int fp32, int heads, float* lse, int Hq, float lse_value,
                            const int* cu, int n_seqs, int T, int S, int D, hipStream_t stream);
+// dq = bf16(dq_accum) over B*S query rows; groups > 1: dk/dv = bf16(sum of
+// the group's partials) over kv_rows key rows.
 hipError_t launch_postprocess(const float* dq_accum, const float* dk_part, const float* dv_part,
                               uint16_t* dq, uint16_t* dk, uint16_t* dv, int B, int S, int Hq, int G,
-                              int D, hipStream_t stream);
+                              int D, long long kv_rows, hipStream_t stream);
 
 hipError_t launch_merge(const uint16_t* o_parts, const float* lse_parts, int n_parts, uint16_t* o, float* lse,
                         int B, int S, int Hq, int D, hipStream_t stream);

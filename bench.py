@@ -137,7 +137,7 @@ def bench_merge(args, w, bd, torch):
 def bench_varlen(args, bd, torch):
     """The whole step over the packed causal pack of sequences: attn_fwd_varlen,
     the preprocess, attn_bwd_varlen (plus the dQ sum on the split path) and
-    the postprocess.  FLOPs are the per-sequence causal-halved counts summed
+    attn_bwd_varlen_postprocess.  FLOPs are the per-sequence causal-halved counts summed
     over the pack; padding rows count nothing."""
     from attention_backward_fwd_amd.synthetic import VARLEN_PACK, varlen_pack_inputs
 
@@ -161,17 +161,17 @@ def bench_varlen(args, bd, torch):
     def step(i=None):
         if i is not None:
             ev["fwd"][2 * i].record(stream)
-        bd.attn_fwd_varlen(q, k, v, o, lse, cu, sh, scale, True, stream)
+        bd.attn_fwd_varlen(q, k, v, o, lse, cu, cu, sh, scale, True, stream)
         if i is not None:
             ev["fwd"][2 * i + 1].record(stream)
         bd.attn_bwd_preprocess(o, do, bb.delta, bb.dq_accum if use_atomic else None, bb.dense, stream)
         if i is not None:
             ev["bwd"][2 * i].record(stream)
-        bd.attn_bwd_varlen(q, k, v, do, lse, bb.delta, bb.dq_accum, bb.dk, bb.dv, bb.workspace, cu, sh, scale,
-                           True, use_atomic, stream)
+        bd.attn_bwd_varlen(q, k, v, do, lse, bb.delta, bb.dq_accum, bb.dk, bb.dv, bb.workspace, cu, cu, sh,
+                           scale, True, use_atomic, stream)
         if i is not None:
             ev["bwd"][2 * i + 1].record(stream)
-        bd.attn_bwd_postprocess(bb.dq_accum, bb.workspace, bb.dq, bb.dk, bb.dv, bb.dense, stream)
+        bd.attn_bwd_varlen_postprocess(bb.dq_accum, bb.workspace, bb.dq, bb.dk, bb.dv, sh, stream)
 
     for _ in range(args.warmup):
         step()

@@ -159,73 +159,90 @@ int attn_merge(const uint16_t* o_parts, const float* lse_parts, int n_parts, uin
                attn_shape shape, void* stream);
 
 /*
- * Packed variable-length sequences ("THD" layout).  The T rows of all
- * sequences are stored back to back and located by int32 cumulative offsets
- * cu_seqlens[0 .. n_seqs], the way the cuDNN frontend pull request "CSA: add
- * fused Compressor forward+backward CuTe-DSL kernels (ported from
- * Megatron-LM)" (NVIDIA cudnn-frontend #427, description) passes packs, rows
- * at or past cu_seqlens[n_seqs] being static token-capacity padding.
- * Attention never crosses sequences: sequence b (rows cu_seqlens[b] ..
- * cu_seqlens[b+1]-1) is ordinary attention over its own rows, causal in its
- * own positions when `causal`.
- *   q, o, dout, dq [T,Hq,D] bf16; k, v, dk, dv [T,Hkv,D] bf16;
- *   lse, delta [Hq,T] fp32; dq_accum [Hq,T,D] fp32 (head-major over rows).
- *   cu_seqlens: DEVICE memory, n_seqs + 1 int32, read by the kernels (so the
- *     host cannot check it).  It must be non-decreasing with every length
- *     <= max_seqlen; the kernels clamp every offset to [0, T] and cut a
- *     sequence to its first max_seqlen rows, so no access leaves the tensors
- *     whatever it holds, but rows past the cut count as padding and
- *     overlapping sequences give unspecified results.
- * Rows outside every sequence (padding, and rows past such a cut) get O = 0,
- * LSE = -inf and dK = dV = 0 (dQ = 0 through dq_accum); their dout is never
- * read by the backward kernel.
+ * Packed variable-length sequences ("THD" layout).  The rows of all
+ * sequences are stored back to back and located by int32 cumulative offsets,
+ * the way the cuDNN frontend pull request "CSA: add fused Compressor
+ * forward+backward CuTe-DSL kernels (ported from Megatron-LM)" (NVIDIA
+ * cudnn-frontend #427, description) passes packs, rows past the last offset
+ * being static token-capacity padding.  Sequence b holds query rows
+ * cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key rows cu_seqlens_k[b] ..
+ * cu_seqlens_k[b+1]-1 (pass the same array twice when queries and keys are
+ * the same tokens).  Attention never crosses sequences: each is ordinary
+ * attention of its lq queries over its lk keys, and under causal masking
+ * query i (0-based in its sequence) sees key j iff j <= i + lk - lq, i.e.
+ * the last query is aligned with the last key (for lq == lk, j <= i).
+ *   q, o, dout, dq [Tq,Hq,D] bf16; k, v, dk, dv [Tk,Hkv,D] bf16;
+ *   lse, delta [Hq,Tq] fp32; dq_accum [Hq,Tq,D] fp32 (head-major).
+ *   cu_seqlens_q/_k: DEVICE memory, n_seqs + 1 int32 each, read by the
+ *     kernels (so the host cannot check them).  Each must be non-decreasing
+ *     with every length <= its max_seqlen; the kernels clamp every offset to
+ *     its tensor and cut a sequence to its first max_seqlen rows, so no access
+ *     leaves the tensors whatever they hold, but rows past such a cut count as
+ *     padding and overlapping sequences give unspecified results.
+ * Query rows that see no key (i < lq - lk under causal masking, lk == 0, or
+ * padding) get O = 0, LSE = -inf and dQ = 0; key rows no query sees get
+ * dK = dV = 0.  The dout of padding rows is never read by attn_bwd_varlen.
  *
- * The preprocess and postprocess are the dense calls with the shape
- *   { batch = 1, seqlen = T, heads_q, groups, head_dim }:
- * the packed tensors are exactly the batch-1 dense tensors of that shape, and
- * the workspace of attn_bwd_varlen starts with the same dK/dV partials.
+ * Order of calls: attn_fwd_varlen; attn_bwd_preprocess with the dense shape
+ * { batch = 1, seqlen = Tq, heads_q, groups, head_dim } (the packed query
+ * tensors are exactly that batch-1 problem's); attn_bwd_varlen;
+ * attn_bwd_varlen_postprocess.
  */
 typedef struct attn_varlen_shape {
-  int32_t n_seqs;     /* >= 0 sequences; cu_seqlens has n_seqs + 1 entries */
-  int32_t total;      /* T >= 0 rows of the packed tensors (capacity) */
-  int32_t max_seqlen; /* >= 0, bound of every sequence length (sizes the grid) */
-  int32_t heads_q;    /* Hq >= 1 */
-  int32_t groups;     /* g >= 1, Hq % g == 0 */
-  int32_t head_dim;   /* 64 or 128 */
+  int32_t n_seqs;       /* >= 0 sequences; each cu_seqlens array has n_seqs + 1 entries */
+  int32_t total_q;      /* Tq >= 0 query rows of the packed tensors (capacity) */
+  int32_t total_k;      /* Tk >= 0 key rows */
+  int32_t max_seqlen_q; /* >= 0, bound of every query length (sizes the grid) */
+  int32_t max_seqlen_k; /* >= 0, bound of every key length */
+  int32_t heads_q;      /* Hq >= 1 */
+  int32_t groups;       /* g >= 1, Hq % g == 0 */
+  int32_t head_dim;     /* 64 or 128 */
 } attn_varlen_shape;
 
 /*
- * Forward over packed sequences: O and LSE of every sequence as attn_fwd
- * computes them, padding rows O = 0 and LSE = -inf.  Every element of o and
- * lse is written.  A call with total == 0 (after the shape, flag and scale
- * checks) enqueues nothing and may pass NULL pointers.
+ * Forward over packed sequences: O and LSE of every sequence, attn_fwd's
+ * arithmetic per sequence.  Every element of o and lse is written.  With
+ * total_q == 0 (after the shape, flag and scale checks) nothing is enqueued
+ * and every pointer may be NULL; k and v may be NULL when total_k == 0.
  */
 int attn_fwd_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
-                    const int32_t* cu_seqlens, attn_varlen_shape shape, float softmax_scale, int causal,
-                    void* stream);
+                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, attn_varlen_shape shape,
+                    float softmax_scale, int causal, void* stream);
 
 /*
- * Workspace bytes of attn_bwd_varlen (0 when none is needed):
- *   groups > 1: fp32 dK and dV partials, [T,Hq,D] each;
- *   use_atomic == 0: fp32 dQ partials, [ceil(max_seqlen / 256),Hq,T,D].
+ * Workspace bytes of attn_bwd_varlen and attn_bwd_varlen_postprocess (0 when
+ * none is needed):
+ *   groups > 1: fp32 dK and dV partials, [Tk,Hq,D] each;
+ *   use_atomic == 0: fp32 dQ partials, [ceil(max_seqlen_k / 256),Hq,Tq,D].
  * Returns 0 for an invalid shape.
  */
 size_t attn_bwd_varlen_workspace_bytes(attn_varlen_shape shape, int causal, int use_atomic);
 
 /*
  * Backward over packed sequences, with attn_bwd's contract per sequence:
- * dq_accum must be zero on entry when use_atomic = 1 (the dense preprocess
- * zeroes it) and is fully overwritten when use_atomic = 0 (sums in ascending
+ * dq_accum must be zero on entry when use_atomic = 1 (the preprocess zeroes
+ * it) and is fully overwritten when use_atomic = 0 (sums in ascending
  * key-block order, bitwise deterministic); groups == 1 writes dk and dv,
- * groups > 1 writes the workspace partials for attn_bwd_postprocess.
- * Padding rows get zero dK/dV (or zero partials) and no dQ contribution.
- * A call with total == 0 (after the shape, flag and scale checks) enqueues
- * nothing and may pass NULL pointers.
+ * groups > 1 writes the workspace partials for attn_bwd_varlen_postprocess.
+ * With total_q == total_k == 0 nothing is enqueued and every pointer may be
+ * NULL; the query-side pointers may be NULL when total_q == 0, the key-side
+ * ones when total_k == 0.
  */
 int attn_bwd_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
                     const float* lse, const float* delta, float* dq_accum, uint16_t* dk, uint16_t* dv,
-                    void* workspace, size_t workspace_bytes, const int32_t* cu_seqlens,
-                    attn_varlen_shape shape, float softmax_scale, int causal, int use_atomic, void* stream);
+                    void* workspace, size_t workspace_bytes, const int32_t* cu_seqlens_q,
+                    const int32_t* cu_seqlens_k, attn_varlen_shape shape, float softmax_scale, int causal,
+                    int use_atomic, void* stream);
+
+/*
+ * Backward postprocess over packed sequences: dq [Tq,Hq,D] = bf16(dq_accum)
+ * (RNE); for groups > 1 also dk/dv [Tk,Hkv,D] from the workspace partials of
+ * attn_bwd_varlen, summed over each group's query heads in ascending order.
+ * Same arguments as attn_bwd_postprocess with the packed shape.
+ */
+int attn_bwd_varlen_postprocess(const float* dq_accum, const void* workspace, size_t workspace_bytes,
+                                uint16_t* dq, uint16_t* dk, uint16_t* dv, attn_varlen_shape shape,
+                                void* stream);
 
 #ifdef __cplusplus
 }

@@ -29,7 +29,8 @@ def test_library_exports_every_header_symbol():
     names = bd.header_functions()
     assert names == sorted(["attn_fwd", "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_bwd",
                             "attn_bwd_postprocess", "attn_merge", "attn_strerror", "attn_fwd_varlen",
-                            "attn_bwd_varlen_workspace_bytes", "attn_bwd_varlen"])
+                            "attn_bwd_varlen_workspace_bytes", "attn_bwd_varlen",
+                            "attn_bwd_varlen_postprocess"])
     for n in names:
         assert hasattr(lib(), n), n
 
@@ -160,44 +161,55 @@ def test_python_shape_helpers():
 
 # ------------------------------------------------------------ packed sequences
 
-def vshp(n=3, t=1000, m=400, hq=8, g=2, d=128):
-    return bd.attn_varlen_shape(n, t, m, hq, g, d)
+def vshp(n=3, t=1000, m=400, hq=8, g=2, d=128, tk=None, mk=None):
+    return bd.attn_varlen_shape(n, t, t if tk is None else tk, m, m if mk is None else mk, hq, g, d)
 
 
 @pytest.mark.parametrize("g", [1, 4])
-@pytest.mark.parametrize("m", [0, 1, 256, 257, 4096])
-def test_varlen_workspace_bytes(g, m):
-    sh = vshp(n=5, t=3000, m=m, hq=8, g=g, d=64)
-    nq = 3000 * 8 * 64
-    gqa = 2 * nq * 4 if g > 1 else 0
+@pytest.mark.parametrize("mk", [0, 1, 256, 257, 4096])
+def test_varlen_workspace_bytes(g, mk):
+    sh = vshp(n=5, t=3000, m=700, hq=8, g=g, d=64, tk=2000, mk=mk)
+    nq, nk = 3000 * 8 * 64, 2000 * 8 * 64
+    gqa = 2 * nk * 4 if g > 1 else 0
     for causal in (0, 1):
         assert lib().attn_bwd_varlen_workspace_bytes(sh, causal, 1) == gqa
-        assert lib().attn_bwd_varlen_workspace_bytes(sh, causal, 0) == gqa + math.ceil(m / 256) * nq * 4
+        assert lib().attn_bwd_varlen_workspace_bytes(sh, causal, 0) == gqa + math.ceil(mk / 256) * nq * 4
     assert lib().attn_bwd_varlen_workspace_bytes(vshp(hq=6, g=4), 0, 0) == 0
     assert lib().attn_bwd_varlen_workspace_bytes(vshp(), 0, 7) == 0
 
 
 def vfwd(**kw):
-    args = dict(q=A, k=A, v=A, o=A, lse=A, cu=A, shape=vshp(), scale=0.1, causal=1, stream=None)
+    args = dict(q=A, k=A, v=A, o=A, lse=A, cu=A, cuk=A, shape=vshp(), scale=0.1, causal=1, stream=None)
     args.update(kw)
-    return lib().attn_fwd_varlen(args["q"], args["k"], args["v"], args["o"], args["lse"], args["cu"],
+    return lib().attn_fwd_varlen(args["q"], args["k"], args["v"], args["o"], args["lse"], args["cu"], args["cuk"],
                                  args["shape"], args["scale"], args["causal"], args["stream"])
 
 
 def vbwd(**kw):
-    args = dict(q=A, k=A, v=A, do=A, lse=A, delta=A, dq=A, dk=A, dv=A, ws=A, wsb=1 << 40, cu=A, shape=vshp(),
-                scale=0.1, causal=1, atomic=1, stream=None)
+    args = dict(q=A, k=A, v=A, do=A, lse=A, delta=A, dq=A, dk=A, dv=A, ws=A, wsb=1 << 40, cu=A, cuk=A,
+                shape=vshp(), scale=0.1, causal=1, atomic=1, stream=None)
     args.update(kw)
     return lib().attn_bwd_varlen(args["q"], args["k"], args["v"], args["do"], args["lse"], args["delta"],
                                  args["dq"], args["dk"], args["dv"], args["ws"], args["wsb"], args["cu"],
-                                 args["shape"], args["scale"], args["causal"], args["atomic"], args["stream"])
+                                 args["cuk"], args["shape"], args["scale"], args["causal"], args["atomic"],
+                                 args["stream"])
+
+
+def vpost(**kw):
+    args = dict(dq_accum=A, ws=A, wsb=1 << 40, dq=A, dk=A, dv=A, shape=vshp(), stream=None)
+    args.update(kw)
+    return lib().attn_bwd_varlen_postprocess(args["dq_accum"], args["ws"], args["wsb"], args["dq"], args["dk"],
+                                             args["dv"], args["shape"], args["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [
-    ({"q": None}, "null"), ({"cu": None}, "null"), ({"lse": None}, "null"),
+    ({"q": None}, "null"), ({"cu": None}, "null"), ({"cuk": None}, "null"), ({"lse": None}, "null"),
+    ({"k": None}, "null"),
     ({"shape": vshp(n=-1)}, "shape"), ({"shape": vshp(t=-1)}, "shape"), ({"shape": vshp(m=-1)}, "shape"),
+    ({"shape": vshp(tk=-5)}, "shape"), ({"shape": vshp(mk=-5)}, "shape"),
     ({"shape": vshp(hq=0)}, "shape"), ({"shape": vshp(hq=6, g=4)}, "shape"), ({"shape": vshp(d=96)}, "hd"),
-    ({"shape": vshp(t=1 << 20, hq=64, g=1)}, "range"), ({"shape": vshp(hq=65536, g=1)}, "range"),
+    ({"shape": vshp(t=1 << 20, hq=64, g=1)}, "range"), ({"shape": vshp(tk=1 << 20, hq=64, g=1)}, "range"),
+    ({"shape": vshp(hq=65536, g=1)}, "range"),
     ({"shape": vshp(n=1 << 20, m=1 << 16, hq=64, g=1, t=1000)}, "range"),
     ({"scale": 0.0}, "range"), ({"causal": 3}, "flag"), ({"o": MIS}, "align"), ({"v": MIS}, "align"),
 ])
@@ -206,7 +218,8 @@ def test_fwd_varlen_errors(kw, code):
 
 
 @pytest.mark.parametrize("kw,code", [
-    ({"dq": None}, "null"), ({"cu": None}, "null"), ({"shape": vshp(g=1), "dv": None}, "null"),
+    ({"dq": None}, "null"), ({"cu": None}, "null"), ({"cuk": None}, "null"), ({"v": None}, "null"),
+    ({"shape": vshp(g=1), "dv": None}, "null"),
     ({"shape": vshp(hq=7, g=2)}, "shape"), ({"shape": vshp(d=32)}, "hd"),
     ({"atomic": 2}, "flag"), ({"scale": float("nan")}, "range"),
     ({"ws": None}, "ws"), ({"wsb": 64}, "ws"), ({"atomic": 0, "shape": vshp(g=1), "ws": None}, "ws"),
@@ -216,20 +229,33 @@ def test_bwd_varlen_errors(kw, code):
     assert vbwd(**kw) == E[code]
 
 
+@pytest.mark.parametrize("kw,code", [
+    ({"dq": None}, "null"), ({"dk": None}, "null"), ({"ws": None}, "ws"), ({"wsb": 16}, "ws"),
+    ({"shape": vshp(t=-3)}, "shape"), ({"dq_accum": MIS}, "align"),
+])
+def test_varlen_postprocess_errors(kw, code):
+    assert vpost(**kw) == E[code]
+
+
 def test_varlen_empty_pack_is_a_no_op():
-    """total == 0: every check still runs, then nothing is enqueued (NULL
+    """No rows: every check still runs, then nothing is enqueued (NULL
     pointers allowed), so this runs without a GPU."""
-    empty = vshp(n=2, t=0, m=5)
-    assert vfwd(q=None, k=None, v=None, o=None, lse=None, cu=None, shape=empty) == 0
+    empty = vshp(n=2, t=0, m=5, tk=0)
+    assert vfwd(q=None, k=None, v=None, o=None, lse=None, cu=None, cuk=None, shape=empty) == 0
+    assert vfwd(q=None, k=None, v=None, o=None, lse=None, cu=None, cuk=None, shape=vshp(t=0, tk=50)) == 0
     assert vbwd(q=None, k=None, v=None, do=None, lse=None, delta=None, dq=None, dk=None, dv=None, ws=None,
-                cu=None, shape=empty) == 0
+                cu=None, cuk=None, shape=empty) == 0
+    assert vpost(dq_accum=None, ws=None, dq=None, dk=None, dv=None, shape=vshp(t=0, tk=0)) == 0
+    assert vpost(dq_accum=None, ws=None, dq=None, dk=None, dv=None, shape=vshp(t=0, tk=9, g=1)) == 0
     assert vfwd(q=None, shape=empty, causal=2) == E["flag"]
-    assert vbwd(q=None, shape=bd.attn_varlen_shape(2, 0, 5, 8, 2, 96)) == E["hd"]
+    assert vbwd(q=None, shape=bd.attn_varlen_shape(2, 0, 0, 5, 5, 8, 2, 96)) == E["hd"]
 
 
 def test_varlen_shape_helper():
     import torch
     q = torch.empty((50, 8, 64))
-    k = torch.empty((50, 2, 64))
-    sh = bd.varlen_shape_of(q, k, 4, 20)
-    assert (sh.n_seqs, sh.total, sh.max_seqlen, sh.heads_q, sh.groups, sh.head_dim) == (4, 50, 20, 8, 4, 64)
+    k = torch.empty((70, 2, 64))
+    sh = bd.varlen_shape_of(q, k, 4, 20, 30)
+    assert (sh.n_seqs, sh.total_q, sh.total_k, sh.max_seqlen_q, sh.max_seqlen_k, sh.heads_q, sh.groups,
+            sh.head_dim) == (4, 50, 70, 20, 30, 8, 4, 64)
+    assert bd.varlen_shape_of(q, k, 4, 20).max_seqlen_k == 20

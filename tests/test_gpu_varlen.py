@@ -28,19 +28,21 @@ def _pack(lengths, pad, hq, hkv, d, seed):
     return {n: x[0] for n, x in inp.items()}
 
 
-def run_varlen(dev, cu, max_seqlen, causal, scale, use_atomic):
+def run_varlen(dev, cu, max_seqlen, causal, scale, use_atomic, cu_k=None, max_seqlen_k=None):
     """fwd -> preprocess -> bwd (-> sum) -> postprocess; every output and
     scratch buffer starts as NaN, so an element left unwritten shows up."""
     q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
+    cu_k = cu if cu_k is None else cu_k
     n_seqs = cu.numel() - 1
-    sh = bd.varlen_shape_of(q, k, n_seqs, max_seqlen)
+    sh = bd.varlen_shape_of(q, k, n_seqs, max_seqlen, max_seqlen_k)
     o = torch.full_like(q, NAN)
     lse = torch.full((q.shape[1], q.shape[0]), NAN, dtype=torch.float32, device=q.device)
-    bd.attn_fwd_varlen(q, k, v, o, lse, cu, sh, scale, causal)
-    bb = bd.VarlenBwdBuffers(q, k, n_seqs, max_seqlen, causal, use_atomic)
+    bd.attn_fwd_varlen(q, k, v, o, lse, cu, cu_k, sh, scale, causal)
+    bb = bd.VarlenBwdBuffers(q, k, n_seqs, max_seqlen, causal, use_atomic, max_seqlen_k)
     for t in (bb.delta, bb.dq_accum, bb.dq, bb.dk, bb.dv) + ((bb.workspace,) if bb.workspace is not None else ()):
         t.fill_(NAN)
-    bd.backward_varlen(q, k, v, o, lse, do, cu, max_seqlen, causal, scale, use_atomic, buffers=bb)
+    bd.backward_varlen(q, k, v, o, lse, do, cu, max_seqlen, causal, scale, use_atomic, buffers=bb, cu_seqlens_k=cu_k,
+                       max_seqlen_k=max_seqlen_k)
     torch.cuda.synchronize()
     return {"o": o, "lse": lse, "delta": bb.delta, "dq": bb.dq, "dk": bb.dk, "dv": bb.dv}
 
@@ -52,7 +54,17 @@ def _padding_rows(cu_list, t, max_seqlen):
     return ~inside
 
 
-def _check(gpu, ref, pad, case):
+def _unseen_keys(cu, cu_k, tk, mq, mk):
+    """Key rows of sequences without queries: no query sees them (with at
+    least one query, the last query sees every key of its sequence)."""
+    out = np.zeros(tk, dtype=bool)
+    for b in range(len(cu) - 1):
+        if min(cu[b + 1] - cu[b], mq) == 0:
+            out[cu_k[b]:cu_k[b] + min(cu_k[b + 1] - cu_k[b], mk)] = True
+    return out
+
+
+def _check(gpu, ref, pad, case, pad_k=None, unseen=None):
     ratios = {n: err_ratio(np64(gpu[n]), ref[n]) for n in ("o", "dq", "dk", "dv", "delta")}
     say(f"{case}: " + " ".join(f"{n}={r:.2e}" for n, r in ratios.items()))
     for n, r in ratios.items():
@@ -62,9 +74,16 @@ def _check(gpu, ref, pad, case):
     fin = np.isfinite(rl)
     err = np.max(np.abs(lse[fin] - rl[fin]) / np.maximum(1.0, np.abs(rl[fin])), initial=0.0)
     assert err <= 1e-3, (case, "lse", err)
-    # capacity padding: exact zeros
-    for n in ("o", "dq", "dk", "dv"):
-        assert np.all(np64(gpu[n])[pad] == 0.0), (case, n, "padding rows not zero")
+    # capacity padding and rows that see no key: exact zeros
+    pad_k = pad if pad_k is None else pad_k
+    empty = np.isneginf(rl).all(axis=0)
+    for n in ("o", "dq"):
+        assert np.all(np64(gpu[n])[pad | empty] == 0.0), (case, n, "padding / empty rows not zero")
+    for n in ("dk", "dv"):
+        assert np.all(np64(gpu[n])[pad_k] == 0.0), (case, n, "padding rows not zero")
+    if unseen is not None:
+        for n in ("dk", "dv"):  # keys no query sees: exact zeros too
+            assert np.all(np64(gpu[n])[unseen] == 0.0), (case, n, "unseen keys not zero")
 
 
 SMALL = [
@@ -145,6 +164,54 @@ def test_varlen_sequence_cut_at_max_seqlen():
     gpu = run_varlen({n: x.cuda() for n, x in inp.items()}, torch.tensor([0, 100, 400], dtype=torch.int32).cuda(),
                      200, True, 0.125, 0)
     _check(gpu, ref, _padding_rows([0, 100, 400], 400, 200), "varlen cut at max_seqlen")
+
+
+# Different query and key lengths per sequence: (query lengths, key lengths,
+# query padding, key padding, hq, hkv, d, causal).  Causal alignment puts the
+# last query on the last key: lq < lk gives every query a key prefix, lq > lk
+# leaves the first lq - lk queries without keys; lk = 0 and lq = 0 sequences.
+RECT = [
+    ([5, 64, 300, 1], [9, 64, 520, 700], 4, 6, 4, 2, 128, True),
+    ([5, 64, 300, 1], [9, 64, 520, 700], 4, 6, 4, 2, 128, False),
+    ([40, 300, 10, 0], [7, 100, 0, 30], 3, 0, 2, 2, 64, True),
+    ([40, 300, 10, 0], [7, 100, 0, 30], 3, 0, 2, 1, 64, False),
+    ([600, 33], [257, 290], 0, 11, 2, 2, 128, True),
+]
+
+
+@pytest.mark.parametrize("use_atomic", [1, 0])
+@pytest.mark.parametrize("lq,lk,pq,pk,hq,hkv,d,causal", RECT)
+def test_varlen_rectangular_against_oracle(lq, lk, pq, pk, hq, hkv, d, causal, use_atomic):
+    tq, tk = sum(lq) + pq, sum(lk) + pk
+    g = torch.Generator().manual_seed(sum(lq) + 7 * sum(lk) + d)
+    inp = {"q": torch.randn((tq, hq, d), generator=g), "k": torch.randn((tk, hkv, d), generator=g),
+           "v": torch.randn((tk, hkv, d), generator=g), "do": torch.randn((tq, hq, d), generator=g)}
+    inp = {n: x.to(torch.bfloat16) for n, x in inp.items()}
+    cu, cu_k = cu_seqlens(lq), cu_seqlens(lk)
+    scale = 1.0 / math.sqrt(d)
+    f = {n: x.double().numpy() for n, x in inp.items()}
+    ref = vl.varlen_bwd(f["q"], f["k"], f["v"], f["do"], cu.tolist(), scale, causal, hq // hkv, cu_k.tolist())
+    case = f"varlen rect Lq={lq} Lk={lk} pad={pq},{pk} hq{hq} hkv{hkv} d{d} causal={causal} atomic={use_atomic}"
+    say(case)
+    gpu = run_varlen({n: x.cuda() for n, x in inp.items()}, cu.cuda(), max(lq), causal, scale, use_atomic,
+                     cu_k.cuda(), max(lk))
+    _check(gpu, ref, _padding_rows(cu.tolist(), tq, max(lq)), case, _padding_rows(cu_k.tolist(), tk, max(lk)),
+           _unseen_keys(cu.tolist(), cu_k.tolist(), tk, max(lq), max(lk)))
+
+
+def test_varlen_no_keys_at_all():
+    """Queries but no key rows anywhere (total_k = 0), and keys but no query
+    rows: O = 0, LSE = -inf, dQ = 0, and dK = dV = 0."""
+    g = torch.Generator().manual_seed(3)
+    q = torch.randn((20, 2, 64), generator=g).to(torch.bfloat16).cuda()
+    kv = torch.randn((24, 2, 64), generator=g).to(torch.bfloat16).cuda()
+    cu = torch.tensor([0, 12, 20], dtype=torch.int32).cuda()
+    cz = torch.tensor([0, 0, 0], dtype=torch.int32).cuda()
+    gpu = run_varlen({"q": q, "k": kv[:0], "v": kv[:0], "do": q.clone()}, cu, 12, True, 0.125, 0, cz, 0)
+    assert torch.all(gpu["o"] == 0) and torch.all(gpu["dq"] == 0) and torch.all(torch.isneginf(gpu["lse"]))
+    cuk = torch.tensor([0, 10, 24], dtype=torch.int32).cuda()
+    gpu = run_varlen({"q": q[:0], "k": kv, "v": kv, "do": q[:0]}, cz, 0, True, 0.125, 1, cuk, 14)
+    assert torch.all(gpu["dk"] == 0) and torch.all(gpu["dv"] == 0)
 
 
 @pytest.mark.parametrize("use_atomic", [1, 0])
