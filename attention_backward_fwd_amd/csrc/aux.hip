@@ -119,15 +119,33 @@ __global__ __launch_bounds__(256) void dq_sum_varlen_kernel(const float* __restr
 // Rows of packed tensors outside every sequence (see seq_of_row): the rows of
 // [T][heads][D] tensors x0 and x1 (bf16, or fp32 when `fp32`; either may be
 // null) set to 0, and those rows of an [Hq][T] LSE (may be null) set to
-// lse_value.  One row per workgroup and step; rows inside a sequence are
-// left untouched.
+// lse_value.  With non-decreasing offsets these rows are the ranges before
+// the first sequence and after the last one, plus the tail of any sequence
+// cut to S rows: workgroups 0 .. 2*kPadSplit-1 share the two outer ranges,
+// workgroup 2*kPadSplit + b takes sequence b's cut tail (normally empty).
+// Every range is clamped to [0, T].
+constexpr int kPadSplit = 128;
 __global__ __launch_bounds__(256) void pad_fill_kernel(void* __restrict__ x0, void* __restrict__ x1, int fp32,
                                                        int heads, float* __restrict__ lse, int Hq, float lse_value,
                                                        const int* __restrict__ cu, int n_seqs, int T, int S, int D) {
   const int per_row = heads * D / (fp32 ? 4 : 8);  // 16-byte chunks per row
-  for (int t = blockIdx.x; t < T; t += gridDim.x) {
-    int start, len;
-    if (seq_of_row(cu, n_seqs, T, S, t, start, len) >= 0) continue;
+  const int first = min(max(cu[0], 0), T);
+  int lo, hi, r0, step;
+  if ((int)blockIdx.x < 2 * kPadSplit) {
+    const bool tail = blockIdx.x >= kPadSplit;
+    lo = tail ? (n_seqs > 0 ? min(max(cu[n_seqs], first), T) : first) : 0;
+    hi = tail ? T : first;
+    r0 = blockIdx.x % kPadSplit;
+    step = kPadSplit;
+  } else {
+    const int b = blockIdx.x - 2 * kPadSplit;
+    const SeqRows r = seq_rows(cu, T, b, S);
+    lo = r.base + r.len;
+    hi = min(max(cu[b + 1], r.base), T);
+    r0 = 0;
+    step = 1;
+  }
+  for (int t = lo + r0; t < hi; t += step) {
     const size_t row = (size_t)t * per_row;
     for (int c = threadIdx.x; c < per_row; c += 256) {
       if (x0) reinterpret_cast<u32x4*>(x0)[row + c] = u32x4{0u, 0u, 0u, 0u};
@@ -226,9 +244,8 @@ hipError_t launch_dq_sum_varlen(const float* dq_part, float* dq_accum, const int
 
 hipError_t launch_pad_fill(void* x0, void* x1, int fp32, int heads, float* lse, int Hq, float lse_value,
                            const int* cu, int n_seqs, int T, int S, int D, hipStream_t stream) {
-  const int g = T < 256 * 64 ? T : 256 * 64;
-  hipLaunchKernelGGL(pad_fill_kernel, dim3(g), dim3(256), 0, stream, x0, x1, fp32, heads, lse, Hq, lse_value, cu,
-                     n_seqs, T, S, D);
+  hipLaunchKernelGGL(pad_fill_kernel, dim3(2 * kPadSplit + n_seqs), dim3(256), 0, stream, x0, x1, fp32, heads, lse,
+                     Hq, lse_value, cu, n_seqs, T, S, D);
   return hipGetLastError();
 }
 

@@ -199,6 +199,23 @@ def test_varlen_rectangular_against_oracle(lq, lk, pq, pk, hq, hkv, d, causal, u
            _unseen_keys(cu.tolist(), cu_k.tolist(), tk, max(lq), max(lk)))
 
 
+@pytest.mark.parametrize("use_atomic", [1, 0])
+def test_varlen_leading_padding(use_atomic):
+    """Offsets that do not start at row 0: rows before the first sequence
+    are padding too."""
+    cu_l, cuk_l = [5, 30, 60], [3, 40, 41]
+    g = torch.Generator().manual_seed(41)
+    inp = {"q": torch.randn((70, 4, 64), generator=g), "k": torch.randn((50, 2, 64), generator=g),
+           "v": torch.randn((50, 2, 64), generator=g), "do": torch.randn((70, 4, 64), generator=g)}
+    inp = {n: x.to(torch.bfloat16) for n, x in inp.items()}
+    f = {n: x.double().numpy() for n, x in inp.items()}
+    ref = vl.varlen_bwd(f["q"], f["k"], f["v"], f["do"], cu_l, 0.125, True, 2, cuk_l)
+    cu, cuk = torch.tensor(cu_l, dtype=torch.int32), torch.tensor(cuk_l, dtype=torch.int32)
+    gpu = run_varlen({n: x.cuda() for n, x in inp.items()}, cu.cuda(), 30, True, 0.125, use_atomic, cuk.cuda(), 37)
+    _check(gpu, ref, _padding_rows(cu_l, 70, 30), f"leading padding atomic={use_atomic}",
+           _padding_rows(cuk_l, 50, 37), _unseen_keys(cu_l, cuk_l, 50, 30, 37))
+
+
 def test_varlen_no_keys_at_all():
     """Queries but no key rows anywhere (total_k = 0), and keys but no query
     rows: O = 0, LSE = -inf, dQ = 0, and dK = dV = 0."""
