@@ -44,6 +44,15 @@ class attn_varlen_shape(ctypes.Structure):
     ]
 
 
+class gla_shape(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("seqlen", ctypes.c_int32),
+        ("heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+    ]
+
+
 _lib = None
 
 
@@ -81,6 +90,10 @@ def library():
                                         ctypes.c_float, ctypes.c_int, ctypes.c_int, P]
         lib.attn_bwd_varlen_postprocess.restype = ctypes.c_int
         lib.attn_bwd_varlen_postprocess.argtypes = [P, P, ctypes.c_size_t, P, P, P, attn_varlen_shape, P]
+        lib.gla_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.gla_chunk_bwd_workspace_bytes.argtypes = [gla_shape]
+        lib.gla_chunk_bwd.restype = ctypes.c_int
+        lib.gla_chunk_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, gla_shape, ctypes.c_float, P]
         _lib = lib
     return _lib
 
@@ -90,7 +103,7 @@ def header_functions():
     with open(HEADER) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:attn|gla)_[a-z_]+)\s*\(", text)))
 
 
 class AttnError(RuntimeError):
@@ -186,6 +199,17 @@ def attn_bwd_varlen_postprocess(dq_accum, workspace, dq, dk, dv, shape, stream=N
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(library().attn_bwd_varlen_postprocess(_ptr(dq_accum), _ptr(workspace), ws_bytes, _ptr(dq), _ptr(dk),
                                                  _ptr(dv), shape, _stream(stream)), "attn_bwd_varlen_postprocess")
+
+
+def gla_chunk_bwd_workspace_bytes(shape):
+    return int(library().gla_chunk_bwd_workspace_bytes(shape))
+
+
+def gla_chunk_bwd(q, k, v, g, dout, dq, dk, dv, dg, workspace, shape, scale, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().gla_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                   _ptr(dg), _ptr(workspace), ws_bytes, shape, float(scale), _stream(stream)),
+           "gla_chunk_bwd")
 
 
 # ------------------------------------------------------------ conveniences
@@ -313,3 +337,28 @@ def backward_varlen(q, k, v, o, lse, do, cu_seqlens_q, max_seqlen_q, causal, sca
                     bb.shape, scale, causal, use_atomic, stream)
     attn_bwd_varlen_postprocess(bb.dq_accum, bb.workspace, bb.dq, bb.dk, bb.dv, bb.shape, stream)
     return bb.dq, bb.dk, bb.dv
+
+
+class GlaBuffers:
+    """Outputs and workspace of one simple-GLA chunk backward problem."""
+
+    def __init__(self, q):
+        b, t, h, d = q.shape
+        self.shape = gla_shape(b, t, h, d)
+        self.dq = torch.empty_like(q)
+        self.dk = torch.empty_like(q)
+        self.dv = torch.empty_like(q)
+        self.dg = torch.empty((b, t, h), dtype=torch.float32, device=q.device)
+        nbytes = gla_chunk_bwd_workspace_bytes(self.shape)
+        self.workspace = torch.empty(nbytes // 4 + 1, dtype=torch.float32, device=q.device)
+
+
+def gla_backward(q, k, v, g, do, scale, buffers=None, stream=None):
+    """dq, dk, dv, dg of simple gated linear attention (q/k/v/do [B,T,H,128]
+    bf16, g [B,T,H] fp32)."""
+    _require_gpu_inputs(q, k, v, do)
+    if not g.is_cuda or g.dtype != torch.float32 or not g.is_contiguous():
+        raise ValueError("g must be a contiguous fp32 GPU tensor")
+    bb = buffers or GlaBuffers(q)
+    gla_chunk_bwd(q, k, v, g, do, bb.dq, bb.dk, bb.dv, bb.dg, bb.workspace, bb.shape, scale, stream)
+    return bb.dq, bb.dk, bb.dv, bb.dg

@@ -67,6 +67,16 @@ size_t ws_varlen_split_bytes(const attn_varlen_shape& s, int use_atomic) {
 // Sequences with rows on both sides exist: the main kernels have work.
 bool varlen_any(const attn_varlen_shape& s) { return s.n_seqs > 0 && s.max_seqlen_q > 0 && s.max_seqlen_k > 0; }
 
+int check_gla(const gla_shape& s) {
+  if (s.batch < 1 || s.seqlen < 1 || s.heads < 1) return ATTN_ERR_BAD_SHAPE;
+  if (s.head_dim != 128) return ATTN_ERR_HEAD_DIM;
+  if ((long long)s.batch * s.seqlen * s.heads * s.head_dim >= (1LL << 31)) return ATTN_ERR_RANGE;
+  if ((long long)s.batch * s.heads > 65535) return ATTN_ERR_RANGE;  // grid y of the chunk stage
+  return ATTN_OK;
+}
+
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
 }  // namespace
 
 extern "C" {
@@ -360,6 +370,27 @@ int attn_bwd_varlen_postprocess(const float* dq_accum, const void* workspace, si
                                        gqa ? (const float*)(ws + nkv_bytes) : nullptr, dq, gqa ? dk : nullptr,
                                        gqa ? dv : nullptr, 1, shape.total_q, shape.heads_q, gqa ? shape.groups : 1,
                                        shape.head_dim, shape.total_k, (hipStream_t)stream));
+}
+
+size_t gla_chunk_bwd_workspace_bytes(gla_shape shape) {
+  if (check_gla(shape) != ATTN_OK) return 0;
+  return gla_bwd_workspace_bytes(shape.batch, shape.seqlen, shape.heads);
+}
+
+int gla_chunk_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g, const uint16_t* dout,
+                  uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dg, void* workspace, size_t workspace_bytes,
+                  gla_shape shape, float scale, void* stream) {
+  if (!q || !k || !v || !g || !dout || !dq || !dk || !dv || !dg) return ATTN_ERR_NULL_PTR;
+  const int st = check_gla(shape);
+  if (st) return st;
+  if (!good_scale(scale)) return ATTN_ERR_RANGE;
+  if (!workspace || workspace_bytes < gla_bwd_workspace_bytes(shape.batch, shape.seqlen, shape.heads))
+    return ATTN_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
+      !aligned16(dv) || !aligned16(workspace) || !aligned4(g) || !aligned4(dg))
+    return ATTN_ERR_ALIGN;
+  return hip_status(launch_gla_bwd(q, k, v, dout, g, dq, dk, dv, dg, workspace, shape.batch, shape.seqlen,
+                                   shape.heads, scale, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -87,6 +87,16 @@ hipError_t launch_postprocess(const float* dq_accum, const float* dk_part, const
                               uint16_t* dq, uint16_t* dk, uint16_t* dv, int B, int S, int Hq, int G,
                               int D, long long kv_rows, hipStream_t stream);
 
+// Simple gated linear attention, chunked backward (head dim 128, chunks of
+// 64): states, per-chunk dq/dk/dv and the gate's reverse running sum.
+// Tensors [B][T][H][128] bf16, g and dg [B][T][H] fp32; the workspace holds
+// the bf16 chunk states and their gradients ([B*H][N][128][128] each) and
+// the per-token dG ([B][T][H] fp32).
+hipError_t launch_gla_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
+                          const float* g, uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dg, void* workspace,
+                          int B, int T, int H, float scale, hipStream_t stream);
+size_t gla_bwd_workspace_bytes(int B, int T, int H);
+
 hipError_t launch_merge(const uint16_t* o_parts, const float* lse_parts, int n_parts, uint16_t* o, float* lse,
                         int B, int S, int Hq, int D, hipStream_t stream);
 

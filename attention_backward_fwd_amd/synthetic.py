@@ -107,3 +107,20 @@ def varlen_pack_inputs(spec=VARLEN_PACK, seed=0):
     t = spec["tokens"] + spec["pad"]
     inp = make_inputs(1, t, spec["heads_q"], spec["heads_kv"], spec["head_dim"], seed=seed)
     return {n: x[0] for n, x in inp.items()}, lengths, cu_seqlens(lengths)
+
+
+# Simple gated linear attention: q, k, v, do standard normal (bf16 RNE) in
+# [batch, seq, heads, dim] order, and the per-token log decay
+# g = log(sigmoid(x)) / 16 with x standard normal (fp32; always < 0, mean
+# about -0.05), drawn after the four tensors from the same generator.
+GLA_WORKLOAD = {"name": "gla_b4_h32_t4096_d128", "batch": 4, "seqlen": 4096, "heads": 32, "head_dim": 128}
+
+
+def gla_inputs(batch, seqlen, heads, head_dim, seed=0):
+    """dict q, k, v, do (bf16) and g (fp32) as CPU tensors."""
+    gen = torch.Generator(device="cpu").manual_seed(seed)
+    shp = (batch, seqlen, heads, head_dim)
+    out = {n: torch.randn(shp, generator=gen, dtype=torch.float32).to(torch.bfloat16) for n in ("q", "k", "v", "do")}
+    x = torch.randn((batch, seqlen, heads), generator=gen, dtype=torch.float32)
+    out["g"] = torch.nn.functional.logsigmoid(x) / 16.0
+    return out

@@ -204,6 +204,55 @@ def bench_varlen(args, bd, torch):
     }), flush=True)
 
 
+def bench_gla(args, bd, torch):
+    """Simple gated linear attention, chunked backward (gla_chunk_bwd: chunk
+    states, per-chunk dq/dk/dv/dG, gate running sum) on the GLA workload.
+    HBM-bound: ``value`` is the algorithmic bytes (q, k, v, do, g read once;
+    dq, dk, dv, dg written once) per second of the whole call."""
+    from attention_backward_fwd_amd.synthetic import GLA_WORKLOAD, gla_inputs
+
+    w = GLA_WORKLOAD
+    b, t, h, d = w["batch"], w["seqlen"], w["heads"], w["head_dim"]
+    dev = torch.device("cuda:0")
+    inp = {n: x.to(dev) for n, x in gla_inputs(b, t, h, d, seed=0).items()}
+    scale = 1.0 / math.sqrt(d)
+    bb = bd.GlaBuffers(inp["q"])
+    stream = torch.cuda.current_stream()
+
+    def call():
+        bd.gla_chunk_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["do"], bb.dq, bb.dk, bb.dv, bb.dg,
+                         bb.workspace, bb.shape, scale, stream)
+
+    for _ in range(args.warmup):
+        call()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[2 * i].record(stream)
+        call()
+        ev[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)) / args.steps
+    n_elem = b * t * h * d
+    nbytes = 4 * n_elem * 2 + b * t * h * 4 + 3 * n_elem * 2 + b * t * h * 4
+    n_chunks = b * h * ((t + 63) // 64)
+    flop = n_chunks * (10 * 64 * d * d + 10 * 64 * 64 * d)  # the chunked algorithm's matrix products
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "simple-GLA chunk backward throughput (algorithmic HBM bytes)", "value": round(gbs, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 (fp32 accumulation, fp32 gate)", "data": "synthetic",
+        "config": {"workload": w["name"], "batch": b, "seq_len": t, "heads": h, "head_dim": d, "chunk": 64},
+        "bwd_ms": round(ms, 4), "tokens_per_s": round(b * t / (ms * 1e-3), 1),
+        "mfma_tflops": round(flop / (ms * 1e-3) / 1e12, 3),
+        "roofline": {"kernel": "gla_states + gla_dqkv + gla_dg", "bound": "hbm", "achieved": round(gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -223,6 +272,9 @@ def main():
     ap.add_argument("--varlen", action="store_true",
                     help="instead of the dense step, time the step over the packed causal pack of "
                          "variable-length sequences (16384 tokens, 32 heads of 128)")
+    ap.add_argument("--gla", action="store_true",
+                    help="instead of the attention step, time the simple gated linear attention chunk backward "
+                         "(B=4, T=4096, H=32, D=128)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -248,6 +300,9 @@ def main():
 
     if args.varlen:
         bench_varlen(args, bd, torch)
+        return
+    if args.gla:
+        bench_gla(args, bd, torch)
         return
     w = WORKLOADS[args.workload]
     if args.merge_parts:

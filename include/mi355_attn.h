@@ -244,6 +244,40 @@ int attn_bwd_varlen_postprocess(const float* dq_accum, const void* workspace, si
                                 uint16_t* dq, uint16_t* dk, uint16_t* dv, attn_varlen_shape shape,
                                 void* stream);
 
+/*
+ * Simple gated linear attention: chunked backward.  The flash-linear-
+ * attention pull request "[Perf] TileLang backends for linear-attention chunk
+ * backward (simple_gla / gla / delta_rule / gdn)" (fla-org/flash-linear-
+ * attention #1046, summary) speeds up the chunk backward of simple_gla among
+ * others; the operation is the standard one, per batch b and head h with the
+ * per-token log decay g (natural log; g <= 0 keeps the state bounded) and
+ * its running sum G:
+ *   o_t = scale * sum_{s<=t} exp(G_t - G_s) (q_t . k_s) v_s
+ * and this call returns the gradients of L = sum_t do_t . o_t:
+ *   dq_t = scale * sum_{s<=t} exp(G_t - G_s) (do_t . v_s) k_s
+ *   dk_s = scale * sum_{t>=s} exp(G_t - G_s) (do_t . v_s) q_t
+ *   dv_s = scale * sum_{t>=s} exp(G_t - G_s) (q_t . k_s) do_t
+ *   dg_r = sum_{t>=r} (q_t . dq_t - k_t . dk_t)
+ * computed in chunks of 64 tokens (chunk states and their gradients in the
+ * workspace, bf16; fp32 accumulation).
+ *   q, k, v, dout, dq, dk, dv [batch, seqlen, heads, 128] bf16 (head_dim 128,
+ *     K = V); g, dg [batch, seqlen, heads] fp32 (4-byte aligned).
+ *   workspace: at least gla_chunk_bwd_workspace_bytes(shape) bytes.
+ * Every element of dq, dk, dv and dg is written.
+ */
+typedef struct gla_shape {
+  int32_t batch;    /* >= 1 */
+  int32_t seqlen;   /* T >= 1 (any length; the last chunk may be partial) */
+  int32_t heads;    /* >= 1, batch * heads <= 65535 */
+  int32_t head_dim; /* 128 */
+} gla_shape;
+
+size_t gla_chunk_bwd_workspace_bytes(gla_shape shape);
+
+int gla_chunk_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g, const uint16_t* dout,
+                  uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dg, void* workspace, size_t workspace_bytes,
+                  gla_shape shape, float scale, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

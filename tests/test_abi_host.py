@@ -30,7 +30,7 @@ def test_library_exports_every_header_symbol():
     assert names == sorted(["attn_fwd", "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_bwd",
                             "attn_bwd_postprocess", "attn_merge", "attn_strerror", "attn_fwd_varlen",
                             "attn_bwd_varlen_workspace_bytes", "attn_bwd_varlen",
-                            "attn_bwd_varlen_postprocess"])
+                            "attn_bwd_varlen_postprocess", "gla_chunk_bwd_workspace_bytes", "gla_chunk_bwd"])
     for n in names:
         assert hasattr(lib(), n), n
 
@@ -259,3 +259,46 @@ def test_varlen_shape_helper():
     assert (sh.n_seqs, sh.total_q, sh.total_k, sh.max_seqlen_q, sh.max_seqlen_k, sh.heads_q, sh.groups,
             sh.head_dim) == (4, 50, 70, 20, 30, 8, 4, 64)
     assert bd.varlen_shape_of(q, k, 4, 20).max_seqlen_k == 20
+
+
+# ------------------------------------------------------------ simple GLA
+
+def gshp(b=2, t=300, h=4, d=128):
+    return bd.gla_shape(b, t, h, d)
+
+
+@pytest.mark.parametrize("t", [1, 64, 65, 4096])
+def test_gla_workspace_bytes(t):
+    n = math.ceil(t / 64)
+    want = 2 * (2 * 4 * n * 128 * 128 * 2) + 2 * t * 4 * 4
+    assert lib().gla_chunk_bwd_workspace_bytes(gshp(t=t)) == want
+    assert lib().gla_chunk_bwd_workspace_bytes(gshp(d=64)) == 0
+    assert lib().gla_chunk_bwd_workspace_bytes(gshp(b=0)) == 0
+
+
+def gbwd(**kw):
+    args = dict(q=A, k=A, v=A, g=A, do=A, dq=A, dk=A, dv=A, dg=A, ws=A, wsb=1 << 40, shape=gshp(), scale=0.1,
+                stream=None)
+    args.update(kw)
+    return lib().gla_chunk_bwd(args["q"], args["k"], args["v"], args["g"], args["do"], args["dq"], args["dk"],
+                               args["dv"], args["dg"], args["ws"], args["wsb"], args["shape"], args["scale"],
+                               args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"q": None}, "null"), ({"g": None}, "null"), ({"dg": None}, "null"),
+    ({"shape": gshp(b=0)}, "shape"), ({"shape": gshp(t=0)}, "shape"), ({"shape": gshp(h=0)}, "shape"),
+    ({"shape": gshp(d=64)}, "hd"), ({"shape": gshp(b=64, t=8192, h=64)}, "range"),
+    ({"shape": gshp(b=300, t=4, h=300)}, "range"),
+    ({"scale": 0.0}, "range"), ({"scale": float("nan")}, "range"),
+    ({"ws": None}, "ws"), ({"wsb": 100}, "ws"),
+    ({"q": MIS}, "align"), ({"ws": MIS}, "align"), ({"g": P(0x10002)}, "align"),
+])
+def test_gla_errors(kw, code):
+    assert gbwd(**kw) == E[code]
+
+
+def test_gla_g_needs_only_4_byte_alignment():
+    """g and dg are fp32 per-token values: 4-byte aligned is enough (the call
+    then fails only on the workspace, which the test leaves too small)."""
+    assert gbwd(g=P(0x10004), dg=P(0x10004), wsb=8) == E["ws"]
