@@ -21,8 +21,8 @@
 //   dv_s     = scale sum_{t>=s} e^{G_t-G_s}(q_t.k_s) do_t + e^{Gl-G_s} k_s dH_{n+1}
 // (Gl: G at the chunk's last token).  Kernels: gla_states (h_n forward and
 // dH_{n+1} backward, bf16 to the workspace), gla_dqkv (one chunk per
-// workgroup: dq, dk, dv and the per-token q.dq - k.dk), gla_dg (reverse
-// running sum over the sequence).
+// workgroup: dq, dk, dv and the per-token q.dq - k.dk, head-major in the
+// workspace), gla_dg (reverse running sum over the sequence).
 #include "common.h"
 #include "kernels.h"
 
@@ -39,18 +39,30 @@ constexpr int kD = 128;  // head dim (K = V)
 // result's elements 0..7), so any pairing of them multiplies matching k.
 //   op_row: tile stored [x][k] (x = the lane's m or n index)
 //   op_tr:  tile stored [k][x]
+// A lane's element offsets are built once (Lofs); a 16-step of k or a
+// 32-block of columns is an XOR of the offset and a block of rows an
+// addition (the swizzle permutes 8-element slots by the row's low 4 bits).
 template <int DT>
-__device__ __forceinline__ bf16x8 op_row(const uint16_t* t, int x0, int k0, int lane) {
-  const int r = x0 + (lane & 31), hi = lane >> 5;
-  const u32x2 a = *reinterpret_cast<const u32x2*>(t + swz_off<DT>(r, k0 + 4 * hi));
-  const u32x2 b = *reinterpret_cast<const u32x2*>(t + swz_off<DT>(r, k0 + 8 + 4 * hi));
-  return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
+struct Lofs {
+  int row, tr0, tr1;
+  __device__ __forceinline__ explicit Lofs(int lane) {
+    const int hi = lane >> 5, L = lane & 15, gp = (lane >> 4) & 1;
+    row = swz_off<DT>(lane & 31, 4 * hi);
+    const int col = 16 * gp + 4 * (L & 3);
+    tr0 = swz_off<DT>(4 * hi + (L >> 2), col);
+    tr1 = swz_off<DT>(8 + 4 * hi + (L >> 2), col);
+  }
+};
+template <int DT>
+__device__ __forceinline__ bf16x8 op_row(const uint16_t* t, const Lofs<DT>& o, int x0, int k0) {
+  const int a = (o.row ^ k0) + x0 * DT;
+  const u32x2 lo = *reinterpret_cast<const u32x2*>(t + a);
+  const u32x2 hi = *reinterpret_cast<const u32x2*>(t + (a ^ 8));
+  return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 template <int DT>
-__device__ __forceinline__ bf16x8 op_tr(const uint16_t* t, int k0, int x0, int lane) {
-  const int hi = lane >> 5, L = lane & 15, gp = (lane >> 4) & 1;
-  const int col = x0 + 16 * gp + 4 * (L & 3);
-  return lds_read_tr8(t + swz_off<DT>(k0 + 4 * hi + (L >> 2), col), t + swz_off<DT>(k0 + 8 + 4 * hi + (L >> 2), col));
+__device__ __forceinline__ bf16x8 op_tr(const uint16_t* t, const Lofs<DT>& o, int k0, int x0) {
+  return lds_read_tr8(t + ((o.tr0 ^ x0) + k0 * DT), t + ((o.tr1 ^ x0) + k0 * DT));
 }
 // The k index (0..15 within a 16-step) of element i of a lane's operand.
 __device__ __forceinline__ int op_k(int i, int hi) { return (i < 4 ? 4 * hi + i : 8 + 4 * hi + (i - 4)); }
@@ -58,11 +70,8 @@ __device__ __forceinline__ int op_k(int i, int hi) { return (i < 4 ? 4 * hi + i 
 // Row of element j of a 32x32 result held by a lane of half hi.
 __device__ __forceinline__ int c_row(int j, int hi) { return 8 * (j >> 2) + 4 * hi + (j & 3); }
 
-// Chunk-local inclusive running sum of g over the chunk's valid rows (rows
-// past nv count 0), into sG[0..63]; one wave.  Returns nothing; callers
-// barrier before reading.
-__device__ __forceinline__ void chunk_cumsum(const float* g, size_t stride, int nv, float* sG, int lane) {
-  float x = lane < nv ? g[(size_t)lane * stride] : 0.f;
+// Inclusive running sum over the 64 lanes of one wave, into sG[0..63].
+__device__ __forceinline__ void chunk_scan(float x, float* sG, int lane) {
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const float y = __shfl_up(x, o, 64);
@@ -70,6 +79,9 @@ __device__ __forceinline__ void chunk_cumsum(const float* g, size_t stride, int 
   }
   sG[lane] = x;
 }
+
+// First chunk of a sweep: 0 forward, N-1 backward.
+__device__ __forceinline__ int first_chunk(int dir, int N) { return dir ? N - 1 : 0; }
 
 // Scale the 8 values of an operand by per-k factors f[k0 + op_k(i)].
 __device__ __forceinline__ bf16x8 scale_op(bf16x8 v, const float* f, int k0, int hi) {
@@ -80,23 +92,29 @@ __device__ __forceinline__ bf16x8 scale_op(bf16x8 v, const float* f, int k0, int
 }
 
 // ------------------------------------------------------------ chunk states
-// Workgroup (b*H + h, vt, dir): 4 waves own the 128 x 64 state tile of value
-// columns 64vt .. 64vt+63 (wave w: rows 32w .. 32w+31, two 32x32 tiles).
+// Workgroup (b*H + h, vt, dir): 4 waves own the 64 x 128 transposed state
+// tile S^T of value columns 64vt .. 64vt+63 (wave w: value rows
+// 64vt + 32(w & 1).., key columns 64(w >> 1) .., two 32x32 tiles; lane =
+// key index, so each lane stores four consecutive values per 8-byte store).
 // dir 0 sweeps chunks forward and writes h_n (the state entering chunk n);
-// dir 1 sweeps backward and writes dH_{n+1} (zero for the last chunk).
-// Per chunk: X (k or q) and Y (v or do) tiles arrive by LDS-DMA one chunk
-// ahead; the update is S = exp(Gl) S + X^T (f o Y) with
-// f_s = exp(Gl - G_s) (forward) or scale * exp(G_t) (backward), 0 past the
-// end of the sequence.
+// dir 1 sweeps backward and writes dH_{n+1} (zero for the last chunk); both
+// as [K][V] bf16.  Per chunk: X (k or q, all 128 columns) and Y (v or do,
+// this workgroup's 64 columns) arrive by LDS-DMA one chunk ahead; the update
+// is S = exp(Gl) S + X^T (f o Y) with f_s = exp(Gl - G_s) (forward) or
+// scale * exp(G_t) (backward), 0 past the end of the sequence.  The state
+// stores stay in flight: each step waits only for its own tile loads.
 __global__ __launch_bounds__(256) void gla_states_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                          const uint16_t* __restrict__ v,
                                                          const uint16_t* __restrict__ dout,
                                                          const float* __restrict__ g, uint16_t* __restrict__ hs,
                                                          uint16_t* __restrict__ dhs, int T, int H, float scale) {
+  // Two buffers.  A buffer's Y tile is followed by the chunk's raw g (64
+  // fp32, LDS-DMA too; one object per buffer keeps the compiler's LDS-DMA
+  // tracking exact, so that it adds no waits of its own).
   __shared__ __attribute__((aligned(16))) uint16_t sX0[kC * kD];
   __shared__ __attribute__((aligned(16))) uint16_t sX1[kC * kD];
-  __shared__ __attribute__((aligned(16))) uint16_t sY0[kC * kD];
-  __shared__ __attribute__((aligned(16))) uint16_t sY1[kC * kD];
+  __shared__ __attribute__((aligned(16))) uint16_t sY0[kC * 64 + 2 * kC];
+  __shared__ __attribute__((aligned(16))) uint16_t sY1[kC * 64 + 2 * kC];
   __shared__ float sG[kC];
   __shared__ float sF[kC];
 
@@ -106,83 +124,111 @@ __global__ __launch_bounds__(256) void gla_states_kernel(const uint16_t* __restr
   const int N = (T + kC - 1) / kC;
   const size_t rs = (size_t)H * kD;
   const uint16_t* X = (dir ? q : k) + ((size_t)b * T * H + h) * kD;
-  const uint16_t* Y = (dir ? dout : v) + ((size_t)b * T * H + h) * kD;
+  const uint16_t* Y = (dir ? dout : v) + ((size_t)b * T * H + h) * kD + 64 * vt;
   const float* gb = g + (size_t)b * T * H + h;
-  uint16_t* out = (dir ? dhs : hs) + (size_t)bh * N * kD * kD;
+  // N + 1 state slots per (b, h): slot N takes the state after the last
+  // step, which nobody reads, so that every step stores (and loads)
+  // unconditionally and the wait count below holds on every path.
+  uint16_t* out = (dir ? dhs : hs) + (size_t)bh * (N + 1) * kD * kD;
+  const int vb = 32 * (w & 1), kb = 64 * (w >> 1);  // this wave's value rows (within the half), key columns
+  const Lofs<kD> oD(lane);
+  const Lofs<64> o64(lane);
 
   f32x16 acc[2] = {f32x16{}, f32x16{}};
   auto load = [&](int n, uint16_t* sx, uint16_t* sy) {
     tile_load_async<kD, kC, 4>(X, rs, n * kC, T, sx, w, lane);
-    tile_load_async<kD, kC, 4>(Y, rs, n * kC, T, sy, w, lane);
+    tile_load_async<64, kC, 4>(Y, rs, n * kC, T, sy, w, lane);
+    if (w == 0) {  // g of the chunk (rows past the end repeat the last row; masked below)
+      const int t = n * kC + min(lane, T - 1 - n * kC);
+      __builtin_amdgcn_global_load_lds(gb + (size_t)t * H, lds_ptr(sy + kC * 64), 4, 0, 0);
+    }
   };
-  auto store = [&](int n) {  // the state tile as bf16, rows 32w.., cols 64vt + 32nb + l32
-    uint16_t* o = out + (size_t)n * kD * kD;
+  // S^T element j of tile nb: value 64vt + vb + c_row(j), key kb + 32nb + l32;
+  // stored at [key][value], four consecutive values per store.
+  auto store = [&](int slot) {
+    uint16_t* o = out + (size_t)slot * kD * kD + 64 * vt + vb;
 #pragma unroll
     for (int nb = 0; nb < 2; nb++)
 #pragma unroll
-      for (int j = 0; j < 16; j++)
-        o[(size_t)(32 * w + c_row(j, hi)) * kD + 64 * vt + 32 * nb + (lane & 31)] = to_bf16(acc[nb][j]);
+      for (int jg = 0; jg < 4; jg++) {
+        const int key = kb + 32 * nb + (lane & 31);
+        *reinterpret_cast<u32x2*>(o + (size_t)key * kD + c_row(4 * jg, hi)) =
+            u32x2{pack_bf16x2(acc[nb][4 * jg], acc[nb][4 * jg + 1]), pack_bf16x2(acc[nb][4 * jg + 2], acc[nb][4 * jg + 3])};
+      }
   };
-  auto chunk = [&](int n, const uint16_t* sx, const uint16_t* sy) {
+  constexpr int kStores = 8;  // store instructions per wave per state
+  // One step: chunk n resident in (sx, sy).  Its operands go to registers,
+  // then the next chunk's loads to the other buffer (so that no read of this
+  // buffer follows them), the update and the store of the next state.
+  // Order of a wave's vector-memory operations: loads of chunk n, then the
+  // stores of the state entering it; waiting for "all but kStores" is
+  // therefore waiting for the loads only.
+  auto step = [&](int n, const uint16_t* sx, const uint16_t* sy, uint16_t* nx, uint16_t* ny) {
     const int nv = min(kC, T - n * kC);
-    if (w == 0) chunk_cumsum(gb + (size_t)n * kC * H, H, nv, sG, lane);
-    lds_barrier();
-    const float gl = sG[nv - 1];
+    const int next = n + (dir ? -1 : 1);
+    const int next_ld = min(max(next, 0), N - 1);          // past either end: reload this chunk
+    const int next_st = (next < 0 || next >= N) ? N : next;  // past either end: the spare slot
+    wait_vmem_but<kStores>();
+    lds_barrier();  // chunk n resident; every wave is done with the previous step
     if (w == 0) {
+      const float* sgr = reinterpret_cast<const float*>(sy + kC * 64);
+      chunk_scan(lane < nv ? sgr[lane] : 0.f, sG, lane);
+      const float gl = __shfl(sG[lane], nv - 1, 64);
       const float f = dir ? scale * __expf(sG[lane]) : __expf(gl - sG[lane]);
       sF[lane] = lane < nv ? f : 0.f;
     }
     lds_barrier();
-    const float decay = __expf(gl);
+    const float decay = __expf(sG[nv - 1]);
+    bf16x8 ao[kC / 16], bo[kC / 16][2];
+#pragma unroll
+    for (int ks = 0; ks < kC / 16; ks++) {
+      ao[ks] = scale_op(op_tr<64>(sy, o64, 16 * ks, vb), sF, 16 * ks, hi);
+#pragma unroll
+      for (int nb = 0; nb < 2; nb++) bo[ks][nb] = op_tr<kD>(sx, oD, 16 * ks, kb + 32 * nb);
+    }
+    asm volatile("" ::: "memory");
+    load(next_ld, nx, ny);
 #pragma unroll
     for (int nb = 0; nb < 2; nb++) acc[nb] *= decay;
 #pragma unroll
-    for (int ks = 0; ks < kC / 16; ks++) {
-      const bf16x8 a = op_tr<kD>(sx, 16 * ks, 32 * w, lane);
+    for (int ks = 0; ks < kC / 16; ks++)
 #pragma unroll
-      for (int nb = 0; nb < 2; nb++) {
-        const bf16x8 bb = scale_op(op_tr<kD>(sy, 16 * ks, 64 * vt + 32 * nb, lane), sF, 16 * ks, hi);
-        acc[nb] = mfma32(a, bb, acc[nb]);
-      }
-    }
+      for (int nb = 0; nb < 2; nb++) acc[nb] = mfma32(ao[ks], bo[ks][nb], acc[nb]);
+    store(next_st);
   };
 
   // Forward: chunks 0, 1, ..., storing the state before each update.
   // Backward: chunks N-1, ..., 0, storing dH_{n+1} before the update.
-  const int first = dir ? N - 1 : 0, stepn = dir ? -1 : 1;
+  const int first = first_chunk(dir, N), stepn = dir ? -1 : 1;
   load(first, sX0, sY0);
+  store(first);
   for (int i = 0; i < N; i += 2) {
     const int n0 = first + stepn * i;
-    store(n0);
-    wait_vmem();
-    lds_barrier();  // chunk n0 resident in buffer 0; buffer 1 free
-    if (i + 1 < N) load(n0 + stepn, sX1, sY1);
-    chunk(n0, sX0, sY0);
-    if (i + 1 < N) {
-      const int n1 = n0 + stepn;
-      store(n1);
-      wait_vmem();
-      lds_barrier();
-      if (i + 2 < N) load(n1 + stepn, sX0, sY0);
-      chunk(n1, sX1, sY1);
-    }
+    step(n0, sX0, sY0, sX1, sY1);
+    if (i + 1 < N) step(n0 + stepn, sX1, sY1, sX0, sY0);
   }
 }
 
 // ------------------------------------------------------------ per-chunk stage
-// Workgroup (chunk n, b*H + h), 4 waves.  LDS: q, k, v, do of the chunk
+// Workgroup (chunk n, b*H + h), 8 waves.  LDS: q, k, v, do of the chunk
 // [64][128], h_n and dH_{n+1} [128][128] (bf16, from the states kernel),
 // the masked score matrices Mqk[t][s] = scale e^{G_t - G_s} (q_t.k_s) and
 // Mdov[t][s] = scale e^{G_t - G_s} (do_t.v_s) for s <= t < nv (0 elsewhere).
+// The outputs are computed transposed (dq^T [d][t], dk^T [d][s], dv^T
+// [v][s]): a lane holds one token, so the state terms' per-token factors
+// scale whole lanes, each lane writes four consecutive features per 8-byte
+// store, and q.dq, k.dk are sums inside the lane.  Wave w owns feature rows
+// 32(w >> 1) .. +31 and tokens 32(w & 1) .. +31 of each output.
 // Outputs: dq, dk, dv (bf16) of the chunk's valid rows and
 // dG_t = q_t.dq_t - k_t.dk_t (fp32), summed over the sequence by gla_dg.
-__global__ __launch_bounds__(256) void gla_dqkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+__global__ __launch_bounds__(512) void gla_dqkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                        const uint16_t* __restrict__ v,
                                                        const uint16_t* __restrict__ dout,
                                                        const float* __restrict__ g, const uint16_t* __restrict__ hs,
                                                        const uint16_t* __restrict__ dhs, uint16_t* __restrict__ dq,
                                                        uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
                                                        float* __restrict__ dG, int T, int H, float scale) {
+  constexpr int NW = 8;
   __shared__ __attribute__((aligned(16))) uint16_t sQ[kC * kD];
   __shared__ __attribute__((aligned(16))) uint16_t sK[kC * kD];
   __shared__ __attribute__((aligned(16))) uint16_t sV[kC * kD];
@@ -191,8 +237,9 @@ __global__ __launch_bounds__(256) void gla_dqkv_kernel(const uint16_t* __restric
   __shared__ __attribute__((aligned(16))) uint16_t sDH[kD * kD];
   __shared__ __attribute__((aligned(16))) uint16_t sMqk[kC * kC];
   __shared__ __attribute__((aligned(16))) uint16_t sMdov[kC * kC];
+  __shared__ float sGr[kC];  // raw g of the chunk (LDS-DMA)
   __shared__ float sG[kC];
-  __shared__ float sdG[2][2][kC];  // [q.dq or k.dk][column half][row], each entry written once
+  __shared__ float sdG[2][4][kC];  // [q.dq or k.dk][feature block][token], each entry written once
 
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), hi = lane >> 5;
   const int l32 = lane & 31;
@@ -202,171 +249,176 @@ __global__ __launch_bounds__(256) void gla_dqkv_kernel(const uint16_t* __restric
   const int nv = min(kC, T - n * kC);
   const size_t rs = (size_t)H * kD;
   const size_t base = ((size_t)b * T * H + h) * kD;
-  const size_t st_off = ((size_t)bh * N + n) * kD * kD;
+  const size_t st_off = ((size_t)bh * (N + 1) + n) * kD * kD;
+  const Lofs<kD> oD(lane);
+  const Lofs<kC> oC(lane);
 
-  tile_load_async<kD, kC, 4>(q + base, rs, n * kC, T, sQ, w, lane);
-  tile_load_async<kD, kC, 4>(k + base, rs, n * kC, T, sK, w, lane);
-  tile_load_async<kD, kC, 4>(v + base, rs, n * kC, T, sV, w, lane);
-  tile_load_async<kD, kC, 4>(dout + base, rs, n * kC, T, sO, w, lane);
-  tile_load_async<kD, kD, 4>(hs + st_off, kD, 0, kD, sH, w, lane);
-  tile_load_async<kD, kD, 4>(dhs + st_off, kD, 0, kD, sDH, w, lane);
-  if (w == 1) chunk_cumsum(g + (size_t)b * T * H + h + (size_t)n * kC * H, H, nv, sG, lane);
-  wait_vmem();
+  // Token tiles and g first, state tiles last, all by LDS-DMA.
+  tile_load_async<kD, kC, NW>(q + base, rs, n * kC, T, sQ, w, lane);
+  tile_load_async<kD, kC, NW>(k + base, rs, n * kC, T, sK, w, lane);
+  tile_load_async<kD, kC, NW>(v + base, rs, n * kC, T, sV, w, lane);
+  tile_load_async<kD, kC, NW>(dout + base, rs, n * kC, T, sO, w, lane);
+  if (w == 0) {  // rows past the end repeat the last row; masked in the scan
+    const int t = n * kC + min(lane, nv - 1);
+    __builtin_amdgcn_global_load_lds(g + ((size_t)b * T + t) * H + h, lds_ptr(sGr), 4, 0, 0);
+  }
+  tile_load_async<kD, kD, NW>(hs + st_off, kD, 0, kD, sH, w, lane);
+  tile_load_async<kD, kD, NW>(dhs + st_off, kD, 0, kD, sDH, w, lane);
+  wait_vmem_but<8>();
+  lds_barrier();
+  if (w == 0) chunk_scan(lane < nv ? sGr[lane] : 0.f, sG, lane);
   lds_barrier();
 
-  // Masked score matrices: wave w computes the 32x32 block (s-block w >> 1,
-  // t-block w & 1) of both, as S^T[s][t] (A = k or v rows, B = q or do rows),
-  // and writes them transposed, [t][s], four s values per 8-byte store.
-  {
-    const int sb = w >> 1, tb = w & 1;
-    f32x16 a_qk = f32x16{}, a_dov = f32x16{};
+  // Masked score matrices: wave w computes the 32x32 block (s-block
+  // (w >> 1) & 1, t-block w & 1) of Mqk (w < 4) or Mdov (w >= 4), as
+  // S^T[s][t] (A = k or v rows, B = q or do rows), and writes it
+  // transposed, [t][s], four s values per 8-byte store.
+  // (Each half of the waves names its tiles directly: a pointer chosen at
+  // run time between LDS arrays hides from the compiler that these reads
+  // cannot touch the state tiles still arriving.)
+  auto scores = [&](const uint16_t* ta, const uint16_t* tb_, uint16_t* dst) {
+    const int sb = (w >> 1) & 1, tb = w & 1;
+    f32x16 acc = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < kD / 16; ks++) {
-      a_qk = mfma32(op_row<kD>(sK, 32 * sb, 16 * ks, lane), op_row<kD>(sQ, 32 * tb, 16 * ks, lane), a_qk);
-      a_dov = mfma32(op_row<kD>(sV, 32 * sb, 16 * ks, lane), op_row<kD>(sO, 32 * tb, 16 * ks, lane), a_dov);
-    }
+    for (int ks = 0; ks < kD / 16; ks++)
+      acc = mfma32(op_row<kD>(ta, oD, 32 * sb, 16 * ks), op_row<kD>(tb_, oD, 32 * tb, 16 * ks), acc);
     const int t = 32 * tb + l32;
     const float gt = sG[t];
 #pragma unroll
     for (int jg = 0; jg < 4; jg++) {
-      float mq[4], md[4];
+      float m[4];
 #pragma unroll
       for (int jj = 0; jj < 4; jj++) {
         const int s = 32 * sb + c_row(4 * jg + jj, hi);
-        const float f = (s <= t && t < nv) ? scale * __expf(gt - sG[s]) : 0.f;
-        mq[jj] = a_qk[4 * jg + jj] * f;
-        md[jj] = a_dov[4 * jg + jj] * f;
+        m[jj] = (s <= t && t < nv) ? acc[4 * jg + jj] * (scale * __expf(gt - sG[s])) : 0.f;
       }
-      const int s0 = 32 * sb + c_row(4 * jg, hi);
-      *reinterpret_cast<u32x2*>(sMqk + swz_off<kC>(t, s0)) = u32x2{pack_bf16x2(mq[0], mq[1]), pack_bf16x2(mq[2], mq[3])};
-      *reinterpret_cast<u32x2*>(sMdov + swz_off<kC>(t, s0)) = u32x2{pack_bf16x2(md[0], md[1]), pack_bf16x2(md[2], md[3])};
+      *reinterpret_cast<u32x2*>(dst + swz_off<kC>(t, 32 * sb + c_row(4 * jg, hi))) =
+          u32x2{pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3])};
     }
-  }
+  };
+  if (w < 4)
+    scores(sK, sQ, sMqk);
+  else
+    scores(sV, sO, sMdov);
   lds_barrier();
 
-  // Output tiles: wave w owns rows 32(w & 1) .. (t or s) and columns
-  // 64(w >> 1) .. +63 (two 32x32 tiles) of each of dq, dk, dv.
-  const int rb = w & 1, cb = w >> 1;
-  const size_t orow = base + (size_t)n * kC * rs;  // element offset of the chunk's first row
-  auto emit = [&](uint16_t* dst, const f32x16* x) {
-#pragma unroll
-    for (int nb = 0; nb < 2; nb++)
-#pragma unroll
-      for (int j = 0; j < 16; j++) {
-        const int r = 32 * rb + c_row(j, hi);
-        if (r < nv) dst[orow + (size_t)r * rs + 64 * cb + 32 * nb + l32] = to_bf16(x[nb][j]);
-      }
-  };
-  // Row sums of x o src over this wave's 64 columns, into sdG[kind][cb]
-  // (fixed-order sums: no atomics, so dG is reproducible bit for bit).
-  auto dg_part = [&](const f32x16* x, const uint16_t* src, int kind) {
-#pragma unroll
-    for (int j = 0; j < 16; j++) {
-      const int r = 32 * rb + c_row(j, hi);
-      float p = 0.f;
-#pragma unroll
-      for (int nb = 0; nb < 2; nb++) p += x[nb][j] * from_bf16(src[swz_off<kD>(r, 64 * cb + 32 * nb + (l32 & ~3)) + (l32 & 3)]);
-#pragma unroll
-      for (int o = 16; o >= 1; o >>= 1) p += __shfl_xor(p, o, 64);
-      if (l32 == 0) sdG[kind][cb][r] = p;
-    }
-  };
-
-  // dq = Mdov k + scale e^{G_t} do h^T
-  {
-    f32x16 a1[2] = {f32x16{}, f32x16{}}, a2[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int ks = 0; ks < kC / 16; ks++) {
-      const bf16x8 am = op_row<kC>(sMdov, 32 * rb, 16 * ks, lane);
-#pragma unroll
-      for (int nb = 0; nb < 2; nb++) a1[nb] = mfma32(am, op_tr<kD>(sK, 16 * ks, 64 * cb + 32 * nb, lane), a1[nb]);
-    }
-#pragma unroll
-    for (int ks = 0; ks < kD / 16; ks++) {
-      const bf16x8 ao = op_row<kD>(sO, 32 * rb, 16 * ks, lane);
-#pragma unroll
-      for (int nb = 0; nb < 2; nb++) a2[nb] = mfma32(ao, op_row<kD>(sH, 64 * cb + 32 * nb, 16 * ks, lane), a2[nb]);
-    }
-#pragma unroll
-    for (int j = 0; j < 16; j++) {
-      const float f = scale * __expf(sG[32 * rb + c_row(j, hi)]);
-#pragma unroll
-      for (int nb = 0; nb < 2; nb++) a1[nb][j] += f * a2[nb][j];
-    }
-    emit(dq, a1);
-    dg_part(a1, sQ, 0);
-  }
+  const int fb = w >> 1, tb = w & 1;  // feature block (32 wide), token block
+  const int tok = 32 * tb + l32;      // this lane's token
   const float gl = sG[nv - 1];
-  // dk = Mdov^T q + e^{Gl - G_s} v dH^T
-  {
-    f32x16 a1[2] = {f32x16{}, f32x16{}}, a2[2] = {f32x16{}, f32x16{}};
+
+  // In-chunk products (transposed):
+  //   dq^T[d][t] = sum_s k[s][d] Mdov[t][s]     dk^T[d][s] = sum_t q[t][d] Mdov[t][s]
+  //   dv^T[v][s] = sum_t do[t][v] Mqk[t][s]
+  f32x16 aq = f32x16{}, ak = f32x16{}, av = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < kC / 16; ks++) {
-      const bf16x8 am = op_tr<kC>(sMdov, 16 * ks, 32 * rb, lane);
-#pragma unroll
-      for (int nb = 0; nb < 2; nb++) a1[nb] = mfma32(am, op_tr<kD>(sQ, 16 * ks, 64 * cb + 32 * nb, lane), a1[nb]);
-    }
-#pragma unroll
-    for (int ks = 0; ks < kD / 16; ks++) {
-      const bf16x8 av = op_row<kD>(sV, 32 * rb, 16 * ks, lane);
-#pragma unroll
-      for (int nb = 0; nb < 2; nb++) a2[nb] = mfma32(av, op_row<kD>(sDH, 64 * cb + 32 * nb, 16 * ks, lane), a2[nb]);
-    }
-#pragma unroll
-    for (int j = 0; j < 16; j++) {
-      const float f = __expf(gl - sG[32 * rb + c_row(j, hi)]);
-#pragma unroll
-      for (int nb = 0; nb < 2; nb++) a1[nb][j] += f * a2[nb][j];
-    }
-    emit(dk, a1);
-    dg_part(a1, sK, 1);
+  for (int ks = 0; ks < kC / 16; ks++) {
+    aq = mfma32(op_tr<kD>(sK, oD, 16 * ks, 32 * fb), op_row<kC>(sMdov, oC, 32 * tb, 16 * ks), aq);
+    ak = mfma32(op_tr<kD>(sQ, oD, 16 * ks, 32 * fb), op_tr<kC>(sMdov, oC, 16 * ks, 32 * tb), ak);
+    av = mfma32(op_tr<kD>(sO, oD, 16 * ks, 32 * fb), op_tr<kC>(sMqk, oC, 16 * ks, 32 * tb), av);
   }
-  // dv = Mqk^T do + e^{Gl - G_s} k dH
-  {
-    f32x16 a1[2] = {f32x16{}, f32x16{}}, a2[2] = {f32x16{}, f32x16{}};
+  wait_vmem();
+  lds_barrier();  // h_n and dH_{n+1} resident
+  // State terms (transposed), scaled per token (per lane):
+  //   dq^T += scale e^{G_t} h do^T        dk^T += e^{Gl - G_s} dH v^T
+  //   dv^T += e^{Gl - G_s} dH^T k^T
+  f32x16 sq = f32x16{}, sk = f32x16{}, sv = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < kC / 16; ks++) {
-      const bf16x8 am = op_tr<kC>(sMqk, 16 * ks, 32 * rb, lane);
+  for (int ks = 0; ks < kD / 16; ks++) {
+    sq = mfma32(op_row<kD>(sH, oD, 32 * fb, 16 * ks), op_row<kD>(sO, oD, 32 * tb, 16 * ks), sq);
+    sk = mfma32(op_row<kD>(sDH, oD, 32 * fb, 16 * ks), op_row<kD>(sV, oD, 32 * tb, 16 * ks), sk);
+    sv = mfma32(op_tr<kD>(sDH, oD, 16 * ks, 32 * fb), op_row<kD>(sK, oD, 32 * tb, 16 * ks), sv);
+  }
+  const float fq = scale * __expf(sG[tok]), fkv = __expf(gl - sG[tok]);
+  aq += fq * sq;
+  ak += fkv * sk;
+  av += fkv * sv;
+
+  // Stores: lane = token, four consecutive features per 8-byte store.
+  const size_t orow = base + (size_t)(n * kC + tok) * rs + 32 * fb;
+  if (tok < nv) {
 #pragma unroll
-      for (int nb = 0; nb < 2; nb++) a1[nb] = mfma32(am, op_tr<kD>(sO, 16 * ks, 64 * cb + 32 * nb, lane), a1[nb]);
+    for (int jg = 0; jg < 4; jg++) {
+      const int f0 = c_row(4 * jg, hi);
+      *reinterpret_cast<u32x2*>(dq + orow + f0) = u32x2{pack_bf16x2(aq[4 * jg], aq[4 * jg + 1]),
+                                                        pack_bf16x2(aq[4 * jg + 2], aq[4 * jg + 3])};
+      *reinterpret_cast<u32x2*>(dk + orow + f0) = u32x2{pack_bf16x2(ak[4 * jg], ak[4 * jg + 1]),
+                                                        pack_bf16x2(ak[4 * jg + 2], ak[4 * jg + 3])};
+      *reinterpret_cast<u32x2*>(dv + orow + f0) = u32x2{pack_bf16x2(av[4 * jg], av[4 * jg + 1]),
+                                                        pack_bf16x2(av[4 * jg + 2], av[4 * jg + 3])};
     }
+  }
+  // q.dq and k.dk over this wave's 32 features: in-lane sums, the other
+  // lane half, then one partial per (feature block, token) in LDS.
+  float pq = 0.f, pk = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < kD / 16; ks++) {
-      const bf16x8 ak = op_row<kD>(sK, 32 * rb, 16 * ks, lane);
+  for (int jg = 0; jg < 4; jg++) {
+    const int f0 = 32 * fb + c_row(4 * jg, hi);
+    const u32x2 qv = *reinterpret_cast<const u32x2*>(sQ + swz_off<kD>(tok, f0));
+    const u32x2 kv = *reinterpret_cast<const u32x2*>(sK + swz_off<kD>(tok, f0));
 #pragma unroll
-      for (int nb = 0; nb < 2; nb++) a2[nb] = mfma32(ak, op_tr<kD>(sDH, 16 * ks, 64 * cb + 32 * nb, lane), a2[nb]);
+    for (int jj = 0; jj < 4; jj++) {
+      const uint32_t wq = qv[jj >> 1], wk = kv[jj >> 1];
+      const float xq = __uint_as_float((jj & 1) ? (wq & 0xffff0000u) : (wq << 16));
+      const float xk = __uint_as_float((jj & 1) ? (wk & 0xffff0000u) : (wk << 16));
+      pq = fmaf(xq, aq[4 * jg + jj], pq);
+      pk = fmaf(xk, ak[4 * jg + jj], pk);
     }
-#pragma unroll
-    for (int j = 0; j < 16; j++) {
-      const float f = __expf(gl - sG[32 * rb + c_row(j, hi)]);
-#pragma unroll
-      for (int nb = 0; nb < 2; nb++) a1[nb][j] += f * a2[nb][j];
-    }
-    emit(dv, a1);
+  }
+  pq = xhalf_sum(pq);
+  pk = xhalf_sum(pk);
+  if (hi == 0) {
+    sdG[0][fb][tok] = pq;
+    sdG[1][fb][tok] = pk;
   }
   lds_barrier();
-  if (w == 0 && lane < nv)
-    dG[(size_t)b * T * H + (size_t)(n * kC + lane) * H + h] =
-        (sdG[0][0][lane] + sdG[0][1][lane]) - (sdG[1][0][lane] + sdG[1][1][lane]);
+  if (w == 0 && lane < nv) {
+    const float a = ((sdG[0][0][lane] + sdG[0][1][lane]) + (sdG[0][2][lane] + sdG[0][3][lane]));
+    const float c = ((sdG[1][0][lane] + sdG[1][1][lane]) + (sdG[1][2][lane] + sdG[1][3][lane]));
+    dG[(size_t)bh * T + n * kC + lane] = a - c;
+  }
 }
 
-// dg[b, t, h] = sum_{t' >= t} dG[b, t', h]: one wave per (b, h), 64 tokens
-// per step from the end, with the running total carried.
-__global__ __launch_bounds__(64) void gla_dg_kernel(const float* __restrict__ dG, float* __restrict__ dg, int T, int H) {
-  const int lane = threadIdx.x, bh = blockIdx.x, b = bh / H, h = bh % H;
-  const float* src = dG + (size_t)b * T * H + h;
+// dg[b, t, h] = sum_{t' >= t} dG[b*H + h][t']: one workgroup per (b, h),
+// segments of 4096 tokens from the end (16 consecutive tokens per thread:
+// in-thread suffix sums, then suffix sums of the thread totals across the
+// wave (shuffles) and the four waves (LDS)), the running total carried.
+__global__ __launch_bounds__(256) void gla_dg_kernel(const float* __restrict__ dG, float* __restrict__ dg, int T, int H) {
+  constexpr int PER = 16, SEG = 256 * PER;
+  __shared__ float sW[4];
+  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
+  const int bh = blockIdx.x, b = bh / H, h = bh % H;
+  const float* src = dG + (size_t)bh * T;
   float* dst = dg + (size_t)b * T * H + h;
   float carry = 0.f;
-  for (int t1 = T; t1 > 0; t1 -= 64) {
-    const int t = t1 - 1 - lane;  // lane 0 takes the last token of the block
-    float x = t >= 0 ? src[(size_t)t * H] : 0.f;
+  for (int seg_end = T; seg_end > 0; seg_end -= SEG) {
+    const int t0 = seg_end - SEG + PER * tid;  // this thread's first token (may be negative)
+    float x[PER];
+    float tot = 0.f;
+#pragma unroll
+    for (int i = PER - 1; i >= 0; i--) {
+      const int t = t0 + i;
+      tot += (t >= 0 ? src[t] : 0.f);
+      x[i] = tot;  // sum of this thread's tokens t0+i .. t0+PER-1
+    }
+    float suf = tot;  // inclusive suffix over the lanes of this wave
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      const float y = __shfl_up(x, o, 64);
-      if (lane >= o) x += y;
+      const float y = __shfl_down(suf, o, 64);
+      if (l + o < 64) suf += y;
     }
-    if (t >= 0) dst[(size_t)t * H] = x + carry;
-    carry += __shfl(x, 63, 64);
+    if (l == 0) sW[w] = suf;
+    __syncthreads();
+    float after_w = 0.f;
+    for (int j = w + 1; j < 4; j++) after_w += sW[j];
+    const float seg_total = (sW[0] + sW[1]) + (sW[2] + sW[3]);
+    const float after = suf - tot + after_w + carry;  // tokens after this thread's block
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+      const int t = t0 + i;
+      if (t >= 0) dst[(size_t)t * H] = x[i] + after;
+    }
+    carry += seg_total;
+    __syncthreads();  // sW reused by the next segment
   }
 }
 
@@ -377,19 +429,19 @@ hipError_t launch_gla_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* 
                           int B, int T, int H, float scale, hipStream_t stream) {
   const int N = (T + kC - 1) / kC;
   uint16_t* hs = (uint16_t*)workspace;
-  uint16_t* dhs = hs + (size_t)B * H * N * kD * kD;
-  float* dG = (float*)(dhs + (size_t)B * H * N * kD * kD);
+  uint16_t* dhs = hs + (size_t)B * H * (N + 1) * kD * kD;
+  float* dG = (float*)(dhs + (size_t)B * H * (N + 1) * kD * kD);
   hipLaunchKernelGGL(gla_states_kernel, dim3(B * H, kD / 64, 2), dim3(256), 0, stream, q, k, v, dout, g, hs, dhs, T,
                      H, scale);
-  hipLaunchKernelGGL(gla_dqkv_kernel, dim3(N, B * H), dim3(256), 0, stream, q, k, v, dout, g, hs, dhs, dq, dk, dv,
+  hipLaunchKernelGGL(gla_dqkv_kernel, dim3(N, B * H), dim3(512), 0, stream, q, k, v, dout, g, hs, dhs, dq, dk, dv,
                      dG, T, H, scale);
-  hipLaunchKernelGGL(gla_dg_kernel, dim3(B * H), dim3(64), 0, stream, dG, dg, T, H);
+  hipLaunchKernelGGL(gla_dg_kernel, dim3(B * H), dim3(256), 0, stream, dG, dg, T, H);
   return hipGetLastError();
 }
 
 size_t gla_bwd_workspace_bytes(int B, int T, int H) {
   const size_t N = (T + kC - 1) / kC;
-  return 2 * (size_t)B * H * N * kD * kD * sizeof(uint16_t) + (size_t)B * T * H * sizeof(float);
+  return 2 * (size_t)B * H * (N + 1) * kD * kD * sizeof(uint16_t) + (size_t)B * T * H * sizeof(float);
 }
 
 }  // namespace mi355

@@ -90,8 +90,8 @@ hipError_t launch_postprocess(const float* dq_accum, const float* dk_part, const
 // Simple gated linear attention, chunked backward (head dim 128, chunks of
 // 64): states, per-chunk dq/dk/dv and the gate's reverse running sum.
 // Tensors [B][T][H][128] bf16, g and dg [B][T][H] fp32; the workspace holds
-// the bf16 chunk states and their gradients ([B*H][N][128][128] each) and
-// the per-token dG ([B][T][H] fp32).
+// the bf16 chunk states and their gradients ([B*H][N+1][128][128] each, one
+// spare slot) and the per-token dG ([B*H][T] fp32).
 hipError_t launch_gla_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
                           const float* g, uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dg, void* workspace,
                           int B, int T, int H, float scale, hipStream_t stream);
