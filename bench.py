@@ -65,6 +65,14 @@ def recorded_traffic(workload, path):
     return entry.get("bytes_per_launch")
 
 
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
+    except Exception:  # threadpoolctl missing: numpy BLAS default
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(w, causal, budget_s):
     """The fp64 oracle on host cores, one KV group at a time until the budget is used."""
     import numpy as np
@@ -73,11 +81,7 @@ def cpu_baseline(w, causal, budget_s):
     from attention_backward_fwd_amd.synthetic import make_inputs
     from oracle import attention as orc
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
-    except Exception:  # threadpoolctl missing: numpy BLAS default
-        cores = os.cpu_count() or 1
+    cores = _blas_threads()
     g = w.groups
     groups_done, t_total = 0, 0.0
     seed = 0
@@ -125,13 +129,26 @@ def bench_merge(args, w, bd, torch):
     rows = w.batch * w.heads_q * w.seqlen
     nbytes = n * (2 * nq + 4 * rows) + 2 * nq + 4 * rows
     gbs = nbytes / (ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import cp
+        bsl = 1  # one batch element of the partials
+        op_ = o_p[:, :bsl].float().cpu().double().numpy()
+        lp_ = l_p[:, :bsl].cpu().double().numpy()
+        t1 = time.perf_counter()
+        cp.merge_partials(op_, lp_)
+        t_cpu = time.perf_counter() - t1
+        cpu = {"value": round(nbytes * bsl / w.batch / t_cpu / 1e9, 4), "unit": "GB/s", "cores": int(_blas_threads()),
+               "kind": "oracle", "sample": f"batch element 0 of {w.batch} ({n} parts), fp64, {t_cpu:.1f} s; "
+                                           f"the same bytes per row"}
     print(json.dumps({"metric": "attn_merge HBM throughput", "value": round(gbs, 1), "unit": "GB/s",
                       "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
                       "higher_is_better": True, "dtype": "bf16 O, fp32 LSE", "data": "synthetic",
                       "config": {"workload": w.name, "parts": n},
                       "roofline": {"kernel": "merge_kernel", "bound": "hbm", "achieved": round(gbs, 1),
                                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                                   "traffic": None}}), flush=True)
+                                   "traffic": None},
+                      **({"cpu_baseline": cpu} if cpu else {})}), flush=True)
 
 
 def bench_varlen(args, bd, torch):
@@ -188,6 +205,23 @@ def bench_varlen(args, bd, torch):
     value = (fwd_f + bwd_f) * args.steps / elapsed / 1e12
     bwd_tflops = bwd_f / (bwd_ms * 1e-3) / 1e12
     path = "atomic" if use_atomic else "split"
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import varlen as vl
+        f = {n: x.to(torch.float64).numpy() for n, x in inp.items()}
+        cul = cu_cpu.tolist()
+        done, flop_done, t_cpu = 0, 0.0, 0.0
+        for a, e in zip(cul[:-1], cul[1:]):  # whole sequences, all heads, in pack order
+            if t_cpu >= args.cpu_budget:
+                break
+            t1 = time.perf_counter()
+            vl.varlen_bwd(f["q"][a:e], f["k"][a:e], f["v"][a:e], f["do"][a:e], [0, e - a], scale, True, 1)
+            t_cpu += time.perf_counter() - t1
+            done += 1
+            flop_done += 14 * (e - a) ** 2 * hq * dim / 2
+        cpu = {"value": round(flop_done / t_cpu / 1e12, 6), "unit": "TFLOP/s", "cores": int(_blas_threads()),
+               "kind": "oracle", "sample": f"{done} of {len(lengths)} sequences (all heads), fwd+bwd in fp64, "
+                                           f"{t_cpu:.1f} s; the same per-sequence causal FLOP count"}
     print(json.dumps({
         "metric": "packed-sequence attention fwd+bwd TFLOP/s (bf16, causal)", "value": round(value, 3),
         "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -201,6 +235,7 @@ def bench_varlen(args, bd, torch):
         "roofline": {"kernel": "bwd_kernel (packed)" + ("" if use_atomic else " + dq_sum_varlen_kernel"),
                      "bound": "mfma", "achieved": round(bwd_tflops, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        **({"cpu_baseline": cpu} if cpu else {}),
     }), flush=True)
 
 
@@ -240,6 +275,21 @@ def bench_gla(args, bd, torch):
     n_chunks = b * h * ((t + 63) // 64)
     flop = n_chunks * (10 * 64 * d * d + 10 * 64 * 64 * d)  # the chunked algorithm's matrix products
     gbs = nbytes / (ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import linear_attn as la
+        f = {n: x.cpu().to(torch.float64).numpy() for n, x in inp.items()}
+        heads, t_cpu = 0, 0.0
+        while t_cpu < args.cpu_budget and heads < b * h:
+            bb_, hh = divmod(heads, h)
+            t1 = time.perf_counter()
+            la.gla_bwd(f["q"][bb_:bb_ + 1], f["k"][bb_:bb_ + 1], f["v"][bb_:bb_ + 1], f["g"][bb_:bb_ + 1],
+                       f["do"][bb_:bb_ + 1], scale, heads=[(0, hh)])
+            t_cpu += time.perf_counter() - t1
+            heads += 1
+        cpu = {"value": round(nbytes * heads / (b * h) / t_cpu / 1e9, 4), "unit": "GB/s", "cores": int(_blas_threads()),
+               "kind": "oracle", "sample": f"{heads} of {b * h} (batch, head) pairs at full length, quadratic fp64 "
+                                           f"form, {t_cpu:.1f} s; the same algorithmic bytes per head"}
     print(json.dumps({
         "metric": "simple-GLA chunk backward throughput (algorithmic HBM bytes)", "value": round(gbs, 1),
         "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -250,6 +300,7 @@ def bench_gla(args, bd, torch):
         "mfma_tflops": round(flop / (ms * 1e-3) / 1e12, 3),
         "roofline": {"kernel": "gla_states + gla_dqkv + gla_dg", "bound": "hbm", "achieved": round(gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+        **({"cpu_baseline": cpu} if cpu else {}),
     }), flush=True)
 
 
