@@ -53,6 +53,17 @@ class gla_shape(ctypes.Structure):
     ]
 
 
+class smla_shape(ctypes.Structure):
+    _fields_ = [
+        ("tokens", ctypes.c_int32),
+        ("kv_tokens", ctypes.c_int32),
+        ("heads", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+        ("dim_qk", ctypes.c_int32),
+        ("dim_v", ctypes.c_int32),
+    ]
+
+
 _lib = None
 
 
@@ -94,6 +105,8 @@ def library():
         lib.gla_chunk_bwd_workspace_bytes.argtypes = [gla_shape]
         lib.gla_chunk_bwd.restype = ctypes.c_int
         lib.gla_chunk_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, gla_shape, ctypes.c_float, P]
+        lib.attn_sparse_mla_fwd.restype = ctypes.c_int
+        lib.attn_sparse_mla_fwd.argtypes = [P, P, P, P, P, smla_shape, ctypes.c_float, P]
         _lib = lib
     return _lib
 
@@ -199,6 +212,11 @@ def attn_bwd_varlen_postprocess(dq_accum, workspace, dq, dk, dv, shape, stream=N
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(library().attn_bwd_varlen_postprocess(_ptr(dq_accum), _ptr(workspace), ws_bytes, _ptr(dq), _ptr(dk),
                                                  _ptr(dv), shape, _stream(stream)), "attn_bwd_varlen_postprocess")
+
+
+def attn_sparse_mla_fwd(q, kv, indices, o, lse, shape, softmax_scale, stream=None):
+    _check(library().attn_sparse_mla_fwd(_ptr(q), _ptr(kv), _ptr(indices), _ptr(o), _ptr(lse), shape,
+                                         float(softmax_scale), _stream(stream)), "attn_sparse_mla_fwd")
 
 
 def gla_chunk_bwd_workspace_bytes(shape):
@@ -362,3 +380,21 @@ def gla_backward(q, k, v, g, do, scale, buffers=None, stream=None):
     bb = buffers or GlaBuffers(q)
     gla_chunk_bwd(q, k, v, g, do, bb.dq, bb.dk, bb.dv, bb.dg, bb.workspace, bb.shape, scale, stream)
     return bb.dq, bb.dk, bb.dv, bb.dg
+
+
+def smla_shape_of(q, kv, indices):
+    t, h, dqk = q.shape
+    return smla_shape(t, kv.shape[0], h, indices.shape[1], dqk, 512)
+
+
+def sparse_mla_forward(q, kv, indices, scale, stream=None):
+    """O [T,H,512], LSE [T,H] of sparse MLA (q [T,H,576], kv [Tk,576] bf16,
+    indices [T,K] int32 on the GPU)."""
+    _require_gpu_inputs(q, kv)
+    if not indices.is_cuda or indices.dtype != torch.int32 or not indices.is_contiguous():
+        raise ValueError("indices must be a contiguous int32 GPU tensor")
+    shape = smla_shape_of(q, kv, indices)
+    o = torch.empty((q.shape[0], q.shape[1], 512), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((q.shape[0], q.shape[1]), dtype=torch.float32, device=q.device)
+    attn_sparse_mla_fwd(q, kv, indices, o, lse, shape, scale, stream)
+    return o, lse

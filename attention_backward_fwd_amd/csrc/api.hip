@@ -77,6 +77,15 @@ int check_gla(const gla_shape& s) {
 
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
+int check_smla(const smla_shape& s) {
+  if (s.tokens < 1 || s.kv_tokens < 1 || s.heads < 1 || s.topk < 1) return ATTN_ERR_BAD_SHAPE;
+  if (s.dim_qk != 576 || s.dim_v != 512) return ATTN_ERR_HEAD_DIM;
+  if ((long long)s.tokens * s.heads * 576 >= (1LL << 31) || (long long)s.kv_tokens * 576 >= (1LL << 31) ||
+      (long long)s.tokens * s.topk >= (1LL << 31) || s.topk > 8192)
+    return ATTN_ERR_RANGE;
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -391,6 +400,17 @@ int gla_chunk_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const
     return ATTN_ERR_ALIGN;
   return hip_status(launch_gla_bwd(q, k, v, dout, g, dq, dk, dv, dg, workspace, shape.batch, shape.seqlen,
                                    shape.heads, scale, (hipStream_t)stream));
+}
+
+int attn_sparse_mla_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* indices, uint16_t* o, float* lse,
+                        smla_shape shape, float softmax_scale, void* stream) {
+  if (!q || !kv || !indices || !o || !lse) return ATTN_ERR_NULL_PTR;
+  const int st = check_smla(shape);
+  if (st) return st;
+  if (!good_scale(softmax_scale)) return ATTN_ERR_RANGE;
+  if (!aligned16(q) || !aligned16(kv) || !aligned16(o) || !aligned4(lse) || !aligned4(indices)) return ATTN_ERR_ALIGN;
+  return hip_status(launch_smla_fwd(q, kv, indices, o, lse, shape.tokens, shape.kv_tokens, shape.heads, shape.topk,
+                                    softmax_scale, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -97,6 +97,12 @@ hipError_t launch_gla_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* 
                           int B, int T, int H, float scale, hipStream_t stream);
 size_t gla_bwd_workspace_bytes(int B, int T, int H);
 
+// Sparse MLA (576-wide latent rows, 512 value channels) over per-token
+// index lists: q [T][H][576], kv [Tk][576], idx [T][K] int32 (-1 or out of
+// range: unused), o [T][H][512] bf16, lse [T][H] fp32.
+hipError_t launch_smla_fwd(const uint16_t* q, const uint16_t* kv, const int* idx, uint16_t* o, float* lse, int T,
+                           int Tk, int H, int K, float scale, hipStream_t stream);
+
 hipError_t launch_merge(const uint16_t* o_parts, const float* lse_parts, int n_parts, uint16_t* o, float* lse,
                         int B, int S, int Hq, int D, hipStream_t stream);
 

@@ -1,0 +1,209 @@
+// Sparse MLA attention: each query token attends to the latent key rows its
+// index list selects (top-k, -1 for an unused slot), the way the Megatron-LM
+// pull request "TileLang implementation of the fused DSA operations" (NVIDIA
+// Megatron-LM #5049, file table and review summary) adds it: 576-wide latent
+// rows as keys, their first 512 channels as values, bf16 in, fp32
+// accumulation.  Per token t and head h, over the valid entries i of idx[t]:
+//   s_i = scale q[t,h] . kv[idx[t,i]],  P = softmax(s),  O = sum_i P_i kv[idx[t,i], :512]
+//   LSE = log sum_i exp(s_i)  (O = 0, LSE = -inf without a valid entry)
+//
+// Forward kernel: one workgroup (4 waves) per (token, 32-head tile).  Per
+// tile of 32 entries the key rows are gathered by LDS-DMA (one buffer ahead)
+// into five swizzled sub-tiles (four of 128 channels, one of 64); the waves
+// split the 576-channel reduction of S^T = KV Q^T (9 k-steps each) and sum
+// the four partials through LDS in a fixed order, so that every wave holds
+// the same scores and runs the same online softmax (a head per lane); wave w
+// then accumulates O^T rows 128w .. 128w+127 = V^T P^T from its own value
+// sub-tile (transposing reads) and the probabilities in registers.
+#include "common.h"
+#include "kernels.h"
+
+namespace mi355 {
+
+namespace {
+
+constexpr int kQK = 576, kVD = 512;
+constexpr int kHT = 32;  // heads per workgroup
+constexpr int kKT = 32;  // entries per tile
+constexpr int kSub = kKT * 128;  // elements of a 128-channel sub-tile of 32 rows
+
+// Element offset of (row, col) in the sub-tile layout of a [32][576] tile:
+// sub-tile col / 128 (the last one 64 wide), each swizzled on its own.
+__device__ __forceinline__ int sub_off(int row, int col) {
+  const int st = col >> 7, c = col & 127;
+  return st * kSub + (st < 4 ? swz_off<128>(row, c) : swz_off<64>(row, c));
+}
+
+// 32x32x16 operands (k order: lane half hi gets k = 4hi..4hi+3, 8+4hi..8+4hi+3
+// of each 16-step, the row order of a 32x32 result's elements 0..7).
+// Row-style: tile [x][k] in the sub-tile layout, k0 a multiple of 16.
+__device__ __forceinline__ bf16x8 sop_row(const uint16_t* t, int x, int k0, int hi) {
+  const u32x2 a = *reinterpret_cast<const u32x2*>(t + sub_off(x, k0 + 4 * hi));
+  const u32x2 b = *reinterpret_cast<const u32x2*>(t + sub_off(x, k0 + 8 + 4 * hi));
+  return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
+}
+// Transposing: tile [k][x] with x inside one 128-channel sub-tile `st`.
+__device__ __forceinline__ bf16x8 sop_tr(const uint16_t* t, int st, int k0, int x0, int lane) {
+  const int hi = lane >> 5, L = lane & 15, gp = (lane >> 4) & 1;
+  const int col = x0 + 16 * gp + 4 * (L & 3);
+  const uint16_t* s = t + st * kSub;
+  return lds_read_tr8(s + swz_off<128>(k0 + 4 * hi + (L >> 2), col), s + swz_off<128>(k0 + 8 + 4 * hi + (L >> 2), col));
+}
+
+// Gather rows rows[r] (r < 32, device row indices, already made valid) of a
+// [*][576] bf16 matrix into a tile in the sub-tile layout, by LDS-DMA.  Per
+// wave: 2 instructions per 128-channel sub-tile, 1 for the 64-channel one.
+__device__ __forceinline__ void gather_rows_async(const uint16_t* g, const int* rows, uint16_t* tile, int w, int lane) {
+#pragma unroll
+  for (int st = 0; st < 4; st++) {
+#pragma unroll
+    for (int jj = 0; jj < 2; jj++) {
+      const int j = w + 4 * jj;             // instruction: rows 4j .. 4j+3
+      const int r = 4 * j + (lane >> 4), slot = lane & 15;
+      const uint16_t* src = g + (size_t)rows[r] * kQK + 128 * st + ((slot ^ swz<128>(r)) << 3);
+      __builtin_amdgcn_global_load_lds(src, lds_ptr(tile + st * kSub + j * 512), 16, 0, 0);
+    }
+  }
+  {
+    const int r = 8 * w + (lane >> 3), slot = lane & 7;  // 8 rows per instruction
+    const uint16_t* src = g + (size_t)rows[r] * kQK + 512 + ((slot ^ swz<64>(r)) << 3);
+    __builtin_amdgcn_global_load_lds(src, lds_ptr(tile + 4 * kSub + w * 512), 16, 0, 0);
+  }
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void smla_fwd_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int* __restrict__ idx,
+    uint16_t* __restrict__ o, float* __restrict__ lse, int T, int Tk, int H, int K, float scale) {
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[4 * kSub + kKT * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t sKV0[4 * kSub + kKT * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t sKV1[4 * kSub + kKT * 64];
+  __shared__ float sSp[4][16 * 64];     // S^T partials, one per wave, in result-register order
+  // Entry lists of three consecutive tiles (tile i in slot i % 3): tile i is
+  // masked while tile i+1 is gathered and tile i+2's list is written.
+  __shared__ int sRow[3][kKT];          // gathered row of each entry (invalid: row 0)
+  __shared__ int sOk[3][kKT];           // entry valid
+
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), hi = lane >> 5;
+  const int l32 = lane & 31;
+  const int n_ht = (H + kHT - 1) / kHT;
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int t = __builtin_amdgcn_readfirstlane(id / n_ht), h0 = __builtin_amdgcn_readfirstlane((id % n_ht) * kHT);
+  const int n_tiles = (K + kKT - 1) / kKT;
+  const int* idx_t = idx + (size_t)t * K;
+
+  // The query tile (heads h0 .. h0+31; heads past H repeat the last one).
+  {
+    const uint16_t* qb = q + ((size_t)t * H) * kQK;
+#pragma unroll
+    for (int st = 0; st < 4; st++) tile_load_async<128, kHT, 4>(qb + 128 * st, kQK, h0, H, sQ + st * kSub, w, lane);
+    tile_load_async<64, kHT, 4>(qb + 512, kQK, h0, H, sQ + 4 * kSub, w, lane);
+  }
+  // Entry list of tile it: rows and validity into slot it % 3 (wave 0).
+  auto entries = [&](int it) {
+    if (w == 0 && lane < kKT) {
+      const int e = it * kKT + lane;
+      const int j = e < K ? idx_t[e] : -1;
+      const bool ok = j >= 0 && j < Tk;
+      sRow[it % 3][lane] = ok ? j : 0;
+      sOk[it % 3][lane] = ok;
+    }
+  };
+  entries(0);
+  lds_barrier();
+  gather_rows_async(kv, sRow[0], sKV0, w, lane);
+  if (n_tiles > 1) entries(1);
+
+  const float c = scale * kLog2e;
+  f32x16 oacc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; dt++) oacc[dt] = f32x16{};
+  float m_i = -INFINITY, l_i = 0.f;
+
+  auto tile = [&](auto buf_tag, int it) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    const uint16_t* cKV = BUF ? sKV1 : sKV0;
+    uint16_t* nKV = BUF ? sKV0 : sKV1;
+    wait_vmem();
+    lds_barrier();  // tile it resident (and its entry list); every wave is done with tile it-1
+    if (it + 1 < n_tiles) gather_rows_async(kv, sRow[(it + 1) % 3], nKV, w, lane);
+    if (it + 2 < n_tiles) entries(it + 2);
+    // S^T partial over channels 144w .. 144w+143.
+    f32x16 sp = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < 9; kk++) {
+      const int d0 = 144 * w + 16 * kk;
+      sp = mfma32(sop_row(cKV, l32, d0, hi), sop_row(sQ, l32, d0, hi), sp);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; j++) sSp[w][j * 64 + lane] = sp[j];
+    lds_barrier();
+    f32x16 s;
+#pragma unroll
+    for (int j = 0; j < 16; j++) s[j] = (sSp[0][j * 64 + lane] + sSp[1][j * 64 + lane]) + (sSp[2][j * 64 + lane] + sSp[3][j * 64 + lane]);
+    // Unused slots and entries past the end of the list: -inf.
+#pragma unroll
+    for (int j = 0; j < 16; j++)
+      if (!sOk[it % 3][8 * (j >> 2) + 4 * hi + (j & 3)]) s[j] = -INFINITY;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 16; j++) mx = fmaxf(mx, s[j]);
+    mx = xhalf_max(mx);
+    const float m_new = fmaxf(m_i, mx);
+    const float mc = (m_new == -INFINITY ? 0.f : m_new) * c;
+    const float alpha = __builtin_amdgcn_exp2f(m_i * c - mc);
+    float rs = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      const float e = __builtin_amdgcn_exp2f(fmaf(s[j], c, -mc));
+      s[j] = e;
+      rs += e;
+    }
+    l_i = fmaf(l_i, alpha, rs);
+    m_i = m_new;
+#pragma unroll
+    for (int dt = 0; dt < 4; dt++) oacc[dt] *= alpha;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; kk++)
+      pb[kk] = pack8(s[8 * kk + 0], s[8 * kk + 1], s[8 * kk + 2], s[8 * kk + 3], s[8 * kk + 4], s[8 * kk + 5],
+                     s[8 * kk + 6], s[8 * kk + 7]);
+    // O^T rows 128w + 32dt .. += V^T P^T (value sub-tile w).
+#pragma unroll
+    for (int kk = 0; kk < 2; kk++)
+#pragma unroll
+      for (int dt = 0; dt < 4; dt++) oacc[dt] = mfma32(sop_tr(cKV, w, 16 * kk, 32 * dt, lane), pb[kk], oacc[dt]);
+  };
+  for (int it = 0; it < n_tiles; it += 2) {
+    tile(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < n_tiles) tile(std::integral_constant<int, 1>{}, it + 1);
+  }
+
+  const float l_tot = xhalf_sum(l_i);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const int h = h0 + l32;
+  if (h < H) {
+    uint16_t* orow = o + ((size_t)t * H + h) * kVD + 128 * w;
+#pragma unroll
+    for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+      for (int jg = 0; jg < 4; jg++) {
+        const int d = 32 * dt + 8 * jg + 4 * hi;
+        *reinterpret_cast<u32x2*>(orow + d) =
+            u32x2{pack_bf16x2(oacc[dt][4 * jg] * inv, oacc[dt][4 * jg + 1] * inv),
+                  pack_bf16x2(oacc[dt][4 * jg + 2] * inv, oacc[dt][4 * jg + 3] * inv)};
+      }
+    if (w == 0 && hi == 0) lse[(size_t)t * H + h] = m_i * scale + __builtin_amdgcn_logf(l_tot) * kLn2;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_smla_fwd(const uint16_t* q, const uint16_t* kv, const int* idx, uint16_t* o, float* lse, int T,
+                           int Tk, int H, int K, float scale, hipStream_t stream) {
+  const int n_ht = (H + kHT - 1) / kHT;
+  hipLaunchKernelGGL(smla_fwd_kernel, dim3((unsigned)((long long)T * n_ht)), dim3(256), 0, stream, q, kv, idx, o,
+                     lse, T, Tk, H, K, scale);
+  return hipGetLastError();
+}
+
+}  // namespace mi355

@@ -124,3 +124,30 @@ def gla_inputs(batch, seqlen, heads, head_dim, seed=0):
     x = torch.randn((batch, seqlen, heads), generator=gen, dtype=torch.float32)
     out["g"] = torch.nn.functional.logsigmoid(x) / 16.0
     return out
+
+
+# Sparse MLA: q [T, H, 576], kv [Tk, 576], do [T, H, 512] standard normal
+# (bf16 RNE, drawn in that order); each token's index list holds
+# min(K, t + 1) distinct keys drawn uniformly from 0 .. t (keys are the same
+# tokens, causal), in random order, then -1 in the unused slots.
+SMLA_WORKLOAD = {"name": "smla_t4096_h128_k2048", "tokens": 4096, "heads": 128, "topk": 2048}
+
+
+def smla_indices(tokens, kv_tokens, topk, seed=0):
+    """int32 [tokens, topk] causal index lists (see above) as a CPU tensor."""
+    gen = torch.Generator(device="cpu").manual_seed(seed + 1)
+    out = torch.full((tokens, topk), -1, dtype=torch.int32)
+    for t in range(tokens):
+        n_keys = min(t + 1, kv_tokens)
+        n = min(topk, n_keys)
+        out[t, :n] = torch.randperm(n_keys, generator=gen)[:n].to(torch.int32)
+    return out
+
+
+def smla_inputs(tokens, kv_tokens, heads, seed=0):
+    """dict q, kv, do (bf16 CPU tensors)."""
+    gen = torch.Generator(device="cpu").manual_seed(seed)
+    q = torch.randn((tokens, heads, 576), generator=gen, dtype=torch.float32)
+    kv = torch.randn((kv_tokens, 576), generator=gen, dtype=torch.float32)
+    do = torch.randn((tokens, heads, 512), generator=gen, dtype=torch.float32)
+    return {n: x.to(torch.bfloat16) for n, x in (("q", q), ("kv", kv), ("do", do))}

@@ -278,6 +278,37 @@ int gla_chunk_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const
                   uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dg, void* workspace, size_t workspace_bytes,
                   gla_shape shape, float scale, void* stream);
 
+/*
+ * Sparse MLA attention over top-k gathered latent keys.  The Megatron-LM
+ * pull request "TileLang implementation of the fused DSA operations" (NVIDIA
+ * Megatron-LM #5049, file table and review summary) adds a sparse MLA
+ * forward and backward (with preprocess and postprocess) for 576-wide latent
+ * rows whose first 512 channels are the values, index lists with -1 as the
+ * unused-slot sentinel, bf16 compute and fp32 accumulation.  Per token t and
+ * head h, over the valid entries i of indices[t] (0 <= j < kv_tokens; any
+ * other value is an unused slot; a key listed twice counts twice):
+ *   s_i = scale * q[t,h] . kv[j_i],   P = softmax(s),
+ *   o[t,h] = sum_i P_i kv[j_i, 0:512],   lse[t,h] = ln sum_i exp(s_i)
+ * and a token with no valid entry gets o = 0, lse = -inf.
+ *   q [tokens, heads, 576] bf16; kv [kv_tokens, 576] bf16 (one latent head
+ *   shared by all query heads); indices [tokens, topk] int32 (device);
+ *   o [tokens, heads, 512] bf16, lse [tokens, heads] fp32 (outputs; every
+ *   element written).  q, kv, o 16-byte aligned; indices and lse 4-byte.
+ * Heads are processed in tiles of 32 (a smaller or ragged head count is
+ * masked inside the tile).
+ */
+typedef struct smla_shape {
+  int32_t tokens;    /* T >= 1 query tokens */
+  int32_t kv_tokens; /* Tk >= 1 latent rows */
+  int32_t heads;     /* H >= 1 query heads */
+  int32_t topk;      /* K, 1 .. 8192 index entries per token */
+  int32_t dim_qk;    /* 576 */
+  int32_t dim_v;     /* 512 */
+} smla_shape;
+
+int attn_sparse_mla_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* indices, uint16_t* o, float* lse,
+                        smla_shape shape, float softmax_scale, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

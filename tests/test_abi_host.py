@@ -30,7 +30,8 @@ def test_library_exports_every_header_symbol():
     assert names == sorted(["attn_fwd", "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_bwd",
                             "attn_bwd_postprocess", "attn_merge", "attn_strerror", "attn_fwd_varlen",
                             "attn_bwd_varlen_workspace_bytes", "attn_bwd_varlen",
-                            "attn_bwd_varlen_postprocess", "gla_chunk_bwd_workspace_bytes", "gla_chunk_bwd"])
+                            "attn_bwd_varlen_postprocess", "gla_chunk_bwd_workspace_bytes", "gla_chunk_bwd",
+                            "attn_sparse_mla_fwd"])
     for n in names:
         assert hasattr(lib(), n), n
 
@@ -302,3 +303,27 @@ def test_gla_g_needs_only_4_byte_alignment():
     """g and dg are fp32 per-token values: 4-byte aligned is enough (the call
     then fails only on the workspace, which the test leaves too small)."""
     assert gbwd(g=P(0x10004), dg=P(0x10004), wsb=8) == E["ws"]
+
+
+# ------------------------------------------------------------ sparse MLA
+
+def mshp(t=8, tk=100, h=16, k=64, dqk=576, dv=512):
+    return bd.smla_shape(t, tk, h, k, dqk, dv)
+
+
+def mfwd(**kw):
+    args = dict(q=A, kv=A, idx=A, o=A, lse=A, shape=mshp(), scale=0.05, stream=None)
+    args.update(kw)
+    return lib().attn_sparse_mla_fwd(args["q"], args["kv"], args["idx"], args["o"], args["lse"], args["shape"],
+                                     args["scale"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"q": None}, "null"), ({"idx": None}, "null"), ({"lse": None}, "null"),
+    ({"shape": mshp(t=0)}, "shape"), ({"shape": mshp(tk=0)}, "shape"), ({"shape": mshp(h=0)}, "shape"),
+    ({"shape": mshp(k=0)}, "shape"), ({"shape": mshp(dqk=512)}, "hd"), ({"shape": mshp(dv=576)}, "hd"),
+    ({"shape": mshp(k=8193)}, "range"), ({"shape": mshp(t=1 << 20, h=64)}, "range"),
+    ({"scale": 0.0}, "range"), ({"q": MIS}, "align"), ({"o": MIS}, "align"), ({"idx": P(0x10002)}, "align"),
+])
+def test_sparse_mla_fwd_errors(kw, code):
+    assert mfwd(**kw) == E[code]

@@ -1,0 +1,73 @@
+"""GPU parity of sparse MLA (attn_sparse_mla_fwd) against the fp64 oracle:
+element by element on small problems (ragged head tiles and entry tiles,
+unused slots, out-of-range entries, keys listed twice, tokens without a valid
+entry) and on sampled tokens of the benchmark workload."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from attention_backward_fwd_amd import binding as bd
+from attention_backward_fwd_amd.synthetic import SMLA_WORKLOAD, smla_indices, smla_inputs
+from oracle import sparse_mla as sm
+from tests.gpu_helpers import TOL, err_ratio, np64, say
+
+pytestmark = pytest.mark.gpu
+
+SCALE = 1.0 / math.sqrt(576)
+
+
+def _indices(t, tk, k, seed):
+    rng = np.random.default_rng(seed)
+    idx = np.full((t, k), -1, dtype=np.int32)
+    for i in range(t):
+        n = int(rng.integers(1, k + 1))
+        idx[i, :n] = rng.choice(tk, size=min(n, tk), replace=False)[:n] if n <= tk else rng.integers(0, tk, n)
+    idx[min(1, t - 1)] = -1                                   # a token without any valid entry
+    if t > 2 and k > 3:
+        idx[2, 0] = tk + 5                                    # out of range: unused
+        idx[2, 1] = idx[2, 2] if idx[2, 2] >= 0 else 0       # a key listed twice
+    return idx
+
+
+def _check(o, lse, ro, rl, case):
+    r = err_ratio(np64(o), ro)
+    lse, rl = np64(lse), np.asarray(rl)
+    assert np.array_equal(np.isneginf(lse), np.isneginf(rl)), (case, "LSE -inf pattern")
+    fin = np.isfinite(rl)
+    le = np.max(np.abs(lse[fin] - rl[fin]) / np.maximum(1.0, np.abs(rl[fin])), initial=0.0)
+    say(f"{case}: o={r:.2e} lse={le:.2e}")
+    assert r <= TOL, (case, r)
+    assert le <= 1e-3, (case, le)
+    empty = np.isneginf(rl)
+    assert np.all(np64(o)[empty] == 0.0), case
+
+
+CASES = [(5, 40, 3, 37), (17, 100, 32, 64), (9, 300, 40, 100), (3, 7, 1, 1), (6, 70, 64, 33)]
+
+
+@pytest.mark.parametrize("t,tk,h,k", CASES)
+def test_smla_fwd_against_oracle(t, tk, h, k):
+    inp = smla_inputs(t, tk, h, seed=t + k)
+    idx = _indices(t, tk, k, seed=h)
+    f = {n: x.double().numpy() for n, x in inp.items()}
+    ro, rl = sm.sparse_mla_fwd(f["q"], f["kv"], idx, SCALE)
+    o, lse = bd.sparse_mla_forward(inp["q"].cuda(), inp["kv"].cuda(), torch.from_numpy(idx).cuda(), SCALE)
+    torch.cuda.synchronize()
+    _check(o, lse, ro, rl, f"smla fwd T{t} Tk{tk} H{h} K{k}")
+
+
+def test_smla_fwd_full_size_sampled():
+    w = SMLA_WORKLOAD
+    t, h, k = w["tokens"], w["heads"], w["topk"]
+    inp = smla_inputs(t, t, h, seed=0)
+    idx = smla_indices(t, t, k, seed=0)
+    say(f"[smla full] {w['name']}: gpu")
+    o, lse = bd.sparse_mla_forward(inp["q"].cuda(), inp["kv"].cuda(), idx.cuda(), SCALE)
+    torch.cuda.synchronize()
+    rows = [0, 1, 63, 2047, 2048, 3000, t - 1]
+    qf = inp["q"][rows].double().numpy()
+    ro, rl = sm.sparse_mla_fwd(qf, inp["kv"].double().numpy(), idx[rows].numpy(), SCALE)
+    _check(o[rows], lse[rows], ro, rl, f"[smla full] {w['name']} tokens {rows}")
