@@ -107,6 +107,12 @@ def library():
         lib.gla_chunk_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, gla_shape, ctypes.c_float, P]
         lib.attn_sparse_mla_fwd.restype = ctypes.c_int
         lib.attn_sparse_mla_fwd.argtypes = [P, P, P, P, P, smla_shape, ctypes.c_float, P]
+        lib.attn_sparse_mla_bwd_preprocess.restype = ctypes.c_int
+        lib.attn_sparse_mla_bwd_preprocess.argtypes = [P, P, P, P, smla_shape, P]
+        lib.attn_sparse_mla_bwd.restype = ctypes.c_int
+        lib.attn_sparse_mla_bwd.argtypes = [P, P, P, P, P, P, P, P, smla_shape, ctypes.c_float, P]
+        lib.attn_sparse_mla_bwd_postprocess.restype = ctypes.c_int
+        lib.attn_sparse_mla_bwd_postprocess.argtypes = [P, P, smla_shape, P]
         _lib = lib
     return _lib
 
@@ -217,6 +223,22 @@ def attn_bwd_varlen_postprocess(dq_accum, workspace, dq, dk, dv, shape, stream=N
 def attn_sparse_mla_fwd(q, kv, indices, o, lse, shape, softmax_scale, stream=None):
     _check(library().attn_sparse_mla_fwd(_ptr(q), _ptr(kv), _ptr(indices), _ptr(o), _ptr(lse), shape,
                                          float(softmax_scale), _stream(stream)), "attn_sparse_mla_fwd")
+
+
+def attn_sparse_mla_bwd_preprocess(o, dout, delta, dkv_accum, shape, stream=None):
+    _check(library().attn_sparse_mla_bwd_preprocess(_ptr(o), _ptr(dout), _ptr(delta), _ptr(dkv_accum), shape,
+                                                    _stream(stream)), "attn_sparse_mla_bwd_preprocess")
+
+
+def attn_sparse_mla_bwd(q, kv, dout, indices, lse, delta, dq, dkv_accum, shape, softmax_scale, stream=None):
+    _check(library().attn_sparse_mla_bwd(_ptr(q), _ptr(kv), _ptr(dout), _ptr(indices), _ptr(lse), _ptr(delta),
+                                         _ptr(dq), _ptr(dkv_accum), shape, float(softmax_scale), _stream(stream)),
+           "attn_sparse_mla_bwd")
+
+
+def attn_sparse_mla_bwd_postprocess(dkv_accum, dkv, shape, stream=None):
+    _check(library().attn_sparse_mla_bwd_postprocess(_ptr(dkv_accum), _ptr(dkv), shape, _stream(stream)),
+           "attn_sparse_mla_bwd_postprocess")
 
 
 def gla_chunk_bwd_workspace_bytes(shape):
@@ -398,3 +420,25 @@ def sparse_mla_forward(q, kv, indices, scale, stream=None):
     lse = torch.empty((q.shape[0], q.shape[1]), dtype=torch.float32, device=q.device)
     attn_sparse_mla_fwd(q, kv, indices, o, lse, shape, scale, stream)
     return o, lse
+
+
+class SmlaBwdBuffers:
+    """Outputs and scratch of one sparse MLA backward problem."""
+
+    def __init__(self, q, kv):
+        t, h, _ = q.shape
+        self.delta = torch.empty((t, h), dtype=torch.float32, device=q.device)
+        self.dq = torch.empty_like(q)
+        self.dkv_accum = torch.empty((kv.shape[0], 576), dtype=torch.float32, device=q.device)
+        self.dkv = torch.empty_like(kv)
+
+
+def sparse_mla_backward(q, kv, indices, o, lse, do, scale, buffers=None, stream=None):
+    """dq [T,H,576], dkv [Tk,576] via preprocess -> backward -> postprocess."""
+    _require_gpu_inputs(q, kv, o, do)
+    shape = smla_shape_of(q, kv, indices)
+    bb = buffers or SmlaBwdBuffers(q, kv)
+    attn_sparse_mla_bwd_preprocess(o, do, bb.delta, bb.dkv_accum, shape, stream)
+    attn_sparse_mla_bwd(q, kv, do, indices, lse, bb.delta, bb.dq, bb.dkv_accum, shape, scale, stream)
+    attn_sparse_mla_bwd_postprocess(bb.dkv_accum, bb.dkv, shape, stream)
+    return bb.dq, bb.dkv

@@ -413,4 +413,37 @@ int attn_sparse_mla_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* in
                                     softmax_scale, (hipStream_t)stream));
 }
 
+int attn_sparse_mla_bwd_preprocess(const uint16_t* o, const uint16_t* dout, float* delta, float* dkv_accum,
+                                   smla_shape shape, void* stream) {
+  if (!o || !dout || !delta) return ATTN_ERR_NULL_PTR;
+  const int st = check_smla(shape);
+  if (st) return st;
+  if (!aligned16(o) || !aligned16(dout) || !aligned4(delta) || (dkv_accum && !aligned16(dkv_accum)))
+    return ATTN_ERR_ALIGN;
+  return hip_status(launch_smla_bwd_pre(o, dout, delta, dkv_accum, shape.tokens, shape.kv_tokens, shape.heads,
+                                        (hipStream_t)stream));
+}
+
+int attn_sparse_mla_bwd(const uint16_t* q, const uint16_t* kv, const uint16_t* dout, const int32_t* indices,
+                        const float* lse, const float* delta, uint16_t* dq, float* dkv_accum, smla_shape shape,
+                        float softmax_scale, void* stream) {
+  if (!q || !kv || !dout || !indices || !lse || !delta || !dq || !dkv_accum) return ATTN_ERR_NULL_PTR;
+  const int st = check_smla(shape);
+  if (st) return st;
+  if (!good_scale(softmax_scale)) return ATTN_ERR_RANGE;
+  if (!aligned16(q) || !aligned16(kv) || !aligned16(dout) || !aligned16(dq) || !aligned16(dkv_accum) ||
+      !aligned4(indices) || !aligned4(lse) || !aligned4(delta))
+    return ATTN_ERR_ALIGN;
+  return hip_status(launch_smla_bwd(q, kv, dout, indices, lse, delta, dq, dkv_accum, shape.tokens, shape.kv_tokens,
+                                    shape.heads, shape.topk, softmax_scale, (hipStream_t)stream));
+}
+
+int attn_sparse_mla_bwd_postprocess(const float* dkv_accum, uint16_t* dkv, smla_shape shape, void* stream) {
+  if (!dkv_accum || !dkv) return ATTN_ERR_NULL_PTR;
+  const int st = check_smla(shape);
+  if (st) return st;
+  if (!aligned16(dkv_accum) || !aligned16(dkv)) return ATTN_ERR_ALIGN;
+  return hip_status(launch_smla_bwd_post(dkv_accum, dkv, shape.kv_tokens, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -32,6 +32,9 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Row of element j of a 32x32 result held by a lane of half hi (= l / 32).
+__device__ __forceinline__ int c_row(int j, int hi) { return 8 * (j >> 2) + 4 * hi + (j & 3); }
+
 // LDS transposing read of four 16-bit values.  Within each group of 16 lanes,
 // element e of lane i comes from the 8-byte chunk addressed by lane 4*e + i/4,
 // at position i % 4.  Four lanes pointing at consecutive 4-element chunks of

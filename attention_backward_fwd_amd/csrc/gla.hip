@@ -67,8 +67,6 @@ __device__ __forceinline__ bf16x8 op_tr(const uint16_t* t, const Lofs<DT>& o, in
 // The k index (0..15 within a 16-step) of element i of a lane's operand.
 __device__ __forceinline__ int op_k(int i, int hi) { return (i < 4 ? 4 * hi + i : 8 + 4 * hi + (i - 4)); }
 
-// Row of element j of a 32x32 result held by a lane of half hi.
-__device__ __forceinline__ int c_row(int j, int hi) { return 8 * (j >> 2) + 4 * hi + (j & 3); }
 
 // Inclusive running sum over the 64 lanes of one wave, into sG[0..63].
 __device__ __forceinline__ void chunk_scan(float x, float* sG, int lane) {

@@ -102,6 +102,14 @@ size_t gla_bwd_workspace_bytes(int B, int T, int H);
 // range: unused), o [T][H][512] bf16, lse [T][H] fp32.
 hipError_t launch_smla_fwd(const uint16_t* q, const uint16_t* kv, const int* idx, uint16_t* o, float* lse, int T,
                            int Tk, int H, int K, float scale, hipStream_t stream);
+// Backward: Delta [T][H] (and zeroing of the fp32 dKV accumulator [Tk][576]
+// when given); dq [T][H][576] bf16 and atomic fp32 dKV; dkv = bf16(accumulator).
+hipError_t launch_smla_bwd_pre(const uint16_t* o, const uint16_t* dout, float* delta, float* dkv_acc, int T, int Tk,
+                               int H, hipStream_t stream);
+hipError_t launch_smla_bwd(const uint16_t* q, const uint16_t* kv, const uint16_t* dout, const int* idx,
+                           const float* lse, const float* delta, uint16_t* dq, float* dkv_acc, int T, int Tk, int H,
+                           int K, float scale, hipStream_t stream);
+hipError_t launch_smla_bwd_post(const float* dkv_acc, uint16_t* dkv, int Tk, hipStream_t stream);
 
 hipError_t launch_merge(const uint16_t* o_parts, const float* lse_parts, int n_parts, uint16_t* o, float* lse,
                         int B, int S, int Hq, int D, hipStream_t stream);

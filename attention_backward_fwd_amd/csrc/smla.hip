@@ -50,6 +50,19 @@ __device__ __forceinline__ bf16x8 sop_tr(const uint16_t* t, int st, int k0, int 
   return lds_read_tr8(s + swz_off<128>(k0 + 4 * hi + (L >> 2), col), s + swz_off<128>(k0 + 8 + 4 * hi + (L >> 2), col));
 }
 
+// Transposing read from the 64-channel sub-tile (channels 512 .. 575).
+__device__ __forceinline__ bf16x8 sop_tr64(const uint16_t* t, int k0, int x0, int lane) {
+  const int hi = lane >> 5, L = lane & 15, gp = (lane >> 4) & 1;
+  const int col = x0 + 16 * gp + 4 * (L & 3);
+  const uint16_t* s = t + 4 * kSub;
+  return lds_read_tr8(s + swz_off<64>(k0 + 4 * hi + (L >> 2), col), s + swz_off<64>(k0 + 8 + 4 * hi + (L >> 2), col));
+}
+// Transposing operand for channel block `dt` (32 channels: 0..15 in the
+// 128-channel sub-tiles, 16 and 17 in the 64-channel one).
+__device__ __forceinline__ bf16x8 sop_tr_ch(const uint16_t* t, int dt, int k0, int lane) {
+  return dt < 16 ? sop_tr(t, dt >> 2, k0, 32 * (dt & 3), lane) : sop_tr64(t, k0, 32 * (dt - 16), lane);
+}
+
 // Gather rows rows[r] (r < 32, device row indices, already made valid) of a
 // [*][576] bf16 matrix into a tile in the sub-tile layout, by LDS-DMA.  Per
 // wave: 2 instructions per 128-channel sub-tile, 1 for the 64-channel one.
@@ -196,7 +209,271 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void s
   }
 }
 
+// ------------------------------------------------------------ backward
+// Preprocess: Delta[t,h] = sum_{d<512} O[t,h,d] dO[t,h,d] (one wave per row,
+// 8 channels per lane); optionally zero the fp32 dKV accumulator.
+__global__ __launch_bounds__(256) void smla_pre_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
+                                                       float* __restrict__ delta, float* __restrict__ dkv_acc,
+                                                       long long rows, long long acc4) {
+  const int lane = threadIdx.x & 63;
+  for (long long r = ((long long)blockIdx.x * 256 + threadIdx.x) / 64; r < rows; r += (long long)gridDim.x * 4) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(o + (size_t)r * kVD + 8 * lane);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(dout + (size_t)r * kVD + 8 * lane);
+    float x = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      x = fmaf(__uint_as_float(a[i] << 16), __uint_as_float(b[i] << 16), x);
+      x = fmaf(__uint_as_float(a[i] & 0xffff0000u), __uint_as_float(b[i] & 0xffff0000u), x);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+    if (lane == 0) delta[r] = x;
+  }
+  if (dkv_acc)
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < acc4; i += (long long)gridDim.x * 256)
+      reinterpret_cast<f32x4*>(dkv_acc)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// Postprocess: dkv = bf16(dkv_acc), 8 values per thread.
+__global__ __launch_bounds__(256) void smla_post_kernel(const float* __restrict__ acc, uint16_t* __restrict__ dkv,
+                                                        long long n8) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n8; i += (long long)gridDim.x * 256) {
+    const f32x4 a = reinterpret_cast<const f32x4*>(acc)[2 * i], b = reinterpret_cast<const f32x4*>(acc)[2 * i + 1];
+    reinterpret_cast<u32x4*>(dkv)[i] = u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+                                              pack_bf16x2(b[2], b[3])};
+  }
+}
+
+// Backward kernel: one workgroup (4 waves) per (token, 32-head tile).  Per
+// tile of 32 entries (gathered as in the forward): S^T (partials over the
+// 576 channels, summed through LDS), P = exp(S - LSE); dP^T = V dO^T
+// (partials over wave w's 128 value channels; dO operands in registers);
+// dS = P (dP - Delta); padded heads and unused entries get P = dS = 0.  Then
+//   dQ^T += KV^T dS^T   (in registers across all tiles; wave w owns channel
+//                        blocks w, w+4, .. of the 18 blocks of 32)
+//   dKV   = scale dS^T Q + P^T dO   for the tile's 32 entries (dS^T, P^T
+//                        through LDS as [entry][head]), added to the fp32
+//                        accumulator row of each valid entry with atomics.
+// dQ (bf16) is written at the end.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void smla_bwd_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const uint16_t* __restrict__ dout,
+    const int* __restrict__ idx, const float* __restrict__ lse, const float* __restrict__ delta,
+    uint16_t* __restrict__ dq, float* __restrict__ dkv_acc, int T, int Tk, int H, int K, float scale) {
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[4 * kSub + kKT * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t sKV0[4 * kSub + kKT * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t sKV1[4 * kSub + kKT * 64];
+  __shared__ float sSp[4][16 * 64];                   // partial sums (S^T, then dP^T)
+  __shared__ __attribute__((aligned(16))) uint16_t sDS[kKT * kHT];  // scale dS as [entry][head]
+  __shared__ __attribute__((aligned(16))) uint16_t sPT[kKT * kHT];  // P as [entry][head]
+  __shared__ int sRow[3][kKT];
+  __shared__ int sOk[3][kKT];
+
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), hi = lane >> 5;
+  const int l32 = lane & 31;
+  const int n_ht = (H + kHT - 1) / kHT;
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int t = __builtin_amdgcn_readfirstlane(id / n_ht), h0 = __builtin_amdgcn_readfirstlane((id % n_ht) * kHT);
+  const int n_tiles = (K + kKT - 1) / kKT;
+  const int* idx_t = idx + (size_t)t * K;
+  const int head = h0 + l32;                   // this lane's head (S^T columns)
+  const bool head_ok = head < H;
+  const int hc = min(head, H - 1);
+  const float lse_l2 = lse[(size_t)t * H + hc] * kLog2e;  // -inf for a token without entries: P = 0 below
+  const float dl = delta[(size_t)t * H + hc];
+  const float c = scale * kLog2e;
+
+  {
+    const uint16_t* qb = q + ((size_t)t * H) * kQK;
+#pragma unroll
+    for (int st = 0; st < 4; st++) tile_load_async<128, kHT, 4>(qb + 128 * st, kQK, h0, H, sQ + st * kSub, w, lane);
+    tile_load_async<64, kHT, 4>(qb + 512, kQK, h0, H, sQ + 4 * kSub, w, lane);
+  }
+  // dO operands, fixed for the whole workgroup:
+  //   dP^T B operand (k = value channel 128w + 16kk .., n = head): dO[head][..]
+  //   dKV  B operand (k = head 16kk' .., n = channel 32 blk + l32): dO[head'][ch]
+  const uint16_t* dob = dout + ((size_t)t * H) * kVD;
+  bf16x8 bdo[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; kk++) {
+    const uint16_t* r = dob + (size_t)hc * kVD + 128 * w + 16 * kk;
+    const u32x2 a = *reinterpret_cast<const u32x2*>(r + 4 * hi);
+    const u32x2 b = *reinterpret_cast<const u32x2*>(r + 8 + 4 * hi);
+    bdo[kk] = __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
+  }
+  bf16x8 vdo[4][2];  // channel blocks w, w+4, w+8, w+12 (< 16): dO[head 16kk + op_k(i)][32 blk + l32]
+#pragma unroll
+  for (int bi = 0; bi < 4; bi++)
+#pragma unroll
+    for (int kk = 0; kk < 2; kk++) {
+      const int ch = 32 * (w + 4 * bi) + l32;
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const int hh = min(h0 + 16 * kk + (i < 4 ? 4 * hi + i : 8 + 4 * hi + (i - 4)), H - 1);
+        x[i] = from_bf16(dob[(size_t)hh * kVD + ch]);
+      }
+      vdo[bi][kk] = pack8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
+    }
+
+  auto entries = [&](int it) {
+    if (w == 0 && lane < kKT) {
+      const int e = it * kKT + lane;
+      const int j = e < K ? idx_t[e] : -1;
+      const bool ok = j >= 0 && j < Tk;
+      sRow[it % 3][lane] = ok ? j : 0;
+      sOk[it % 3][lane] = ok;
+    }
+  };
+  entries(0);
+  lds_barrier();
+  gather_rows_async(kv, sRow[0], sKV0, w, lane);
+  if (n_tiles > 1) entries(1);
+
+  const int nblk = w < 2 ? 5 : 4;  // channel blocks of this wave: w, w+4, w+8, w+12, (w+16)
+  f32x16 dqa[5];
+#pragma unroll
+  for (int bi = 0; bi < 5; bi++) dqa[bi] = f32x16{};
+
+  auto tile = [&](auto buf_tag, int it) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    const uint16_t* cKV = BUF ? sKV1 : sKV0;
+    uint16_t* nKV = BUF ? sKV0 : sKV1;
+    const int slot = it % 3;
+    wait_vmem();
+    lds_barrier();  // tile it resident; every wave is done with tile it-1
+    if (it + 1 < n_tiles) gather_rows_async(kv, sRow[(it + 1) % 3], nKV, w, lane);
+    if (it + 2 < n_tiles) entries(it + 2);
+    // S^T partial over channels 144w .. 144w+143.
+    f32x16 sp = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < 9; kk++) {
+      const int d0 = 144 * w + 16 * kk;
+      sp = mfma32(sop_row(cKV, l32, d0, hi), sop_row(sQ, l32, d0, hi), sp);
+    }
+    // dP^T partial over value channels 128w .. 128w+127.
+    f32x16 dpp = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < 8; kk++) dpp = mfma32(sop_row(cKV, l32, 128 * w + 16 * kk, hi), bdo[kk], dpp);
+#pragma unroll
+    for (int j = 0; j < 16; j++) sSp[w][j * 64 + lane] = sp[j];
+    lds_barrier();
+    f32x16 p;
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      const float sv = (sSp[0][j * 64 + lane] + sSp[1][j * 64 + lane]) + (sSp[2][j * 64 + lane] + sSp[3][j * 64 + lane]);
+      const bool ok = head_ok && sOk[slot][c_row(j, hi)];
+      p[j] = ok ? __builtin_amdgcn_exp2f(fmaf(sv, c, -lse_l2)) : 0.f;
+    }
+    lds_barrier();  // S sums read by every wave: the buffer takes the dP partials
+#pragma unroll
+    for (int j = 0; j < 16; j++) sSp[w][j * 64 + lane] = dpp[j];
+    lds_barrier();
+    f32x16 ds;
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      const float dpv = (sSp[0][j * 64 + lane] + sSp[1][j * 64 + lane]) + (sSp[2][j * 64 + lane] + sSp[3][j * 64 + lane]);
+      ds[j] = p[j] * (dpv - dl);
+    }
+    // dS^T and P^T to LDS as [entry][head] (wave 0 writes; all read below).
+    if (w == 0) {
+#pragma unroll
+      for (int j = 0; j < 16; j++) {
+        const int e = c_row(j, hi);
+        sDS[e * kHT + l32] = to_bf16(scale * ds[j]);
+        sPT[e * kHT + l32] = to_bf16(p[j]);
+      }
+    }
+    // dQ^T += KV^T dS^T (dS^T from registers, entries in operand k order).
+    bf16x8 bds[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; kk++)
+      bds[kk] = pack8(ds[8 * kk + 0], ds[8 * kk + 1], ds[8 * kk + 2], ds[8 * kk + 3], ds[8 * kk + 4], ds[8 * kk + 5],
+                      ds[8 * kk + 6], ds[8 * kk + 7]);
+#pragma unroll
+    for (int bi = 0; bi < 5; bi++)
+      if (bi < nblk)
+#pragma unroll
+        for (int kk = 0; kk < 2; kk++) dqa[bi] = mfma32(sop_tr_ch(cKV, w + 4 * bi, 16 * kk, lane), bds[kk], dqa[bi]);
+    lds_barrier();  // sDS / sPT complete
+    // dKV rows of the tile's entries: C[entry][channel], channel blocks of this wave.
+    bf16x8 ads[2], apt[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; kk++) {
+      const uint16_t* rd = sDS + l32 * kHT + 16 * kk;
+      const uint16_t* rp = sPT + l32 * kHT + 16 * kk;
+      const u32x2 a0 = *reinterpret_cast<const u32x2*>(rd + 4 * hi), a1 = *reinterpret_cast<const u32x2*>(rd + 8 + 4 * hi);
+      const u32x2 b0 = *reinterpret_cast<const u32x2*>(rp + 4 * hi), b1 = *reinterpret_cast<const u32x2*>(rp + 8 + 4 * hi);
+      ads[kk] = __builtin_bit_cast(bf16x8, u32x4{a0[0], a0[1], a1[0], a1[1]});
+      apt[kk] = __builtin_bit_cast(bf16x8, u32x4{b0[0], b0[1], b1[0], b1[1]});
+    }
+#pragma unroll
+    for (int bi = 0; bi < 5; bi++) {
+      if (bi >= nblk) continue;
+      const int blk = w + 4 * bi;
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < 2; kk++) {
+        acc = mfma32(ads[kk], sop_tr_ch(sQ, blk, 16 * kk, lane), acc);
+        if (blk < 16) acc = mfma32(apt[kk], vdo[bi][kk], acc);
+      }
+#pragma unroll
+      for (int j = 0; j < 16; j++) {
+        const int e = c_row(j, hi);
+        if (sOk[slot][e]) unsafeAtomicAdd(dkv_acc + (size_t)sRow[slot][e] * kQK + 32 * blk + l32, acc[j]);
+      }
+    }
+  };
+  for (int it = 0; it < n_tiles; it += 2) {
+    tile(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < n_tiles) tile(std::integral_constant<int, 1>{}, it + 1);
+  }
+
+  // dq[t, head, channel]: dQ^T element j of block blk is channel
+  // 32 blk + c_row(j), head l32; four consecutive channels per store.
+  if (head_ok) {
+    uint16_t* dqr = dq + ((size_t)t * H + head) * kQK;
+#pragma unroll
+    for (int bi = 0; bi < 5; bi++) {
+      if (bi >= nblk) continue;
+      const int blk = w + 4 * bi;
+#pragma unroll
+      for (int jg = 0; jg < 4; jg++)
+        *reinterpret_cast<u32x2*>(dqr + 32 * blk + c_row(4 * jg, hi)) =
+            u32x2{pack_bf16x2(scale * dqa[bi][4 * jg], scale * dqa[bi][4 * jg + 1]),
+                  pack_bf16x2(scale * dqa[bi][4 * jg + 2], scale * dqa[bi][4 * jg + 3])};
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_smla_bwd_pre(const uint16_t* o, const uint16_t* dout, float* delta, float* dkv_acc, int T, int Tk,
+                               int H, hipStream_t stream) {
+  const long long rows = (long long)T * H, acc4 = dkv_acc ? (long long)Tk * kQK / 4 : 0;
+  long long g = (rows + 3) / 4;
+  if (acc4 / 256 > g) g = acc4 / 256;
+  if (g > 256LL * 64) g = 256LL * 64;
+  if (g < 1) g = 1;
+  hipLaunchKernelGGL(smla_pre_kernel, dim3((unsigned)g), dim3(256), 0, stream, o, dout, delta, dkv_acc, rows, acc4);
+  return hipGetLastError();
+}
+
+hipError_t launch_smla_bwd(const uint16_t* q, const uint16_t* kv, const uint16_t* dout, const int* idx,
+                           const float* lse, const float* delta, uint16_t* dq, float* dkv_acc, int T, int Tk, int H,
+                           int K, float scale, hipStream_t stream) {
+  const int n_ht = (H + kHT - 1) / kHT;
+  hipLaunchKernelGGL(smla_bwd_kernel, dim3((unsigned)((long long)T * n_ht)), dim3(256), 0, stream, q, kv, dout, idx,
+                     lse, delta, dq, dkv_acc, T, Tk, H, K, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_smla_bwd_post(const float* dkv_acc, uint16_t* dkv, int Tk, hipStream_t stream) {
+  const long long n8 = (long long)Tk * kQK / 8;
+  long long g = (n8 + 255) / 256;
+  if (g > 256LL * 64) g = 256LL * 64;
+  hipLaunchKernelGGL(smla_post_kernel, dim3((unsigned)g), dim3(256), 0, stream, dkv_acc, dkv, n8);
+  return hipGetLastError();
+}
 
 hipError_t launch_smla_fwd(const uint16_t* q, const uint16_t* kv, const int* idx, uint16_t* o, float* lse, int T,
                            int Tk, int H, int K, float scale, hipStream_t stream) {

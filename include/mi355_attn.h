@@ -309,6 +309,31 @@ typedef struct smla_shape {
 int attn_sparse_mla_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* indices, uint16_t* o, float* lse,
                         smla_shape shape, float softmax_scale, void* stream);
 
+/*
+ * Sparse MLA backward, the same preprocess / backward / postprocess split as
+ * the dense path (the gradients of sum o . dout):
+ *   preprocess: delta[t,h] = sum_{d<512} o[t,h,d] dout[t,h,d] (fp32
+ *     [tokens, heads]); dkv_accum (fp32 [kv_tokens, 576], may be NULL) is
+ *     set to zero.
+ *   backward: with P and dS = P (dP - delta) recomputed from q, kv, lse,
+ *     dP_i = dout[t,h] . kv[j_i, 0:512]:
+ *       dq[t,h]      = scale * sum_i dS_i kv[j_i]         (bf16, written)
+ *       dkv_accum[j_i] += scale * sum_h dS_i q[t,h], and its first 512
+ *                         channels += sum_h P_i dout[t,h]  (fp32 atomic adds
+ *                         of each token's 32-head tile; must hold zeros or a
+ *                         running sum on entry; the order of the additions,
+ *                         and so the last bits, may differ run to run)
+ *   postprocess: dkv = bf16(dkv_accum) (RNE), [kv_tokens, 576].
+ * lse is the forward's.  Arguments otherwise as attn_sparse_mla_fwd
+ * (dout [tokens, heads, 512] bf16; dq 16-byte aligned; delta 4-byte).
+ */
+int attn_sparse_mla_bwd_preprocess(const uint16_t* o, const uint16_t* dout, float* delta, float* dkv_accum,
+                                   smla_shape shape, void* stream);
+int attn_sparse_mla_bwd(const uint16_t* q, const uint16_t* kv, const uint16_t* dout, const int32_t* indices,
+                        const float* lse, const float* delta, uint16_t* dq, float* dkv_accum, smla_shape shape,
+                        float softmax_scale, void* stream);
+int attn_sparse_mla_bwd_postprocess(const float* dkv_accum, uint16_t* dkv, smla_shape shape, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

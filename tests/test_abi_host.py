@@ -31,7 +31,8 @@ def test_library_exports_every_header_symbol():
                             "attn_bwd_postprocess", "attn_merge", "attn_strerror", "attn_fwd_varlen",
                             "attn_bwd_varlen_workspace_bytes", "attn_bwd_varlen",
                             "attn_bwd_varlen_postprocess", "gla_chunk_bwd_workspace_bytes", "gla_chunk_bwd",
-                            "attn_sparse_mla_fwd"])
+                            "attn_sparse_mla_fwd", "attn_sparse_mla_bwd_preprocess", "attn_sparse_mla_bwd",
+                            "attn_sparse_mla_bwd_postprocess"])
     for n in names:
         assert hasattr(lib(), n), n
 
@@ -327,3 +328,29 @@ def mfwd(**kw):
 ])
 def test_sparse_mla_fwd_errors(kw, code):
     assert mfwd(**kw) == E[code]
+
+
+def mbwd(**kw):
+    args = dict(q=A, kv=A, do=A, idx=A, lse=A, delta=A, dq=A, acc=A, shape=mshp(), scale=0.05, stream=None)
+    args.update(kw)
+    return lib().attn_sparse_mla_bwd(args["q"], args["kv"], args["do"], args["idx"], args["lse"], args["delta"],
+                                     args["dq"], args["acc"], args["shape"], args["scale"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"acc": None}, "null"), ({"delta": None}, "null"), ({"shape": mshp(k=0)}, "shape"),
+    ({"shape": mshp(dqk=128)}, "hd"), ({"scale": float("inf")}, "range"), ({"dq": MIS}, "align"),
+    ({"acc": MIS}, "align"), ({"delta": P(0x10001)}, "align"),
+])
+def test_sparse_mla_bwd_errors(kw, code):
+    assert mbwd(**kw) == E[code]
+
+
+def test_sparse_mla_pre_post_errors():
+    f = lib().attn_sparse_mla_bwd_preprocess
+    assert f(None, A, A, None, mshp(), None) == E["null"]
+    assert f(A, A, A, MIS, mshp(), None) == E["align"]
+    assert f(A, A, A, None, mshp(h=0), None) == E["shape"]
+    g = lib().attn_sparse_mla_bwd_postprocess
+    assert g(None, A, mshp(), None) == E["null"]
+    assert g(A, MIS, mshp(), None) == E["align"]

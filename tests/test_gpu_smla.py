@@ -71,3 +71,57 @@ def test_smla_fwd_full_size_sampled():
     qf = inp["q"][rows].double().numpy()
     ro, rl = sm.sparse_mla_fwd(qf, inp["kv"].double().numpy(), idx[rows].numpy(), SCALE)
     _check(o[rows], lse[rows], ro, rl, f"[smla full] {w['name']} tokens {rows}")
+
+
+def _run_bwd(inp, idx):
+    q, kv, do = inp["q"].cuda(), inp["kv"].cuda(), inp["do"].cuda()
+    ix = idx.cuda() if isinstance(idx, torch.Tensor) else torch.from_numpy(idx).cuda()
+    o, lse = bd.sparse_mla_forward(q, kv, ix, SCALE)
+    bb = bd.SmlaBwdBuffers(q, kv)
+    for x in (bb.delta, bb.dq, bb.dkv_accum, bb.dkv):
+        x.fill_(float("nan"))
+    dq, dkv = bd.sparse_mla_backward(q, kv, ix, o, lse, do, SCALE, buffers=bb)
+    torch.cuda.synchronize()
+    return {"dq": dq, "dkv": dkv, "delta": bb.delta, "o": o}
+
+
+@pytest.mark.parametrize("t,tk,h,k", CASES)
+def test_smla_bwd_against_oracle(t, tk, h, k):
+    inp = smla_inputs(t, tk, h, seed=t + k)
+    idx = _indices(t, tk, k, seed=h)
+    f = {n: x.double().numpy() for n, x in inp.items()}
+    ref = sm.sparse_mla_bwd(f["q"], f["kv"], idx, f["do"], SCALE)
+    gpu = _run_bwd(inp, idx)
+    case = f"smla bwd T{t} Tk{tk} H{h} K{k}"
+    ratios = {n: err_ratio(np64(gpu[n]), ref[n]) for n in ("dq", "dkv", "delta")}
+    say(f"{case}: " + " ".join(f"{n}={r:.2e}" for n, r in ratios.items()))
+    for n, r in ratios.items():
+        assert r <= TOL, (case, n, r)
+    # keys nobody selected get exact zeros; tokens without entries get dq = 0
+    unused = np.all(ref["dkv"] == 0.0, axis=1)
+    assert np.all(np64(gpu["dkv"])[unused] == 0.0), case
+    assert np.all(np64(gpu["dq"])[1] == 0.0), case
+
+
+def test_smla_bwd_full_size():
+    """The benchmark workload: dq of sampled tokens against the oracle, and
+    over all keys the sums sum_j dkv[j, :512] = sum_{t,h} dO[t,h] and
+    sum_j dkv[j, 512:] = 0 (softmax rows sum to one; dS rows sum to zero)."""
+    w = SMLA_WORKLOAD
+    t, h, k = w["tokens"], w["heads"], w["topk"]
+    inp = smla_inputs(t, t, h, seed=0)
+    idx = smla_indices(t, t, k, seed=0)
+    say(f"[smla full bwd] {w['name']}: gpu")
+    gpu = _run_bwd(inp, idx)
+    rows = [0, 5, 2047, 2048, 3001, t - 1]
+    sub = sm.sparse_mla_bwd(inp["q"][rows].double().numpy(), inp["kv"].double().numpy(), idx[rows].numpy(),
+                            inp["do"][rows].double().numpy(), SCALE)
+    r = err_ratio(np64(gpu["dq"][rows]), sub["dq"])
+    dkv = gpu["dkv"].double()
+    want_v = inp["do"].cuda().double().sum(dim=(0, 1))
+    err_v = (dkv[:, :512].sum(dim=0) - want_v).abs().max().item() / dkv[:, :512].abs().sum(dim=0).max().item()
+    err_k = dkv[:, 512:].sum(dim=0).abs().max().item() / dkv[:, 512:].abs().sum(dim=0).max().item()
+    say(f"[smla full bwd] dq(sampled)={r:.2e} sum dkv[:, :512] err={err_v:.2e} sum dkv[:, 512:] err={err_k:.2e}")
+    assert r <= TOL
+    assert err_v <= 2e-2 and err_k <= 2e-2
+    assert torch.all(torch.isfinite(gpu["dkv"].float())) and torch.all(torch.isfinite(gpu["dq"].float()))
