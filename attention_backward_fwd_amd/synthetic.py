@@ -130,7 +130,9 @@ def gla_inputs(batch, seqlen, heads, head_dim, seed=0):
 # (bf16 RNE, drawn in that order); each token's index list holds
 # min(K, t + 1) distinct keys drawn uniformly from 0 .. t (keys are the same
 # tokens, causal), in random order, then -1 in the unused slots.
-SMLA_WORKLOAD = {"name": "smla_t4096_h128_k2048", "tokens": 4096, "heads": 128, "topk": 2048}
+# Workload: 4096 tokens, 32 heads (a 128-head model split four ways), 2048
+# entries per token.
+SMLA_WORKLOAD = {"name": "smla_t4096_h32_k2048", "tokens": 4096, "heads": 32, "topk": 2048}
 
 
 def smla_indices(tokens, kv_tokens, topk, seed=0):

@@ -304,6 +304,92 @@ def bench_gla(args, bd, torch):
     }), flush=True)
 
 
+def bench_smla(args, bd, torch):
+    """Sparse MLA forward + backward (preprocess, backward, postprocess) on
+    the sparse MLA workload.  FLOPs: per (token, head, valid entry)
+    2*(576 + 512) forward and 2*(576 + 512 + 576 + 576 + 512) backward (S, dP,
+    dQ, dK, dV).  The backward kernel's dKV goes out as fp32 atomic adds,
+    576 per (token, valid entry) and 32-head tile; ``atomics`` reports their
+    rate."""
+    from attention_backward_fwd_amd.synthetic import SMLA_WORKLOAD, smla_indices, smla_inputs
+
+    w = SMLA_WORKLOAD
+    t, h, k = w["tokens"], w["heads"], w["topk"]
+    dev = torch.device("cuda:0")
+    inp = {n: x.to(dev) for n, x in smla_inputs(t, t, h, seed=0).items()}
+    idx_cpu = smla_indices(t, t, k, seed=0)
+    idx = idx_cpu.to(dev)
+    scale = 1.0 / math.sqrt(576)
+    q, kv, do = inp["q"], inp["kv"], inp["do"]
+    shape = bd.smla_shape_of(q, kv, idx)
+    o = torch.empty((t, h, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((t, h), dtype=torch.float32, device=dev)
+    bb = bd.SmlaBwdBuffers(q, kv)
+    stream = torch.cuda.current_stream()
+    ev = {n: [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)] for n in ("fwd", "bwd")}
+
+    def step(i=None):
+        if i is not None:
+            ev["fwd"][2 * i].record(stream)
+        bd.attn_sparse_mla_fwd(q, kv, idx, o, lse, shape, scale, stream)
+        if i is not None:
+            ev["fwd"][2 * i + 1].record(stream)
+        bd.attn_sparse_mla_bwd_preprocess(o, do, bb.delta, bb.dkv_accum, shape, stream)
+        if i is not None:
+            ev["bwd"][2 * i].record(stream)
+        bd.attn_sparse_mla_bwd(q, kv, do, idx, lse, bb.delta, bb.dq, bb.dkv_accum, shape, scale, stream)
+        if i is not None:
+            ev["bwd"][2 * i + 1].record(stream)
+        bd.attn_sparse_mla_bwd_postprocess(bb.dkv_accum, bb.dkv, shape, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    n_valid = int((idx_cpu >= 0).sum())
+    fwd_f = 2.0 * n_valid * h * (576 + 512)
+    bwd_f = 2.0 * n_valid * h * (576 + 512 + 576 + 576 + 512)
+    fwd_ms = sum(ev["fwd"][2 * i].elapsed_time(ev["fwd"][2 * i + 1]) for i in range(args.steps)) / args.steps
+    bwd_ms = sum(ev["bwd"][2 * i].elapsed_time(ev["bwd"][2 * i + 1]) for i in range(args.steps)) / args.steps
+    value = (fwd_f + bwd_f) * args.steps / elapsed / 1e12
+    n_atomics = n_valid * 576 * ((h + 31) // 32)
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import sparse_mla as sm
+        qf, kvf, dof = q.cpu().double().numpy(), kv.cpu().double().numpy(), do.cpu().double().numpy()
+        done, flop_done, t_cpu = 0, 0.0, 0.0
+        for tok in range(t - 1, -1, -4):  # every 4th token, full lists first
+            if t_cpu >= args.cpu_budget:
+                break
+            t1 = time.perf_counter()
+            sm.sparse_mla_bwd(qf[tok:tok + 1], kvf, idx_cpu[tok:tok + 1].numpy(), dof[tok:tok + 1], scale)
+            t_cpu += time.perf_counter() - t1
+            nv = int((idx_cpu[tok] >= 0).sum())
+            flop_done += 2.0 * nv * h * (576 + 512) * 2 + 2.0 * nv * h * (576 + 512 + 576 + 576 + 512)
+            done += 1
+        cpu = {"value": round(flop_done / t_cpu / 1e12, 6), "unit": "TFLOP/s", "cores": int(_blas_threads()),
+               "kind": "oracle", "sample": f"{done} of {t} tokens (every 4th from the last), fwd+bwd in fp64, "
+                                           f"{t_cpu:.1f} s; the same per-entry FLOP count"}
+    print(json.dumps({
+        "metric": "sparse MLA fwd+bwd TFLOP/s (bf16)", "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w["name"], "tokens": t, "kv_tokens": t, "heads": h, "topk": k,
+                   "valid_entries": n_valid, "dim_qk": 576, "dim_v": 512},
+        "fwd_kernel_ms": round(fwd_ms, 4), "fwd_tflops": round(fwd_f / (fwd_ms * 1e-3) / 1e12, 3),
+        "bwd_kernel_ms": round(bwd_ms, 4), "bwd_tflops": round(bwd_f / (bwd_ms * 1e-3) / 1e12, 3),
+        "atomics": {"count": n_atomics, "per_s": round(n_atomics / (bwd_ms * 1e-3) / 1e9, 1), "unit": "G/s"},
+        "roofline": {"kernel": "smla_bwd_kernel", "bound": "mfma", "achieved": round(bwd_f / (bwd_ms * 1e-3) / 1e12, 3),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(bwd_f / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        **({"cpu_baseline": cpu} if cpu else {}),
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -326,6 +412,9 @@ def main():
     ap.add_argument("--gla", action="store_true",
                     help="instead of the attention step, time the simple gated linear attention chunk backward "
                          "(B=4, T=4096, H=32, D=128)")
+    ap.add_argument("--smla", action="store_true",
+                    help="instead of the attention step, time sparse MLA forward + backward "
+                         "(4096 tokens, 32 heads, 2048 entries per token)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -354,6 +443,9 @@ def main():
         return
     if args.gla:
         bench_gla(args, bd, torch)
+        return
+    if args.smla:
+        bench_smla(args, bd, torch)
         return
     w = WORKLOADS[args.workload]
     if args.merge_parts:
