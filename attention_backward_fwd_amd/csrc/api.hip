@@ -80,7 +80,7 @@ bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 int check_smla(const smla_shape& s) {
   if (s.tokens < 1 || s.kv_tokens < 1 || s.heads < 1 || s.topk < 1) return ATTN_ERR_BAD_SHAPE;
   if (s.dim_qk != 576 || s.dim_v != 512) return ATTN_ERR_HEAD_DIM;
-  if ((long long)s.tokens * s.heads * 576 >= (1LL << 31) || (long long)s.kv_tokens * 576 >= (1LL << 31) ||
+  if ((long long)s.tokens * s.heads * 576 >= (1LL << 31) || s.kv_tokens > kSmlaMaxKvTokens ||
       (long long)s.tokens * s.topk >= (1LL << 31) || s.topk > 8192)
     return ATTN_ERR_RANGE;
   return ATTN_OK;

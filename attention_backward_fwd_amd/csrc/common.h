@@ -192,6 +192,33 @@ __device__ __forceinline__ void lds_store_b64_addr(uint32_t addr, u32x2 v) {
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)lds_ptr(const_cast<void*>(p));
 }
+// LDS-DMA loads issued as inline assembly (16 or 4 bytes per lane, from a
+// per-lane global address to `lds` + 16 (or 4) * lane; `lds` wave-uniform,
+// placed in M0 by the compiler).  The compiler does not know that they write
+// LDS, so it adds no waits of its own for them: the caller waits
+// (wait_vmem / wait_vmem_but) and synchronises (lds_barrier) before any LDS
+// read of the data.  The s_nop separates the M0 write from the load.
+__device__ __forceinline__ void dma_b128_asm(const void* g, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void dma_b32_asm(const void* g, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+}
+// 16-byte LDS store and load the compiler does not track either (see
+// lds_store_b64_asm).  A load's result is only ready after lds_wait4().
+__device__ __forceinline__ void lds_store_b128_addr(uint32_t addr, f32x4 v) {
+  asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(v));
+}
+__device__ __forceinline__ f32x4 lds_load_b128_addr(uint32_t addr) {
+  f32x4 v;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+  return v;
+}
+// Wait for this wave's LDS accesses; the four registers pass through the
+// wait, so that nothing reads them before it.
+__device__ __forceinline__ void lds_wait4(f32x4& a, f32x4& b, f32x4& c, f32x4& d) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
 
 // Asynchronous global -> LDS copy of n <= 64 consecutive fp32 values (one per
 // lane, lanes >= n read the last one again) to lds[0 .. 63].

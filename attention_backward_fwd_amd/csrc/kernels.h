@@ -97,6 +97,10 @@ hipError_t launch_gla_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* 
                           int B, int T, int H, float scale, hipStream_t stream);
 size_t gla_bwd_workspace_bytes(int B, int T, int H);
 
+// Largest kv_tokens of the sparse MLA calls (keeps every byte offset of the
+// fp32 dKV accumulator below 2^31).
+constexpr int kSmlaMaxKvTokens = 1 << 19;
+
 // Sparse MLA (576-wide latent rows, 512 value channels) over per-token
 // index lists: q [T][H][576], kv [Tk][576], idx [T][K] int32 (-1 or out of
 // range: unused), o [T][H][512] bf16, lse [T][H] fp32.

@@ -8,13 +8,15 @@
 //   LSE = log sum_i exp(s_i)  (O = 0, LSE = -inf without a valid entry)
 //
 // Forward kernel: one workgroup (4 waves) per (token, 32-head tile).  Per
-// tile of 32 entries the key rows are gathered by LDS-DMA (one buffer ahead)
-// into five swizzled sub-tiles (four of 128 channels, one of 64); the waves
-// split the 576-channel reduction of S^T = KV Q^T (9 k-steps each) and sum
-// the four partials through LDS in a fixed order, so that every wave holds
-// the same scores and runs the same online softmax (a head per lane); wave w
-// then accumulates O^T rows 128w .. 128w+127 = V^T P^T from its own value
-// sub-tile (transposing reads) and the probabilities in registers.
+// tile of 32 entries the key rows are gathered by LDS-DMA (two tiles ahead,
+// three buffers) into five swizzled sub-tiles (four of 128 channels, one of
+// 64); the waves split the 576-channel reduction of S^T = KV Q^T (9 k-steps
+// each, query operands in registers) and sum the four partials through LDS
+// in a fixed order, so that every wave holds the same scores and runs the
+// same online softmax (a head per lane); wave w then accumulates O^T rows
+// 128w .. 128w+127 = V^T P^T from its own value sub-tile (transposing reads)
+// and the probabilities in registers.  Tiles past the last valid entry of
+// the list are skipped.
 #include "common.h"
 #include "kernels.h"
 
@@ -26,6 +28,13 @@ constexpr int kQK = 576, kVD = 512;
 constexpr int kHT = 32;  // heads per workgroup
 constexpr int kKT = 32;  // entries per tile
 constexpr int kSub = kKT * 128;  // elements of a 128-channel sub-tile of 32 rows
+// Backward: the dKV atomics of a tile that may still be in flight when the
+// next tile starts (each wave issues 64 or 80 per tile; the counter holds 63).
+constexpr int kAtomSlack = 48;
+// Byte offset past the end of any dKV accumulator (at most kSmlaMaxKvTokens
+// rows of 576 fp32): atomics sent there are dropped.
+constexpr uint32_t kDropOffset = 0x7FFFFFF0u;
+static_assert((uint64_t)kSmlaMaxKvTokens * kQK * 4 < kDropOffset, "drop offset inside the accumulator");
 
 // Element offset of (row, col) in the sub-tile layout of a [32][576] tile:
 // sub-tile col / 128 (the last one 64 wide), each swizzled on its own.
@@ -63,68 +72,135 @@ __device__ __forceinline__ bf16x8 sop_tr_ch(const uint16_t* t, int dt, int k0, i
   return dt < 16 ? sop_tr(t, dt >> 2, k0, 32 * (dt & 3), lane) : sop_tr64(t, k0, 32 * (dt - 16), lane);
 }
 
-// Gather rows rows[r] (r < 32, device row indices, already made valid) of a
+// Entry lists.  Wave 0 copies the raw indices of tile it (entries
+// 32it .. 32it+31, addresses clamped to the list) into an LDS slot by
+// LDS-DMA; an entry is used iff it lies inside the list and 0 <= j < Tk.
+__device__ __forceinline__ void load_entries_async(const int* idx_t, int it, int K, int* slot, int w, int lane) {
+  if (w == 0 && lane < kKT) dma_b32_asm(idx_t + min(it * kKT + lane, K - 1), lds_addr(slot));
+}
+__device__ __forceinline__ bool entry_ok(const int* slot, int r, int e0, int K, int Tk) {
+  const int j = slot[r];
+  return e0 + r < K && j >= 0 && j < Tk;
+}
+__device__ __forceinline__ int entry_row(const int* slot, int r, int e0, int K, int Tk) {
+  return entry_ok(slot, r, e0, K, Tk) ? slot[r] : 0;
+}
+
+// Gather the rows of tile entries r < 32 (unused entries: row 0) of a
 // [*][576] bf16 matrix into a tile in the sub-tile layout, by LDS-DMA.  Per
-// wave: 2 instructions per 128-channel sub-tile, 1 for the 64-channel one.
-__device__ __forceinline__ void gather_rows_async(const uint16_t* g, const int* rows, uint16_t* tile, int w, int lane) {
+// wave: 2 instructions per 128-channel sub-tile, 1 for the 64-channel one
+// (9 in all).
+__device__ __forceinline__ void gather_rows_async(const uint16_t* g, const int* slot, int e0, int K, int Tk,
+                                                  uint16_t* tile, int w, int lane) {
 #pragma unroll
   for (int st = 0; st < 4; st++) {
 #pragma unroll
     for (int jj = 0; jj < 2; jj++) {
       const int j = w + 4 * jj;             // instruction: rows 4j .. 4j+3
-      const int r = 4 * j + (lane >> 4), slot = lane & 15;
-      const uint16_t* src = g + (size_t)rows[r] * kQK + 128 * st + ((slot ^ swz<128>(r)) << 3);
-      __builtin_amdgcn_global_load_lds(src, lds_ptr(tile + st * kSub + j * 512), 16, 0, 0);
+      const int r = 4 * j + (lane >> 4), cs = lane & 15;
+      const uint16_t* src = g + (size_t)entry_row(slot, r, e0, K, Tk) * kQK + 128 * st + ((cs ^ swz<128>(r)) << 3);
+      dma_b128_asm(src, lds_addr(tile + st * kSub + j * 512));
     }
   }
   {
-    const int r = 8 * w + (lane >> 3), slot = lane & 7;  // 8 rows per instruction
-    const uint16_t* src = g + (size_t)rows[r] * kQK + 512 + ((slot ^ swz<64>(r)) << 3);
-    __builtin_amdgcn_global_load_lds(src, lds_ptr(tile + 4 * kSub + w * 512), 16, 0, 0);
+    const int r = 8 * w + (lane >> 3), cs = lane & 7;  // 8 rows per instruction
+    const uint16_t* src = g + (size_t)entry_row(slot, r, e0, K, Tk) * kQK + 512 + ((cs ^ swz<64>(r)) << 3);
+    dma_b128_asm(src, lds_addr(tile + 4 * kSub + w * 512));
   }
+}
+
+// Partial results of the four waves (16 fp32 per lane, one 32x32 result
+// each) are summed through LDS in a fixed order: each wave stores its
+// partial (store_partial), a barrier follows, and every wave adds the four
+// (sum_partials).  Layout [wave][j / 4][lane][j % 4], 16-byte accesses.  The
+// accesses are inline assembly: compiler-visible LDS accesses to this buffer
+// were made to wait for the gathers in flight to the other buffers.
+__device__ __forceinline__ void store_partial(uint32_t base, int w, int lane, const f32x16& v) {
+  const uint32_t a = base + (uint32_t)(w * 4096 + lane * 16);
+#pragma unroll
+  for (int jg = 0; jg < 4; jg++)
+    lds_store_b128_addr(a + 1024u * jg, f32x4{v[4 * jg], v[4 * jg + 1], v[4 * jg + 2], v[4 * jg + 3]});
+}
+__device__ __forceinline__ f32x16 sum_partials(uint32_t base, int lane) {
+  const uint32_t a = base + (uint32_t)(lane * 16);
+  f32x16 out;
+#pragma unroll
+  for (int jg = 0; jg < 4; jg++) {
+    f32x4 p0 = lds_load_b128_addr(a + 1024u * jg), p1 = lds_load_b128_addr(a + 4096u + 1024u * jg);
+    f32x4 p2 = lds_load_b128_addr(a + 8192u + 1024u * jg), p3 = lds_load_b128_addr(a + 12288u + 1024u * jg);
+    lds_wait4(p0, p1, p2, p3);
+    const f32x4 r = (p0 + p1) + (p2 + p3);
+#pragma unroll
+    for (int i = 0; i < 4; i++) out[4 * jg + i] = r[i];
+  }
+  return out;
+}
+
+// Number of 32-entry tiles up to and including the last valid entry of the
+// list idx_t[0 .. K) (0 when it has none): tiles past it hold only unused
+// slots and are skipped.  All 256 threads take part; `red` is 4 ints of LDS.
+__device__ __forceinline__ int live_tiles(const int* idx_t, int K, int Tk, int* red, int w, int lane) {
+  int last = -1;
+  for (int e = threadIdx.x; e < K; e += 256) {
+    const int j = idx_t[e];
+    if (j >= 0 && j < Tk) last = e;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) last = max(last, __shfl_xor(last, off, 64));
+  if (lane == 0) red[w] = last;
+  lds_barrier();
+  last = max(max(red[0], red[1]), max(red[2], red[3]));
+  return __builtin_amdgcn_readfirstlane((last + kKT) / kKT);
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void smla_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int* __restrict__ idx,
     uint16_t* __restrict__ o, float* __restrict__ lse, int T, int Tk, int H, int K, float scale) {
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[4 * kSub + kKT * 64];
-  __shared__ __attribute__((aligned(16))) uint16_t sKV0[4 * kSub + kKT * 64];
-  __shared__ __attribute__((aligned(16))) uint16_t sKV1[4 * kSub + kKT * 64];
-  __shared__ float sSp[4][16 * 64];     // S^T partials, one per wave, in result-register order
-  // Entry lists of three consecutive tiles (tile i in slot i % 3): tile i is
-  // masked while tile i+1 is gathered and tile i+2's list is written.
-  __shared__ int sRow[3][kKT];          // gathered row of each entry (invalid: row 0)
-  __shared__ int sOk[3][kKT];           // entry valid
+  constexpr int kTile = 4 * kSub + kKT * 64;  // elements of a gathered 32 x 576 tile
+  // Three gathered tiles: tile i in buffer i % 3, gathered two tiles ahead.
+  __shared__ __attribute__((aligned(16))) uint16_t sKV[3 * kTile];
+  __shared__ __attribute__((aligned(16))) float sSp[4 * 16 * 64];  // S^T partials (store_partial)
+  // Raw entry lists (tile i in slot i % 4), loaded three tiles ahead.
+  __shared__ __attribute__((aligned(16))) int sIdx[4][kKT];
+  __shared__ int sRed[4];
 
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), hi = lane >> 5;
   const int l32 = lane & 31;
   const int n_ht = (H + kHT - 1) / kHT;
-  const int id = xcd_remap(blockIdx.x, gridDim.x);
-  const int t = __builtin_amdgcn_readfirstlane(id / n_ht), h0 = __builtin_amdgcn_readfirstlane((id % n_ht) * kHT);
-  const int n_tiles = (K + kKT - 1) / kKT;
+  // Workgroups go to the XCDs round-robin, so consecutive ids spread a run
+  // of tokens over all of them (list lengths, and so costs, change slowly
+  // along the tokens); the last tokens, whose lists are usually the
+  // longest, start first.
+  const int id = blockIdx.x;
+  const int t = __builtin_amdgcn_readfirstlane(T - 1 - id / n_ht), h0 = __builtin_amdgcn_readfirstlane((id % n_ht) * kHT);
   const int* idx_t = idx + (size_t)t * K;
 
-  // The query tile (heads h0 .. h0+31; heads past H repeat the last one).
+  // Query operands of wave w's share of S^T (channels 144w .. 144w+143) in
+  // registers: lane (head l32, half hi) holds channels d0 + 4hi .. +3 and
+  // d0 + 8 + 4hi .. +3 of each 16-channel step d0 (heads past H repeat the
+  // last one).
+  bf16x8 bq[9];
   {
-    const uint16_t* qb = q + ((size_t)t * H) * kQK;
+    const uint16_t* qr = q + ((size_t)t * H + min(h0 + l32, H - 1)) * kQK + 144 * w + 4 * hi;
 #pragma unroll
-    for (int st = 0; st < 4; st++) tile_load_async<128, kHT, 4>(qb + 128 * st, kQK, h0, H, sQ + st * kSub, w, lane);
-    tile_load_async<64, kHT, 4>(qb + 512, kQK, h0, H, sQ + 4 * kSub, w, lane);
-  }
-  // Entry list of tile it: rows and validity into slot it % 3 (wave 0).
-  auto entries = [&](int it) {
-    if (w == 0 && lane < kKT) {
-      const int e = it * kKT + lane;
-      const int j = e < K ? idx_t[e] : -1;
-      const bool ok = j >= 0 && j < Tk;
-      sRow[it % 3][lane] = ok ? j : 0;
-      sOk[it % 3][lane] = ok;
+    for (int kk = 0; kk < 9; kk++) {
+      const u32x2 a = *reinterpret_cast<const u32x2*>(qr + 16 * kk);
+      const u32x2 b = *reinterpret_cast<const u32x2*>(qr + 16 * kk + 8);
+      bq[kk] = __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
     }
-  };
-  entries(0);
-  lds_barrier();
-  gather_rows_async(kv, sRow[0], sKV0, w, lane);
-  if (n_tiles > 1) entries(1);
+  }
+  const int n_tiles = live_tiles(idx_t, K, Tk, sRed, w, lane);
+  // All loads of the loop (entry lists, gathers) are LDS-DMA issued as
+  // inline assembly; the waits at the start of each tile cover them.
+  if (n_tiles > 0) {
+    load_entries_async(idx_t, 0, K, sIdx[0], w, lane);
+    if (n_tiles > 1) load_entries_async(idx_t, 1, K, sIdx[1], w, lane);
+    wait_vmem();
+    lds_barrier();
+    gather_rows_async(kv, sIdx[0], 0, K, Tk, sKV, w, lane);
+    if (n_tiles > 2) load_entries_async(idx_t, 2, K, sIdx[2], w, lane);
+    if (n_tiles > 1) gather_rows_async(kv, sIdx[1], kKT, K, Tk, sKV + kTile, w, lane);
+  }
 
   const float c = scale * kLog2e;
   f32x16 oacc[4];
@@ -132,31 +208,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void s
   for (int dt = 0; dt < 4; dt++) oacc[dt] = f32x16{};
   float m_i = -INFINITY, l_i = 0.f;
 
-  auto tile = [&](auto buf_tag, int it) {
-    constexpr int BUF = decltype(buf_tag)::value;
-    const uint16_t* cKV = BUF ? sKV1 : sKV0;
-    uint16_t* nKV = BUF ? sKV0 : sKV1;
-    wait_vmem();
-    lds_barrier();  // tile it resident (and its entry list); every wave is done with tile it-1
-    if (it + 1 < n_tiles) gather_rows_async(kv, sRow[(it + 1) % 3], nKV, w, lane);
-    if (it + 2 < n_tiles) entries(it + 2);
+  for (int it = 0; it < n_tiles; it++) {
+    const uint16_t* cKV = sKV + (it % 3) * kTile;
+    // Tile it resident: it was gathered before the 9 gather instructions of
+    // tile it+1 (the latest loads of this wave, when there is a tile it+1),
+    // and so was the list of tile it+2.
+    if (it + 1 < n_tiles)
+      wait_vmem_but<9>();
+    else
+      wait_vmem();
+    lds_barrier();  // tile it and the list of tile it+2 resident; every wave is done with tile it-1
+    if (it + 3 < n_tiles) load_entries_async(idx_t, it + 3, K, sIdx[(it + 3) % 4], w, lane);
+    if (it + 2 < n_tiles)
+      gather_rows_async(kv, sIdx[(it + 2) % 4], (it + 2) * kKT, K, Tk, sKV + ((it + 2) % 3) * kTile, w, lane);
     // S^T partial over channels 144w .. 144w+143.
     f32x16 sp = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < 9; kk++) {
-      const int d0 = 144 * w + 16 * kk;
-      sp = mfma32(sop_row(cKV, l32, d0, hi), sop_row(sQ, l32, d0, hi), sp);
-    }
-#pragma unroll
-    for (int j = 0; j < 16; j++) sSp[w][j * 64 + lane] = sp[j];
+    for (int kk = 0; kk < 9; kk++) sp = mfma32(sop_row(cKV, l32, 144 * w + 16 * kk, hi), bq[kk], sp);
+    store_partial(lds_addr(sSp), w, lane, sp);
     lds_barrier();
-    f32x16 s;
-#pragma unroll
-    for (int j = 0; j < 16; j++) s[j] = (sSp[0][j * 64 + lane] + sSp[1][j * 64 + lane]) + (sSp[2][j * 64 + lane] + sSp[3][j * 64 + lane]);
+    f32x16 s = sum_partials(lds_addr(sSp), lane);
     // Unused slots and entries past the end of the list: -inf.
 #pragma unroll
     for (int j = 0; j < 16; j++)
-      if (!sOk[it % 3][8 * (j >> 2) + 4 * hi + (j & 3)]) s[j] = -INFINITY;
+      if (!entry_ok(sIdx[it % 4], c_row(j, hi), it * kKT, K, Tk)) s[j] = -INFINITY;
     float mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 16; j++) mx = fmaxf(mx, s[j]);
@@ -185,10 +260,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void s
     for (int kk = 0; kk < 2; kk++)
 #pragma unroll
       for (int dt = 0; dt < 4; dt++) oacc[dt] = mfma32(sop_tr(cKV, w, 16 * kk, 32 * dt, lane), pb[kk], oacc[dt]);
-  };
-  for (int it = 0; it < n_tiles; it += 2) {
-    tile(std::integral_constant<int, 0>{}, it);
-    if (it + 1 < n_tiles) tile(std::integral_constant<int, 1>{}, it + 1);
   }
 
   const float l_tot = xhalf_sum(l_i);
@@ -262,18 +333,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void s
   __shared__ __attribute__((aligned(16))) uint16_t sQ[4 * kSub + kKT * 64];
   __shared__ __attribute__((aligned(16))) uint16_t sKV0[4 * kSub + kKT * 64];
   __shared__ __attribute__((aligned(16))) uint16_t sKV1[4 * kSub + kKT * 64];
-  __shared__ float sSp[4][16 * 64];                   // partial sums (S^T, then dP^T)
+  __shared__ __attribute__((aligned(16))) float sSp[4 * 16 * 64];  // partials (S^T, then dP^T)
   __shared__ __attribute__((aligned(16))) uint16_t sDS[kKT * kHT];  // scale dS as [entry][head]
   __shared__ __attribute__((aligned(16))) uint16_t sPT[kKT * kHT];  // P as [entry][head]
-  __shared__ int sRow[3][kKT];
-  __shared__ int sOk[3][kKT];
+  __shared__ __attribute__((aligned(16))) int sIdx[3][kKT];  // raw entry lists, as in the forward
+  __shared__ int sRed[4];
 
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), hi = lane >> 5;
   const int l32 = lane & 31;
   const int n_ht = (H + kHT - 1) / kHT;
-  const int id = xcd_remap(blockIdx.x, gridDim.x);
-  const int t = __builtin_amdgcn_readfirstlane(id / n_ht), h0 = __builtin_amdgcn_readfirstlane((id % n_ht) * kHT);
-  const int n_tiles = (K + kKT - 1) / kKT;
+  // Workgroups go to the XCDs round-robin, so consecutive ids spread a run
+  // of tokens over all of them (list lengths, and so costs, change slowly
+  // along the tokens); the last tokens, whose lists are usually the
+  // longest, start first.
+  const int id = blockIdx.x;
+  const int t = __builtin_amdgcn_readfirstlane(T - 1 - id / n_ht), h0 = __builtin_amdgcn_readfirstlane((id % n_ht) * kHT);
   const int* idx_t = idx + (size_t)t * K;
   const int head = h0 + l32;                   // this lane's head (S^T columns)
   const bool head_ok = head < H;
@@ -315,19 +389,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void s
       vdo[bi][kk] = pack8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
     }
 
-  auto entries = [&](int it) {
-    if (w == 0 && lane < kKT) {
-      const int e = it * kKT + lane;
-      const int j = e < K ? idx_t[e] : -1;
-      const bool ok = j >= 0 && j < Tk;
-      sRow[it % 3][lane] = ok ? j : 0;
-      sOk[it % 3][lane] = ok;
-    }
-  };
-  entries(0);
-  lds_barrier();
-  gather_rows_async(kv, sRow[0], sKV0, w, lane);
-  if (n_tiles > 1) entries(1);
+  const int n_tiles = live_tiles(idx_t, K, Tk, sRed, w, lane);
+  // Entry lists and gathers as in the forward kernel.
+  if (n_tiles > 0) {
+    load_entries_async(idx_t, 0, K, sIdx[0], w, lane);
+    if (n_tiles > 1) load_entries_async(idx_t, 1, K, sIdx[1], w, lane);
+    wait_vmem();
+    lds_barrier();
+    gather_rows_async(kv, sIdx[0], 0, K, Tk, sKV0, w, lane);
+  }
+  // dKV accumulator as a buffer resource: an unused entry's atomics get an
+  // offset past its end, which the hardware drops, so that every wave issues
+  // the same number of atomics per tile whatever the entries (the wait at the
+  // start of the next tile counts on that).
+  const __amdgpu_buffer_rsrc_t acc_rs = buffer_rsrc(dkv_acc, (uint32_t)Tk * (uint32_t)(kQK * 4));
 
   const int nblk = w < 2 ? 5 : 4;  // channel blocks of this wave: w, w+4, w+8, w+12, (w+16)
   f32x16 dqa[5];
@@ -339,10 +414,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void s
     const uint16_t* cKV = BUF ? sKV1 : sKV0;
     uint16_t* nKV = BUF ? sKV0 : sKV1;
     const int slot = it % 3;
-    wait_vmem();
-    lds_barrier();  // tile it resident; every wave is done with tile it-1
-    if (it + 1 < n_tiles) gather_rows_async(kv, sRow[(it + 1) % 3], nKV, w, lane);
-    if (it + 2 < n_tiles) entries(it + 2);
+    // Tile it resident.  It was gathered before the previous tile's dKV
+    // atomics (at least 64 per wave, issued after the gather), which may
+    // stay in flight: the counter retires in issue order.
+    if (it > 0)
+      wait_vmem_but<kAtomSlack>();
+    else
+      wait_vmem();
+    lds_barrier();  // tile it and the list of tile it+1 resident; every wave is done with tile it-1
+    if (it + 2 < n_tiles) load_entries_async(idx_t, it + 2, K, sIdx[(it + 2) % 3], w, lane);
+    if (it + 1 < n_tiles) gather_rows_async(kv, sIdx[(it + 1) % 3], (it + 1) * kKT, K, Tk, nKV, w, lane);
+    const int* cIdx = sIdx[slot];
+    const int e0 = it * kKT;
     // S^T partial over channels 144w .. 144w+143.
     f32x16 sp = f32x16{};
 #pragma unroll
@@ -354,26 +437,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void s
     f32x16 dpp = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < 8; kk++) dpp = mfma32(sop_row(cKV, l32, 128 * w + 16 * kk, hi), bdo[kk], dpp);
-#pragma unroll
-    for (int j = 0; j < 16; j++) sSp[w][j * 64 + lane] = sp[j];
+    const uint32_t sp_base = lds_addr(sSp);
+    store_partial(sp_base, w, lane, sp);
     lds_barrier();
+    const f32x16 ssum = sum_partials(sp_base, lane);
     f32x16 p;
 #pragma unroll
     for (int j = 0; j < 16; j++) {
-      const float sv = (sSp[0][j * 64 + lane] + sSp[1][j * 64 + lane]) + (sSp[2][j * 64 + lane] + sSp[3][j * 64 + lane]);
-      const bool ok = head_ok && sOk[slot][c_row(j, hi)];
-      p[j] = ok ? __builtin_amdgcn_exp2f(fmaf(sv, c, -lse_l2)) : 0.f;
+      const bool ok = head_ok && entry_ok(cIdx, c_row(j, hi), e0, K, Tk);
+      p[j] = ok ? __builtin_amdgcn_exp2f(fmaf(ssum[j], c, -lse_l2)) : 0.f;
     }
     lds_barrier();  // S sums read by every wave: the buffer takes the dP partials
-#pragma unroll
-    for (int j = 0; j < 16; j++) sSp[w][j * 64 + lane] = dpp[j];
+    store_partial(sp_base, w, lane, dpp);
     lds_barrier();
+    const f32x16 dpsum = sum_partials(sp_base, lane);
     f32x16 ds;
 #pragma unroll
-    for (int j = 0; j < 16; j++) {
-      const float dpv = (sSp[0][j * 64 + lane] + sSp[1][j * 64 + lane]) + (sSp[2][j * 64 + lane] + sSp[3][j * 64 + lane]);
-      ds[j] = p[j] * (dpv - dl);
-    }
+    for (int j = 0; j < 16; j++) ds[j] = p[j] * (dpsum[j] - dl);
     // dS^T and P^T to LDS as [entry][head] (wave 0 writes; all read below).
     if (w == 0) {
 #pragma unroll
@@ -419,7 +499,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void s
 #pragma unroll
       for (int j = 0; j < 16; j++) {
         const int e = c_row(j, hi);
-        if (sOk[slot][e]) unsafeAtomicAdd(dkv_acc + (size_t)sRow[slot][e] * kQK + 32 * blk + l32, acc[j]);
+        const uint32_t off = entry_ok(cIdx, e, e0, K, Tk)
+                                 ? (uint32_t)cIdx[e] * (uint32_t)(kQK * 4) + (uint32_t)(32 * blk + l32) * 4u
+                                 : kDropOffset;
+        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[j], acc_rs, off, 0, 0);
       }
     }
   };
@@ -427,6 +510,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void s
     tile(std::integral_constant<int, 0>{}, it);
     if (it + 1 < n_tiles) tile(std::integral_constant<int, 1>{}, it + 1);
   }
+  if (n_tiles == 0) wait_vmem();  // the query tile's loads
 
   // dq[t, head, channel]: dQ^T element j of block blk is channel
   // 32 blk + c_row(j), head l32; four consecutive channels per store.

@@ -299,7 +299,7 @@ int gla_chunk_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const
  */
 typedef struct smla_shape {
   int32_t tokens;    /* T >= 1 query tokens */
-  int32_t kv_tokens; /* Tk >= 1 latent rows */
+  int32_t kv_tokens; /* Tk, 1 .. 524288 latent rows */
   int32_t heads;     /* H >= 1 query heads */
   int32_t topk;      /* K, 1 .. 8192 index entries per token */
   int32_t dim_qk;    /* 576 */

@@ -324,6 +324,7 @@ def mfwd(**kw):
     ({"shape": mshp(t=0)}, "shape"), ({"shape": mshp(tk=0)}, "shape"), ({"shape": mshp(h=0)}, "shape"),
     ({"shape": mshp(k=0)}, "shape"), ({"shape": mshp(dqk=512)}, "hd"), ({"shape": mshp(dv=576)}, "hd"),
     ({"shape": mshp(k=8193)}, "range"), ({"shape": mshp(t=1 << 20, h=64)}, "range"),
+    ({"shape": mshp(tk=(1 << 19) + 1)}, "range"),
     ({"scale": 0.0}, "range"), ({"q": MIS}, "align"), ({"o": MIS}, "align"), ({"idx": P(0x10002)}, "align"),
 ])
 def test_sparse_mla_fwd_errors(kw, code):
@@ -340,7 +341,7 @@ def mbwd(**kw):
 @pytest.mark.parametrize("kw,code", [
     ({"acc": None}, "null"), ({"delta": None}, "null"), ({"shape": mshp(k=0)}, "shape"),
     ({"shape": mshp(dqk=128)}, "hd"), ({"scale": float("inf")}, "range"), ({"dq": MIS}, "align"),
-    ({"acc": MIS}, "align"), ({"delta": P(0x10001)}, "align"),
+    ({"acc": MIS}, "align"), ({"delta": P(0x10001)}, "align"), ({"shape": mshp(tk=(1 << 19) + 1)}, "range"),
 ])
 def test_sparse_mla_bwd_errors(kw, code):
     assert mbwd(**kw) == E[code]
