@@ -201,6 +201,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 __device__ __forceinline__ void dma_b128_asm(const void* g, uint32_t lds) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
 }
+// The same from g + OFF bytes.  The instruction's immediate offset moves
+// the LDS destination as well as the global address, so M0 takes lds - OFF
+// (lds >= OFF).
+template <int OFF>
+__device__ __forceinline__ void dma_b128_asm_off(const void* g, uint32_t lds) {
+  static_assert(OFF >= 0 && OFF < 4096, "immediate offset");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2" ::"v"(g), "{m0}"(lds - OFF), "i"(OFF)
+               : "memory");
+}
 __device__ __forceinline__ void dma_b32_asm(const void* g, uint32_t lds) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds) : "memory");
 }

@@ -88,25 +88,35 @@ __device__ __forceinline__ int entry_row(const int* slot, int r, int e0, int K, 
 
 // Gather the rows of tile entries r < 32 (unused entries: row 0) of a
 // [*][576] bf16 matrix into a tile in the sub-tile layout, by LDS-DMA.  Per
-// wave: 2 instructions per 128-channel sub-tile, 1 for the 64-channel one
-// (9 in all).
+// wave: 2 instructions per 128-channel sub-tile (rows 4w + lane/16 and
+// 16 + 4w + lane/16, one 256-byte row piece per 16 lanes), 1 for the
+// 64-channel one (rows 8w + lane/8), 9 in all.  `cb` and `cb64` are the
+// lane's swizzled byte offsets inside the row pieces (gather_cols).
+struct GatherCols {
+  uint32_t cb, cb64;
+};
+__device__ __forceinline__ GatherCols gather_cols(int w, int lane) {
+  const int r = 4 * w + (lane >> 4), r64 = 8 * w + (lane >> 3);
+  return {(uint32_t)(((lane & 15) ^ swz<128>(r)) << 4), (uint32_t)(1024 + (((lane & 7) ^ swz<64>(r64)) << 4))};
+}
 __device__ __forceinline__ void gather_rows_async(const uint16_t* g, const int* slot, int e0, int K, int Tk,
-                                                  uint16_t* tile, int w, int lane) {
-#pragma unroll
-  for (int st = 0; st < 4; st++) {
-#pragma unroll
-    for (int jj = 0; jj < 2; jj++) {
-      const int j = w + 4 * jj;             // instruction: rows 4j .. 4j+3
-      const int r = 4 * j + (lane >> 4), cs = lane & 15;
-      const uint16_t* src = g + (size_t)entry_row(slot, r, e0, K, Tk) * kQK + 128 * st + ((cs ^ swz<128>(r)) << 3);
-      dma_b128_asm(src, lds_addr(tile + st * kSub + j * 512));
-    }
-  }
-  {
-    const int r = 8 * w + (lane >> 3), cs = lane & 7;  // 8 rows per instruction
-    const uint16_t* src = g + (size_t)entry_row(slot, r, e0, K, Tk) * kQK + 512 + ((cs ^ swz<64>(r)) << 3);
-    dma_b128_asm(src, lds_addr(tile + 4 * kSub + w * 512));
-  }
+                                                  uint16_t* tile, GatherCols gc, int w, int lane) {
+  // The three rows of this lane (rows r and r + 16 share the swizzle).
+  const int r = 4 * w + (lane >> 4);
+  const char* gb = reinterpret_cast<const char*>(g);
+  const char* p0 = gb + (size_t)entry_row(slot, r, e0, K, Tk) * (kQK * 2) + gc.cb;
+  const char* p1 = gb + (size_t)entry_row(slot, r + 16, e0, K, Tk) * (kQK * 2) + gc.cb;
+  const char* p2 = gb + (size_t)entry_row(slot, 8 * w + (lane >> 3), e0, K, Tk) * (kQK * 2) + gc.cb64;
+  const uint32_t tb = lds_addr(tile);
+  dma_b128_asm_off<0>(p0, tb + 2 * (w * 512));
+  dma_b128_asm_off<0>(p1, tb + 2 * ((w + 4) * 512));
+  dma_b128_asm_off<256>(p0, tb + 2 * (kSub + w * 512));
+  dma_b128_asm_off<256>(p1, tb + 2 * (kSub + (w + 4) * 512));
+  dma_b128_asm_off<512>(p0, tb + 2 * (2 * kSub + w * 512));
+  dma_b128_asm_off<512>(p1, tb + 2 * (2 * kSub + (w + 4) * 512));
+  dma_b128_asm_off<768>(p0, tb + 2 * (3 * kSub + w * 512));
+  dma_b128_asm_off<768>(p1, tb + 2 * (3 * kSub + (w + 4) * 512));
+  dma_b128_asm_off<0>(p2, tb + 2 * (4 * kSub + w * 512));
 }
 
 // Partial results of the four waves (16 fp32 per lane, one 32x32 result
@@ -190,6 +200,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void s
     }
   }
   const int n_tiles = live_tiles(idx_t, K, Tk, sRed, w, lane);
+  const GatherCols gcols = gather_cols(w, lane);
   // All loads of the loop (entry lists, gathers) are LDS-DMA issued as
   // inline assembly; the waits at the start of each tile cover them.
   if (n_tiles > 0) {
@@ -197,16 +208,43 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void s
     if (n_tiles > 1) load_entries_async(idx_t, 1, K, sIdx[1], w, lane);
     wait_vmem();
     lds_barrier();
-    gather_rows_async(kv, sIdx[0], 0, K, Tk, sKV, w, lane);
+    gather_rows_async(kv, sIdx[0], 0, K, Tk, sKV, gcols, w, lane);
     if (n_tiles > 2) load_entries_async(idx_t, 2, K, sIdx[2], w, lane);
-    if (n_tiles > 1) gather_rows_async(kv, sIdx[1], kKT, K, Tk, sKV + kTile, w, lane);
+    if (n_tiles > 1) gather_rows_async(kv, sIdx[1], kKT, K, Tk, sKV + kTile, gcols, w, lane);
+  }
+
+  // Per-lane byte offsets inside a gathered tile, fixed for the kernel:
+  // the row reads of the S^T product (two 8-byte halves per k-step) and the
+  // transposing reads of the O^T product (sub-tile w, two per (kk, dt)).
+  uint32_t offS[9][2], offO[2][4][2];
+#pragma unroll
+  for (int kk = 0; kk < 9; kk++) {
+    const int k0 = 144 * w + 16 * kk;
+    offS[kk][0] = 2u * (uint32_t)sub_off(l32, k0 + 4 * hi);
+    offS[kk][1] = 2u * (uint32_t)sub_off(l32, k0 + 8 + 4 * hi);
+  }
+  {
+    const int L = lane & 15, gp = (lane >> 4) & 1;
+#pragma unroll
+    for (int kk = 0; kk < 2; kk++)
+#pragma unroll
+      for (int dt = 0; dt < 4; dt++) {
+        const int col = 32 * dt + 16 * gp + 4 * (L & 3);
+        offO[kk][dt][0] = 2u * (uint32_t)(w * kSub + swz_off<128>(16 * kk + 4 * hi + (L >> 2), col));
+        offO[kk][dt][1] = 2u * (uint32_t)(w * kSub + swz_off<128>(16 * kk + 8 + 4 * hi + (L >> 2), col));
+      }
   }
 
   const float c = scale * kLog2e;
   f32x16 oacc[4];
 #pragma unroll
   for (int dt = 0; dt < 4; dt++) oacc[dt] = f32x16{};
-  float m_i = -INFINITY, l_i = 0.f;
+  // Online softmax in log2 units with a lazily moved reference: M moves
+  // only when a tile's maximum exceeds it by more than kLazy (so the
+  // exponentials stay below 2^kLazy); O and l are rescaled only then.  The
+  // result does not depend on the reference.
+  constexpr float kLazy = 8.f;
+  float M = -INFINITY, l_i = 0.f;
 
   for (int it = 0; it < n_tiles; it++) {
     const uint16_t* cKV = sKV + (it % 3) * kTile;
@@ -220,25 +258,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void s
     lds_barrier();  // tile it and the list of tile it+2 resident; every wave is done with tile it-1
     if (it + 3 < n_tiles) load_entries_async(idx_t, it + 3, K, sIdx[(it + 3) % 4], w, lane);
     if (it + 2 < n_tiles)
-      gather_rows_async(kv, sIdx[(it + 2) % 4], (it + 2) * kKT, K, Tk, sKV + ((it + 2) % 3) * kTile, w, lane);
+      gather_rows_async(kv, sIdx[(it + 2) % 4], (it + 2) * kKT, K, Tk, sKV + ((it + 2) % 3) * kTile, gcols, w, lane);
+    // Validity of the tile's 32 entries as one wave-uniform mask.
+    const int* cl = sIdx[it % 4];
+    const uint32_t vmask =
+        (uint32_t)__builtin_amdgcn_ballot_w64(lane < kKT ? entry_ok(cl, lane, it * kKT, K, Tk) : false);
     // S^T partial over channels 144w .. 144w+143.
     f32x16 sp = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < 9; kk++) sp = mfma32(sop_row(cKV, l32, 144 * w + 16 * kk, hi), bq[kk], sp);
+    for (int kk = 0; kk < 9; kk++) {
+      const u32x2 a = *reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(cKV) + offS[kk][0]);
+      const u32x2 b = *reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(cKV) + offS[kk][1]);
+      sp = mfma32(__builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]}), bq[kk], sp);
+    }
     store_partial(lds_addr(sSp), w, lane, sp);
     lds_barrier();
     f32x16 s = sum_partials(lds_addr(sSp), lane);
     // Unused slots and entries past the end of the list: -inf.
+    if (vmask != 0xFFFFFFFFu) {
+      const uint32_t ml = vmask >> (4 * hi);
 #pragma unroll
-    for (int j = 0; j < 16; j++)
-      if (!entry_ok(sIdx[it % 4], c_row(j, hi), it * kKT, K, Tk)) s[j] = -INFINITY;
+      for (int j = 0; j < 16; j++)
+        if (!((ml >> (8 * (j >> 2) + (j & 3))) & 1u)) s[j] = -INFINITY;
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 16; j++) mx = fmaxf(mx, s[j]);
-    mx = xhalf_max(mx);
-    const float m_new = fmaxf(m_i, mx);
-    const float mc = (m_new == -INFINITY ? 0.f : m_new) * c;
-    const float alpha = __builtin_amdgcn_exp2f(m_i * c - mc);
+    const float mxc = xhalf_max(mx) * c;
+    if (__builtin_amdgcn_ballot_w64(mxc > M + kLazy) != 0) {
+      const float Mn = fmaxf(M, mxc);
+      const float alpha = Mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(M - Mn);
+      l_i *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; dt++) oacc[dt] *= alpha;
+      M = Mn;
+    }
+    const float mc = M == -INFINITY ? 0.f : M;
     float rs = 0.f;
 #pragma unroll
     for (int j = 0; j < 16; j++) {
@@ -246,10 +301,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void s
       s[j] = e;
       rs += e;
     }
-    l_i = fmaf(l_i, alpha, rs);
-    m_i = m_new;
-#pragma unroll
-    for (int dt = 0; dt < 4; dt++) oacc[dt] *= alpha;
+    l_i += rs;
     bf16x8 pb[2];
 #pragma unroll
     for (int kk = 0; kk < 2; kk++)
@@ -259,7 +311,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void s
 #pragma unroll
     for (int kk = 0; kk < 2; kk++)
 #pragma unroll
-      for (int dt = 0; dt < 4; dt++) oacc[dt] = mfma32(sop_tr(cKV, w, 16 * kk, 32 * dt, lane), pb[kk], oacc[dt]);
+      for (int dt = 0; dt < 4; dt++)
+        oacc[dt] = mfma32(lds_tr8_at(cKV, offO[kk][dt][0], offO[kk][dt][1]), pb[kk], oacc[dt]);
   }
 
   const float l_tot = xhalf_sum(l_i);
@@ -276,7 +329,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void s
             u32x2{pack_bf16x2(oacc[dt][4 * jg] * inv, oacc[dt][4 * jg + 1] * inv),
                   pack_bf16x2(oacc[dt][4 * jg + 2] * inv, oacc[dt][4 * jg + 3] * inv)};
       }
-    if (w == 0 && hi == 0) lse[(size_t)t * H + h] = m_i * scale + __builtin_amdgcn_logf(l_tot) * kLn2;
+    if (w == 0 && hi == 0) lse[(size_t)t * H + h] = (M + __builtin_amdgcn_logf(l_tot)) * kLn2;
   }
 }
 
@@ -390,13 +443,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void s
     }
 
   const int n_tiles = live_tiles(idx_t, K, Tk, sRed, w, lane);
+  const GatherCols gcols = gather_cols(w, lane);
   // Entry lists and gathers as in the forward kernel.
   if (n_tiles > 0) {
     load_entries_async(idx_t, 0, K, sIdx[0], w, lane);
     if (n_tiles > 1) load_entries_async(idx_t, 1, K, sIdx[1], w, lane);
     wait_vmem();
     lds_barrier();
-    gather_rows_async(kv, sIdx[0], 0, K, Tk, sKV0, w, lane);
+    gather_rows_async(kv, sIdx[0], 0, K, Tk, sKV0, gcols, w, lane);
   }
   // dKV accumulator as a buffer resource: an unused entry's atomics get an
   // offset past its end, which the hardware drops, so that every wave issues
@@ -423,7 +477,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void s
       wait_vmem();
     lds_barrier();  // tile it and the list of tile it+1 resident; every wave is done with tile it-1
     if (it + 2 < n_tiles) load_entries_async(idx_t, it + 2, K, sIdx[(it + 2) % 3], w, lane);
-    if (it + 1 < n_tiles) gather_rows_async(kv, sIdx[(it + 1) % 3], (it + 1) * kKT, K, Tk, nKV, w, lane);
+    if (it + 1 < n_tiles) gather_rows_async(kv, sIdx[(it + 1) % 3], (it + 1) * kKT, K, Tk, nKV, gcols, w, lane);
     const int* cIdx = sIdx[slot];
     const int e0 = it * kKT;
     // S^T partial over channels 144w .. 144w+143.
