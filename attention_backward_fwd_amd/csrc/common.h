@@ -213,6 +213,27 @@ __device__ __forceinline__ void dma_b128_asm_off(const void* g, uint32_t lds) {
 __device__ __forceinline__ void dma_b32_asm(const void* g, uint32_t lds) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds) : "memory");
 }
+// The same copy issued as inline assembly (dma_b128_asm): the compiler adds
+// no waits for it; the caller waits explicitly.  NI / NW instructions per
+// wave (all waves when the tile is at least NW KB).
+template <int D, int R, int NW = 4>
+__device__ __forceinline__ void tile_load_async_asm(const uint16_t* g, size_t rs, int row0, int nrows,
+                                                    uint16_t* tile, int w, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int RPI = 64 / CPR;
+  constexpr int NI = R / RPI;
+  static_assert(NI % NW == 0, "tile must split evenly over the waves");
+  const int rl = lane / CPR, slot = lane % CPR;
+  const char* base = reinterpret_cast<const char*>(g + (size_t)row0 * rs);
+  const int last = nrows - 1 - row0;
+#pragma unroll
+  for (int j = w; j < NI; j += NW) {
+    const int r = j * RPI + rl;
+    const uint32_t off = ((uint32_t)min(r, last) * (uint32_t)rs + (uint32_t)((slot ^ swz<D>(r)) << 3)) * 2u;
+    dma_b128_asm(base + off, lds_addr(tile + j * 512));
+  }
+}
+
 // 16-byte LDS store and load the compiler does not track either (see
 // lds_store_b64_asm).  A load's result is only ready after lds_wait4().
 __device__ __forceinline__ void lds_store_b128_addr(uint32_t addr, f32x4 v) {

@@ -90,61 +90,68 @@ __device__ __forceinline__ bf16x8 scale_op(bf16x8 v, const float* f, int k0, int
 }
 
 // ------------------------------------------------------------ chunk states
-// Workgroup (b*H + h, vt, dir): 4 waves own the 64 x 128 transposed state
-// tile S^T of value columns 64vt .. 64vt+63 (wave w: value rows
-// 64vt + 32(w & 1).., key columns 64(w >> 1) .., two 32x32 tiles; lane =
-// key index, so each lane stores four consecutive values per 8-byte store).
+// Workgroup (b*H + h, dir): 8 waves own the 128 x 128 transposed state
+// tile S^T (wave w: value rows 32(w & 3).., key columns 64(w >> 2) .., two
+// 32x32 tiles; lane = key index, so each lane stores four consecutive values
+// per 8-byte store).  Keeping the whole state in one workgroup reads each
+// chunk's X once; the kernel moves about 1.1 GB per call on the benchmark
+// workload and is bound by HBM bandwidth.
 // dir 0 sweeps chunks forward and writes h_n (the state entering chunk n);
 // dir 1 sweeps backward and writes dH_{n+1} (zero for the last chunk); both
-// as [K][V] bf16.  Per chunk: X (k or q, all 128 columns) and Y (v or do,
-// this workgroup's 64 columns) arrive by LDS-DMA one chunk ahead; the update
+// as [K][V] bf16.  Per chunk: X (k or q) and Y (v or do) arrive by LDS-DMA
+// two chunks ahead; the update
 // is S = exp(Gl) S + X^T (f o Y) with f_s = exp(Gl - G_s) (forward) or
 // scale * exp(G_t) (backward), 0 past the end of the sequence.  The state
 // stores stay in flight: each step waits only for its own tile loads.
-__global__ __launch_bounds__(256) void gla_states_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+__global__ __launch_bounds__(512) void gla_states_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                          const uint16_t* __restrict__ v,
                                                          const uint16_t* __restrict__ dout,
                                                          const float* __restrict__ g, uint16_t* __restrict__ hs,
                                                          uint16_t* __restrict__ dhs, int T, int H, float scale) {
-  // Two buffers.  A buffer's Y tile is followed by the chunk's raw g (64
-  // fp32, LDS-DMA too; one object per buffer keeps the compiler's LDS-DMA
-  // tracking exact, so that it adds no waits of its own).
-  __shared__ __attribute__((aligned(16))) uint16_t sX0[kC * kD];
-  __shared__ __attribute__((aligned(16))) uint16_t sX1[kC * kD];
-  __shared__ __attribute__((aligned(16))) uint16_t sY0[kC * 64 + 2 * kC];
-  __shared__ __attribute__((aligned(16))) uint16_t sY1[kC * 64 + 2 * kC];
-  __shared__ float sG[kC];
-  __shared__ float sF[kC];
+  // Three buffers, chunk i of the sweep in buffer i % 3, loaded two steps
+  // ahead.  A buffer's Y tile is followed by the chunk's raw g (64 fp32).
+  // The loads are LDS-DMA issued as inline assembly and waited for
+  // explicitly.
+  constexpr int NW = 8;
+  constexpr int kXT = kC * kD, kYT = kC * kD + 2 * kC;
+  __shared__ __attribute__((aligned(16))) uint16_t sX[3 * kXT];
+  __shared__ __attribute__((aligned(16))) uint16_t sY[3 * kYT];
+  __shared__ float sG[NW][kC];  // per-wave copies: running sums of g, token factors
+  __shared__ float sF[NW][kC];
 
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), hi = lane >> 5;
-  const int bh = blockIdx.x, vt = blockIdx.y, dir = blockIdx.z;
+  const int bh = blockIdx.x, dir = blockIdx.z;
   const int b = bh / H, h = bh % H;
   const int N = (T + kC - 1) / kC;
   const size_t rs = (size_t)H * kD;
   const uint16_t* X = (dir ? q : k) + ((size_t)b * T * H + h) * kD;
-  const uint16_t* Y = (dir ? dout : v) + ((size_t)b * T * H + h) * kD + 64 * vt;
+  const uint16_t* Y = (dir ? dout : v) + ((size_t)b * T * H + h) * kD;
   const float* gb = g + (size_t)b * T * H + h;
   // N + 1 state slots per (b, h): slot N takes the state after the last
   // step, which nobody reads, so that every step stores (and loads)
-  // unconditionally and the wait count below holds on every path.
+  // unconditionally and the wait counts below hold on every path.
   uint16_t* out = (dir ? dhs : hs) + (size_t)bh * (N + 1) * kD * kD;
-  const int vb = 32 * (w & 1), kb = 64 * (w >> 1);  // this wave's value rows (within the half), key columns
+  const int vb = 32 * (w & 3), kb = 64 * (w >> 2);  // this wave's value rows, key columns
   const Lofs<kD> oD(lane);
-  const Lofs<64> o64(lane);
+  float* wG = sG[w];
+  float* wF = sF[w];
 
   f32x16 acc[2] = {f32x16{}, f32x16{}};
-  auto load = [&](int n, uint16_t* sx, uint16_t* sy) {
-    tile_load_async<kD, kC, 4>(X, rs, n * kC, T, sx, w, lane);
-    tile_load_async<64, kC, 4>(Y, rs, n * kC, T, sy, w, lane);
+  // Loads of a chunk: 2 + 2 instructions per wave, one more (g) for wave 0.
+  auto load = [&](int n, int buf) {
+    uint16_t* sx = sX + buf * kXT;
+    uint16_t* sy = sY + buf * kYT;
+    tile_load_async_asm<kD, kC, NW>(X, rs, n * kC, T, sx, w, lane);
+    tile_load_async_asm<kD, kC, NW>(Y, rs, n * kC, T, sy, w, lane);
     if (w == 0) {  // g of the chunk (rows past the end repeat the last row; masked below)
       const int t = n * kC + min(lane, T - 1 - n * kC);
-      __builtin_amdgcn_global_load_lds(gb + (size_t)t * H, lds_ptr(sy + kC * 64), 4, 0, 0);
+      dma_b32_asm(gb + (size_t)t * H, lds_addr(sy + kC * kD));
     }
   };
-  // S^T element j of tile nb: value 64vt + vb + c_row(j), key kb + 32nb + l32;
+  // S^T element j of tile nb: value vb + c_row(j), key kb + 32nb + l32;
   // stored at [key][value], four consecutive values per store.
   auto store = [&](int slot) {
-    uint16_t* o = out + (size_t)slot * kD * kD + 64 * vt + vb;
+    uint16_t* o = out + (size_t)slot * kD * kD + vb;
 #pragma unroll
     for (int nb = 0; nb < 2; nb++)
 #pragma unroll
@@ -154,38 +161,45 @@ __global__ __launch_bounds__(256) void gla_states_kernel(const uint16_t* __restr
             u32x2{pack_bf16x2(acc[nb][4 * jg], acc[nb][4 * jg + 1]), pack_bf16x2(acc[nb][4 * jg + 2], acc[nb][4 * jg + 3])};
       }
   };
-  constexpr int kStores = 8;  // store instructions per wave per state
-  // One step: chunk n resident in (sx, sy).  Its operands go to registers,
-  // then the next chunk's loads to the other buffer (so that no read of this
-  // buffer follows them), the update and the store of the next state.
-  // Order of a wave's vector-memory operations: loads of chunk n, then the
-  // stores of the state entering it; waiting for "all but kStores" is
-  // therefore waiting for the loads only.
-  auto step = [&](int n, const uint16_t* sx, const uint16_t* sy, uint16_t* nx, uint16_t* ny) {
+  // Order of a wave's vector-memory operations: loads of the first two
+  // chunks (the initial state's store between them), then per step i the
+  // loads of chunk i+2 and the store of a state (8 instructions).  At step
+  // i >= 2, chunk i's loads are followed by 8 + 4 + 8 = 20 operations of
+  // waves 1-7 (21 of wave 0); at steps 0 and 1 by 8 + 4 = 12 (13).  Waiting
+  // for "all but that many" is waiting for chunk i.
+  const int first = first_chunk(dir, N), stepn = dir ? -1 : 1;
+  auto chunk_of = [&](int i) { return min(max(first + stepn * i, 0), N - 1); };  // past either end: a valid chunk
+  load(chunk_of(0), 0);
+  store(first);
+  load(chunk_of(1), 1);
+  for (int i = 0; i < N; i++) {
+    const int n = first + stepn * i;
+    const int buf = i % 3;
+    const uint16_t* sx = sX + buf * kXT;
+    const uint16_t* sy = sY + buf * kYT;
     const int nv = min(kC, T - n * kC);
-    const int next = n + (dir ? -1 : 1);
-    const int next_ld = min(max(next, 0), N - 1);          // past either end: reload this chunk
+    const int next = n + stepn;
     const int next_st = (next < 0 || next >= N) ? N : next;  // past either end: the spare slot
-    wait_vmem_but<kStores>();
-    lds_barrier();  // chunk n resident; every wave is done with the previous step
-    if (w == 0) {
-      const float* sgr = reinterpret_cast<const float*>(sy + kC * 64);
-      chunk_scan(lane < nv ? sgr[lane] : 0.f, sG, lane);
-      const float gl = __shfl(sG[lane], nv - 1, 64);
-      const float f = dir ? scale * __expf(sG[lane]) : __expf(gl - sG[lane]);
-      sF[lane] = lane < nv ? f : 0.f;
-    }
-    lds_barrier();
-    const float decay = __expf(sG[nv - 1]);
+    if (i >= 2)
+      wait_vmem_but<20>();
+    else
+      wait_vmem_but<12>();
+    lds_barrier();  // chunk n resident; every wave is done with step i-1 (and its buffer)
+    // Every wave scans the chunk's g itself (no second barrier).
+    chunk_scan(lane < nv ? reinterpret_cast<const float*>(sy + kC * kD)[lane] : 0.f, wG, lane);
+    const float gl = wG[nv - 1];
+    const float f = dir ? scale * __expf(wG[lane]) : __expf(gl - wG[lane]);
+    wF[lane] = lane < nv ? f : 0.f;
+    const float decay = __expf(gl);
     bf16x8 ao[kC / 16], bo[kC / 16][2];
 #pragma unroll
     for (int ks = 0; ks < kC / 16; ks++) {
-      ao[ks] = scale_op(op_tr<64>(sy, o64, 16 * ks, vb), sF, 16 * ks, hi);
+      ao[ks] = scale_op(op_tr<kD>(sy, oD, 16 * ks, vb), wF, 16 * ks, hi);
 #pragma unroll
       for (int nb = 0; nb < 2; nb++) bo[ks][nb] = op_tr<kD>(sx, oD, 16 * ks, kb + 32 * nb);
     }
     asm volatile("" ::: "memory");
-    load(next_ld, nx, ny);
+    load(chunk_of(i + 2), (i + 2) % 3);
 #pragma unroll
     for (int nb = 0; nb < 2; nb++) acc[nb] *= decay;
 #pragma unroll
@@ -193,18 +207,8 @@ __global__ __launch_bounds__(256) void gla_states_kernel(const uint16_t* __restr
 #pragma unroll
       for (int nb = 0; nb < 2; nb++) acc[nb] = mfma32(ao[ks], bo[ks][nb], acc[nb]);
     store(next_st);
-  };
-
-  // Forward: chunks 0, 1, ..., storing the state before each update.
-  // Backward: chunks N-1, ..., 0, storing dH_{n+1} before the update.
-  const int first = first_chunk(dir, N), stepn = dir ? -1 : 1;
-  load(first, sX0, sY0);
-  store(first);
-  for (int i = 0; i < N; i += 2) {
-    const int n0 = first + stepn * i;
-    step(n0, sX0, sY0, sX1, sY1);
-    if (i + 1 < N) step(n0 + stepn, sX1, sY1, sX0, sY0);
   }
+  wait_vmem();  // the last loads (into buffers nobody reads) before the LDS goes away
 }
 
 // ------------------------------------------------------------ per-chunk stage
@@ -429,8 +433,8 @@ hipError_t launch_gla_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* 
   uint16_t* hs = (uint16_t*)workspace;
   uint16_t* dhs = hs + (size_t)B * H * (N + 1) * kD * kD;
   float* dG = (float*)(dhs + (size_t)B * H * (N + 1) * kD * kD);
-  hipLaunchKernelGGL(gla_states_kernel, dim3(B * H, kD / 64, 2), dim3(256), 0, stream, q, k, v, dout, g, hs, dhs, T,
-                     H, scale);
+  hipLaunchKernelGGL(gla_states_kernel, dim3(B * H, 1, 2), dim3(512), 0, stream, q, k, v, dout, g, hs, dhs, T, H,
+                     scale);
   hipLaunchKernelGGL(gla_dqkv_kernel, dim3(N, B * H), dim3(512), 0, stream, q, k, v, dout, g, hs, dhs, dq, dk, dv,
                      dG, T, H, scale);
   hipLaunchKernelGGL(gla_dg_kernel, dim3(B * H), dim3(256), 0, stream, dG, dg, T, H);
