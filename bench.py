@@ -390,6 +390,69 @@ def bench_smla(args, bd, torch):
     }), flush=True)
 
 
+def bench_sweep(args, bd, torch):
+    """Every workload, causal setting and dQ path: each call of the path timed
+    on its own with HIP events (20 warm-up, 50 timed calls, medians), a 512 MB
+    buffer written before each timed call so that no input is still in the
+    256 MB MALL.  One JSON line per case."""
+    from attention_backward_fwd_amd.synthetic import WORKLOADS, workload_inputs
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(512 << 18, dtype=torch.float32, device=dev)
+    n_warm, n_time = 20, 50
+
+    def timed(fn):
+        for _ in range(n_warm):
+            fn()
+        ts = []
+        for _ in range(n_time):
+            flush.fill_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            ts.append((e0, e1))
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in ts)[n_time // 2]
+
+    for w in WORKLOADS.values():
+        inp = {n: t.to(dev) for n, t in workload_inputs(w).items()}
+        q, k, v, do = inp["q"], inp["k"], inp["v"], inp["do"]
+        sh = bd.shape_of(q, k)
+        o = torch.empty_like(q)
+        lse = torch.empty((w.batch, w.heads_q, w.seqlen), dtype=torch.float32, device=dev)
+        nq = q.numel()
+        nkv = k.numel()
+        rows = w.batch * w.heads_q * w.seqlen
+        for causal in w.causal:
+            for path in w.paths:
+                ua = path == "atomic"
+                bb = bd.BwdBuffers(q, k, causal, ua)
+                t_fwd = timed(lambda: bd.attn_fwd(q, k, v, o, lse, sh, w.scale, causal, stream))
+                t_pre = timed(lambda: bd.attn_bwd_preprocess(o, do, bb.delta, bb.dq_accum if ua else None, sh, stream))
+                t_bwd = timed(lambda: bd.attn_bwd(q, k, v, do, lse, bb.delta, bb.dq_accum, bb.dk, bb.dv, bb.workspace,
+                                                  sh, w.scale, causal, ua, stream))
+                t_post = timed(lambda: bd.attn_bwd_postprocess(bb.dq_accum, bb.workspace, bb.dq, bb.dk, bb.dv, sh,
+                                                               stream))
+                fwd_f, bwd_f = flops(w, causal)
+                pre_bytes = 4 * nq + 4 * rows + (4 * nq if ua else 0)
+                post_bytes = 6 * nq + ((8 * nq + 4 * nkv) if w.groups > 1 else 0)
+                t_back = t_pre + t_bwd + t_post
+                print(json.dumps({
+                    "mode": "sweep", "workload": w.name, "causal": causal, "dq_path": path,
+                    "fwd_ms": round(t_fwd, 4), "fwd_tflops": round(fwd_f / t_fwd / 1e9, 1),
+                    "preprocess_ms": round(t_pre, 4), "preprocess_gbs": round(pre_bytes / t_pre / 1e6, 1),
+                    "bwd_call_ms": round(t_bwd, 4), "bwd_call_tflops": round(bwd_f / t_bwd / 1e9, 1),
+                    "postprocess_ms": round(t_post, 4), "postprocess_gbs": round(post_bytes / t_post / 1e6, 1),
+                    "backward_ms": round(t_back, 4), "backward_tflops": round(bwd_f / t_back / 1e9, 1),
+                    "backward_pct_of_peak": round(100 * bwd_f / t_back / 1e9 / PEAK_BF16_TFLOPS, 2),
+                    "fwd_bwd_tflops": round((fwd_f + bwd_f) / (t_fwd + t_back) / 1e9, 1),
+                    "timing": f"median of {n_time} calls after {n_warm} warm-up, HIP events, MALL flushed"}),
+                    flush=True)
+                del bb
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -415,6 +478,8 @@ def main():
     ap.add_argument("--smla", action="store_true",
                     help="instead of the attention step, time sparse MLA forward + backward "
                          "(4096 tokens, 32 heads, 2048 entries per token)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time fwd / preprocess / bwd / postprocess separately for every workload and dQ path")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -438,6 +503,9 @@ def main():
         print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "launches": 3}))
         return
 
+    if args.sweep:
+        bench_sweep(args, bd, torch)
+        return
     if args.varlen:
         bench_varlen(args, bd, torch)
         return
@@ -463,7 +531,7 @@ def main():
     bb = bd.BwdBuffers(q, k, causal, use_atomic)
     stream = torch.cuda.current_stream()
 
-    ev = {n: [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)] for n in ("fwd", "bwd")}
+    ev = {n: [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)] for n in ("fwd", "bwd", "back")}
 
     def step(i=None):
         if i is not None:
@@ -471,6 +539,7 @@ def main():
         bd.attn_fwd(q, k, v, o, lse, sh, w.scale, causal, stream)
         if i is not None:
             ev["fwd"][2 * i + 1].record(stream)
+            ev["back"][2 * i].record(stream)
         bd.attn_bwd_preprocess(o, do, bb.delta, bb.dq_accum if use_atomic else None, sh, stream)
         if i is not None:
             ev["bwd"][2 * i].record(stream)
@@ -479,6 +548,8 @@ def main():
         if i is not None:
             ev["bwd"][2 * i + 1].record(stream)
         bd.attn_bwd_postprocess(bb.dq_accum, bb.workspace, bb.dq, bb.dk, bb.dv, sh, stream)
+        if i is not None:
+            ev["back"][2 * i + 1].record(stream)
 
     for _ in range(args.warmup):
         step()
@@ -494,6 +565,7 @@ def main():
     value = (fwd_f + bwd_f) * args.steps / elapsed / 1e12
     fwd_ms = sum(ev["fwd"][2 * i].elapsed_time(ev["fwd"][2 * i + 1]) for i in range(args.steps)) / args.steps
     bwd_ms = sum(ev["bwd"][2 * i].elapsed_time(ev["bwd"][2 * i + 1]) for i in range(args.steps)) / args.steps
+    back_ms = sum(ev["back"][2 * i].elapsed_time(ev["back"][2 * i + 1]) for i in range(args.steps)) / args.steps
     bwd_tflops = bwd_f / (bwd_ms * 1e-3) / 1e12
     path = "atomic" if use_atomic else "split"
     kernel = "bwd_kernel" if use_atomic else "bwd_kernel + dq_sum_kernel"
@@ -518,6 +590,8 @@ def main():
         "fwd_kernel_ms": round(fwd_ms, 4),
         "fwd_tflops": round(fwd_f / (fwd_ms * 1e-3) / 1e12, 3),
         "bwd_kernel_ms": round(bwd_ms, 4),
+        "backward_ms": round(back_ms, 4),
+        "backward_tflops": round(bwd_f / (back_ms * 1e-3) / 1e12, 3),
         "roofline": {"kernel": kernel, "bound": "mfma", "achieved": round(bwd_tflops, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic(w.name, path)},
