@@ -255,17 +255,21 @@ __global__ __launch_bounds__(512) void gla_dqkv_kernel(const uint16_t* __restric
   const Lofs<kD> oD(lane);
   const Lofs<kC> oC(lane);
 
-  // Token tiles and g first, state tiles last, all by LDS-DMA.
-  tile_load_async<kD, kC, NW>(q + base, rs, n * kC, T, sQ, w, lane);
-  tile_load_async<kD, kC, NW>(k + base, rs, n * kC, T, sK, w, lane);
-  tile_load_async<kD, kC, NW>(v + base, rs, n * kC, T, sV, w, lane);
-  tile_load_async<kD, kC, NW>(dout + base, rs, n * kC, T, sO, w, lane);
+  // Token tiles and g first, state tiles last, all by LDS-DMA issued as
+  // inline assembly: the compiler adds no waits of its own, so the state
+  // tiles keep arriving during the scan and the score products; the explicit
+  // waits below (all but the 8 state-tile loads of this wave, then all) are
+  // the only ones.
+  tile_load_async_asm<kD, kC, NW>(q + base, rs, n * kC, T, sQ, w, lane);
+  tile_load_async_asm<kD, kC, NW>(k + base, rs, n * kC, T, sK, w, lane);
+  tile_load_async_asm<kD, kC, NW>(v + base, rs, n * kC, T, sV, w, lane);
+  tile_load_async_asm<kD, kC, NW>(dout + base, rs, n * kC, T, sO, w, lane);
   if (w == 0) {  // rows past the end repeat the last row; masked in the scan
     const int t = n * kC + min(lane, nv - 1);
-    __builtin_amdgcn_global_load_lds(g + ((size_t)b * T + t) * H + h, lds_ptr(sGr), 4, 0, 0);
+    dma_b32_asm(g + ((size_t)b * T + t) * H + h, lds_addr(sGr));
   }
-  tile_load_async<kD, kD, NW>(hs + st_off, kD, 0, kD, sH, w, lane);
-  tile_load_async<kD, kD, NW>(dhs + st_off, kD, 0, kD, sDH, w, lane);
+  tile_load_async_asm<kD, kD, NW>(hs + st_off, kD, 0, kD, sH, w, lane);
+  tile_load_async_asm<kD, kD, NW>(dhs + st_off, kD, 0, kD, sDH, w, lane);
   wait_vmem_but<8>();
   lds_barrier();
   if (w == 0) chunk_scan(lane < nv ? sGr[lane] : 0.f, sG, lane);
@@ -335,20 +339,6 @@ __global__ __launch_bounds__(512) void gla_dqkv_kernel(const uint16_t* __restric
   ak += fkv * sk;
   av += fkv * sv;
 
-  // Stores: lane = token, four consecutive features per 8-byte store.
-  const size_t orow = base + (size_t)(n * kC + tok) * rs + 32 * fb;
-  if (tok < nv) {
-#pragma unroll
-    for (int jg = 0; jg < 4; jg++) {
-      const int f0 = c_row(4 * jg, hi);
-      *reinterpret_cast<u32x2*>(dq + orow + f0) = u32x2{pack_bf16x2(aq[4 * jg], aq[4 * jg + 1]),
-                                                        pack_bf16x2(aq[4 * jg + 2], aq[4 * jg + 3])};
-      *reinterpret_cast<u32x2*>(dk + orow + f0) = u32x2{pack_bf16x2(ak[4 * jg], ak[4 * jg + 1]),
-                                                        pack_bf16x2(ak[4 * jg + 2], ak[4 * jg + 3])};
-      *reinterpret_cast<u32x2*>(dv + orow + f0) = u32x2{pack_bf16x2(av[4 * jg], av[4 * jg + 1]),
-                                                        pack_bf16x2(av[4 * jg + 2], av[4 * jg + 3])};
-    }
-  }
   // q.dq and k.dk over this wave's 32 features: in-lane sums, the other
   // lane half, then one partial per (feature block, token) in LDS.
   float pq = 0.f, pk = 0.f;
@@ -372,11 +362,44 @@ __global__ __launch_bounds__(512) void gla_dqkv_kernel(const uint16_t* __restric
     sdG[0][fb][tok] = pq;
     sdG[1][fb][tok] = pk;
   }
-  lds_barrier();
+  lds_barrier();  // every wave is done with the state tiles; the q.dq / k.dk partials are complete
+  // The outputs go out as whole rows: staged as bf16 [token][feature] tiles
+  // (swizzled) in the state tiles' space, then copied with 16-byte stores,
+  // each 256-byte row written by 16 consecutive lanes of one instruction.
+  // (Rows assembled from 8-byte pieces of four waves reached HBM as partial
+  // line writes, about 1.8 times the output bytes.)
+  uint16_t* stq = sH;
+  uint16_t* stk = sH + kC * kD;
+  uint16_t* stv = sDH;
+#pragma unroll
+  for (int jg = 0; jg < 4; jg++) {
+    const int o = swz_off<kD>(tok, 32 * fb + c_row(4 * jg, hi));
+    *reinterpret_cast<u32x2*>(stq + o) = u32x2{pack_bf16x2(aq[4 * jg], aq[4 * jg + 1]),
+                                               pack_bf16x2(aq[4 * jg + 2], aq[4 * jg + 3])};
+    *reinterpret_cast<u32x2*>(stk + o) = u32x2{pack_bf16x2(ak[4 * jg], ak[4 * jg + 1]),
+                                               pack_bf16x2(ak[4 * jg + 2], ak[4 * jg + 3])};
+    *reinterpret_cast<u32x2*>(stv + o) = u32x2{pack_bf16x2(av[4 * jg], av[4 * jg + 1]),
+                                               pack_bf16x2(av[4 * jg + 2], av[4 * jg + 3])};
+  }
   if (w == 0 && lane < nv) {
     const float a = ((sdG[0][0][lane] + sdG[0][1][lane]) + (sdG[0][2][lane] + sdG[0][3][lane]));
     const float c = ((sdG[1][0][lane] + sdG[1][1][lane]) + (sdG[1][2][lane] + sdG[1][3][lane]));
     dG[(size_t)bh * T + n * kC + lane] = a - c;
+  }
+  lds_barrier();  // staged tiles complete
+  {
+    const int cs = lane & 15;
+#pragma unroll
+    for (int jj = 0; jj < 2; jj++) {
+      const int r = 4 * (w + NW * jj) + (lane >> 4);  // token row of this lane
+      if (r < nv) {
+        const int o = swz_off<kD>(r, 8 * cs);
+        const size_t g0 = base + (size_t)(n * kC + r) * rs + 8 * cs;
+        *reinterpret_cast<u32x4*>(dq + g0) = *reinterpret_cast<const u32x4*>(stq + o);
+        *reinterpret_cast<u32x4*>(dk + g0) = *reinterpret_cast<const u32x4*>(stk + o);
+        *reinterpret_cast<u32x4*>(dv + g0) = *reinterpret_cast<const u32x4*>(stv + o);
+      }
+    }
   }
 }
 
