@@ -37,21 +37,22 @@ def flops(w, causal):
 
 
 BWD_SOURCES = ("bwd.hip", "common.h", "kernels.h")  # what the backward kernel is built from
+GLA_SOURCES = ("gla.hip", "common.h", "kernels.h")  # what the GLA chunk backward is built from
 
 
-def kernel_source_hash():
-    """Hash of the backward kernel's sources: recorded counters stay valid
-    until one of these files changes."""
+def kernel_source_hash(sources=BWD_SOURCES):
+    """Hash of a kernel's sources: recorded counters stay valid until one of
+    these files changes."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "attention_backward_fwd_amd", "csrc")
-    for name in BWD_SOURCES:
+    for name in sources:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload, path):
-    """HBM bytes per bwd launch from the committed counter summary, if it still
+def recorded_traffic(workload, path, sources=BWD_SOURCES):
+    """HBM bytes per launch from the committed counter summary, if it still
     describes the current kernel sources; else None."""
     fn = os.path.join(ROOT, "profiles", "traffic.json")
     try:
@@ -60,7 +61,7 @@ def recorded_traffic(workload, path):
     except (OSError, ValueError):
         return None
     entry = rec.get(f"{workload}/{path}")
-    if not entry or entry.get("source_hash") != kernel_source_hash():
+    if not entry or entry.get("source_hash") != kernel_source_hash(sources):
         return None
     return entry.get("bytes_per_launch")
 
@@ -299,7 +300,8 @@ def bench_gla(args, bd, torch):
         "bwd_ms": round(ms, 4), "tokens_per_s": round(b * t / (ms * 1e-3), 1),
         "mfma_tflops": round(flop / (ms * 1e-3) / 1e12, 3),
         "roofline": {"kernel": "gla_states + gla_dqkv + gla_dg", "bound": "hbm", "achieved": round(gbs, 1),
-                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": recorded_traffic(w["name"], "chunk_bwd", GLA_SOURCES)},
         **({"cpu_baseline": cpu} if cpu else {}),
     }), flush=True)
 
