@@ -38,6 +38,8 @@ def flops(w, causal):
 
 BWD_SOURCES = ("bwd.hip", "common.h", "kernels.h")  # what the backward kernel is built from
 GLA_SOURCES = ("gla.hip", "common.h", "kernels.h")  # what the GLA chunk backward is built from
+SMLA_SOURCES = ("smla.hip", "common.h", "kernels.h")  # ... the sparse MLA kernels
+MERGE_SOURCES = ("merge.hip", "common.h", "kernels.h")  # ... the partial-merge kernel
 
 
 def kernel_source_hash(sources=BWD_SOURCES):
@@ -148,7 +150,7 @@ def bench_merge(args, w, bd, torch):
                       "config": {"workload": w.name, "parts": n},
                       "roofline": {"kernel": "merge_kernel", "bound": "hbm", "achieved": round(gbs, 1),
                                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                                   "traffic": None},
+                                   "traffic": recorded_traffic(w.name, f"merge{n}", MERGE_SOURCES)},
                       **({"cpu_baseline": cpu} if cpu else {})}), flush=True)
 
 
@@ -235,7 +237,8 @@ def bench_varlen(args, bd, torch):
         "bwd_kernel_ms": round(bwd_ms, 4),
         "roofline": {"kernel": "bwd_kernel (packed)" + ("" if use_atomic else " + dq_sum_varlen_kernel"),
                      "bound": "mfma", "achieved": round(bwd_tflops, 3), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": recorded_traffic(spec["name"], path)},
         **({"cpu_baseline": cpu} if cpu else {}),
     }), flush=True)
 
@@ -387,7 +390,8 @@ def bench_smla(args, bd, torch):
         "atomics": {"count": n_atomics, "per_s": round(n_atomics / (bwd_ms * 1e-3) / 1e9, 1), "unit": "G/s"},
         "roofline": {"kernel": "smla_bwd_kernel", "bound": "mfma", "achieved": round(bwd_f / (bwd_ms * 1e-3) / 1e12, 3),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(bwd_f / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(bwd_f / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": recorded_traffic(w["name"], "bwd", SMLA_SOURCES)},
         **({"cpu_baseline": cpu} if cpu else {}),
     }), flush=True)
 
