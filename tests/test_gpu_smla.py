@@ -125,3 +125,36 @@ def test_smla_bwd_full_size():
     assert r <= TOL
     assert err_v <= 2e-2 and err_k <= 2e-2
     assert torch.all(torch.isfinite(gpu["dkv"].float())) and torch.all(torch.isfinite(gpu["dq"].float()))
+
+
+def _gappy_indices(t, tk, k, seed):
+    """Lists whose second 32-entry tile holds no valid entry, with unused and
+    out-of-range entries scattered through the other tiles and valid entries
+    after the gap."""
+    rng = np.random.default_rng(seed)
+    idx = np.stack([rng.choice(tk, size=k, replace=False) for _ in range(t)]).astype(np.int32)
+    idx[:, 32:64] = -1                                        # a whole tile of unused slots
+    mask = rng.random((t, k)) < 0.2
+    idx[mask] = -1                                            # scattered unused slots
+    idx[:, 5] = tk + 11                                       # out of range
+    idx[:, 70] = -3                                           # another negative sentinel
+    return idx
+
+
+def test_smla_gaps_and_scattered_sentinels():
+    t, tk, h, k = 6, 400, 40, 130
+    inp = smla_inputs(t, tk, h, seed=21)
+    idx = _gappy_indices(t, tk, k, seed=22)
+    f = {n: x.double().numpy() for n, x in inp.items()}
+    ro, rl = sm.sparse_mla_fwd(f["q"], f["kv"], idx, SCALE)
+    o, lse = bd.sparse_mla_forward(inp["q"].cuda(), inp["kv"].cuda(), torch.from_numpy(idx).cuda(), SCALE)
+    torch.cuda.synchronize()
+    _check(o, lse, ro, rl, "smla fwd gaps")
+    ref = sm.sparse_mla_bwd(f["q"], f["kv"], idx, f["do"], SCALE)
+    gpu = _run_bwd(inp, idx)
+    ratios = {n: err_ratio(np64(gpu[n]), ref[n]) for n in ("dq", "dkv")}
+    say("smla bwd gaps: " + " ".join(f"{n}={r:.2e}" for n, r in ratios.items()))
+    for n, r in ratios.items():
+        assert r <= TOL, (n, r)
+    unused = np.all(ref["dkv"] == 0.0, axis=1)
+    assert np.all(np64(gpu["dkv"])[unused] == 0.0)
