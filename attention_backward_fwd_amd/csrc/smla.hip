@@ -377,8 +377,12 @@ __global__ __launch_bounds__(256) void smla_post_kernel(const float* __restrict_
 //                        blocks w, w+4, .. of the 18 blocks of 32)
 //   dKV   = scale dS^T Q + P^T dO   for the tile's 32 entries (dS^T, P^T
 //                        through LDS as [entry][head]), added to the fp32
-//                        accumulator row of each valid entry with atomics.
-// dQ (bf16) is written at the end.
+//                        accumulator row of each valid entry with buffer
+//                        atomics that stay in flight into the next tile.
+// dQ (bf16) is written at the end.  As in the forward, tokens are dealt to
+// the XCDs round-robin and tiles past the last valid entry are skipped.  The
+// atomic rate of the memory system (~340 G fp32 adds/s), not the matrix
+// work, bounds this kernel: 576 adds per (token, valid entry).
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void smla_bwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const uint16_t* __restrict__ dout,
     const int* __restrict__ idx, const float* __restrict__ lse, const float* __restrict__ delta,

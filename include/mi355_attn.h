@@ -295,7 +295,13 @@ int gla_chunk_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const
  *   o [tokens, heads, 512] bf16, lse [tokens, heads] fp32 (outputs; every
  *   element written).  q, kv, o 16-byte aligned; indices and lse 4-byte.
  * Heads are processed in tiles of 32 (a smaller or ragged head count is
- * masked inside the tile).
+ * masked inside the tile).  Errors, all detected on the host before any
+ * launch: ATTN_ERR_NULL_PTR, ATTN_ERR_BAD_SHAPE (a size < 1),
+ * ATTN_ERR_HEAD_DIM (dims other than 576 / 512), ATTN_ERR_RANGE (topk > 8192,
+ * kv_tokens > 524288, tokens * heads * 576 or tokens * topk >= 2^31, a
+ * softmax_scale that is not finite and > 0), ATTN_ERR_ALIGN; ATTN_ERR_HIP if
+ * the launch fails.  Index values are not checked (they live on the device):
+ * anything outside [0, kv_tokens) is an unused slot.
  */
 typedef struct smla_shape {
   int32_t tokens;    /* T >= 1 query tokens */
