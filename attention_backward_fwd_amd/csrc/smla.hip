@@ -8,15 +8,16 @@
 //   LSE = log sum_i exp(s_i)  (O = 0, LSE = -inf without a valid entry)
 //
 // Forward kernel: one workgroup (4 waves) per (token, 32-head tile).  Per
-// tile of 32 entries the key rows are gathered by LDS-DMA (two tiles ahead,
-// three buffers) into five swizzled sub-tiles (four of 128 channels, one of
-// 64); the waves split the 576-channel reduction of S^T = KV Q^T (9 k-steps
-// each, query operands in registers) and sum the four partials through LDS
-// in a fixed order, so that every wave holds the same scores and runs the
-// same online softmax (a head per lane); wave w then accumulates O^T rows
-// 128w .. 128w+127 = V^T P^T from its own value sub-tile (transposing reads)
-// and the probabilities in registers.  Tiles past the last valid entry of
-// the list are skipped.
+// tile of 32 entries the key rows are gathered by LDS-DMA (one tile ahead)
+// into five swizzled sub-tiles (four of 128 channels, one of 64).  Wave w
+// owns heads h0 + 16(w & 1) .. +15 and entries 16(w >> 1) .. +15 of each
+// tile and computes their scores S^T = KV Q^T over all 576 channels with
+// 16x16x32 products (query operands in registers); the two waves sharing a
+// head set swap their tile maxima through LDS (one common softmax reference
+// per head, moved lazily) and their probabilities (each needs all 32
+// entries for its 256 output channels O^T = V^T P^T, transposing reads).
+// Tiles past the last valid entry of the list are skipped; tokens are dealt
+// to the XCDs round-robin, longest lists first.
 #include "common.h"
 #include "kernels.h"
 
@@ -163,173 +164,139 @@ __device__ __forceinline__ int live_tiles(const int* idx_t, int K, int Tk, int* 
   return __builtin_amdgcn_readfirstlane((last + kKT) / kKT);
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void smla_fwd_kernel(
+// Forward kernel.  Two gather buffers (one tile ahead) keep the LDS at
+// ~78 KB and the registers under 256, so that two workgroups share a CU.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void smla_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int* __restrict__ idx,
     uint16_t* __restrict__ o, float* __restrict__ lse, int T, int Tk, int H, int K, float scale) {
-  constexpr int kTile = 4 * kSub + kKT * 64;  // elements of a gathered 32 x 576 tile
-  // Three gathered tiles: tile i in buffer i % 3, gathered two tiles ahead.
-  __shared__ __attribute__((aligned(16))) uint16_t sKV[3 * kTile];
-  __shared__ __attribute__((aligned(16))) float sSp[4 * 16 * 64];  // S^T partials (store_partial)
-  // Raw entry lists (tile i in slot i % 4), loaded three tiles ahead.
-  __shared__ __attribute__((aligned(16))) int sIdx[4][kKT];
+  constexpr int kTile = 4 * kSub + kKT * 64;
+  __shared__ __attribute__((aligned(16))) uint16_t sKV[2 * kTile];
+  __shared__ __attribute__((aligned(16))) int sIdx[3][kKT];
   __shared__ int sRed[4];
+  __shared__ float sMx[4][64];
+  __shared__ __attribute__((aligned(16))) u32x2 sPx[4][64];
+  __shared__ float sL[4][64];
 
-  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), hi = lane >> 5;
-  const int l32 = lane & 31;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, r = lane & 15;
+  const int hh = w & 1, eh = w >> 1, partner = w ^ 2;
   const int n_ht = (H + kHT - 1) / kHT;
-  // Workgroups go to the XCDs round-robin, so consecutive ids spread a run
-  // of tokens over all of them (list lengths, and so costs, change slowly
-  // along the tokens); the last tokens, whose lists are usually the
-  // longest, start first.
   const int id = blockIdx.x;
   const int t = __builtin_amdgcn_readfirstlane(T - 1 - id / n_ht), h0 = __builtin_amdgcn_readfirstlane((id % n_ht) * kHT);
   const int* idx_t = idx + (size_t)t * K;
 
-  // Query operands of wave w's share of S^T (channels 144w .. 144w+143) in
-  // registers: lane (head l32, half hi) holds channels d0 + 4hi .. +3 and
-  // d0 + 8 + 4hi .. +3 of each 16-channel step d0 (heads past H repeat the
-  // last one).
-  bf16x8 bq[9];
+  // Query operands (B of the 16x16x32 product, k = channel, n = head):
+  // lane (head 16hh + r, group g) holds channels 32ks + 8g .. +7.
+  bf16x8 bq[18];
   {
-    const uint16_t* qr = q + ((size_t)t * H + min(h0 + l32, H - 1)) * kQK + 144 * w + 4 * hi;
+    const uint16_t* qr = q + ((size_t)t * H + min(h0 + 16 * hh + r, H - 1)) * kQK + 8 * g;
 #pragma unroll
-    for (int kk = 0; kk < 9; kk++) {
-      const u32x2 a = *reinterpret_cast<const u32x2*>(qr + 16 * kk);
-      const u32x2 b = *reinterpret_cast<const u32x2*>(qr + 16 * kk + 8);
-      bq[kk] = __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
-    }
+    for (int ks = 0; ks < 18; ks++) bq[ks] = *reinterpret_cast<const bf16x8*>(qr + 32 * ks);
+    // Complete these loads here, once: waits the compiler would otherwise
+    // place at their first use inside the tile loop would run every tile
+    // and drain the gathers in flight.
+    asm volatile("s_waitcnt vmcnt(0)"
+                 : "+v"(bq[0]), "+v"(bq[1]), "+v"(bq[2]), "+v"(bq[3]), "+v"(bq[4]), "+v"(bq[5]), "+v"(bq[6]),
+                   "+v"(bq[7]), "+v"(bq[8]), "+v"(bq[9]), "+v"(bq[10]), "+v"(bq[11]), "+v"(bq[12]), "+v"(bq[13]),
+                   "+v"(bq[14]), "+v"(bq[15]), "+v"(bq[16]), "+v"(bq[17]));
   }
   const int n_tiles = live_tiles(idx_t, K, Tk, sRed, w, lane);
   const GatherCols gcols = gather_cols(w, lane);
-  // All loads of the loop (entry lists, gathers) are LDS-DMA issued as
-  // inline assembly; the waits at the start of each tile cover them.
   if (n_tiles > 0) {
     load_entries_async(idx_t, 0, K, sIdx[0], w, lane);
     if (n_tiles > 1) load_entries_async(idx_t, 1, K, sIdx[1], w, lane);
     wait_vmem();
     lds_barrier();
     gather_rows_async(kv, sIdx[0], 0, K, Tk, sKV, gcols, w, lane);
-    if (n_tiles > 2) load_entries_async(idx_t, 2, K, sIdx[2], w, lane);
-    if (n_tiles > 1) gather_rows_async(kv, sIdx[1], kKT, K, Tk, sKV + kTile, gcols, w, lane);
   }
-
-  // Per-lane byte offsets inside a gathered tile, fixed for the kernel:
-  // the row reads of the S^T product (two 8-byte halves per k-step) and the
-  // transposing reads of the O^T product (sub-tile w, two per (kk, dt)).
-  uint32_t offS[9][2], offO[2][4][2];
+  // Per-lane byte offsets in a gathered tile.  S: row 16eh + r, channels
+  // 32ks + 8g .. +7 (one 16-byte read).  O: V^T operand of channel block cb
+  // (channels 256eh + 16cb ..), entries 4g .. 4g+3 and 16 + 4g .. (the
+  // order of the probabilities: this wave's result rows for half eh, the
+  // partner's for the other half), transposing reads.
+  uint32_t offA[18], offV[16][2];
 #pragma unroll
-  for (int kk = 0; kk < 9; kk++) {
-    const int k0 = 144 * w + 16 * kk;
-    offS[kk][0] = 2u * (uint32_t)sub_off(l32, k0 + 4 * hi);
-    offS[kk][1] = 2u * (uint32_t)sub_off(l32, k0 + 8 + 4 * hi);
-  }
-  {
-    const int L = lane & 15, gp = (lane >> 4) & 1;
+  for (int ks = 0; ks < 18; ks++) offA[ks] = 2u * (uint32_t)sub_off(16 * eh + r, 32 * ks + 8 * g);
 #pragma unroll
-    for (int kk = 0; kk < 2; kk++)
-#pragma unroll
-      for (int dt = 0; dt < 4; dt++) {
-        const int col = 32 * dt + 16 * gp + 4 * (L & 3);
-        offO[kk][dt][0] = 2u * (uint32_t)(w * kSub + swz_off<128>(16 * kk + 4 * hi + (L >> 2), col));
-        offO[kk][dt][1] = 2u * (uint32_t)(w * kSub + swz_off<128>(16 * kk + 8 + 4 * hi + (L >> 2), col));
-      }
+  for (int cb = 0; cb < 16; cb++) {
+    const int ch0 = 256 * eh + 16 * cb, st = ch0 >> 7, c = (ch0 & 127) + 4 * (r & 3);
+    offV[cb][0] = 2u * (uint32_t)(st * kSub + swz_off<128>(4 * g + (r >> 2), c));
+    offV[cb][1] = 2u * (uint32_t)(st * kSub + swz_off<128>(16 + 4 * g + (r >> 2), c));
   }
 
   const float c = scale * kLog2e;
-  f32x16 oacc[4];
+  f32x4 oacc[16];
 #pragma unroll
-  for (int dt = 0; dt < 4; dt++) oacc[dt] = f32x16{};
-  // Online softmax in log2 units with a lazily moved reference: M moves
-  // only when a tile's maximum exceeds it by more than kLazy (so the
-  // exponentials stay below 2^kLazy); O and l are rescaled only then.  The
-  // result does not depend on the reference.
+  for (int cb = 0; cb < 16; cb++) oacc[cb] = f32x4{};
   constexpr float kLazy = 8.f;
   float M = -INFINITY, l_i = 0.f;
 
   for (int it = 0; it < n_tiles; it++) {
-    const uint16_t* cKV = sKV + (it % 3) * kTile;
-    // Tile it resident: it was gathered before the 9 gather instructions of
-    // tile it+1 (the latest loads of this wave, when there is a tile it+1),
-    // and so was the list of tile it+2.
+    const uint16_t* cKV = sKV + (it & 1) * kTile;
+    wait_vmem();
+    lds_barrier();
+    if (it + 2 < n_tiles) load_entries_async(idx_t, it + 2, K, sIdx[(it + 2) % 3], w, lane);
     if (it + 1 < n_tiles)
-      wait_vmem_but<9>();
-    else
-      wait_vmem();
-    lds_barrier();  // tile it and the list of tile it+2 resident; every wave is done with tile it-1
-    if (it + 3 < n_tiles) load_entries_async(idx_t, it + 3, K, sIdx[(it + 3) % 4], w, lane);
-    if (it + 2 < n_tiles)
-      gather_rows_async(kv, sIdx[(it + 2) % 4], (it + 2) * kKT, K, Tk, sKV + ((it + 2) % 3) * kTile, gcols, w, lane);
-    // Validity of the tile's 32 entries as one wave-uniform mask.
-    const int* cl = sIdx[it % 4];
+      gather_rows_async(kv, sIdx[(it + 1) % 3], (it + 1) * kKT, K, Tk, sKV + ((it + 1) & 1) * kTile, gcols, w, lane);
+    const int* cl = sIdx[it % 3];
     const uint32_t vmask =
         (uint32_t)__builtin_amdgcn_ballot_w64(lane < kKT ? entry_ok(cl, lane, it * kKT, K, Tk) : false);
-    // S^T partial over channels 144w .. 144w+143.
-    f32x16 sp = f32x16{};
+    f32x4 s = f32x4{};
 #pragma unroll
-    for (int kk = 0; kk < 9; kk++) {
-      const u32x2 a = *reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(cKV) + offS[kk][0]);
-      const u32x2 b = *reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(cKV) + offS[kk][1]);
-      sp = mfma32(__builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]}), bq[kk], sp);
-    }
-    store_partial(lds_addr(sSp), w, lane, sp);
-    lds_barrier();
-    f32x16 s = sum_partials(lds_addr(sSp), lane);
-    // Unused slots and entries past the end of the list: -inf.
+    for (int ks = 0; ks < 18; ks++) s = mfma16(lds_b128_at(cKV, offA[ks]), bq[ks], s);
     if (vmask != 0xFFFFFFFFu) {
-      const uint32_t ml = vmask >> (4 * hi);
+      const uint32_t ml = vmask >> (16 * eh + 4 * g);
 #pragma unroll
-      for (int j = 0; j < 16; j++)
-        if (!((ml >> (8 * (j >> 2) + (j & 3))) & 1u)) s[j] = -INFINITY;
+      for (int j = 0; j < 4; j++)
+        if (!((ml >> j) & 1u)) s[j] = -INFINITY;
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 16; j++) mx = fmaxf(mx, s[j]);
-    const float mxc = xhalf_max(mx) * c;
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    sMx[w][lane] = mx;
+    lds_barrier();
+    const float mxc = fmaxf(mx, sMx[partner][lane]) * c;
     if (__builtin_amdgcn_ballot_w64(mxc > M + kLazy) != 0) {
       const float Mn = fmaxf(M, mxc);
       const float alpha = Mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(M - Mn);
       l_i *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < 4; dt++) oacc[dt] *= alpha;
+      for (int cb = 0; cb < 16; cb++) oacc[cb] *= alpha;
       M = Mn;
     }
     const float mc = M == -INFINITY ? 0.f : M;
-    float rs = 0.f;
+    float e[4];
 #pragma unroll
-    for (int j = 0; j < 16; j++) {
-      const float e = __builtin_amdgcn_exp2f(fmaf(s[j], c, -mc));
-      s[j] = e;
-      rs += e;
+    for (int j = 0; j < 4; j++) {
+      e[j] = __builtin_amdgcn_exp2f(fmaf(s[j], c, -mc));
+      l_i += e[j];
     }
-    l_i += rs;
-    bf16x8 pb[2];
+    const u32x2 pw = u32x2{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3])};
+    sPx[w][lane] = pw;
+    lds_barrier();
+    const u32x2 pp = sPx[partner][lane];
+    const u32x2 p0 = eh ? pp : pw, p1 = eh ? pw : pp;
+    const bf16x8 bp = __builtin_bit_cast(bf16x8, u32x4{p0[0], p0[1], p1[0], p1[1]});
 #pragma unroll
-    for (int kk = 0; kk < 2; kk++)
-      pb[kk] = pack8(s[8 * kk + 0], s[8 * kk + 1], s[8 * kk + 2], s[8 * kk + 3], s[8 * kk + 4], s[8 * kk + 5],
-                     s[8 * kk + 6], s[8 * kk + 7]);
-    // O^T rows 128w + 32dt .. += V^T P^T (value sub-tile w).
-#pragma unroll
-    for (int kk = 0; kk < 2; kk++)
-#pragma unroll
-      for (int dt = 0; dt < 4; dt++)
-        oacc[dt] = mfma32(lds_tr8_at(cKV, offO[kk][dt][0], offO[kk][dt][1]), pb[kk], oacc[dt]);
+    for (int cb = 0; cb < 16; cb++) oacc[cb] = mfma16(lds_tr8_at(cKV, offV[cb][0], offV[cb][1]), bp, oacc[cb]);
   }
 
-  const float l_tot = xhalf_sum(l_i);
+  // Row sums: this wave's 16 entries (the four lane groups), then the
+  // partner's (same reference).
+  l_i += __shfl_xor(l_i, 16, 64);
+  l_i += __shfl_xor(l_i, 32, 64);
+  sL[w][lane] = l_i;
+  lds_barrier();
+  const float l_tot = eh ? sL[partner][lane] + l_i : l_i + sL[partner][lane];
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  const int h = h0 + l32;
+  const int h = h0 + 16 * hh + r;
   if (h < H) {
-    uint16_t* orow = o + ((size_t)t * H + h) * kVD + 128 * w;
+    uint16_t* orow = o + ((size_t)t * H + h) * kVD + 256 * eh + 4 * g;
 #pragma unroll
-    for (int dt = 0; dt < 4; dt++)
-#pragma unroll
-      for (int jg = 0; jg < 4; jg++) {
-        const int d = 32 * dt + 8 * jg + 4 * hi;
-        *reinterpret_cast<u32x2*>(orow + d) =
-            u32x2{pack_bf16x2(oacc[dt][4 * jg] * inv, oacc[dt][4 * jg + 1] * inv),
-                  pack_bf16x2(oacc[dt][4 * jg + 2] * inv, oacc[dt][4 * jg + 3] * inv)};
-      }
-    if (w == 0 && hi == 0) lse[(size_t)t * H + h] = (M + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    for (int cb = 0; cb < 16; cb++)
+      *reinterpret_cast<u32x2*>(orow + 16 * cb) =
+          u32x2{pack_bf16x2(oacc[cb][0] * inv, oacc[cb][1] * inv), pack_bf16x2(oacc[cb][2] * inv, oacc[cb][3] * inv)};
+    if (eh == 0 && g == 0) lse[(size_t)t * H + h] = (M + __builtin_amdgcn_logf(l_tot)) * kLn2;
   }
 }
 
