@@ -53,6 +53,22 @@ def _compile(hipcc, src, extra):
     return obj
 
 
+def _check_stubs(lib):
+    """Fail if a kernel's host launch stub is left unresolved.
+
+    The host pass can drop a kernel's stub without any diagnostic (the kernel
+    body is only checked, not compiled, there), and the library then fails
+    only when the GPU loader resolves it.
+    """
+    nm = shutil.which("nm") or "/usr/bin/nm"
+    res = subprocess.run([nm, "-u", lib], capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"nm failed on {lib}:\n{res.stderr}")
+    missing = [ln.split()[-1] for ln in res.stdout.splitlines() if "__device_stub__" in ln]
+    if missing:
+        raise RuntimeError("kernel launch stubs left undefined: " + ", ".join(missing))
+
+
 def build(verbose: bool = False, extra=()) -> str:
     hipcc = _hipcc()
     os.makedirs(BUILD, exist_ok=True)
@@ -64,6 +80,7 @@ def build(verbose: bool = False, extra=()) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
+    _check_stubs(tmp)
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
