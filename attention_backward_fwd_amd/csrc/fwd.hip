@@ -16,8 +16,9 @@
 // rescale factor of the online softmax is a per-lane scalar.
 //
 // Workgroup: 4 waves x 32 queries = 128 queries; key/value tiles of 64 rows,
-// double-buffered in LDS and filled by LDS-DMA loads one tile ahead (one
-// workgroup barrier per tile).  Scores stay fp32; P is rounded
+// double-buffered in LDS and filled by LDS-DMA buffer loads one tile ahead
+// (one workgroup barrier per tile), whose per-lane offsets are computed once
+// per kernel rather than per tile.  Scores stay fp32; P is rounded
 // to bf16 only as an MFMA operand; O is written as bf16 (RNE) and LSE as fp32
 // natural log including the scale.
 #include <type_traits>
@@ -108,9 +109,43 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
   const int n_end = CAUSAL ? max(0, min(Sk, mb * BM + BM + off)) : Sk;
   const int n_tiles = (n_end + BN - 1) / BN;
 
+  // K and V tiles arrive by LDS-DMA buffer loads, 16 bytes per lane: row r
+  // of the tile lands unpadded at LDS row r with its 16-byte slots swizzled
+  // (swz), as the reads below expect.  Each wave issues NLD of the tile's
+  // 1 KB instructions.  The per-lane byte offsets of a full tile are the same
+  // for every tile and for K and V (same row stride), so they are computed
+  // once; the last tile of a sequence reads its final row again for rows
+  // past the end (those keys are masked).
+  constexpr int CPR = D / 8, RPI = 64 / CPR;  // 16-byte slots per row, rows per instruction
+  constexpr int NLD = (BN * D / 512) / 4;     // instructions per wave per tile
+  const uint32_t rowb = (uint32_t)kvrs * 2u;  // bytes per key row
+  uint32_t voff[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; i++) {
+    const int r = (w + 4 * i) * RPI + lane / CPR;
+    voff[i] = (uint32_t)r * rowb + (uint32_t)(((lane % CPR) ^ swz<D>(r)) << 4);
+  }
+  auto load_kv = [&](const uint16_t* g, int row0, uint16_t* tile) {
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(g + (size_t)row0 * kvrs, (uint32_t)BN * rowb);
+    if (row0 + BN <= Sk) {
+#pragma unroll
+      for (int i = 0; i < NLD; i++) {
+        const uint32_t o = voff[i];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_ptr(tile + (w + 4 * i) * 512), 16, o, 0, 0, 0);
+      }
+    } else {
+      const int last = Sk - 1 - row0;
+#pragma unroll
+      for (int i = 0; i < NLD; i++) {
+        const int r = (w + 4 * i) * RPI + lane / CPR;
+        const uint32_t o = (uint32_t)min(r, last) * rowb + (uint32_t)(((lane % CPR) ^ swz<D>(r)) << 4);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_ptr(tile + (w + 4 * i) * 512), 16, o, 0, 0, 0);
+      }
+    }
+  };
   if (n_tiles > 0) {
-    tile_load_async<D, BN>(Kb, kvrs, 0, Sk, sK0, w, lane);
-    tile_load_async<D, BN>(Vb, kvrs, 0, Sk, sV0, w, lane);
+    load_kv(Kb, 0, sK0);
+    load_kv(Vb, 0, sV0);
   }
 
   bf16x8 qf[NKS];
@@ -148,8 +183,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     wait_vmem();
     lds_barrier();  // tile it resident; every wave is done with tile it-1
     if (it + 1 < n_tiles) {
-      tile_load_async<D, BN>(Kb, kvrs, n0 + BN, Sk, nK, w, lane);
-      tile_load_async<D, BN>(Vb, kvrs, n0 + BN, Sk, nV, w, lane);
+      load_kv(Kb, n0 + BN, nK);
+      load_kv(Vb, n0 + BN, nV);
     }
     // A wave whose queries all precede the tile has nothing to do in it.
     if (CAUSAL && n0 > q0 + 31 + off) return;
