@@ -54,6 +54,32 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const uint16_t* __restr
 // dq_accum[b,h,s,:] = sum_{j=0..J(s)} part[j][b,h,s,:], ascending j, where
 // J(s) is the last key block (causal: the block holding key s).  Both are
 // head-major fp32 [B][Hq][S][D].
+// acc + part[0] + part[1] + ... + part[n-1] (16-byte slots `slot` floats
+// apart), added one at a time in ascending order, so the bits do not depend on
+// how the loads are grouped; the loads are issued up to eight at a time so
+// that they are in flight together instead of one memory latency apart.
+__device__ __forceinline__ f32x4 sum_slots(f32x4 acc, const float* part, size_t slot, int n) {
+  auto ld = [&](int j) { return *reinterpret_cast<const f32x4*>(part + (size_t)j * slot); };
+  int j = 0;
+  for (; j + 8 <= n; j += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; u++) v[u] = ld(j + u);
+#pragma unroll
+    for (int u = 0; u < 8; u++) acc += v[u];
+  }
+  if (j + 4 <= n) {
+    f32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; u++) v[u] = ld(j + u);
+#pragma unroll
+    for (int u = 0; u < 4; u++) acc += v[u];
+    j += 4;
+  }
+  for (; j < n; j++) acc += ld(j);
+  return acc;
+}
+
 __global__ __launch_bounds__(256) void dq_sum_kernel(const float* __restrict__ part,
                                                      float* __restrict__ dq, long long n4, int S,
                                                      int D, int n_nblk, int causal) {
@@ -63,8 +89,7 @@ __global__ __launch_bounds__(256) void dq_sum_kernel(const float* __restrict__ p
     const int s = (int)((e / D) % S);
     const int last = causal ? s / kBwdBlockN : n_nblk - 1;
     const float* src = part + e;
-    f32x4 acc = *reinterpret_cast<const f32x4*>(src);
-    for (int j = 1; j <= last; j++) acc += *reinterpret_cast<const f32x4*>(src + (size_t)j * slot);
+    const f32x4 acc = sum_slots(*reinterpret_cast<const f32x4*>(src), src + slot, slot, last);
     *reinterpret_cast<f32x4*>(dq + e) = acc;
   }
 }
@@ -109,8 +134,7 @@ __global__ __launch_bounds__(256) void dq_sum_varlen_kernel(const float* __restr
       const int lk = seq_rows(cu_k, Tk, b, Sk).len;
       const int last_key = causal ? min(t - start + lk - len, lk - 1) : lk - 1;
       const float* src = part + e;
-      if (last_key >= 0)
-        for (int j = 0; j <= last_key / kBwdBlockN; j++) acc += *reinterpret_cast<const f32x4*>(src + (size_t)j * slot);
+      if (last_key >= 0) acc = sum_slots(acc, src, slot, last_key / kBwdBlockN + 1);
     }
     *reinterpret_cast<f32x4*>(dq + e) = acc;
   }
