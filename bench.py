@@ -602,6 +602,13 @@ def main():
                      "unit": "TFLOP/s", "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic(w.name, path)},
     }
+    if use_atomic:
+        # The atomic path's other bound: every query row receives one fp32 add
+        # per element from each key block (256 keys) it sees.
+        n_blk = -(-w.seqlen // 256)
+        blocks_seen = sum(s // 256 + 1 for s in range(w.seqlen)) if causal else w.seqlen * n_blk
+        n_atomics = blocks_seen * w.batch * w.heads_q * w.head_dim
+        out["dq_atomics"] = {"count": n_atomics, "per_s": round(n_atomics / (bwd_ms * 1e-3) / 1e9, 1), "unit": "G/s"}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, causal, args.cpu_budget)
     print(json.dumps(out), flush=True)
