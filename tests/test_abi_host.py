@@ -37,6 +37,22 @@ def test_library_exports_every_header_symbol():
         assert hasattr(lib(), n), n
 
 
+def test_every_kernel_launch_stub_is_defined():
+    """A kernel whose host launch stub the compiler dropped leaves the symbol
+    undefined; the library then loads lazily on the host but fails on the GPU
+    when the loader resolves it."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    und = subprocess.run([nm, "-u", bd.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    assert "__device_stub__" not in und
+    defined = subprocess.run([nm, "--defined-only", bd.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    for kernel in ("fwd_kernel", "bwd_kernel", "dq_sum_kernel", "preprocess_kernel", "postprocess_kernel"):
+        assert f"__device_stub__{kernel}" in defined, kernel
+
+
 def test_strerror_covers_every_code():
     msgs = {lib().attn_strerror(c).decode() for c in range(0, -9, -1)}
     assert len(msgs) == 9
