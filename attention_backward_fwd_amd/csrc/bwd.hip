@@ -113,10 +113,10 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
 
   // Tile order: each XCD gets a contiguous range of (batch, KV head) groups
   // (packed sequences: every eighth group, so that sequences of unequal
-  // length load the XCDs evenly) and works through them one at a time (their
-  // Q/dO rows stay in its L2); inside a group, key blocks run heaviest-first
-  // (block 0 sees every query under causal masking) with the group's query
-  // heads side by side.
+  // length load the XCDs evenly) and works through them two at a time (one
+  // at a time for packed sequences; their Q/dO rows stay in its L2); key
+  // blocks run heaviest-first (block 0 sees every query under causal
+  // masking) with a group's query heads side by side.
   const int nwg = gridDim.x, NG = p.B * Hkv;
   int t = blockIdx.x, x = 0, nx = 1, NGx = NG;
   if (NG % 8 == 0) {
@@ -130,9 +130,21 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
   // (Integer division runs on the vector unit; readfirstlane returns the
   // results to scalar registers, where everything derived from them stays.)
   const int per_group = n_nblk * G;
-  const int grp = p.cu ? (t / per_group) * nx + x : x * NGx + t / per_group;
-  const int jb = __builtin_amdgcn_readfirstlane((t % per_group) / G);
-  const int r = t % G;
+  int grp, jbv, r;
+  if (!p.cu && nx == 8 && NGx % 2 == 0) {
+    // Dense problems: two groups at a time, their key blocks interleaved
+    // heaviest-first.  Group after group, the last group's heaviest block
+    // would start near the end and run alone while the XCD's other CUs idle.
+    const int pair = t / (2 * per_group), u = t % (2 * per_group);
+    jbv = u / (2 * G);
+    grp = x * NGx + 2 * pair + (u / G) % 2;
+    r = u % G;
+  } else {
+    grp = p.cu ? (t / per_group) * nx + x : x * NGx + t / per_group;
+    jbv = (t % per_group) / G;
+    r = t % G;
+  }
+  const int jb = __builtin_amdgcn_readfirstlane(jbv);
   const int b = __builtin_amdgcn_readfirstlane(grp / Hkv), kvh = __builtin_amdgcn_readfirstlane(grp % Hkv);
   const int h = __builtin_amdgcn_readfirstlane(kvh * G + r);
   const int n0 = jb * BN;

@@ -65,10 +65,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
 
   // Tile order: each XCD gets a contiguous range of (batch, KV head) groups
   // (packed sequences: every eighth group, so that sequences of unequal
-  // length load the XCDs evenly) and works through them one at a time, so a
-  // group's K/V stay in its L2; inside a group, query blocks run
-  // heaviest-first under causal masking, with the group's query heads side by
-  // side.
+  // length load the XCDs evenly) and works through them two at a time (one
+  // at a time for packed sequences), so the groups' K/V stay in its L2;
+  // query blocks run heaviest-first under causal masking, with a group's
+  // query heads side by side.
   const int nwg = gridDim.x, NG = p.B * Hkv;
   int t = blockIdx.x, x = 0, nx = 1, NGx = NG;
   if (NG % 8 == 0) {
@@ -80,9 +80,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     NGx = NG / 8;
   }
   const int per_group = n_mblk * G;
-  const int grp = p.cu ? (t / per_group) * nx + x : x * NGx + t / per_group;
-  const int mbo = (t % per_group) / G;
-  const int r = t % G;
+  int grp, mbo, r;
+  if (!p.cu && nx == 8 && NGx % 2 == 0) {
+    // Dense problems: two groups at a time, their blocks interleaved
+    // heaviest-first.  Group after group, the last group's heaviest block
+    // would start near the end and run alone while the XCD's other CUs idle.
+    const int pair = t / (2 * per_group), u = t % (2 * per_group);
+    mbo = u / (2 * G);
+    grp = x * NGx + 2 * pair + (u / G) % 2;
+    r = u % G;
+  } else {
+    grp = p.cu ? (t / per_group) * nx + x : x * NGx + t / per_group;
+    mbo = (t % per_group) / G;
+    r = t % G;
+  }
   const int b = __builtin_amdgcn_readfirstlane(grp / Hkv), kvh = __builtin_amdgcn_readfirstlane(grp % Hkv);
   const int h = __builtin_amdgcn_readfirstlane(kvh * G + r);
   // This sequence's query and key rows (packed sequences: their own
