@@ -113,8 +113,8 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
 
   // Tile order: each XCD gets a contiguous range of (batch, KV head) groups
   // (packed sequences: every eighth group, so that sequences of unequal
-  // length load the XCDs evenly) and works through them a few at a time (one
-  // at a time for packed sequences; their Q/dO rows stay in its L2); key
+  // length load the XCDs evenly) and works through them a few at a time
+  // (their Q/dO rows stay in its L2); key
   // blocks run heaviest-first (block 0 sees every query under causal
   // masking) with a group's query heads side by side.
   const int nwg = gridDim.x, NG = p.B * Hkv;
@@ -131,20 +131,21 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
   // results to scalar registers, where everything derived from them stays.)
   const int per_group = n_nblk * G;
   int grp, jbv, r;
-  // Dense problems take CH groups at a time: as many as keep about 8 MB of
+  // Each XCD takes CH groups at a time: as many as keep about 8 MB of
   // shared rows in flight (Q and dO rows of one group's query heads (bf16)), at least 2, a power of two dividing
   // the XCD's group count (none: one at a time).
   const long long gbytes = 4LL * p.S * D * G;
   int CH = 2;
   while (2 * CH <= NGx && 2LL * CH * gbytes <= (8LL << 20)) CH *= 2;
   while (CH > 1 && NGx % CH) CH >>= 1;
-  if (!p.cu && nx == 8 && CH > 1) {
+  if (nx == 8 && CH > 1) {
     // Their key blocks interleaved heaviest-first: group after group, the
     // last group's heaviest block would start near the end and run alone
     // while the XCD's other CUs idle.
     const int chunk = t / (CH * per_group), u = t % (CH * per_group);
     jbv = u / (CH * G);
-    grp = x * NGx + CH * chunk + (u / G) % CH;
+    const int gl = CH * chunk + (u / G) % CH;  // group within this XCD's share
+    grp = p.cu ? gl * nx + x : x * NGx + gl;
     r = u % G;
   } else {
     grp = p.cu ? (t / per_group) * nx + x : x * NGx + t / per_group;
