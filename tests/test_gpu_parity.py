@@ -84,6 +84,27 @@ def test_long_sweep(d, causal):
         _compare(f"s1100 d{d} causal={causal} atomic={use_atomic}", gpu, ref)
 
 
+# (batch, heads_q, heads_kv, seqlen, head_dim): enough (batch, KV head) groups
+# (a multiple of 8) that each XCD's share of the grid is walked a few groups
+# at a time with their blocks interleaved, compared element by element.
+INTERLEAVED = [
+    (2, 8, 8, 300, 128),   # 16 groups: 2 per XCD
+    (4, 16, 8, 520, 64),   # 32 groups: 4 per XCD, GQA-2
+    (8, 8, 8, 257, 64),    # 64 groups: 8 per XCD, ragged tail
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("b,hq,hkv,s,d", INTERLEAVED)
+def test_interleaved_group_order(b, hq, hkv, s, d, causal):
+    inp = make_inputs(b, s, hq, hkv, d, seed=b * 100 + s)
+    scale = 1.0 / math.sqrt(d)
+    ref = _oracle(inp, causal, scale, hq // hkv)
+    for use_atomic in (1, 0):
+        gpu = run_path(to_dev(inp), causal, scale, use_atomic)
+        _compare(f"b{b} hq{hq} hkv{hkv} s{s} d{d} causal={causal} atomic={use_atomic}", gpu, ref)
+
+
 def test_group_of_eight_odd_length():
     inp = make_inputs(1, 333, 16, 2, 128, seed=5, qk_mult=1.5)
     scale = 1.0 / math.sqrt(128)
