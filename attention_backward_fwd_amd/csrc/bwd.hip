@@ -18,7 +18,8 @@
 // registers; that is already the A-operand layout of P^T and dS^T for the dV
 // and dK products, so those never leave registers.  dQ needs dS with queries
 // in lanes, so dS^T goes through LDS; dQ (32 queries x D) is split over the
-// waves as 16x16 tiles.
+// waves: for D = 128 waves 0-3 (one per SIMD) each form a 32x32 tile, for
+// D = 64 every wave a 16x16 tile.
 //
 // Why 256 keys: every key block adds its dQ contribution once per query
 // block, so the dQ traffic leaving the workgroups (fp32 atomics, or the split
@@ -34,7 +35,8 @@
 // is divided by the scale, once, at the end.
 //
 // Q and dO blocks are double-buffered in LDS and filled by LDS-DMA loads
-// issued one block ahead; two workgroup barriers per query block.
+// issued one block ahead; one workgroup barrier per query block, after which
+// the dQ of the previous block is formed from its completed dS^T tile.
 //
 // dQ leaves the workgroup either as fp32 atomic adds into one accumulator
 // (the page's atomic variant, with fp32 rather than bf16 atomics) or as a
