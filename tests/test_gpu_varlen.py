@@ -93,6 +93,9 @@ SMALL = [
     ([300, 1, 0, 257, 520, 33], 40, 4, 1, 128, True),
     ([600, 256, 700], 0, 2, 2, 64, False),
     ([64, 511, 96, 1], 17, 2, 2, 128, True),
+    # 4 sequences x 4 KV heads = 16 groups: two per XCD, interleaved
+    ([300, 1, 257, 40], 5, 8, 4, 64, True),
+    ([300, 1, 257, 40], 5, 8, 4, 128, False),
 ]
 
 
