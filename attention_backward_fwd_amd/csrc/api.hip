@@ -3,6 +3,8 @@
 // enqueued; the library never allocates, frees or synchronises.
 #include <math.h>
 
+#include <mutex>
+
 #include "kernels.h"
 #include "mi355_attn.h"
 
@@ -86,6 +88,30 @@ int check_smla(const smla_shape& s) {
   return ATTN_OK;
 }
 
+// Scratch of attn_bwd_noalloc: a fixed device array in the library's code
+// object, one copy per GPU for the life of the process.  On the host its
+// name stands for a host-side shadow, so kernels get the device address
+// hipGetSymbolAddress returns, looked up once per device.
+constexpr size_t kScratchBytes = 64u << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_current_device(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_ERR_HIP;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return ATTN_ERR_HIP;
+    scratch_ptr[dev] = ptr;
+  }
+  *out = (char*)scratch_ptr[dev];
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -103,6 +129,7 @@ const char* attn_strerror(int status) {
     case ATTN_ERR_WORKSPACE: return "workspace is NULL or smaller than attn_bwd_workspace_bytes()";
     case ATTN_ERR_HIP: return "HIP runtime reported a launch error";
     case ATTN_ERR_FLAG: return "causal and use_atomic must be 0 or 1";
+    case ATTN_ERR_SCRATCH: return "problem needs more than the library's fixed 64 MiB scratch array";
     default: return "unknown status";
   }
 }
@@ -205,6 +232,33 @@ int attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint
   if (!use_atomic)
     e = launch_dq_sum(p.dq_part, dq_accum, p.B, p.S, p.Hq, p.D, causal, s);
   return hip_status(e);
+}
+
+int attn_bwd_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
+                     const float* lse, const float* delta, float* dq_accum, uint16_t* dk, uint16_t* dv,
+                     attn_shape shape, float softmax_scale, int causal, void* stream) {
+  if (!q || !k || !v || !dout || !lse || !delta || !dq_accum || !dk || !dv) return ATTN_ERR_NULL_PTR;
+  const int st = check_shape(shape);
+  if (st) return st;
+  if (causal != 0 && causal != 1) return ATTN_ERR_FLAG;
+  if (!good_scale(softmax_scale)) return ATTN_ERR_RANGE;
+  const size_t need = ws_gqa_bytes(shape) + ws_split_bytes(shape, 0);
+  if (need > kScratchBytes) return ATTN_ERR_SCRATCH;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(lse) ||
+      !aligned16(delta) || !aligned16(dq_accum) || !aligned16(dk) || !aligned16(dv))
+    return ATTN_ERR_ALIGN;
+  char* ws = nullptr;
+  const int sst = scratch_of_current_device(&ws);
+  if (sst) return sst;
+  // attn_bwd's split path on the scratch array.  Every scratch element a
+  // kernel reads was written earlier in this call, so nothing is cleared.
+  const int bst = attn_bwd(q, k, v, dout, lse, delta, dq_accum, dk, dv, ws, kScratchBytes, shape, softmax_scale,
+                           causal, 0, stream);
+  if (bst || shape.groups == 1) return bst;
+  const size_t nq_bytes = elems_q(shape) * sizeof(float);
+  return hip_status(launch_gqa_reduce((const float*)ws, (const float*)(ws + nq_bytes), dk, dv, shape.seqlen,
+                                      shape.heads_q, shape.groups, shape.head_dim,
+                                      (long long)shape.batch * shape.seqlen, (hipStream_t)stream));
 }
 
 int attn_bwd_postprocess(const float* dq_accum, const void* workspace, size_t workspace_bytes, uint16_t* dq,

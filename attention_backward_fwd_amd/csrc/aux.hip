@@ -283,4 +283,14 @@ hipError_t launch_postprocess(const float* dq_accum, const float* dk_part, const
   return hipGetLastError();
 }
 
+// The dK/dV half of the postprocess alone: dk/dv[b,s,kv,:] = bf16(sum over
+// r < G, ascending, of the per-query-head partials).
+hipError_t launch_gqa_reduce(const float* dk_part, const float* dv_part, uint16_t* dk, uint16_t* dv, int S, int Hq,
+                             int G, int D, long long kv_rows, hipStream_t stream) {
+  const long long nkv8 = kv_rows * (Hq / G) * D / 8;
+  hipLaunchKernelGGL(postprocess_kernel, dim3(grid_for(nkv8, 256)), dim3(256), 0, stream, nullptr, dk_part,
+                     dv_part, nullptr, dk, dv, 0LL, nkv8, G, D, S, Hq);
+  return hipGetLastError();
+}
+
 }  // namespace mi355

@@ -86,6 +86,8 @@ hipError_t launch_pad_fill(void* x0, void* x1, int fp32, int heads, float* lse, 
 hipError_t launch_postprocess(const float* dq_accum, const float* dk_part, const float* dv_part,
                               uint16_t* dq, uint16_t* dk, uint16_t* dv, int B, int S, int Hq, int G,
                               int D, long long kv_rows, hipStream_t stream);
+hipError_t launch_gqa_reduce(const float* dk_part, const float* dv_part, uint16_t* dk, uint16_t* dv, int S, int Hq,
+                             int G, int D, long long kv_rows, hipStream_t stream);
 
 // Simple gated linear attention, chunked backward (head dim 128, chunks of
 // 64): states, per-chunk dq/dk/dv and the gate's reverse running sum.

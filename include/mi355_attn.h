@@ -62,7 +62,8 @@ enum {
                               or softmax_scale is not finite and > 0 */
   ATTN_ERR_WORKSPACE = -6, /* workspace NULL or smaller than attn_bwd_workspace_bytes() */
   ATTN_ERR_HIP = -7,       /* the HIP runtime reported a launch error */
-  ATTN_ERR_FLAG = -8       /* causal or use_atomic is not 0 or 1 */
+  ATTN_ERR_FLAG = -8,      /* causal or use_atomic is not 0 or 1 */
+  ATTN_ERR_SCRATCH = -9    /* attn_bwd_noalloc: the problem needs more than its scratch array */
 };
 
 /* Static message for a status code (never NULL). */
@@ -122,6 +123,33 @@ int attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint
              const float* lse, const float* delta, float* dq_accum, uint16_t* dk, uint16_t* dv,
              void* workspace, size_t workspace_bytes, attn_shape shape, float softmax_scale,
              int causal, int use_atomic, void* stream);
+
+/*
+ * attn_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc).  It runs attn_bwd with use_atomic = 0 (dQ through
+ * per-KV-block partials summed in ascending block order: bitwise
+ * deterministic) on a scratch array that the library holds in its own code
+ * object: 64 MiB of device memory on every GPU the library runs on, kept
+ * until the process ends.  The call allocates and frees nothing.
+ *   Arguments and outputs as attn_bwd (dq_accum is fully overwritten), with
+ *   one difference: dk and dv are always required and always written as
+ *   bf16 [B,S,Hkv,D]; for groups > 1 the ascending-r reduction that
+ *   attn_bwd_postprocess applies to attn_bwd's partials happens here.  Run
+ *   attn_bwd_postprocess(dq_accum, NULL, 0, dq, NULL, NULL, shape with
+ *   groups = 1, stream) afterwards for the bf16 dQ.
+ *   Scratch needed: (groups > 1 ? 2 : 0) * B*S*Hq*D * 4 bytes plus
+ *   ceil(S / 256) * B*S*Hq*D * 4 bytes; beyond 64 MiB the call returns
+ *   ATTN_ERR_SCRATCH and launches nothing.
+ *   The scratch of a GPU is shared by every call on it and holds what the
+ *   last call left: calls that may overlap on one GPU (on different streams
+ *   or from different threads without ordering) race and give wrong results.
+ *   The stream must belong to the current device; the first call on a
+ *   device looks up that device's scratch address (hipGetSymbolAddress).
+ */
+int attn_bwd_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
+                     const float* lse, const float* delta, float* dq_accum, uint16_t* dk, uint16_t* dv,
+                     attn_shape shape, float softmax_scale, int causal, void* stream);
 
 /*
  * Backward postprocess (flashattn_bwd_postprocess of the TileLang #940

@@ -28,7 +28,7 @@ def shp(b=2, s=300, hq=8, g=2, d=128):
 def test_library_exports_every_header_symbol():
     names = bd.header_functions()
     assert names == sorted(["attn_fwd", "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_bwd",
-                            "attn_bwd_postprocess", "attn_merge", "attn_strerror", "attn_fwd_varlen",
+                            "attn_bwd_postprocess", "attn_bwd_noalloc", "attn_merge", "attn_strerror", "attn_fwd_varlen",
                             "attn_bwd_varlen_workspace_bytes", "attn_bwd_varlen",
                             "attn_bwd_varlen_postprocess", "gla_chunk_bwd_workspace_bytes", "gla_chunk_bwd",
                             "attn_sparse_mla_fwd", "attn_sparse_mla_bwd_preprocess", "attn_sparse_mla_bwd",
@@ -54,8 +54,8 @@ def test_every_kernel_launch_stub_is_defined():
 
 
 def test_strerror_covers_every_code():
-    msgs = {lib().attn_strerror(c).decode() for c in range(0, -9, -1)}
-    assert len(msgs) == 9
+    msgs = {lib().attn_strerror(c).decode() for c in range(0, -10, -1)}
+    assert len(msgs) == 10
     assert lib().attn_strerror(-99).decode() == "unknown status"
 
 
@@ -106,7 +106,16 @@ def post(**kw):
                                       args["shape"], args["stream"])
 
 
-E = {"null": -1, "shape": -2, "hd": -3, "align": -4, "range": -5, "ws": -6, "flag": -8}
+def noalloc(**kw):
+    args = dict(q=A, k=A, v=A, do=A, lse=A, delta=A, dq=A, dk=A, dv=A, shape=shp(), scale=0.1, causal=1,
+                stream=None)
+    args.update(kw)
+    return lib().attn_bwd_noalloc(args["q"], args["k"], args["v"], args["do"], args["lse"], args["delta"],
+                                  args["dq"], args["dk"], args["dv"], args["shape"], args["scale"], args["causal"],
+                                  args["stream"])
+
+
+E = {"null": -1, "shape": -2, "hd": -3, "align": -4, "range": -5, "ws": -6, "flag": -8, "scratch": -9}
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -371,3 +380,19 @@ def test_sparse_mla_pre_post_errors():
     g = lib().attn_sparse_mla_bwd_postprocess
     assert g(None, A, mshp(), None) == E["null"]
     assert g(A, MIS, mshp(), None) == E["align"]
+
+
+# Scratch of attn_bwd_noalloc: 64 MiB; need = (2 if groups > 1) * nq * 4 + ceil(S/256) * nq * 4.
+@pytest.mark.parametrize("kw,code", [
+    ({"dk": None, "shape": shp(g=1)}, "null"), ({"dv": None}, "null"), ({"delta": None}, "null"),
+    ({"shape": shp(hq=6, g=4)}, "shape"), ({"shape": shp(d=96)}, "hd"), ({"causal": 2}, "flag"),
+    ({"scale": 0.0}, "range"),
+    # B1 S4096 Hq8 D128, MHA: 16 blocks * 4 Mi floats * 4 B = 256 MiB.
+    ({"shape": shp(b=1, s=4096, hq=8, g=1, d=128)}, "scratch"),
+    # B2 S1024 Hq16 D64, GQA: (2 + 4) * 2 Mi floats * 4 B = 48 MiB fits; Hq32 (96 MiB) does not.
+    ({"shape": shp(b=2, s=1024, hq=32, g=4, d=64)}, "scratch"),
+    ({"shape": shp(b=2, s=1024, hq=16, g=4, d=64), "dq": MIS}, "align"),
+    ({"q": MIS}, "align"),
+])
+def test_noalloc_errors(kw, code):
+    assert noalloc(**kw) == E[code]
