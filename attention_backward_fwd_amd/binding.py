@@ -89,6 +89,8 @@ def library():
         lib.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, attn_shape, ctypes.c_float,
                                  ctypes.c_int, ctypes.c_int, P]
         lib.attn_bwd_postprocess.restype = ctypes.c_int
+        lib.attn_bwd_dq_sum.restype = ctypes.c_int
+        lib.attn_bwd_dq_sum.argtypes = [P, ctypes.c_size_t, P, attn_shape, ctypes.c_int, P]
         lib.attn_bwd_noalloc.restype = ctypes.c_int
         lib.attn_bwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, attn_shape, ctypes.c_float, ctypes.c_int, P]
         lib.attn_bwd_postprocess.argtypes = [P, P, ctypes.c_size_t, P, P, P, attn_shape, P]
@@ -184,6 +186,12 @@ def attn_bwd(q, k, v, dout, lse, delta, dq_accum, dk, dv, workspace, shape, soft
     _check(library().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq_accum),
                               _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, shape, float(softmax_scale),
                               int(causal), int(use_atomic), _stream(stream)), "attn_bwd")
+
+
+def attn_bwd_dq_sum(workspace, dq_accum, shape, causal, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().attn_bwd_dq_sum(_ptr(workspace), ws_bytes, _ptr(dq_accum), shape, int(causal),
+                                     _stream(stream)), "attn_bwd_dq_sum")
 
 
 def attn_bwd_noalloc(q, k, v, dout, lse, delta, dq_accum, dk, dv, shape, softmax_scale, causal, stream=None):

@@ -234,6 +234,19 @@ int attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint
   return hip_status(e);
 }
 
+int attn_bwd_dq_sum(const void* workspace, size_t workspace_bytes, float* dq_accum, attn_shape shape, int causal,
+                    void* stream) {
+  if (!workspace || !dq_accum) return ATTN_ERR_NULL_PTR;
+  const int st = check_shape(shape);
+  if (st) return st;
+  if (causal != 0 && causal != 1) return ATTN_ERR_FLAG;
+  if (workspace_bytes < ws_gqa_bytes(shape) + ws_split_bytes(shape, 0)) return ATTN_ERR_WORKSPACE;
+  if (!aligned16(workspace) || !aligned16(dq_accum)) return ATTN_ERR_ALIGN;
+  const float* part = (const float*)((const char*)workspace + ws_gqa_bytes(shape));
+  return hip_status(launch_dq_sum(part, dq_accum, shape.batch, shape.seqlen, shape.heads_q, shape.head_dim, causal,
+                                  (hipStream_t)stream));
+}
+
 int attn_bwd_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
                      const float* lse, const float* delta, float* dq_accum, uint16_t* dk, uint16_t* dv,
                      attn_shape shape, float softmax_scale, int causal, void* stream) {

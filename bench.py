@@ -68,6 +68,23 @@ def recorded_traffic(workload, path, sources=BWD_SOURCES):
     return entry.get("bytes_per_launch")
 
 
+def recorded_util(workload, path, sources=BWD_SOURCES):
+    """Matrix-core utilisation of the backward kernel from the committed
+    counter summary (SQ_VALU_MFMA_BUSY_CYCLES over the XCD-average clock's
+    cycles x 1024 SIMDs), if it still describes the current kernel sources;
+    else None.  Unlike `frac`, it does not depend on the clock the GPU ran at."""
+    fn = os.path.join(ROOT, "profiles", "mfma_util.json")
+    try:
+        with open(fn) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(f"{workload}/{path}")
+    if not entry or entry.get("source_hash") != kernel_source_hash(sources):
+        return None
+    return entry
+
+
 def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -459,6 +476,65 @@ def bench_sweep(args, bd, torch):
                 del bb
 
 
+def time_other_path(args, w, bd, torch, inp, o, lse, causal, use_atomic, stream):
+    """The dQ path the headline did not take, on the same inputs and forward
+    outputs, timed after the headline's timed region: per step preprocess ->
+    attn_bwd -> postprocess (HIP events around the attn_bwd call and around
+    the three), and on the split path the fixed-order sum once more on its
+    own (attn_bwd_dq_sum), so that the call splits into kernel and sum."""
+    q, k, v, do = inp["q"], inp["k"], inp["v"], inp["do"]
+    sh = bd.shape_of(q, k)
+    bb = bd.BwdBuffers(q, k, causal, use_atomic)
+    n = args.steps
+    ev = {m: [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)] for m in ("call", "back", "sum")}
+
+    def step(i=None):
+        def rec(m, j):
+            if i is not None:
+                ev[m][2 * i + j].record(stream)
+        rec("back", 0)
+        bd.attn_bwd_preprocess(o, do, bb.delta, bb.dq_accum if use_atomic else None, sh, stream)
+        rec("call", 0)
+        bd.attn_bwd(q, k, v, do, lse, bb.delta, bb.dq_accum, bb.dk, bb.dv, bb.workspace, sh, w.scale, causal,
+                    use_atomic, stream)
+        rec("call", 1)
+        bd.attn_bwd_postprocess(bb.dq_accum, bb.workspace, bb.dq, bb.dk, bb.dv, sh, stream)
+        rec("back", 1)
+        if not use_atomic:
+            rec("sum", 0)
+            bd.attn_bwd_dq_sum(bb.workspace, bb.dq_accum, sh, causal, stream)
+            rec("sum", 1)
+
+    for _ in range(args.warmup):
+        step()
+    for i in range(n):
+        step(i)
+    torch.cuda.synchronize()
+
+    def avg(m):
+        return sum(ev[m][2 * i].elapsed_time(ev[m][2 * i + 1]) for i in range(n)) / n
+
+    _, bwd_f = flops(w, causal)
+    call_ms, back_ms = avg("call"), avg("back")
+    out = {"bwd_call_ms": round(call_ms, 4)}
+    if use_atomic:
+        kernel_ms = call_ms
+    else:
+        sum_ms = avg("sum")
+        kernel_ms = call_ms - sum_ms
+        out["sum_ms"] = round(sum_ms, 4)
+        out["kernel_ms"] = round(kernel_ms, 4)
+    out.update({
+        "backward_ms": round(back_ms, 4),
+        "backward_tflops": round(bwd_f / (back_ms * 1e-3) / 1e12, 3),
+        "frac": round(bwd_f / (back_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "kernel_tflops": round(bwd_f / (kernel_ms * 1e-3) / 1e12, 3),
+        "kernel_frac": round(bwd_f / (kernel_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+    })
+    del bb
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -469,6 +545,8 @@ def main():
     ap.add_argument("--use-atomic", type=int, default=1, choices=(0, 1))
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-path", action="store_true",
+                    help="skip timing the other dQ path (split when the headline is atomic, and vice versa)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run a plain fp32 copy kernel over MIB MiB "
                          "(reference for scaling the HBM byte counters)")
@@ -602,6 +680,19 @@ def main():
                      "unit": "TFLOP/s", "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic(w.name, path)},
     }
+    rl = out["roofline"]
+    rl["traffic_source"] = (f"recorded, not measured in this run: rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE of the "
+                            f"backward kernel at sources hash {kernel_source_hash()} (profiles/traffic.json); "
+                            "null when the sources changed since")
+    util = recorded_util(w.name, path)
+    rl["clock_adjusted_util"] = util["mfma_busy_frac"] if util else None
+    rl["clock_adjusted_util_source"] = (
+        f"recorded, not measured in this run: SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs) of "
+        f"the backward kernel (profiles/mfma_util.json, XCD-average clock "
+        f"{util['clock_ghz'] if util else 'n/a'} GHz); null when the sources changed since")
+    if not args.no_other_path:
+        other = "split" if use_atomic else "atomic"
+        out[other] = time_other_path(args, w, bd, torch, inp, o, lse, causal, 1 - use_atomic, stream)
     if use_atomic:
         # The atomic path's other bound: every query row receives one fp32 add
         # per element from each key block (256 keys) it sees.

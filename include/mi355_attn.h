@@ -125,6 +125,21 @@ int attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint
              int causal, int use_atomic, void* stream);
 
 /*
+ * The fixed-order dQ sum that attn_bwd ends with when use_atomic = 0 (the
+ * "sum" half of the split+sum template of TileLang #940), on its own:
+ * dq_accum[b,h,s,:] = sum over key blocks j = 0 .. J(s), ascending, of the
+ * fp32 partials attn_bwd(use_atomic = 0) left in `workspace`, where J(s) is
+ * the last key block (causal: the block holding key s).  dq_accum is fully
+ * overwritten with the same bits attn_bwd wrote.  For callers that keep the
+ * partials and need dQ again, and for timing the two halves of the split
+ * path separately.
+ *   workspace/workspace_bytes: the buffer of that attn_bwd call, at least
+ *     attn_bwd_workspace_bytes(shape, causal, 0) bytes; causal as in it.
+ */
+int attn_bwd_dq_sum(const void* workspace, size_t workspace_bytes, float* dq_accum, attn_shape shape, int causal,
+                    void* stream);
+
+/*
  * attn_bwd without a workspace argument, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, hosts
  * that forbid hipMalloc).  It runs attn_bwd with use_atomic = 0 (dQ through

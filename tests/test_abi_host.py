@@ -28,7 +28,7 @@ def shp(b=2, s=300, hq=8, g=2, d=128):
 def test_library_exports_every_header_symbol():
     names = bd.header_functions()
     assert names == sorted(["attn_fwd", "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_bwd",
-                            "attn_bwd_postprocess", "attn_bwd_noalloc", "attn_merge", "attn_strerror", "attn_fwd_varlen",
+                            "attn_bwd_postprocess", "attn_bwd_dq_sum", "attn_bwd_noalloc", "attn_merge", "attn_strerror", "attn_fwd_varlen",
                             "attn_bwd_varlen_workspace_bytes", "attn_bwd_varlen",
                             "attn_bwd_varlen_postprocess", "gla_chunk_bwd_workspace_bytes", "gla_chunk_bwd",
                             "attn_sparse_mla_fwd", "attn_sparse_mla_bwd_preprocess", "attn_sparse_mla_bwd",
@@ -396,3 +396,20 @@ def test_sparse_mla_pre_post_errors():
 ])
 def test_noalloc_errors(kw, code):
     assert noalloc(**kw) == E[code]
+
+
+def dqsum(**kw):
+    args = dict(ws=A, wsb=1 << 40, dq=A, shape=shp(), causal=1, stream=None)
+    args.update(kw)
+    return lib().attn_bwd_dq_sum(args["ws"], args["wsb"], args["dq"], args["shape"], args["causal"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"ws": None}, "null"), ({"dq": None}, "null"), ({"shape": shp(hq=6, g=4)}, "shape"),
+    ({"shape": shp(d=32)}, "hd"), ({"causal": 3}, "flag"),
+    # B2 S300 Hq8 D128, GQA-2: (2 + 2 blocks) x 614400 floats x 4 B is one byte more than given.
+    ({"wsb": 4 * 614400 * 4 - 1}, "ws"),
+    ({"ws": MIS}, "align"), ({"dq": MIS}, "align"),
+])
+def test_dq_sum_errors(kw, code):
+    assert dqsum(**kw) == E[code]

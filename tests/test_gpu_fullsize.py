@@ -1,4 +1,5 @@
-"""Full-size workloads on the GPU, checked against the oracle on samples.
+"""Full-size workloads on the GPU, checked against the oracle on samples and
+on whole slices.
 
 At these sizes the oracle computes selected outputs one at a time: O, LSE,
 Delta and dQ of sampled query rows (each needs only its own softmax row) and
@@ -7,6 +8,10 @@ group that sees the key).  Properties that hold at any size are checked on
 whole tensors: sum over keys of dK is zero (adding a constant vector to every
 key leaves the output unchanged) and sum over keys of dV equals the sum of
 the group's dO rows (softmax rows sum to one).
+
+The slice test compares, element by element, every row of O, LSE and dQ of
+the query heads of one KV group of one batch entry, and every key of that
+group's dK and dV, with the oracle run on that batch entry and group alone.
 """
 
 import numpy as np
@@ -21,11 +26,13 @@ pytestmark = pytest.mark.gpu
 
 FULL = [
     ("mha_causal_b8_h32_s1024_d64", True, 1),
+    ("mha_causal_b8_h32_s1024_d64", True, 0),
     ("gqa4_causal_b8_h32_s2048_d128", True, 1),
     ("gqa4_causal_b8_h32_s2048_d128", True, 0),
     ("mha_causal_b4_h32_s4096_d128", True, 1),
     ("mha_causal_b4_h32_s4096_d128", True, 0),
     ("gqa8_b1_h64_s8192_d128", False, 1),
+    ("gqa8_b1_h64_s8192_d128", False, 0),
     ("gqa8_b1_h64_s8192_d128", True, 1),
     ("gqa8_b1_h64_s8192_d128", True, 0),
 ]
@@ -79,6 +86,34 @@ def test_full_size_sampled(name, causal, use_atomic):
     assert dv_err <= 2e-2 * dv_scale
     for n in ("o", "lse", "dq", "dk", "dv"):
         assert torch.isfinite(gpu[n].float()).all(), n
+
+
+SLICES = [(name, use_atomic) for name in ("mha_causal_b8_h32_s1024_d64", "gqa4_causal_b8_h32_s2048_d128",
+                                         "mha_causal_b4_h32_s4096_d128") for use_atomic in (1, 0)]
+
+
+@pytest.mark.parametrize("name,use_atomic", SLICES)
+def test_full_size_whole_group_slice(name, use_atomic):
+    w = WORKLOADS[name]
+    causal = True
+    B, S, Hq, G = w.batch, w.seqlen, w.heads_q, w.groups
+    b, kv = B - 1, Hq // G - 1
+    say(f"[slice] {name} atomic={use_atomic}: batch {b}, KV head {kv}")
+    inp = workload_inputs(w)
+    dev = to_dev(inp)
+    gpu = run_path(dev, causal, w.scale, use_atomic)
+    sl = {n: t[b:b + 1].to(torch.float64).numpy() for n, t in inp.items()}
+    ref = orc.attention_bwd(sl["q"], sl["k"], sl["v"], sl["do"], w.scale, causal, G, heads=[kv])
+    hs = list(range(kv * G, kv * G + G))
+    zs = float(np.max(np.abs(ref["dv"][0, :, kv])))
+    got = {"o": np64(gpu["o"][b][:, hs]), "lse": np64(gpu["lse"][b][hs]), "delta": np64(gpu["delta"][b][hs]),
+           "dq": np64(gpu["dq"][b][:, hs]), "dk": np64(gpu["dk"][b][:, kv]), "dv": np64(gpu["dv"][b][:, kv])}
+    want = {"o": ref["o"][0][:, hs], "lse": ref["lse"][0][hs], "delta": ref["delta"][0][hs],
+            "dq": ref["dq"][0][:, hs], "dk": ref["dk"][0][:, kv], "dv": ref["dv"][0][:, kv]}
+    ratios = {n: err_ratio(got[n], want[n], zero_scale=zs) for n in got}
+    say(f"[slice] {name} atomic={use_atomic}: " + " ".join(f"{n}={r:.2e}" for n, r in ratios.items()))
+    for n in ("o", "lse", "dq", "dk", "dv"):
+        assert ratios[n] <= TOL, (n, ratios[n])
 
 
 def test_split_bitwise_deterministic_full_size():

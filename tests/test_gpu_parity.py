@@ -91,6 +91,8 @@ INTERLEAVED = [
     (2, 8, 8, 300, 128),   # 16 groups: 2 per XCD
     (4, 16, 8, 520, 64),   # 32 groups: 4 per XCD, GQA-2
     (8, 8, 8, 257, 64),    # 64 groups: 8 per XCD, ragged tail
+    (16, 8, 8, 130, 64),   # 128 groups: 16 per XCD, all 16 interleaved
+    (32, 8, 8, 130, 64),   # 256 groups: 32 per XCD, all 32 interleaved (as at B8 H32 S1024 D64)
 ]
 
 
@@ -134,6 +136,28 @@ def test_split_path_bitwise_deterministic(d):
     for n in ("dq", "dk", "dv", "o", "lse", "dq_accum"):
         for r in runs[1:]:
             assert torch.equal(bits(runs[0][n]), bits(r[n])), n
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dq_sum_alone_repeats_the_split_sum(causal):
+    """attn_bwd_dq_sum over the partials attn_bwd(use_atomic = 0) left in the
+    workspace rewrites dq_accum with the same bits."""
+    from attention_backward_fwd_amd import binding as bd
+    inp = to_dev(make_inputs(2, 700, 4, 2, 128, seed=13))
+    q, k, v, do = inp["q"], inp["k"], inp["v"], inp["do"]
+    scale = 1.0 / math.sqrt(128)
+    sh = bd.shape_of(q, k)
+    o, lse = bd.forward(q, k, v, causal, scale)
+    bb = bd.BwdBuffers(q, k, causal, 0)
+    bd.attn_bwd_preprocess(o, do, bb.delta, None, sh)
+    bd.attn_bwd(q, k, v, do, lse, bb.delta, bb.dq_accum, bb.dk, bb.dv, bb.workspace, sh, scale, causal, 0)
+    torch.cuda.synchronize()
+    first = bb.dq_accum.clone()
+    assert torch.isfinite(first).all()
+    bb.dq_accum.fill_(float("nan"))
+    bd.attn_bwd_dq_sum(bb.workspace, bb.dq_accum, sh, causal)
+    torch.cuda.synchronize()
+    assert torch.equal(first.view(torch.int32), bb.dq_accum.view(torch.int32))
 
 
 def test_atomic_and_split_agree():

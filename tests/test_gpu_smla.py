@@ -127,6 +127,22 @@ def test_smla_bwd_full_size():
     assert torch.all(torch.isfinite(gpu["dkv"].float())) and torch.all(torch.isfinite(gpu["dq"].float()))
 
 
+def test_smla_bwd_mid_size_elementwise():
+    """The benchmark workload's structure (32 heads, causal index lists in
+    random order) at 1024 tokens and top-512: dq, dkv and Delta of every
+    token and key against the oracle."""
+    t, h, k = 1024, 32, 512
+    inp = smla_inputs(t, t, h, seed=4)
+    idx = smla_indices(t, t, k, seed=4)
+    f = {n: x.double().numpy() for n, x in inp.items()}
+    ref = sm.sparse_mla_bwd(f["q"], f["kv"], idx.numpy(), f["do"], SCALE)
+    gpu = _run_bwd(inp, idx)
+    ratios = {n: err_ratio(np64(gpu[n]), ref[n]) for n in ("dq", "dkv", "delta")}
+    say(f"smla bwd T{t} H{h} K{k}: " + " ".join(f"{n}={r:.2e}" for n, r in ratios.items()))
+    for n, r in ratios.items():
+        assert r <= TOL, (n, r)
+
+
 def _gappy_indices(t, tk, k, seed):
     """Lists whose second 32-entry tile holds no valid entry, with unused and
     out-of-range entries scattered through the other tiles and valid entries
