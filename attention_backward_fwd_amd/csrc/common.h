@@ -216,6 +216,11 @@ __device__ __forceinline__ void dma_b32_asm(const void* g, uint32_t lds) {
 // The same copy issued as inline assembly (dma_b128_asm): the compiler adds
 // no waits for it; the caller waits explicitly.  NI / NW instructions per
 // wave (all waves when the tile is at least NW KB).
+// LDS-DMA instructions tile_load_async_asm<D, R, NW> issues per wave.
+template <int D, int R, int NW>
+constexpr int tile_load_ops() {
+  return R / (64 / (D / 8)) / NW;
+}
 template <int D, int R, int NW = 4>
 __device__ __forceinline__ void tile_load_async_asm(const uint16_t* g, size_t rs, int row0, int nrows,
                                                     uint16_t* tile, int w, int lane) {

@@ -149,24 +149,33 @@ __global__ __launch_bounds__(512) void gla_states_kernel(const uint16_t* __restr
     }
   };
   // S^T element j of tile nb: value vb + c_row(j), key kb + 32nb + l32;
-  // stored at [key][value], four consecutive values per store.
+  // stored at [key][value], four consecutive values per store: one buffer
+  // store instruction each, kStoreOps in all.
+  constexpr int kStoreOps = 2 * 4;
   auto store = [&](int slot) {
-    uint16_t* o = out + (size_t)slot * kD * kD + vb;
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(out + (size_t)slot * kD * kD, (uint32_t)(kD * kD * 2));
+    const uint32_t voff = (uint32_t)(((kb + (lane & 31)) * kD + vb + c_row(0, hi)) * 2);
 #pragma unroll
     for (int nb = 0; nb < 2; nb++)
 #pragma unroll
       for (int jg = 0; jg < 4; jg++) {
-        const int key = kb + 32 * nb + (lane & 31);
-        *reinterpret_cast<u32x2*>(o + (size_t)key * kD + c_row(4 * jg, hi)) =
-            u32x2{pack_bf16x2(acc[nb][4 * jg], acc[nb][4 * jg + 1]), pack_bf16x2(acc[nb][4 * jg + 2], acc[nb][4 * jg + 3])};
+        const u32x2 v = u32x2{pack_bf16x2(acc[nb][4 * jg], acc[nb][4 * jg + 1]),
+                              pack_bf16x2(acc[nb][4 * jg + 2], acc[nb][4 * jg + 3])};
+        // c_row(4jg, hi) - c_row(0, hi) = 8jg values; tile nb is 32 keys further.
+        __builtin_amdgcn_raw_buffer_store_b64(v, rs, voff, (int)((32 * nb * kD + 8 * jg) * 2), 0);
       }
   };
   // Order of a wave's vector-memory operations: loads of the first two
   // chunks (the initial state's store between them), then per step i the
-  // loads of chunk i+2 and the store of a state (8 instructions).  At step
-  // i >= 2, chunk i's loads are followed by 8 + 4 + 8 = 20 operations of
-  // waves 1-7 (21 of wave 0); at steps 0 and 1 by 8 + 4 = 12 (13).  Waiting
-  // for "all but that many" is waiting for chunk i.
+  // loads of chunk i+2 (kLoadOps: the X and Y tiles; wave 0 adds one for
+  // g, which only makes its waits below stricter) and the store of a state
+  // (kStoreOps).  At step i >= 2, chunk i's loads are followed by a store,
+  // chunk i+1's loads and another store; at steps 0 and 1 by a store and
+  // one chunk's loads.  Waiting for "all but that many" is waiting for
+  // chunk i.
+  constexpr int kLoadOps = 2 * tile_load_ops<kD, kC, NW>();
+  static_assert(kLoadOps == 4 && kStoreOps == 8, "wait counts below assume 4 loads and 8 stores per step");
+  constexpr int kWaitLater = 2 * kStoreOps + kLoadOps, kWaitFirst = kStoreOps + kLoadOps;
   const int first = first_chunk(dir, N), stepn = dir ? -1 : 1;
   auto chunk_of = [&](int i) { return min(max(first + stepn * i, 0), N - 1); };  // past either end: a valid chunk
   load(chunk_of(0), 0);
@@ -181,9 +190,9 @@ __global__ __launch_bounds__(512) void gla_states_kernel(const uint16_t* __restr
     const int next = n + stepn;
     const int next_st = (next < 0 || next >= N) ? N : next;  // past either end: the spare slot
     if (i >= 2)
-      wait_vmem_but<20>();
+      wait_vmem_but<kWaitLater>();
     else
-      wait_vmem_but<12>();
+      wait_vmem_but<kWaitFirst>();
     lds_barrier();  // chunk n resident; every wave is done with step i-1 (and its buffer)
     // Every wave scans the chunk's g itself (no second barrier).
     chunk_scan(lane < nv ? reinterpret_cast<const float*>(sy + kC * kD)[lane] : 0.f, wG, lane);
