@@ -19,10 +19,13 @@
 //   dq_t     = scale [sum_{s<=t} e^{G_t-G_s}(do_t.v_s) k_s + e^{G_t} do_t h_n^T]
 //   dk_s     = scale sum_{t>=s} e^{G_t-G_s}(do_t.v_s) q_t + e^{Gl-G_s} v_s dH_{n+1}^T
 //   dv_s     = scale sum_{t>=s} e^{G_t-G_s}(q_t.k_s) do_t + e^{Gl-G_s} k_s dH_{n+1}
-// (Gl: G at the chunk's last token).  Kernels: gla_states (h_n forward and
-// dH_{n+1} backward, bf16 to the workspace), gla_dqkv (one chunk per
-// workgroup: dq, dk, dv and the per-token q.dq - k.dk, head-major in the
-// workspace), gla_dg (reverse running sum over the sequence).
+// (Gl: G at the chunk's last token).  Kernels: gla_sweep (per (b, h) one
+// workgroup walks the chunks forward carrying h_n and writes dq, another
+// walks them backward carrying dH_{n+1} and writes dk, dv; both keep the
+// state on chip, so it never goes to HBM, and write per-token partials of
+// q.dq and k.dk to the workspace), gla_dg (reverse running sum of
+// q.dq - k.dk over the sequence).  This follows the page's account of where
+// the gains come from: state kept on chip and HBM round trips cut.
 #include "common.h"
 #include "kernels.h"
 
@@ -44,10 +47,11 @@ constexpr int kD = 128;  // head dim (K = V)
 // addition (the swizzle permutes 8-element slots by the row's low 4 bits).
 template <int DT>
 struct Lofs {
-  int row, tr0, tr1;
+  int row, row16, tr0, tr1;
   __device__ __forceinline__ explicit Lofs(int lane) {
     const int hi = lane >> 5, L = lane & 15, gp = (lane >> 4) & 1;
     row = swz_off<DT>(lane & 31, 4 * hi);
+    row16 = swz_off<DT>(lane & 31, 8 * hi);
     const int col = 16 * gp + 4 * (L & 3);
     tr0 = swz_off<DT>(4 * hi + (L >> 2), col);
     tr1 = swz_off<DT>(8 + 4 * hi + (L >> 2), col);
@@ -60,6 +64,13 @@ __device__ __forceinline__ bf16x8 op_row(const uint16_t* t, const Lofs<DT>& o, i
   const u32x2 hi = *reinterpret_cast<const u32x2*>(t + (a ^ 8));
   return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
+// Row operand with the k index in natural order (lane half hi: k = 8hi ..
+// 8hi+7, one 16-byte read); only for products whose other operand is read
+// the same way.
+template <int DT>
+__device__ __forceinline__ bf16x8 op_row16(const uint16_t* t, const Lofs<DT>& o, int x0, int k0) {
+  return *reinterpret_cast<const bf16x8*>(t + ((o.row16 ^ k0) + x0 * DT));
+}
 template <int DT>
 __device__ __forceinline__ bf16x8 op_tr(const uint16_t* t, const Lofs<DT>& o, int k0, int x0) {
   return lds_read_tr8(t + ((o.tr0 ^ x0) + k0 * DT), t + ((o.tr1 ^ x0) + k0 * DT));
@@ -68,360 +79,364 @@ __device__ __forceinline__ bf16x8 op_tr(const uint16_t* t, const Lofs<DT>& o, in
 __device__ __forceinline__ int op_k(int i, int hi) { return (i < 4 ? 4 * hi + i : 8 + 4 * hi + (i - 4)); }
 
 
-// Inclusive running sum over the 64 lanes of one wave, into sG[0..63].
-__device__ __forceinline__ void chunk_scan(float x, float* sG, int lane) {
+// ------------------------------------------------------------ chunk sweeps
+// One workgroup of 8 waves per (b*H + h, dir) walks the chunks of its
+// sequence in order, dir 0 forward with h_n, dir 1 backward with dH_{n+1},
+// and keeps that state on chip for the whole walk: fp32 in registers, as
+// the transposed tile S^T[value][key] in the 32x32 MFMA result layout (wave
+// w: value rows 32(w & 3).., key columns 64(w >> 2).., two tiles; lane = key
+// index), and as a bf16 [key][value] copy in LDS that the state terms read.
+// Per chunk, with its q, k, v, do tiles arriving by LDS-DMA one chunk ahead:
+//   dir 0: dq (in-chunk term from k and M_dov, state term from h_n and do),
+//          the per-token partials of q.dq, then h_{n+1};
+//   dir 1: dk, dv (in-chunk terms from q, do and M_dov, M_qk; state terms
+//          from dH_{n+1} and v, k), the partials of k.dk, then dH_n.
+// The masked score tiles M_dov[t][s] = scale e^{G_t - G_s} (do_t . v_s) and
+// M_qk[t][s] (s <= t) never leave registers: every wave forms the two 32x32
+// tiles its own output columns need, in the result layout that is already
+// the operand layout of the in-chunk products (the four waves of a token
+// block form the same tiles: cheaper than a trip through LDS and two more
+// barriers).  Outputs are computed transposed (dq^T [d][t], dk^T [d][s],
+// dv^T [v][s]; wave w: feature rows 32(w >> 1).., tokens 32(w & 1)..), so a
+// lane holds one token: per-token factors scale whole lanes and each lane
+// stores four consecutive features per 8-byte store.
+//
+// Every load is LDS-DMA and every store a buffer store, one instruction
+// each, issued in a fixed order per step: the next chunk's q, k, do (and g,
+// wave 0), its v after the first barrier, then this chunk's stores (kStF /
+// kStB per wave); waiting for "all but the stores" at the top of a step is
+// waiting for the chunk.  The chunk the last step loads is clamped to a
+// valid one (never used).
+constexpr int kStF = 2 + 1;      // dq (2 x 16 bytes of whole rows) + q.dq partial
+constexpr int kStB = 2 * 2 + 1;  // dk, dv + k.dk partial
+
+// The value a wave-uniform lane holds (v_readlane: no LDS round trip).
+__device__ __forceinline__ float lane_value(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
+// Inclusive running sum over the 64 lanes of one wave.
+__device__ __forceinline__ float wave_scan(float x, int lane) {
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const float y = __shfl_up(x, o, 64);
     if (lane >= o) x += y;
   }
-  sG[lane] = x;
+  return x;
 }
 
-// First chunk of a sweep: 0 forward, N-1 backward.
-__device__ __forceinline__ int first_chunk(int dir, int N) { return dir ? N - 1 : 0; }
-
-// Scale the 8 values of an operand by per-k factors f[k0 + op_k(i)].
-__device__ __forceinline__ bf16x8 scale_op(bf16x8 v, const float* f, int k0, int hi) {
-  float x[8];
-#pragma unroll
-  for (int i = 0; i < 8; i++) x[i] = (float)v[i] * f[k0 + op_k(i, hi)];
-  return pack8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
+// Per-lane LDS offsets for one phase of a step, rebuilt from an opaque lane
+// id behind a scheduling fence rather than kept live: every XOR-swizzled
+// operand address is its own register, and the compiler would otherwise
+// compute all of them once, keep them across the chunk loop and spill.
+__device__ __forceinline__ Lofs<kD> phase_lofs(int lane) {
+  const Lofs<kD> o(opaque_v(lane));
+  __builtin_amdgcn_sched_barrier(0);
+  return o;
 }
 
-// ------------------------------------------------------------ chunk states
-// Workgroup (b*H + h, dir): 8 waves own the 128 x 128 transposed state
-// tile S^T (wave w: value rows 32(w & 3).., key columns 64(w >> 2) .., two
-// 32x32 tiles; lane = key index, so each lane stores four consecutive values
-// per 8-byte store).  Keeping the whole state in one workgroup reads each
-// chunk's X once; the kernel moves about 1.1 GB per call on the benchmark
-// workload and is bound by HBM bandwidth.
-// dir 0 sweeps chunks forward and writes h_n (the state entering chunk n);
-// dir 1 sweeps backward and writes dH_{n+1} (zero for the last chunk); both
-// as [K][V] bf16.  Per chunk: X (k or q) and Y (v or do) arrive by LDS-DMA
-// two chunks ahead; the update
-// is S = exp(Gl) S + X^T (f o Y) with f_s = exp(Gl - G_s) (forward) or
-// scale * exp(G_t) (backward), 0 past the end of the sequence.  The state
-// stores stay in flight: each step waits only for its own tile loads.
-__global__ __launch_bounds__(512) void gla_states_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                                         const uint16_t* __restrict__ v,
-                                                         const uint16_t* __restrict__ dout,
-                                                         const float* __restrict__ g, uint16_t* __restrict__ hs,
-                                                         uint16_t* __restrict__ dhs, int T, int H, float scale) {
-  // Three buffers, chunk i of the sweep in buffer i % 3, loaded two steps
-  // ahead.  A buffer's Y tile is followed by the chunk's raw g (64 fp32).
-  // The loads are LDS-DMA issued as inline assembly and waited for
-  // explicitly.
+template <int DIR>
+__device__ __forceinline__ void gla_sweep(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                          const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+                                          const float* __restrict__ g, uint16_t* __restrict__ dx0,
+                                          uint16_t* __restrict__ dx1, float* __restrict__ dGp, int T, int H,
+                                          float scale, uint16_t (*sQ)[kC * kD], uint16_t (*sK)[kC * kD],
+                                          uint16_t* sV, uint16_t (*sO)[kC * kD], uint16_t* sS, float (*sG)[kC]) {
   constexpr int NW = 8;
-  constexpr int kXT = kC * kD, kYT = kC * kD + 2 * kC;
-  __shared__ __attribute__((aligned(16))) uint16_t sX[3 * kXT];
-  __shared__ __attribute__((aligned(16))) uint16_t sY[3 * kYT];
-  __shared__ float sG[NW][kC];  // per-wave copies: running sums of g, token factors
-  __shared__ float sF[NW][kC];
-
+  constexpr int kSt = DIR ? kStB : kStF;
+  static_assert(tile_load_ops<kD, kC, NW>() == 2, "two LDS-DMA instructions per wave and tile");
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), hi = lane >> 5;
-  const int bh = blockIdx.x, dir = blockIdx.z;
-  const int b = bh / H, h = bh % H;
+  const int l32 = lane & 31;
+  const int bh = blockIdx.x, b = bh / H, h = bh % H;
   const int N = (T + kC - 1) / kC;
   const size_t rs = (size_t)H * kD;
-  const uint16_t* X = (dir ? q : k) + ((size_t)b * T * H + h) * kD;
-  const uint16_t* Y = (dir ? dout : v) + ((size_t)b * T * H + h) * kD;
-  const float* gb = g + (size_t)b * T * H + h;
-  // N + 1 state slots per (b, h): slot N takes the state after the last
-  // step, which nobody reads, so that every step stores (and loads)
-  // unconditionally and the wait counts below hold on every path.
-  uint16_t* out = (dir ? dhs : hs) + (size_t)bh * (N + 1) * kD * kD;
-  const int vb = 32 * (w & 3), kb = 64 * (w >> 2);  // this wave's value rows, key columns
-  const Lofs<kD> oD(lane);
-  float* wG = sG[w];
-  float* wF = sF[w];
+  const size_t base = ((size_t)b * T * H + h) * kD;
+  const int vb = 32 * (w & 3), kb = 64 * (w >> 2);  // state tiles of this wave
+  const int fb = w >> 1, tb = w & 1;                // output tile: feature block, token block
+  const int tok = 32 * tb + l32;                    // this lane's token within the chunk
+  // Score tiles, exchanged as ready-made MFMA operands through the state
+  // copy's space while it is not in use: tile id, 32-token half, lane, 16
+  // bytes each (2 KB per tile).
+  bf16x8* sM = reinterpret_cast<bf16x8*>(sS);
 
-  f32x16 acc[2] = {f32x16{}, f32x16{}};
-  // Loads of a chunk: 2 + 2 instructions per wave, one more (g) for wave 0.
-  auto load = [&](int n, int buf) {
-    uint16_t* sx = sX + buf * kXT;
-    uint16_t* sy = sY + buf * kYT;
-    tile_load_async_asm<kD, kC, NW>(X, rs, n * kC, T, sx, w, lane);
-    tile_load_async_asm<kD, kC, NW>(Y, rs, n * kC, T, sy, w, lane);
-    if (w == 0) {  // g of the chunk (rows past the end repeat the last row; masked below)
-      const int t = n * kC + min(lane, T - 1 - n * kC);
-      dma_b32_asm(gb + (size_t)t * H, lds_addr(sy + kC * kD));
-    }
+  auto chunk_at = [&](int i) { return DIR ? N - 1 - min(i, N - 1) : min(i, N - 1); };
+  // q, k, do of a chunk (double-buffered) and its g (wave 0; rows past the
+  // end read the last row and are masked), issued after the step's scan;
+  // v (single buffer) once every wave is done with it, after the step's
+  // first barrier.  All are LDS-DMA, waited for explicitly.
+  auto load_main = [&](int n, int buf) {
+    tile_load_async_asm<kD, kC, NW>(q + base, rs, n * kC, T, sQ[buf], w, lane);
+    tile_load_async_asm<kD, kC, NW>(k + base, rs, n * kC, T, sK[buf], w, lane);
+    tile_load_async_asm<kD, kC, NW>(dout + base, rs, n * kC, T, sO[buf], w, lane);
+    if (w == 0) dma_b32_asm(g + ((size_t)b * T + min(n * kC + lane, T - 1)) * H + h, lds_addr(sG[buf]));
   };
-  // S^T element j of tile nb: value vb + c_row(j), key kb + 32nb + l32;
-  // stored at [key][value], four consecutive values per store: one buffer
-  // store instruction each, kStoreOps in all.
-  constexpr int kStoreOps = 2 * 4;
-  auto store = [&](int slot) {
-    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(out + (size_t)slot * kD * kD, (uint32_t)(kD * kD * 2));
-    const uint32_t voff = (uint32_t)(((kb + (lane & 31)) * kD + vb + c_row(0, hi)) * 2);
+  auto load_v = [&](int n) { tile_load_async_asm<kD, kC, NW>(v + base, rs, n * kC, T, sV, w, lane); };
+
+  // The state starts at zero: its bf16 copy too (made visible by the first
+  // step's barrier).
+  f32x16 st[2] = {f32x16{}, f32x16{}};
+  auto store_state = [&]() {
 #pragma unroll
     for (int nb = 0; nb < 2; nb++)
 #pragma unroll
       for (int jg = 0; jg < 4; jg++) {
-        const u32x2 v = u32x2{pack_bf16x2(acc[nb][4 * jg], acc[nb][4 * jg + 1]),
-                              pack_bf16x2(acc[nb][4 * jg + 2], acc[nb][4 * jg + 3])};
-        // c_row(4jg, hi) - c_row(0, hi) = 8jg values; tile nb is 32 keys further.
-        __builtin_amdgcn_raw_buffer_store_b64(v, rs, voff, (int)((32 * nb * kD + 8 * jg) * 2), 0);
+        const int key = kb + 32 * nb + l32;
+        *reinterpret_cast<u32x2*>(sS + swz_off<kD>(key, vb + c_row(4 * jg, hi))) =
+            u32x2{pack_bf16x2(st[nb][4 * jg], st[nb][4 * jg + 1]), pack_bf16x2(st[nb][4 * jg + 2], st[nb][4 * jg + 3])};
       }
   };
-  // Order of a wave's vector-memory operations: loads of the first two
-  // chunks (the initial state's store between them), then per step i the
-  // loads of chunk i+2 (kLoadOps: the X and Y tiles; wave 0 adds one for
-  // g, which only makes its waits below stricter) and the store of a state
-  // (kStoreOps).  At step i >= 2, chunk i's loads are followed by a store,
-  // chunk i+1's loads and another store; at steps 0 and 1 by a store and
-  // one chunk's loads.  Waiting for "all but that many" is waiting for
-  // chunk i.
-  constexpr int kLoadOps = 2 * tile_load_ops<kD, kC, NW>();
-  static_assert(kLoadOps == 4 && kStoreOps == 8, "wait counts below assume 4 loads and 8 stores per step");
-  constexpr int kWaitLater = 2 * kStoreOps + kLoadOps, kWaitFirst = kStoreOps + kLoadOps;
-  const int first = first_chunk(dir, N), stepn = dir ? -1 : 1;
-  auto chunk_of = [&](int i) { return min(max(first + stepn * i, 0), N - 1); };  // past either end: a valid chunk
-  load(chunk_of(0), 0);
-  store(first);
-  load(chunk_of(1), 1);
+  store_state();
+  load_main(chunk_at(0), 0);
+  load_v(chunk_at(0));
+  wait_vmem();
+
   for (int i = 0; i < N; i++) {
-    const int n = first + stepn * i;
-    const int buf = i % 3;
-    const uint16_t* sx = sX + buf * kXT;
-    const uint16_t* sy = sY + buf * kYT;
+    const int n = chunk_at(i);
+    const int buf = i & 1;
+    const uint16_t* cQ = sQ[buf];
+    const uint16_t* cK = sK[buf];
+    const uint16_t* cV = sV;
+    const uint16_t* cO = sO[buf];
     const int nv = min(kC, T - n * kC);
-    const int next = n + stepn;
-    const int next_st = (next < 0 || next >= N) ? N : next;  // past either end: the spare slot
-    if (i >= 2)
-      wait_vmem_but<kWaitLater>();
-    else
-      wait_vmem_but<kWaitFirst>();
-    lds_barrier();  // chunk n resident; every wave is done with step i-1 (and its buffer)
-    // Every wave scans the chunk's g itself (no second barrier).
-    chunk_scan(lane < nv ? reinterpret_cast<const float*>(sy + kC * kD)[lane] : 0.f, wG, lane);
-    const float gl = wG[nv - 1];
-    const float f = dir ? scale * __expf(wG[lane]) : __expf(gl - wG[lane]);
-    wF[lane] = lane < nv ? f : 0.f;
+    wait_vmem_but<kSt>();  // all but the previous step's stores: chunk n's tiles and g have landed
+    lds_barrier();         // chunk n resident, the state copy complete; every wave is done with step i-1
+
+    // G_t of the chunk in every lane t, its last value gl.
+    const float Gl = wave_scan(lane < nv ? sG[buf][lane] : 0.f, lane);
+    load_main(chunk_at(i + 1), buf ^ 1);
+    const float gl = lane_value(Gl, nv - 1);
     const float decay = __expf(gl);
-    bf16x8 ao[kC / 16], bo[kC / 16][2];
+    const float G_tok = __shfl(Gl, tok, 64);
+
+    // 32x32 product over the 128 features of rows 32 ra.. of ta and rows
+    // 32 rb.. of tb_: row = ta's token, column (lane) = tb_'s token.
+    auto score = [&](const uint16_t* ta, int ra, const uint16_t* tb_, int rb) {
+      const Lofs<kD> oD = phase_lofs(lane);
+      f32x16 acc = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < kC / 16; ks++) {
-      ao[ks] = scale_op(op_tr<kD>(sy, oD, 16 * ks, vb), wF, 16 * ks, hi);
+      for (int ks = 0; ks < kD / 16; ks++)
+        acc = mfma32(op_row16<kD>(ta, oD, 32 * ra, 16 * ks), op_row16<kD>(tb_, oD, 32 * rb, 16 * ks), acc);
+      return acc;
+    };
+    // Mask and scale of a score tile whose lanes are the tokens 32 lb.. and
+    // registers the tokens 32 rb + c_row(j): scale e^{G_t - G_s} for s <= t
+    // (dir 0: lane = t, register = s; dir 1: lane = s, register = t), t
+    // within the chunk, else 0; then the tile's two 16-token operand halves
+    // go to the exchange area as tile `id`.
+    auto publish = [&](const f32x16& acc, int lb, int rb, int id) {
+      const int own = 32 * lb + l32;
+      const float G_own = __shfl(Gl, own, 64);
+      float f[16];
 #pragma unroll
-      for (int nb = 0; nb < 2; nb++) bo[ks][nb] = op_tr<kD>(sx, oD, 16 * ks, kb + 32 * nb);
+      for (int j = 0; j < 16; j++) {
+        // The register's token depends on the lane only through hi: two lane
+        // reads, both taken (a conditional one would run in divergent control
+        // flow, where the source register's other lanes are not defined).
+        const int oth = 32 * rb + c_row(j, hi);
+        const float G_lo = lane_value(Gl, 32 * rb + c_row(j, 0)), G_hi = lane_value(Gl, 32 * rb + c_row(j, 1));
+        const float G_oth = hi ? G_hi : G_lo;
+        const bool keep = DIR ? (own <= oth && oth < nv) : (oth <= own && own < nv);
+        f[j] = keep ? scale * __expf(DIR ? G_oth - G_own : G_own - G_oth) : 0.f;
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; hh++) {
+        const int o = 8 * hh;
+        sM[(2 * id + hh) * 64 + lane] =
+            pack8(acc[o] * f[o], acc[o + 1] * f[o + 1], acc[o + 2] * f[o + 2], acc[o + 3] * f[o + 3],
+                  acc[o + 4] * f[o + 4], acc[o + 5] * f[o + 5], acc[o + 6] * f[o + 6], acc[o + 7] * f[o + 7]);
+      }
+    };
+    // Per-token factor of a state update, for the 8 tokens of operand
+    // k-step ks (lane t holds f_t).
+    auto scale_by = [&](bf16x8 x, float f_lane, int ks) {
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        const float f_lo = lane_value(f_lane, 16 * ks + op_k(e, 0)), f_hi = lane_value(f_lane, 16 * ks + op_k(e, 1));
+        y[e] = (float)x[e] * (hi ? f_hi : f_lo);
+      }
+      return pack8(y[0], y[1], y[2], y[3], y[4], y[5], y[6], y[7]);
+    };
+    // State update: st^T[value][key] = e^{gl} st^T + sum_x f_x ty[x][value] tx[x][key].
+    auto update = [&](const uint16_t* ty, const uint16_t* tx, float f_lane) {
+      const Lofs<kD> oD = phase_lofs(lane);
+#pragma unroll
+      for (int nb = 0; nb < 2; nb++) st[nb] *= decay;
+#pragma unroll
+      for (int ks = 0; ks < kC / 16; ks++) {
+        const bf16x8 a = scale_by(op_tr<kD>(ty, oD, 16 * ks, vb), f_lane, ks);
+#pragma unroll
+        for (int nb = 0; nb < 2; nb++) st[nb] = mfma32(a, op_tr<kD>(tx, oD, 16 * ks, kb + 32 * nb), st[nb]);
+      }
+    };
+
+    // Outputs leave as whole rows: a wave puts its 32 tokens x 32 features
+    // into a staging tile ([token][feature], swizzled like the input tiles;
+    // four features per 8-byte write), and after a barrier each wave copies
+    // 8 of the 64 rows out, 16 lanes per 256-byte row (two 16-byte stores
+    // per lane).  Rows past the end of the sequence fall outside the buffer
+    // range and are dropped.
+    auto stage = [&](uint16_t* tile, const f32x16& a) {
+#pragma unroll
+      for (int jg = 0; jg < 4; jg++)
+        *reinterpret_cast<u32x2*>(tile + swz_off<kD>(tok, 32 * fb + c_row(4 * jg, hi))) =
+            u32x2{pack_bf16x2(a[4 * jg], a[4 * jg + 1]), pack_bf16x2(a[4 * jg + 2], a[4 * jg + 3])};
+    };
+    auto store_rows = [&](uint16_t* dst, const uint16_t* tile) {
+      const __amdgpu_buffer_rsrc_t ro =
+          buffer_rsrc(dst + base + (size_t)n * kC * rs, (uint32_t)(((size_t)(nv - 1) * rs + kD) * 2));
+      const int cs = lane & 15;
+#pragma unroll
+      for (int jj = 0; jj < 2; jj++) {
+        const int r = 4 * (w + NW * jj) + (lane >> 4);  // token row of this lane
+        const u32x4 x = *reinterpret_cast<const u32x4*>(tile + swz_off<kD>(r, 8 * cs));
+        __builtin_amdgcn_raw_buffer_store_b128(x, ro, (uint32_t)(((size_t)r * rs + 8 * cs) * 2), 0, 0);
+      }
+    };
+    // x_t . d_t over this wave's 32 features (x from the chunk tile), one
+    // partial per (feature block, token): dGp[DIR][bh][fb][t].
+    auto store_dot = [&](const uint16_t* tx, const f32x16& a) {
+      float p = 0.f;
+#pragma unroll
+      for (int jg = 0; jg < 4; jg++) {
+        const u32x2 xv = *reinterpret_cast<const u32x2*>(tx + swz_off<kD>(tok, 32 * fb + c_row(4 * jg, hi)));
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) {
+          const uint32_t wx = xv[jj >> 1];
+          p = fmaf(__uint_as_float((jj & 1) ? (wx & 0xffff0000u) : (wx << 16)), a[4 * jg + jj], p);
+        }
+      }
+      p = xhalf_sum(p);
+      const __amdgpu_buffer_rsrc_t rd =
+          buffer_rsrc(dGp + (((size_t)DIR * gridDim.x + bh) * 4 + fb) * T + (size_t)n * kC, (uint32_t)(nv * 4));
+      // lanes of the upper half write past the range (dropped)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(p), rd, hi ? 0x40000000u : (uint32_t)(tok * 4), 0, 0);
+    };
+
+    // Phases of a step: (S) state terms, reading the state copy; (M) score
+    // tiles, one per wave (dir 0: four tiles; there every wave also updates
+    // the state here); barrier; the next chunk's v goes out, the tiles
+    // replace the state copy; barrier; (I) in-chunk terms, outputs staged
+    // (dir 1: then the state update); barrier; rows out (dir 1: barrier);
+    // the new state copy.
+    if constexpr (DIR == 0) {
+      // dq^T[d][t] = scale e^{G_t} sum_v h[d][v] do[t][v] + sum_s k[s][d] M_dov[t][s]
+      f32x16 aq = f32x16{};
+      {
+        const Lofs<kD> oD = phase_lofs(lane);
+#pragma unroll
+        for (int ks = 0; ks < kD / 16; ks++)
+          aq = mfma32(op_row16<kD>(sS, oD, 32 * fb, 16 * ks), op_row16<kD>(cO, oD, 32 * tb, 16 * ks), aq);
+      }
+      aq *= scale * __expf(G_tok);
+      // h_{n+1} = e^{gl} h_n + sum_s e^{gl - G_s} k_s^T v_s (s < nv)
+      const float f_lane = lane < nv ? __expf(gl - Gl) : 0.f;
+      f32x16 m;
+      if (w < 4) m = score(cV, w >> 1, cO, w & 1);  // M_dov^T[s][t]: s block w >> 1, t block w & 1
+      update(cV, cK, f_lane);
+      lds_barrier();  // every wave is done with the state copy and with v
+      load_v(chunk_at(i + 1));
+      if (w < 4) publish(m, w & 1, w >> 1, w);
+      lds_barrier();  // score tiles complete
+      {
+        const Lofs<kD> oD = phase_lofs(lane);
+#pragma unroll
+        for (int ks = 0; ks < kC / 16; ks++)
+          aq = mfma32(op_tr<kD>(cK, oD, 16 * ks, 32 * fb), sM[(2 * ((ks >> 1) * 2 + tb) + (ks & 1)) * 64 + lane], aq);
+      }
+      store_dot(cQ, aq);
+      // dq is staged where this wave's lanes just read q (no other wave reads
+      // the q tile after the first barrier).
+      uint16_t* tq = sQ[buf];
+      stage(tq, aq);
+      lds_barrier();  // staged rows complete; every wave is done with the score tiles
+      store_rows(dx0, tq);
+    } else {
+      // dk^T[d][s] = e^{gl - G_s} sum_v dH[d][v] v[s][v] + sum_t q[t][d] M_dov[t][s]
+      // dv^T[v][s] = e^{gl - G_s} sum_k dH[k][v] k[s][k] + sum_t do[t][v] M_qk[t][s]
+      f32x16 ak = f32x16{}, av = f32x16{};
+      {
+        const Lofs<kD> oD = phase_lofs(lane);
+#pragma unroll
+        for (int ks = 0; ks < kD / 16; ks++) {
+          ak = mfma32(op_row16<kD>(sS, oD, 32 * fb, 16 * ks), op_row16<kD>(cV, oD, 32 * tb, 16 * ks), ak);
+          av = mfma32(op_tr<kD>(sS, oD, 16 * ks, 32 * fb), op_row<kD>(cK, oD, 32 * tb, 16 * ks), av);
+        }
+      }
+      const float fkv = __expf(gl - G_tok);
+      ak *= fkv;
+      av *= fkv;
+      // Tile w: type w >> 2 (M_dov, M_qk), t block (w >> 1) & 1, s block w & 1.
+      const f32x16 m = (w >> 2) ? score(cQ, (w >> 1) & 1, cK, w & 1) : score(cO, (w >> 1) & 1, cV, w & 1);
+      lds_barrier();  // every wave is done with the state copy and with v
+      load_v(chunk_at(i + 1));
+      publish(m, w & 1, (w >> 1) & 1, w);
+      lds_barrier();  // score tiles complete
+      {
+        const Lofs<kD> oD = phase_lofs(lane);
+#pragma unroll
+        for (int ks = 0; ks < kC / 16; ks++) {
+          const int id = (ks >> 1) * 2 + tb;
+          ak = mfma32(op_tr<kD>(cQ, oD, 16 * ks, 32 * fb), sM[(2 * id + (ks & 1)) * 64 + lane], ak);
+          av = mfma32(op_tr<kD>(cO, oD, 16 * ks, 32 * fb), sM[(2 * (4 + id) + (ks & 1)) * 64 + lane], av);
+        }
+      }
+      store_dot(cK, ak);
+      // dk is staged where this wave's lanes just read k (no other wave reads
+      // the k tile after the first barrier), dv in the half of the state
+      // copy's space the score tiles leave free.
+      uint16_t* tk = sK[buf];
+      uint16_t* tv = sS + kC * kD;
+      stage(tk, ak);
+      stage(tv, av);
+      // dH_n = e^{gl} dH_{n+1} + scale sum_t e^{G_t} q_t^T do_t (t < nv)
+      update(cO, cQ, lane < nv ? scale * __expf(Gl) : 0.f);
+      lds_barrier();  // staged rows complete; every wave is done with the score tiles
+      store_rows(dx0, tk);
+      store_rows(dx1, tv);
+      lds_barrier();  // every wave is done with the staged dv
     }
-    asm volatile("" ::: "memory");
-    load(chunk_of(i + 2), (i + 2) % 3);
-#pragma unroll
-    for (int nb = 0; nb < 2; nb++) acc[nb] *= decay;
-#pragma unroll
-    for (int ks = 0; ks < kC / 16; ks++)
-#pragma unroll
-      for (int nb = 0; nb < 2; nb++) acc[nb] = mfma32(ao[ks], bo[ks][nb], acc[nb]);
-    store(next_st);
+    store_state();
   }
   wait_vmem();  // the last loads (into buffers nobody reads) before the LDS goes away
 }
 
-// ------------------------------------------------------------ per-chunk stage
-// Workgroup (chunk n, b*H + h), 8 waves.  LDS: q, k, v, do of the chunk
-// [64][128], h_n and dH_{n+1} [128][128] (bf16, from the states kernel),
-// the masked score matrices Mqk[t][s] = scale e^{G_t - G_s} (q_t.k_s) and
-// Mdov[t][s] = scale e^{G_t - G_s} (do_t.v_s) for s <= t < nv (0 elsewhere).
-// The outputs are computed transposed (dq^T [d][t], dk^T [d][s], dv^T
-// [v][s]): a lane holds one token, so the state terms' per-token factors
-// scale whole lanes, each lane writes four consecutive features per 8-byte
-// store, and q.dq, k.dk are sums inside the lane.  Wave w owns feature rows
-// 32(w >> 1) .. +31 and tokens 32(w & 1) .. +31 of each output.
-// Outputs: dq, dk, dv (bf16) of the chunk's valid rows and
-// dG_t = q_t.dq_t - k_t.dk_t (fp32), summed over the sequence by gla_dg.
-__global__ __launch_bounds__(512) void gla_dqkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                                       const uint16_t* __restrict__ v,
-                                                       const uint16_t* __restrict__ dout,
-                                                       const float* __restrict__ g, const uint16_t* __restrict__ hs,
-                                                       const uint16_t* __restrict__ dhs, uint16_t* __restrict__ dq,
-                                                       uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
-                                                       float* __restrict__ dG, int T, int H, float scale) {
-  constexpr int NW = 8;
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[kC * kD];
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kC * kD];
+__global__ __launch_bounds__(512) void gla_sweep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                        const uint16_t* __restrict__ v,
+                                                        const uint16_t* __restrict__ dout,
+                                                        const float* __restrict__ g, uint16_t* __restrict__ dq,
+                                                        uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+                                                        float* __restrict__ dGp, int T, int H, float scale) {
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][kC * kD];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kC * kD];
+  __shared__ __attribute__((aligned(16))) uint16_t sO[2][kC * kD];
   __shared__ __attribute__((aligned(16))) uint16_t sV[kC * kD];
-  __shared__ __attribute__((aligned(16))) uint16_t sO[kC * kD];  // dO
-  __shared__ __attribute__((aligned(16))) uint16_t sH[kD * kD];
-  __shared__ __attribute__((aligned(16))) uint16_t sDH[kD * kD];
-  __shared__ __attribute__((aligned(16))) uint16_t sMqk[kC * kC];
-  __shared__ __attribute__((aligned(16))) uint16_t sMdov[kC * kC];
-  __shared__ float sGr[kC];  // raw g of the chunk (LDS-DMA)
-  __shared__ float sG[kC];
-  __shared__ float sdG[2][4][kC];  // [q.dq or k.dk][feature block][token], each entry written once
-
-  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), hi = lane >> 5;
-  const int l32 = lane & 31;
-  const int n = blockIdx.x, bh = blockIdx.y;
-  const int b = bh / H, h = bh % H;
-  const int N = (T + kC - 1) / kC;
-  const int nv = min(kC, T - n * kC);
-  const size_t rs = (size_t)H * kD;
-  const size_t base = ((size_t)b * T * H + h) * kD;
-  const size_t st_off = ((size_t)bh * (N + 1) + n) * kD * kD;
-  const Lofs<kD> oD(lane);
-  const Lofs<kC> oC(lane);
-
-  // Token tiles and g first, state tiles last, all by LDS-DMA issued as
-  // inline assembly: the compiler adds no waits of its own, so the state
-  // tiles keep arriving during the scan and the score products; the explicit
-  // waits below (all but the 8 state-tile loads of this wave, then all) are
-  // the only ones.
-  tile_load_async_asm<kD, kC, NW>(q + base, rs, n * kC, T, sQ, w, lane);
-  tile_load_async_asm<kD, kC, NW>(k + base, rs, n * kC, T, sK, w, lane);
-  tile_load_async_asm<kD, kC, NW>(v + base, rs, n * kC, T, sV, w, lane);
-  tile_load_async_asm<kD, kC, NW>(dout + base, rs, n * kC, T, sO, w, lane);
-  if (w == 0) {  // rows past the end repeat the last row; masked in the scan
-    const int t = n * kC + min(lane, nv - 1);
-    dma_b32_asm(g + ((size_t)b * T + t) * H + h, lds_addr(sGr));
-  }
-  tile_load_async_asm<kD, kD, NW>(hs + st_off, kD, 0, kD, sH, w, lane);
-  tile_load_async_asm<kD, kD, NW>(dhs + st_off, kD, 0, kD, sDH, w, lane);
-  wait_vmem_but<8>();
-  lds_barrier();
-  if (w == 0) chunk_scan(lane < nv ? sGr[lane] : 0.f, sG, lane);
-  lds_barrier();
-
-  // Masked score matrices: wave w computes the 32x32 block (s-block
-  // (w >> 1) & 1, t-block w & 1) of Mqk (w < 4) or Mdov (w >= 4), as
-  // S^T[s][t] (A = k or v rows, B = q or do rows), and writes it
-  // transposed, [t][s], four s values per 8-byte store.
-  // (Each half of the waves names its tiles directly: a pointer chosen at
-  // run time between LDS arrays hides from the compiler that these reads
-  // cannot touch the state tiles still arriving.)
-  auto scores = [&](const uint16_t* ta, const uint16_t* tb_, uint16_t* dst) {
-    const int sb = (w >> 1) & 1, tb = w & 1;
-    f32x16 acc = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < kD / 16; ks++)
-      acc = mfma32(op_row<kD>(ta, oD, 32 * sb, 16 * ks), op_row<kD>(tb_, oD, 32 * tb, 16 * ks), acc);
-    const int t = 32 * tb + l32;
-    const float gt = sG[t];
-#pragma unroll
-    for (int jg = 0; jg < 4; jg++) {
-      float m[4];
-#pragma unroll
-      for (int jj = 0; jj < 4; jj++) {
-        const int s = 32 * sb + c_row(4 * jg + jj, hi);
-        m[jj] = (s <= t && t < nv) ? acc[4 * jg + jj] * (scale * __expf(gt - sG[s])) : 0.f;
-      }
-      *reinterpret_cast<u32x2*>(dst + swz_off<kC>(t, 32 * sb + c_row(4 * jg, hi))) =
-          u32x2{pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3])};
-    }
-  };
-  if (w < 4)
-    scores(sK, sQ, sMqk);
+  __shared__ __attribute__((aligned(16))) uint16_t sS[kD * kD];
+  __shared__ __attribute__((aligned(16))) float sG[2][kC];
+  if (blockIdx.y == 0)
+    gla_sweep<0>(q, k, v, dout, g, dq, nullptr, dGp, T, H, scale, sQ, sK, sV, sO, sS, sG);
   else
-    scores(sV, sO, sMdov);
-  lds_barrier();
-
-  const int fb = w >> 1, tb = w & 1;  // feature block (32 wide), token block
-  const int tok = 32 * tb + l32;      // this lane's token
-  const float gl = sG[nv - 1];
-
-  // In-chunk products (transposed):
-  //   dq^T[d][t] = sum_s k[s][d] Mdov[t][s]     dk^T[d][s] = sum_t q[t][d] Mdov[t][s]
-  //   dv^T[v][s] = sum_t do[t][v] Mqk[t][s]
-  f32x16 aq = f32x16{}, ak = f32x16{}, av = f32x16{};
-#pragma unroll
-  for (int ks = 0; ks < kC / 16; ks++) {
-    aq = mfma32(op_tr<kD>(sK, oD, 16 * ks, 32 * fb), op_row<kC>(sMdov, oC, 32 * tb, 16 * ks), aq);
-    ak = mfma32(op_tr<kD>(sQ, oD, 16 * ks, 32 * fb), op_tr<kC>(sMdov, oC, 16 * ks, 32 * tb), ak);
-    av = mfma32(op_tr<kD>(sO, oD, 16 * ks, 32 * fb), op_tr<kC>(sMqk, oC, 16 * ks, 32 * tb), av);
-  }
-  wait_vmem();
-  lds_barrier();  // h_n and dH_{n+1} resident
-  // State terms (transposed), scaled per token (per lane):
-  //   dq^T += scale e^{G_t} h do^T        dk^T += e^{Gl - G_s} dH v^T
-  //   dv^T += e^{Gl - G_s} dH^T k^T
-  f32x16 sq = f32x16{}, sk = f32x16{}, sv = f32x16{};
-#pragma unroll
-  for (int ks = 0; ks < kD / 16; ks++) {
-    sq = mfma32(op_row<kD>(sH, oD, 32 * fb, 16 * ks), op_row<kD>(sO, oD, 32 * tb, 16 * ks), sq);
-    sk = mfma32(op_row<kD>(sDH, oD, 32 * fb, 16 * ks), op_row<kD>(sV, oD, 32 * tb, 16 * ks), sk);
-    sv = mfma32(op_tr<kD>(sDH, oD, 16 * ks, 32 * fb), op_row<kD>(sK, oD, 32 * tb, 16 * ks), sv);
-  }
-  const float fq = scale * __expf(sG[tok]), fkv = __expf(gl - sG[tok]);
-  aq += fq * sq;
-  ak += fkv * sk;
-  av += fkv * sv;
-
-  // q.dq and k.dk over this wave's 32 features: in-lane sums, the other
-  // lane half, then one partial per (feature block, token) in LDS.
-  float pq = 0.f, pk = 0.f;
-#pragma unroll
-  for (int jg = 0; jg < 4; jg++) {
-    const int f0 = 32 * fb + c_row(4 * jg, hi);
-    const u32x2 qv = *reinterpret_cast<const u32x2*>(sQ + swz_off<kD>(tok, f0));
-    const u32x2 kv = *reinterpret_cast<const u32x2*>(sK + swz_off<kD>(tok, f0));
-#pragma unroll
-    for (int jj = 0; jj < 4; jj++) {
-      const uint32_t wq = qv[jj >> 1], wk = kv[jj >> 1];
-      const float xq = __uint_as_float((jj & 1) ? (wq & 0xffff0000u) : (wq << 16));
-      const float xk = __uint_as_float((jj & 1) ? (wk & 0xffff0000u) : (wk << 16));
-      pq = fmaf(xq, aq[4 * jg + jj], pq);
-      pk = fmaf(xk, ak[4 * jg + jj], pk);
-    }
-  }
-  pq = xhalf_sum(pq);
-  pk = xhalf_sum(pk);
-  if (hi == 0) {
-    sdG[0][fb][tok] = pq;
-    sdG[1][fb][tok] = pk;
-  }
-  lds_barrier();  // every wave is done with the state tiles; the q.dq / k.dk partials are complete
-  // The outputs go out as whole rows: staged as bf16 [token][feature] tiles
-  // (swizzled) in the state tiles' space, then copied with 16-byte stores,
-  // each 256-byte row written by 16 consecutive lanes of one instruction.
-  // (Rows assembled from 8-byte pieces of four waves reached HBM as partial
-  // line writes, about 1.8 times the output bytes.)
-  uint16_t* stq = sH;
-  uint16_t* stk = sH + kC * kD;
-  uint16_t* stv = sDH;
-#pragma unroll
-  for (int jg = 0; jg < 4; jg++) {
-    const int o = swz_off<kD>(tok, 32 * fb + c_row(4 * jg, hi));
-    *reinterpret_cast<u32x2*>(stq + o) = u32x2{pack_bf16x2(aq[4 * jg], aq[4 * jg + 1]),
-                                               pack_bf16x2(aq[4 * jg + 2], aq[4 * jg + 3])};
-    *reinterpret_cast<u32x2*>(stk + o) = u32x2{pack_bf16x2(ak[4 * jg], ak[4 * jg + 1]),
-                                               pack_bf16x2(ak[4 * jg + 2], ak[4 * jg + 3])};
-    *reinterpret_cast<u32x2*>(stv + o) = u32x2{pack_bf16x2(av[4 * jg], av[4 * jg + 1]),
-                                               pack_bf16x2(av[4 * jg + 2], av[4 * jg + 3])};
-  }
-  if (w == 0 && lane < nv) {
-    const float a = ((sdG[0][0][lane] + sdG[0][1][lane]) + (sdG[0][2][lane] + sdG[0][3][lane]));
-    const float c = ((sdG[1][0][lane] + sdG[1][1][lane]) + (sdG[1][2][lane] + sdG[1][3][lane]));
-    dG[(size_t)bh * T + n * kC + lane] = a - c;
-  }
-  lds_barrier();  // staged tiles complete
-  {
-    const int cs = lane & 15;
-#pragma unroll
-    for (int jj = 0; jj < 2; jj++) {
-      const int r = 4 * (w + NW * jj) + (lane >> 4);  // token row of this lane
-      if (r < nv) {
-        const int o = swz_off<kD>(r, 8 * cs);
-        const size_t g0 = base + (size_t)(n * kC + r) * rs + 8 * cs;
-        *reinterpret_cast<u32x4*>(dq + g0) = *reinterpret_cast<const u32x4*>(stq + o);
-        *reinterpret_cast<u32x4*>(dk + g0) = *reinterpret_cast<const u32x4*>(stk + o);
-        *reinterpret_cast<u32x4*>(dv + g0) = *reinterpret_cast<const u32x4*>(stv + o);
-      }
-    }
-  }
+    gla_sweep<1>(q, k, v, dout, g, dk, dv, dGp, T, H, scale, sQ, sK, sV, sO, sS, sG);
 }
 
-// dg[b, t, h] = sum_{t' >= t} dG[b*H + h][t']: one workgroup per (b, h),
-// segments of 4096 tokens from the end (16 consecutive tokens per thread:
-// in-thread suffix sums, then suffix sums of the thread totals across the
-// wave (shuffles) and the four waves (LDS)), the running total carried.
-__global__ __launch_bounds__(256) void gla_dg_kernel(const float* __restrict__ dG, float* __restrict__ dg, int T, int H) {
+// dg[b, t, h] = sum_{t' >= t} dG_{t'} with dG_t = q_t.dq_t - k_t.dk_t, each
+// dot summed from its four feature-block partials in a fixed order: one
+// workgroup per (b, h), segments of 4096 tokens from the end (16
+// consecutive tokens per thread: in-thread suffix sums, then suffix sums of
+// the thread totals across the wave (shuffles) and the four waves (LDS)),
+// the running total carried.
+__global__ __launch_bounds__(256) void gla_dg_kernel(const float* __restrict__ dGp, float* __restrict__ dg, int T, int H) {
   constexpr int PER = 16, SEG = 256 * PER;
   __shared__ float sW[4];
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
   const int bh = blockIdx.x, b = bh / H, h = bh % H;
-  const float* src = dG + (size_t)bh * T;
+  const float* pq = dGp + (size_t)bh * 4 * T;
+  const float* pk = dGp + ((size_t)gridDim.x + bh) * 4 * T;
+  auto src_at = [&](int t) {
+    const float a = (pq[t] + pq[T + t]) + (pq[2 * T + t] + pq[3 * T + t]);
+    const float c = (pk[t] + pk[T + t]) + (pk[2 * T + t] + pk[3 * T + t]);
+    return a - c;
+  };
   float* dst = dg + (size_t)b * T * H + h;
   float carry = 0.f;
   for (int seg_end = T; seg_end > 0; seg_end -= SEG) {
@@ -431,7 +446,7 @@ __global__ __launch_bounds__(256) void gla_dg_kernel(const float* __restrict__ d
 #pragma unroll
     for (int i = PER - 1; i >= 0; i--) {
       const int t = t0 + i;
-      tot += (t >= 0 ? src[t] : 0.f);
+      tot += (t >= 0 ? src_at(t) : 0.f);
       x[i] = tot;  // sum of this thread's tokens t0+i .. t0+PER-1
     }
     float suf = tot;  // inclusive suffix over the lanes of this wave
@@ -461,21 +476,13 @@ __global__ __launch_bounds__(256) void gla_dg_kernel(const float* __restrict__ d
 hipError_t launch_gla_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
                           const float* g, uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dg, void* workspace,
                           int B, int T, int H, float scale, hipStream_t stream) {
-  const int N = (T + kC - 1) / kC;
-  uint16_t* hs = (uint16_t*)workspace;
-  uint16_t* dhs = hs + (size_t)B * H * (N + 1) * kD * kD;
-  float* dG = (float*)(dhs + (size_t)B * H * (N + 1) * kD * kD);
-  hipLaunchKernelGGL(gla_states_kernel, dim3(B * H, 1, 2), dim3(512), 0, stream, q, k, v, dout, g, hs, dhs, T, H,
-                     scale);
-  hipLaunchKernelGGL(gla_dqkv_kernel, dim3(N, B * H), dim3(512), 0, stream, q, k, v, dout, g, hs, dhs, dq, dk, dv,
-                     dG, T, H, scale);
-  hipLaunchKernelGGL(gla_dg_kernel, dim3(B * H), dim3(256), 0, stream, dG, dg, T, H);
+  float* dGp = (float*)workspace;
+  hipLaunchKernelGGL(gla_sweep_kernel, dim3(B * H, 2), dim3(512), 0, stream, q, k, v, dout, g, dq, dk, dv, dGp, T,
+                     H, scale);
+  hipLaunchKernelGGL(gla_dg_kernel, dim3(B * H), dim3(256), 0, stream, dGp, dg, T, H);
   return hipGetLastError();
 }
 
-size_t gla_bwd_workspace_bytes(int B, int T, int H) {
-  const size_t N = (T + kC - 1) / kC;
-  return 2 * (size_t)B * H * (N + 1) * kD * kD * sizeof(uint16_t) + (size_t)B * T * H * sizeof(float);
-}
+size_t gla_bwd_workspace_bytes(int B, int T, int H) { return 2 * 4 * (size_t)B * H * T * sizeof(float); }
 
 }  // namespace mi355

@@ -261,8 +261,9 @@ def bench_varlen(args, bd, torch):
 
 
 def bench_gla(args, bd, torch):
-    """Simple gated linear attention, chunked backward (gla_chunk_bwd: chunk
-    states, per-chunk dq/dk/dv/dG, gate running sum) on the GLA workload.
+    """Simple gated linear attention, chunked backward (gla_chunk_bwd: the two
+    chunk sweeps with on-chip state, then the gate's running sum) on the GLA
+    workload.
     HBM-bound: ``value`` is the algorithmic bytes (q, k, v, do, g read once;
     dq, dk, dv, dg written once) per second of the whole call."""
     from attention_backward_fwd_amd.synthetic import GLA_WORKLOAD, gla_inputs
@@ -319,7 +320,7 @@ def bench_gla(args, bd, torch):
         "config": {"workload": w["name"], "batch": b, "seq_len": t, "heads": h, "head_dim": d, "chunk": 64},
         "bwd_ms": round(ms, 4), "tokens_per_s": round(b * t / (ms * 1e-3), 1),
         "mfma_tflops": round(flop / (ms * 1e-3) / 1e12, 3),
-        "roofline": {"kernel": "gla_states + gla_dqkv + gla_dg", "bound": "hbm", "achieved": round(gbs, 1),
+        "roofline": {"kernel": "gla_sweep + gla_dg", "bound": "hbm", "achieved": round(gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "traffic": recorded_traffic(w["name"], "chunk_bwd", GLA_SOURCES)},
         **({"cpu_baseline": cpu} if cpu else {}),
