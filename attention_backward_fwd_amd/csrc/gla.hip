@@ -22,8 +22,8 @@
 // (Gl: G at the chunk's last token).  Kernels: gla_sweep (per (b, h) one
 // workgroup walks the chunks forward carrying h_n and writes dq, another
 // walks them backward carrying dH_{n+1} and writes dk, dv; both keep the
-// state on chip, so it never goes to HBM, and write per-token partials of
-// q.dq and k.dk to the workspace), gla_dg (reverse running sum of
+// state on chip, so it never goes to HBM, and write the per-token q.dq and
+// k.dk to the workspace), gla_dg (reverse running sum of
 // q.dq - k.dk over the sequence).  This follows the page's account of where
 // the gains come from: state kept on chip and HBM round trips cut.
 #include "common.h"
@@ -36,37 +36,29 @@ namespace {
 constexpr int kC = 64;   // chunk length
 constexpr int kD = 128;  // head dim (K = V)
 
-// 32x32x16 operands from swizzled LDS tiles of DT-wide rows.  Both readers
-// hand out the k index of each 16-step in the same order (lane half hi gets
-// k = 4hi .. 4hi+3 and 8+4hi .. 8+4hi+3, the order of the rows of a 32x32
-// result's elements 0..7), so any pairing of them multiplies matching k.
-//   op_row: tile stored [x][k] (x = the lane's m or n index)
-//   op_tr:  tile stored [k][x]
+// 32x32x16 operands from swizzled LDS tiles of DT-wide rows, in two k
+// orders.  A product pairs operands of the same order:
+//   op_row16 (tile stored [x][k], x = the lane's m or n index) and op_trc
+//     (tile stored [k][x]): lane half hi gets k = 8hi .. 8hi+7;
+//   op_tr (tile stored [k][x]): k = 4hi .. 4hi+3 and 8+4hi .. 8+4hi+3, the
+//     order of the rows of a 32x32 result's elements 0..7, so it pairs with
+//     operands taken straight from MFMA results.
 // A lane's element offsets are built once (Lofs); a 16-step of k or a
 // 32-block of columns is an XOR of the offset and a block of rows an
 // addition (the swizzle permutes 8-element slots by the row's low 4 bits).
 template <int DT>
 struct Lofs {
-  int row, row16, tr0, tr1;
+  int row16, tr0, tr1, trc0, trc1;
   __device__ __forceinline__ explicit Lofs(int lane) {
     const int hi = lane >> 5, L = lane & 15, gp = (lane >> 4) & 1;
-    row = swz_off<DT>(lane & 31, 4 * hi);
     row16 = swz_off<DT>(lane & 31, 8 * hi);
     const int col = 16 * gp + 4 * (L & 3);
     tr0 = swz_off<DT>(4 * hi + (L >> 2), col);
     tr1 = swz_off<DT>(8 + 4 * hi + (L >> 2), col);
+    trc0 = swz_off<DT>(8 * hi + (L >> 2), col);
+    trc1 = swz_off<DT>(8 * hi + 4 + (L >> 2), col);
   }
 };
-template <int DT>
-__device__ __forceinline__ bf16x8 op_row(const uint16_t* t, const Lofs<DT>& o, int x0, int k0) {
-  const int a = (o.row ^ k0) + x0 * DT;
-  const u32x2 lo = *reinterpret_cast<const u32x2*>(t + a);
-  const u32x2 hi = *reinterpret_cast<const u32x2*>(t + (a ^ 8));
-  return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-}
-// Row operand with the k index in natural order (lane half hi: k = 8hi ..
-// 8hi+7, one 16-byte read); only for products whose other operand is read
-// the same way.
 template <int DT>
 __device__ __forceinline__ bf16x8 op_row16(const uint16_t* t, const Lofs<DT>& o, int x0, int k0) {
   return *reinterpret_cast<const bf16x8*>(t + ((o.row16 ^ k0) + x0 * DT));
@@ -74,6 +66,10 @@ __device__ __forceinline__ bf16x8 op_row16(const uint16_t* t, const Lofs<DT>& o,
 template <int DT>
 __device__ __forceinline__ bf16x8 op_tr(const uint16_t* t, const Lofs<DT>& o, int k0, int x0) {
   return lds_read_tr8(t + ((o.tr0 ^ x0) + k0 * DT), t + ((o.tr1 ^ x0) + k0 * DT));
+}
+template <int DT>
+__device__ __forceinline__ bf16x8 op_trc(const uint16_t* t, const Lofs<DT>& o, int k0, int x0) {
+  return lds_read_tr8(t + ((o.trc0 ^ x0) + k0 * DT), t + ((o.trc1 ^ x0) + k0 * DT));
 }
 // The k index (0..15 within a 16-step) of element i of a lane's operand.
 __device__ __forceinline__ int op_k(int i, int hi) { return (i < 4 ? 4 * hi + i : 8 + 4 * hi + (i - 4)); }
@@ -86,29 +82,31 @@ __device__ __forceinline__ int op_k(int i, int hi) { return (i < 4 ? 4 * hi + i 
 // the transposed tile S^T[value][key] in the 32x32 MFMA result layout (wave
 // w: value rows 32(w & 3).., key columns 64(w >> 2).., two tiles; lane = key
 // index), and as a bf16 [key][value] copy in LDS that the state terms read.
-// Per chunk, with its q, k, v, do tiles arriving by LDS-DMA one chunk ahead:
+// Per chunk, with its tiles arriving by LDS-DMA one chunk ahead (q, k, do
+// double-buffered; v single-buffered, reloaded once every wave is past its
+// last use):
 //   dir 0: dq (in-chunk term from k and M_dov, state term from h_n and do),
-//          the per-token partials of q.dq, then h_{n+1};
+//          q.dq per token, then h_{n+1};
 //   dir 1: dk, dv (in-chunk terms from q, do and M_dov, M_qk; state terms
-//          from dH_{n+1} and v, k), the partials of k.dk, then dH_n.
+//          from dH_{n+1} and v, k), k.dk per token, then dH_n.
 // The masked score tiles M_dov[t][s] = scale e^{G_t - G_s} (do_t . v_s) and
-// M_qk[t][s] (s <= t) never leave registers: every wave forms the two 32x32
-// tiles its own output columns need, in the result layout that is already
-// the operand layout of the in-chunk products (the four waves of a token
-// block form the same tiles: cheaper than a trip through LDS and two more
-// barriers).  Outputs are computed transposed (dq^T [d][t], dk^T [d][s],
-// dv^T [v][s]; wave w: feature rows 32(w >> 1).., tokens 32(w & 1)..), so a
-// lane holds one token: per-token factors scale whole lanes and each lane
-// stores four consecutive features per 8-byte store.
+// M_qk[t][s] (s <= t) are formed once per chunk, one 32x32 tile per wave,
+// in the result layout that is already the operand layout of the in-chunk
+// products, and exchanged as ready-made operands (16 bytes per lane) through
+// the state copy's LDS space, which the state terms have finished with by
+// then.  Outputs are computed transposed (dq^T [d][t], dk^T [d][s], dv^T
+// [v][s]; wave w: feature rows 32(w >> 1).., tokens 32(w & 1)..), so a lane
+// holds one token and per-token factors scale whole lanes; they leave as
+// whole rows through LDS staging.
 //
 // Every load is LDS-DMA and every store a buffer store, one instruction
 // each, issued in a fixed order per step: the next chunk's q, k, do (and g,
 // wave 0), its v after the first barrier, then this chunk's stores (kStF /
-// kStB per wave); waiting for "all but the stores" at the top of a step is
-// waiting for the chunk.  The chunk the last step loads is clamped to a
-// valid one (never used).
-constexpr int kStF = 2 + 1;      // dq (2 x 16 bytes of whole rows) + q.dq partial
-constexpr int kStB = 2 * 2 + 1;  // dk, dv + k.dk partial
+// kStB per wave, one more for wave 0); waiting for "all but the stores" at
+// the top of a step is waiting for the chunk.  The chunk the last step
+// loads is clamped to a valid one (never used).
+constexpr int kStF = 2;      // dq (2 x 16 bytes of whole rows); wave 0 adds the q.dq store
+constexpr int kStB = 2 * 2;  // dk, dv; wave 0 adds the k.dk store
 
 // The value a wave-uniform lane holds (v_readlane: no LDS round trip).
 __device__ __forceinline__ float lane_value(float x, int l) {
@@ -125,12 +123,17 @@ __device__ __forceinline__ float wave_scan(float x, int lane) {
   return x;
 }
 
-// Per-lane LDS offsets for one phase of a step, rebuilt from an opaque lane
-// id behind a scheduling fence rather than kept live: every XOR-swizzled
-// operand address is its own register, and the compiler would otherwise
+// Per-lane LDS offsets for one phase of a step: opaque copies of the base
+// offsets behind a scheduling fence.  Every XOR-swizzled operand
+// address is its own register; with the bases visible the compiler would
 // compute all of them once, keep them across the chunk loop and spill.
-__device__ __forceinline__ Lofs<kD> phase_lofs(int lane) {
-  const Lofs<kD> o(opaque_v(lane));
+__device__ __forceinline__ Lofs<kD> phase_lofs(const Lofs<kD>& b) {
+  Lofs<kD> o = b;
+  o.row16 = opaque_v(o.row16);
+  o.tr0 = opaque_v(o.tr0);
+  o.tr1 = opaque_v(o.tr1);
+  o.trc0 = opaque_v(o.trc0);
+  o.trc1 = opaque_v(o.trc1);
   __builtin_amdgcn_sched_barrier(0);
   return o;
 }
@@ -141,7 +144,8 @@ __device__ __forceinline__ void gla_sweep(const uint16_t* __restrict__ q, const 
                                           const float* __restrict__ g, uint16_t* __restrict__ dx0,
                                           uint16_t* __restrict__ dx1, float* __restrict__ dGp, int T, int H,
                                           float scale, uint16_t (*sQ)[kC * kD], uint16_t (*sK)[kC * kD],
-                                          uint16_t* sV, uint16_t (*sO)[kC * kD], uint16_t* sS, float (*sG)[kC]) {
+                                          uint16_t* sV, uint16_t (*sO)[kC * kD], uint16_t* sS, float (*sG)[kC],
+                                          float (*sD)[kC], float (*sW)[2][kC]) {
   constexpr int NW = 8;
   constexpr int kSt = DIR ? kStB : kStF;
   static_assert(tile_load_ops<kD, kC, NW>() == 2, "two LDS-DMA instructions per wave and tile");
@@ -154,6 +158,12 @@ __device__ __forceinline__ void gla_sweep(const uint16_t* __restrict__ q, const 
   const int vb = 32 * (w & 3), kb = 64 * (w >> 2);  // state tiles of this wave
   const int fb = w >> 1, tb = w & 1;                // output tile: feature block, token block
   const int tok = 32 * tb + l32;                    // this lane's token within the chunk
+  const Lofs<kD> lofs(lane);
+  // Per-token values of this wave, read back by the lanes that need them
+  // (16 bytes = 4 consecutive tokens per read): G of the chunk, and the
+  // factors of the state update.
+  float* wG = sW[w][0];
+  float* wF = sW[w][1];
   // Score tiles, exchanged as ready-made MFMA operands through the state
   // copy's space while it is not in use: tile id, 32-token half, lane, 16
   // bytes each (2 KB per tile).
@@ -198,20 +208,25 @@ __device__ __forceinline__ void gla_sweep(const uint16_t* __restrict__ q, const 
     const uint16_t* cV = sV;
     const uint16_t* cO = sO[buf];
     const int nv = min(kC, T - n * kC);
-    wait_vmem_but<kSt>();  // all but the previous step's stores: chunk n's tiles and g have landed
+    // All but the previous step's stores: chunk n's tiles and g have landed.
+    if (w == 0)
+      wait_vmem_but<kSt + 1>();
+    else
+      wait_vmem_but<kSt>();
     lds_barrier();         // chunk n resident, the state copy complete; every wave is done with step i-1
 
     // G_t of the chunk in every lane t, its last value gl.
     const float Gl = wave_scan(lane < nv ? sG[buf][lane] : 0.f, lane);
     load_main(chunk_at(i + 1), buf ^ 1);
+    wG[lane] = Gl;
     const float gl = lane_value(Gl, nv - 1);
     const float decay = __expf(gl);
-    const float G_tok = __shfl(Gl, tok, 64);
+    const float G_tok = wG[tok];
 
     // 32x32 product over the 128 features of rows 32 ra.. of ta and rows
     // 32 rb.. of tb_: row = ta's token, column (lane) = tb_'s token.
     auto score = [&](const uint16_t* ta, int ra, const uint16_t* tb_, int rb) {
-      const Lofs<kD> oD = phase_lofs(lane);
+      const Lofs<kD> oD = phase_lofs(lofs);
       f32x16 acc = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < kD / 16; ks++)
@@ -225,16 +240,12 @@ __device__ __forceinline__ void gla_sweep(const uint16_t* __restrict__ q, const 
     // go to the exchange area as tile `id`.
     auto publish = [&](const f32x16& acc, int lb, int rb, int id) {
       const int own = 32 * lb + l32;
-      const float G_own = __shfl(Gl, own, 64);
+      const float G_own = wG[own];
       float f[16];
 #pragma unroll
       for (int j = 0; j < 16; j++) {
-        // The register's token depends on the lane only through hi: two lane
-        // reads, both taken (a conditional one would run in divergent control
-        // flow, where the source register's other lanes are not defined).
         const int oth = 32 * rb + c_row(j, hi);
-        const float G_lo = lane_value(Gl, 32 * rb + c_row(j, 0)), G_hi = lane_value(Gl, 32 * rb + c_row(j, 1));
-        const float G_oth = hi ? G_hi : G_lo;
+        const float G_oth = reinterpret_cast<const f32x4*>(wG + 32 * rb + c_row(4 * (j >> 2), hi))[0][j & 3];
         const bool keep = DIR ? (own <= oth && oth < nv) : (oth <= own && own < nv);
         f[j] = keep ? scale * __expf(DIR ? G_oth - G_own : G_own - G_oth) : 0.f;
       }
@@ -246,25 +257,23 @@ __device__ __forceinline__ void gla_sweep(const uint16_t* __restrict__ q, const 
                   acc[o + 4] * f[o + 4], acc[o + 5] * f[o + 5], acc[o + 6] * f[o + 6], acc[o + 7] * f[o + 7]);
       }
     };
-    // Per-token factor of a state update, for the 8 tokens of operand
-    // k-step ks (lane t holds f_t).
-    auto scale_by = [&](bf16x8 x, float f_lane, int ks) {
-      float y[8];
-#pragma unroll
-      for (int e = 0; e < 8; e++) {
-        const float f_lo = lane_value(f_lane, 16 * ks + op_k(e, 0)), f_hi = lane_value(f_lane, 16 * ks + op_k(e, 1));
-        y[e] = (float)x[e] * (hi ? f_hi : f_lo);
-      }
-      return pack8(y[0], y[1], y[2], y[3], y[4], y[5], y[6], y[7]);
+    // Per-token factor of a state update for the 8 tokens of operand k-step
+    // ks (from wF: tokens 16 ks + op_k(e), two runs of four).
+    auto scale_by = [&](bf16x8 x, int ks) {
+      const f32x4 f0 = *reinterpret_cast<const f32x4*>(wF + 16 * ks + op_k(0, hi));
+      const f32x4 f1 = *reinterpret_cast<const f32x4*>(wF + 16 * ks + op_k(4, hi));
+      return pack8((float)x[0] * f0[0], (float)x[1] * f0[1], (float)x[2] * f0[2], (float)x[3] * f0[3],
+                   (float)x[4] * f1[0], (float)x[5] * f1[1], (float)x[6] * f1[2], (float)x[7] * f1[3]);
     };
     // State update: st^T[value][key] = e^{gl} st^T + sum_x f_x ty[x][value] tx[x][key].
     auto update = [&](const uint16_t* ty, const uint16_t* tx, float f_lane) {
-      const Lofs<kD> oD = phase_lofs(lane);
+      wF[lane] = f_lane;
+      const Lofs<kD> oD = phase_lofs(lofs);
 #pragma unroll
       for (int nb = 0; nb < 2; nb++) st[nb] *= decay;
 #pragma unroll
       for (int ks = 0; ks < kC / 16; ks++) {
-        const bf16x8 a = scale_by(op_tr<kD>(ty, oD, 16 * ks, vb), f_lane, ks);
+        const bf16x8 a = scale_by(op_tr<kD>(ty, oD, 16 * ks, vb), ks);
 #pragma unroll
         for (int nb = 0; nb < 2; nb++) st[nb] = mfma32(a, op_tr<kD>(tx, oD, 16 * ks, kb + 32 * nb), st[nb]);
       }
@@ -293,9 +302,10 @@ __device__ __forceinline__ void gla_sweep(const uint16_t* __restrict__ q, const 
         __builtin_amdgcn_raw_buffer_store_b128(x, ro, (uint32_t)(((size_t)r * rs + 8 * cs) * 2), 0, 0);
       }
     };
-    // x_t . d_t over this wave's 32 features (x from the chunk tile), one
-    // partial per (feature block, token): dGp[DIR][bh][fb][t].
-    auto store_dot = [&](const uint16_t* tx, const f32x16& a) {
+    // x_t . d_t over this wave's 32 features (x from the chunk tile) into
+    // LDS, one partial per (feature block, token); after the next barrier
+    // wave 0 sums the four in a fixed order and writes dGp[DIR][bh][t].
+    auto dot_partial = [&](const uint16_t* tx, const f32x16& a) {
       float p = 0.f;
 #pragma unroll
       for (int jg = 0; jg < 4; jg++) {
@@ -307,10 +317,15 @@ __device__ __forceinline__ void gla_sweep(const uint16_t* __restrict__ q, const 
         }
       }
       p = xhalf_sum(p);
-      const __amdgpu_buffer_rsrc_t rd =
-          buffer_rsrc(dGp + (((size_t)DIR * gridDim.x + bh) * 4 + fb) * T + (size_t)n * kC, (uint32_t)(nv * 4));
-      // lanes of the upper half write past the range (dropped)
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(p), rd, hi ? 0x40000000u : (uint32_t)(tok * 4), 0, 0);
+      if (hi == 0) sD[fb][tok] = p;
+    };
+    auto store_dot = [&]() {
+      if (w == 0) {
+        const float x = (sD[0][lane] + sD[1][lane]) + (sD[2][lane] + sD[3][lane]);
+        const __amdgpu_buffer_rsrc_t rd =
+            buffer_rsrc(dGp + ((size_t)DIR * gridDim.x + bh) * T + (size_t)n * kC, (uint32_t)(nv * 4));
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rd, (uint32_t)(lane * 4), 0, 0);
+      }
     };
 
     // Phases of a step: (S) state terms, reading the state copy; (M) score
@@ -323,7 +338,7 @@ __device__ __forceinline__ void gla_sweep(const uint16_t* __restrict__ q, const 
       // dq^T[d][t] = scale e^{G_t} sum_v h[d][v] do[t][v] + sum_s k[s][d] M_dov[t][s]
       f32x16 aq = f32x16{};
       {
-        const Lofs<kD> oD = phase_lofs(lane);
+        const Lofs<kD> oD = phase_lofs(lofs);
 #pragma unroll
         for (int ks = 0; ks < kD / 16; ks++)
           aq = mfma32(op_row16<kD>(sS, oD, 32 * fb, 16 * ks), op_row16<kD>(cO, oD, 32 * tb, 16 * ks), aq);
@@ -339,28 +354,29 @@ __device__ __forceinline__ void gla_sweep(const uint16_t* __restrict__ q, const 
       if (w < 4) publish(m, w & 1, w >> 1, w);
       lds_barrier();  // score tiles complete
       {
-        const Lofs<kD> oD = phase_lofs(lane);
+        const Lofs<kD> oD = phase_lofs(lofs);
 #pragma unroll
         for (int ks = 0; ks < kC / 16; ks++)
           aq = mfma32(op_tr<kD>(cK, oD, 16 * ks, 32 * fb), sM[(2 * ((ks >> 1) * 2 + tb) + (ks & 1)) * 64 + lane], aq);
       }
-      store_dot(cQ, aq);
+      dot_partial(cQ, aq);
       // dq is staged where this wave's lanes just read q (no other wave reads
       // the q tile after the first barrier).
       uint16_t* tq = sQ[buf];
       stage(tq, aq);
-      lds_barrier();  // staged rows complete; every wave is done with the score tiles
+      lds_barrier();  // staged rows and dot partials complete; every wave is done with the score tiles
       store_rows(dx0, tq);
+      store_dot();
     } else {
       // dk^T[d][s] = e^{gl - G_s} sum_v dH[d][v] v[s][v] + sum_t q[t][d] M_dov[t][s]
       // dv^T[v][s] = e^{gl - G_s} sum_k dH[k][v] k[s][k] + sum_t do[t][v] M_qk[t][s]
       f32x16 ak = f32x16{}, av = f32x16{};
       {
-        const Lofs<kD> oD = phase_lofs(lane);
+        const Lofs<kD> oD = phase_lofs(lofs);
 #pragma unroll
         for (int ks = 0; ks < kD / 16; ks++) {
           ak = mfma32(op_row16<kD>(sS, oD, 32 * fb, 16 * ks), op_row16<kD>(cV, oD, 32 * tb, 16 * ks), ak);
-          av = mfma32(op_tr<kD>(sS, oD, 16 * ks, 32 * fb), op_row<kD>(cK, oD, 32 * tb, 16 * ks), av);
+          av = mfma32(op_trc<kD>(sS, oD, 16 * ks, 32 * fb), op_row16<kD>(cK, oD, 32 * tb, 16 * ks), av);
         }
       }
       const float fkv = __expf(gl - G_tok);
@@ -373,7 +389,7 @@ __device__ __forceinline__ void gla_sweep(const uint16_t* __restrict__ q, const 
       publish(m, w & 1, (w >> 1) & 1, w);
       lds_barrier();  // score tiles complete
       {
-        const Lofs<kD> oD = phase_lofs(lane);
+        const Lofs<kD> oD = phase_lofs(lofs);
 #pragma unroll
         for (int ks = 0; ks < kC / 16; ks++) {
           const int id = (ks >> 1) * 2 + tb;
@@ -381,7 +397,7 @@ __device__ __forceinline__ void gla_sweep(const uint16_t* __restrict__ q, const 
           av = mfma32(op_tr<kD>(cO, oD, 16 * ks, 32 * fb), sM[(2 * (4 + id) + (ks & 1)) * 64 + lane], av);
         }
       }
-      store_dot(cK, ak);
+      dot_partial(cK, ak);
       // dk is staged where this wave's lanes just read k (no other wave reads
       // the k tile after the first barrier), dv in the half of the state
       // copy's space the score tiles leave free.
@@ -391,9 +407,10 @@ __device__ __forceinline__ void gla_sweep(const uint16_t* __restrict__ q, const 
       stage(tv, av);
       // dH_n = e^{gl} dH_{n+1} + scale sum_t e^{G_t} q_t^T do_t (t < nv)
       update(cO, cQ, lane < nv ? scale * __expf(Gl) : 0.f);
-      lds_barrier();  // staged rows complete; every wave is done with the score tiles
+      lds_barrier();  // staged rows and dot partials complete; every wave is done with the score tiles
       store_rows(dx0, tk);
       store_rows(dx1, tv);
+      store_dot();
       lds_barrier();  // every wave is done with the staged dv
     }
     store_state();
@@ -413,61 +430,81 @@ __global__ __launch_bounds__(512) void gla_sweep_kernel(const uint16_t* __restri
   __shared__ __attribute__((aligned(16))) uint16_t sV[kC * kD];
   __shared__ __attribute__((aligned(16))) uint16_t sS[kD * kD];
   __shared__ __attribute__((aligned(16))) float sG[2][kC];
+  __shared__ __attribute__((aligned(16))) float sD[4][kC];
+  __shared__ __attribute__((aligned(16))) float sW[8][2][kC];
   if (blockIdx.y == 0)
-    gla_sweep<0>(q, k, v, dout, g, dq, nullptr, dGp, T, H, scale, sQ, sK, sV, sO, sS, sG);
+    gla_sweep<0>(q, k, v, dout, g, dq, nullptr, dGp, T, H, scale, sQ, sK, sV, sO, sS, sG, sD, sW);
   else
-    gla_sweep<1>(q, k, v, dout, g, dk, dv, dGp, T, H, scale, sQ, sK, sV, sO, sS, sG);
+    gla_sweep<1>(q, k, v, dout, g, dk, dv, dGp, T, H, scale, sQ, sK, sV, sO, sS, sG, sD, sW);
 }
 
-// dg[b, t, h] = sum_{t' >= t} dG_{t'} with dG_t = q_t.dq_t - k_t.dk_t, each
-// dot summed from its four feature-block partials in a fixed order: one
-// workgroup per (b, h), segments of 4096 tokens from the end (16
-// consecutive tokens per thread: in-thread suffix sums, then suffix sums of
-// the thread totals across the wave (shuffles) and the four waves (LDS)),
-// the running total carried.
-__global__ __launch_bounds__(256) void gla_dg_kernel(const float* __restrict__ dGp, float* __restrict__ dg, int T, int H) {
-  constexpr int PER = 16, SEG = 256 * PER;
-  __shared__ float sW[4];
-  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
-  const int bh = blockIdx.x, b = bh / H, h = bh % H;
-  const float* pq = dGp + (size_t)bh * 4 * T;
-  const float* pk = dGp + ((size_t)gridDim.x + bh) * 4 * T;
-  auto src_at = [&](int t) {
-    const float a = (pq[t] + pq[T + t]) + (pq[2 * T + t] + pq[3 * T + t]);
-    const float c = (pk[t] + pk[T + t]) + (pk[2 * T + t] + pk[3 * T + t]);
-    return a - c;
-  };
+// dg[b, t, h] = sum_{t' >= t} dG_{t'} with dG_t = q_t.dq_t - k_t.dk_t.  One
+// workgroup per (b, 4 consecutive heads), 256 threads per head; segments of
+// 4096 tokens from the end, 16 consecutive tokens per thread: in-thread
+// suffix sums, an exclusive suffix over the 256 thread totals of a head (one
+// wave per head, four totals per lane, shuffles), the running total carried
+// to the next segment.  The threads of a head group are interleaved so that
+// each store covers 4 heads of a token (16 contiguous bytes of dg).
+constexpr int kDgHeads = 4, kDgThreads = 256, kDgPer = 16;
+__global__ __launch_bounds__(kDgHeads * kDgThreads) void gla_dg_kernel(const float* __restrict__ dGp,
+                                                                        float* __restrict__ dg, int T, int H,
+                                                                        int BH) {
+  constexpr int SEG = kDgThreads * kDgPer, NPL = kDgThreads / 64;  // totals per lane in the head scan
+  __shared__ float sT[kDgHeads][kDgThreads];
+  __shared__ float sTot[kDgHeads];
+  const int tid = threadIdx.x, hl = tid % kDgHeads, tq = tid / kDgHeads;
+  const int lane = tid & 63, w = tid >> 6;
+  const int b = blockIdx.x, h = blockIdx.y * kDgHeads + hl;
+  const bool on = h < H;
+  const int bh = b * H + (on ? h : 0);
+  const float* pq = dGp + (size_t)bh * T;
+  const float* pk = dGp + ((size_t)BH + bh) * T;
   float* dst = dg + (size_t)b * T * H + h;
   float carry = 0.f;
   for (int seg_end = T; seg_end > 0; seg_end -= SEG) {
-    const int t0 = seg_end - SEG + PER * tid;  // this thread's first token (may be negative)
-    float x[PER];
+    const int t0 = seg_end - SEG + kDgPer * tq;  // this thread's first token (may be negative)
+    float x[kDgPer];
     float tot = 0.f;
 #pragma unroll
-    for (int i = PER - 1; i >= 0; i--) {
+    for (int i = kDgPer - 1; i >= 0; i--) {
       const int t = t0 + i;
-      tot += (t >= 0 ? src_at(t) : 0.f);
-      x[i] = tot;  // sum of this thread's tokens t0+i .. t0+PER-1
+      tot += (t >= 0 ? pq[t] - pk[t] : 0.f);
+      x[i] = tot;  // sum of this thread's tokens t0+i .. t0+kDgPer-1
     }
-    float suf = tot;  // inclusive suffix over the lanes of this wave
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float y = __shfl_down(suf, o, 64);
-      if (l + o < 64) suf += y;
-    }
-    if (l == 0) sW[w] = suf;
+    sT[hl][tq] = tot;
     __syncthreads();
-    float after_w = 0.f;
-    for (int j = w + 1; j < 4; j++) after_w += sW[j];
-    const float seg_total = (sW[0] + sW[1]) + (sW[2] + sW[3]);
-    const float after = suf - tot + after_w + carry;  // tokens after this thread's block
+    if (w < kDgHeads) {  // wave w: exclusive suffix over the totals of head w
+      float a[NPL], part = 0.f;
 #pragma unroll
-    for (int i = 0; i < PER; i++) {
-      const int t = t0 + i;
-      if (t >= 0) dst[(size_t)t * H] = x[i] + after;
+      for (int i = NPL - 1; i >= 0; i--) {
+        a[i] = sT[w][NPL * lane + i];
+        part += a[i];
+      }
+      float suf = part;  // inclusive suffix over the lanes
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const float y = __shfl_down(suf, o, 64);
+        if (lane + o < 64) suf += y;
+      }
+      float run = suf - part;
+#pragma unroll
+      for (int i = NPL - 1; i >= 0; i--) {
+        sT[w][NPL * lane + i] = run;
+        run += a[i];
+      }
+      if (lane == 0) sTot[w] = suf;
     }
-    carry += seg_total;
-    __syncthreads();  // sW reused by the next segment
+    __syncthreads();
+    const float after = sT[hl][tq] + carry;  // tokens of this head after this thread's block
+    if (on) {
+#pragma unroll
+      for (int i = 0; i < kDgPer; i++) {
+        const int t = t0 + i;
+        if (t >= 0) dst[(size_t)t * H] = x[i] + after;
+      }
+    }
+    carry += sTot[hl];
+    __syncthreads();  // sT and sTot reused by the next segment
   }
 }
 
@@ -479,10 +516,11 @@ hipError_t launch_gla_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* 
   float* dGp = (float*)workspace;
   hipLaunchKernelGGL(gla_sweep_kernel, dim3(B * H, 2), dim3(512), 0, stream, q, k, v, dout, g, dq, dk, dv, dGp, T,
                      H, scale);
-  hipLaunchKernelGGL(gla_dg_kernel, dim3(B * H), dim3(256), 0, stream, dGp, dg, T, H);
+  hipLaunchKernelGGL(gla_dg_kernel, dim3(B, (H + kDgHeads - 1) / kDgHeads), dim3(kDgHeads * kDgThreads), 0, stream,
+                     dGp, dg, T, H, B * H);
   return hipGetLastError();
 }
 
-size_t gla_bwd_workspace_bytes(int B, int T, int H) { return 2 * 4 * (size_t)B * H * T * sizeof(float); }
+size_t gla_bwd_workspace_bytes(int B, int T, int H) { return 2 * (size_t)B * H * T * sizeof(float); }
 
 }  // namespace mi355

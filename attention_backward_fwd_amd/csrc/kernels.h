@@ -93,7 +93,7 @@ hipError_t launch_gqa_reduce(const float* dk_part, const float* dv_part, uint16_
 // 64): a forward sweep (state h, dq) and a backward sweep (state dH, dk, dv)
 // in one launch, then the gate's reverse running sum.  Tensors
 // [B][T][H][128] bf16, g and dg [B][T][H] fp32; the workspace holds the
-// per-token partials of q.dq and k.dk ([2][B*H][4 feature blocks][T] fp32).
+// per-token q.dq and k.dk ([2][B*H][T] fp32).
 hipError_t launch_gla_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
                           const float* g, uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dg, void* workspace,
                           int B, int T, int H, float scale, hipStream_t stream);

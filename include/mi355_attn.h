@@ -304,8 +304,7 @@ int attn_bwd_varlen_postprocess(const float* dq_accum, const void* workspace, si
  * computed in chunks of 64 tokens: one pass over the chunks in each
  * direction carries the chunk state (forward) and its gradient (backward)
  * on chip, fp32 with a bf16 operand copy; the workspace holds only the
- * per-token partials of q.dq and k.dk (fp32) that the gate's reverse
- * running sum reads.
+ * per-token q.dq and k.dk (fp32) that the gate's reverse running sum reads.
  *   q, k, v, dout, dq, dk, dv [batch, seqlen, heads, 128] bf16 (head_dim 128,
  *     K = V); g, dg [batch, seqlen, heads] fp32 (4-byte aligned).
  *   workspace: at least gla_chunk_bwd_workspace_bytes(shape) bytes.

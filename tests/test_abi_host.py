@@ -296,8 +296,8 @@ def gshp(b=2, t=300, h=4, d=128):
 
 @pytest.mark.parametrize("t", [1, 64, 65, 4096])
 def test_gla_workspace_bytes(t):
-    # per-token partials of q.dq and k.dk: [2][B*H][4 feature blocks][T] fp32
-    want = 2 * (2 * 4) * 4 * t * 4
+    # per-token q.dq and k.dk: [2][B*H][T] fp32
+    want = 2 * (2 * 4) * t * 4
     assert lib().gla_chunk_bwd_workspace_bytes(gshp(t=t)) == want
     assert lib().gla_chunk_bwd_workspace_bytes(gshp(d=64)) == 0
     assert lib().gla_chunk_bwd_workspace_bytes(gshp(b=0)) == 0
