@@ -28,7 +28,10 @@ int check_shape(const attn_shape& s) {
 bool good_scale(float x) { return isfinite(x) && x > 0.f; }
 
 size_t elems_q(const attn_shape& s) { return (size_t)s.batch * s.seqlen * s.heads_q * s.head_dim; }
-int n_key_blocks(const attn_shape& s) { return (s.seqlen + kBwdBlockN - 1) / kBwdBlockN; }
+int n_key_blocks(const attn_shape& s) {
+  const int bn = bwd_block_n(s.head_dim);
+  return (s.seqlen + bn - 1) / bn;
+}
 
 // Workspace layout: [dK partials | dV partials] when groups > 1, then the
 // split path's dQ partials.  Every region is a multiple of 256 bytes.
@@ -62,7 +65,7 @@ size_t ws_varlen_gqa_bytes(const attn_varlen_shape& s) {
   return s.groups > 1 ? 2 * (size_t)s.total_k * s.heads_q * s.head_dim * 4 : 0;
 }
 size_t ws_varlen_split_bytes(const attn_varlen_shape& s, int use_atomic) {
-  const int nblk = (s.max_seqlen_k + kBwdBlockN - 1) / kBwdBlockN;
+  const int bn = bwd_block_n(s.head_dim), nblk = (s.max_seqlen_k + bn - 1) / bn;
   return use_atomic ? 0 : (size_t)nblk * s.total_q * s.heads_q * s.head_dim * 4;
 }
 

@@ -82,12 +82,12 @@ __device__ __forceinline__ f32x4 sum_slots(f32x4 acc, const float* part, size_t 
 
 __global__ __launch_bounds__(256) void dq_sum_kernel(const float* __restrict__ part,
                                                      float* __restrict__ dq, long long n4, int S,
-                                                     int D, int n_nblk, int causal) {
+                                                     int D, int n_nblk, int bn, int causal) {
   const size_t slot = (size_t)n4 * 4;
   for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long long)gridDim.x * 256) {
     const long long e = i * 4;
     const int s = (int)((e / D) % S);
-    const int last = causal ? s / kBwdBlockN : n_nblk - 1;
+    const int last = causal ? s / bn : n_nblk - 1;
     const float* src = part + e;
     const f32x4 acc = sum_slots(*reinterpret_cast<const f32x4*>(src), src + slot, slot, last);
     *reinterpret_cast<f32x4*>(dq + e) = acc;
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(256) void dq_sum_varlen_kernel(const float* __restr
                                                             float* __restrict__ dq, const int* __restrict__ cu,
                                                             const int* __restrict__ cu_k, int n_seqs, int T,
                                                             int Tk, int S, int Sk, long long n4, int D,
-                                                            int causal) {
+                                                            int bn, int causal) {
   const size_t slot = (size_t)n4 * 4;
   for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long long)gridDim.x * 256) {
     const long long e = i * 4;
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(256) void dq_sum_varlen_kernel(const float* __restr
       const int lk = seq_rows(cu_k, Tk, b, Sk).len;
       const int last_key = causal ? min(t - start + lk - len, lk - 1) : lk - 1;
       const float* src = part + e;
-      if (last_key >= 0) acc = sum_slots(acc, src, slot, last_key / kBwdBlockN + 1);
+      if (last_key >= 0) acc = sum_slots(acc, src, slot, last_key / bn + 1);
     }
     *reinterpret_cast<f32x4*>(dq + e) = acc;
   }
@@ -252,9 +252,9 @@ hipError_t launch_preprocess(const uint16_t* o, const uint16_t* dout, float* del
 hipError_t launch_dq_sum(const float* dq_part, float* dq_accum, int B, int S, int Hq, int D, int causal,
                          hipStream_t stream) {
   const long long n4 = (long long)B * S * Hq * D / 4;
-  const int n_nblk = (S + kBwdBlockN - 1) / kBwdBlockN;
+  const int bn = bwd_block_n(D), n_nblk = (S + bn - 1) / bn;
   hipLaunchKernelGGL(dq_sum_kernel, dim3(grid_for(n4, 256)), dim3(256), 0, stream, dq_part, dq_accum, n4, S, D,
-                     n_nblk, causal);
+                     n_nblk, bn, causal);
   return hipGetLastError();
 }
 
@@ -262,7 +262,7 @@ hipError_t launch_dq_sum_varlen(const float* dq_part, float* dq_accum, const int
                                 int T, int Tk, int S, int Sk, int Hq, int D, int causal, hipStream_t stream) {
   const long long n4 = (long long)T * Hq * D / 4;
   hipLaunchKernelGGL(dq_sum_varlen_kernel, dim3(grid_for(n4, 256)), dim3(256), 0, stream, dq_part, dq_accum, cu,
-                     cu_k, n_seqs, T, Tk, S, Sk, n4, D, causal);
+                     cu_k, n_seqs, T, Tk, S, Sk, n4, D, bwd_block_n(D), causal);
   return hipGetLastError();
 }
 

@@ -2,9 +2,10 @@
 //
 // Decomposition as in the FlashAttention backward examples of TileLang #940
 // (flashattn_bwd_atomic_add / flashattn_bwd_split): one workgroup owns a block
-// of 256 keys of one (batch, query head), keeps its dK/dV accumulators on
-// chip for the whole sweep and walks the query blocks that see those keys.
-// Each of the 8 waves owns 32 of the keys.  Per 32-query block the five tile
+// of keys of one (batch, query head), keeps its dK/dV accumulators on chip
+// for the whole sweep and walks the query blocks that see those keys.  Each
+// of the 8 waves owns 32-key tiles of the block: one at D = 128 (256 keys per
+// block), two at D = 64 (512 keys).  Per 32-query block the five tile
 // contractions run on the matrix cores:
 //
 //   S  = Q K^T            A = Q (LDS, row reads)      B = K (LDS, row reads)
@@ -21,13 +22,16 @@
 // waves: for D = 128 waves 0-3 (one per SIMD) each form a 32x32 tile, for
 // D = 64 every wave a 16x16 tile.
 //
-// Why 256 keys: every key block adds its dQ contribution once per query
-// block, so the dQ traffic leaving the workgroups (fp32 atomics, or the split
-// path's partials) is inversely proportional to the key-block height, and
-// the fp32 atomic rate of the memory system, not the matrix cores, bounds a
-// 128-key version.  The dK/dV accumulators of 256 keys fill half of the
-// register file; V lives in registers (it is only ever a B operand of dP),
-// which leaves LDS for K, double-buffered Q/dO blocks and dS^T.
+// Why tall key blocks: every key block adds its dQ contribution once per
+// query block, so the dQ traffic leaving the workgroups (fp32 atomics, or the
+// split path's partials) is inversely proportional to the key-block height,
+// and the fp32 atomic rate of the memory system, not the matrix cores, bounds
+// a 128-key version.  The dK/dV accumulators of 256 keys at D = 128 (512 at
+// D = 64) fill half of the register file; V lives in registers (it is only
+// ever a B operand of dP), which leaves LDS for K, double-buffered Q/dO
+// blocks and dS^T.  At D = 64 the two tiles of a wave run one after the
+// other within a step, and the step's fixed costs (barrier, dQ emission)
+// are shared by twice the keys.
 //
 // The softmax scale is folded into the exponent: the kernel forms
 // P' = scale * P = exp2(S*scale*log2e - (LSE*log2e - log2(scale))), so that
@@ -56,12 +60,10 @@ namespace mi355 {
 
 namespace {
 
-constexpr int kBN = kBwdBlockN;  // keys per workgroup
-constexpr int kBM = 32;          // queries per step
-constexpr int kNW = 8;           // waves per workgroup, 32 keys each
-static_assert(kBN == 32 * kNW, "one 32-key slice per wave");
+constexpr int kBM = 32;  // queries per step
+constexpr int kNW = 8;   // waves per workgroup
 
-// dS'^T tile [256 keys][32 queries] bf16, 64-byte rows.  The 8-byte chunk
+// dS'^T tile [block keys][32 queries] bf16, 64-byte rows.  The 8-byte chunk
 // index of row r is XORed with fS(r) (bits 3, 2, 4 of r to chunk bits 2, 1,
 // 0), which keeps both of its access patterns free of bank conflicts: the
 // writes (32 consecutive keys, one chunk) and the transposing reads of the
@@ -77,7 +79,11 @@ __device__ __forceinline__ int dst_off(int row, int col) {
 // MFMA accumulator in VGPRs.
 template <int D, bool CAUSAL, bool ATOMIC, bool PARTIAL>
 __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) void bwd_kernel(BwdParams p) {
-  constexpr int BN = kBN, BM = kBM, NW = kNW;
+  // Keys per workgroup: KT tiles of 32 keys per wave (tile tt of wave w:
+  // keys 256tt + 32w ..), one tile at D = 128, two at D = 64.
+  constexpr int BN = bwd_block_n(D), BM = kBM, NW = kNW;
+  constexpr int KT = BN / (32 * NW);
+  static_assert(BN == 32 * NW * KT && (KT == 1 || KT == 2), "32-key tiles, one or two per wave");
   constexpr int TQ = BM * D;  // elements of one Q or dO block
   constexpr int NKS = D / 16, NDT = D / 32;
   // dQ tiles (16 queries x 16 d) per wave: D = 128 has 16 tiles (wave w
@@ -204,21 +210,24 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
   // end read the last row (their P is masked to zero).  The first step
   // waits for every load anyway; waiting here, before the loop, lets the
   // compiler see that V is ready inside it.
-  const int key_l = n0 + 32 * w + l32;
-  bf16x8 vb[NKS];
-  {
+  bf16x8 vb[KT][NKS];
+#pragma unroll
+  for (int tt = 0; tt < KT; tt++) {
+    const int key_l = n0 + 256 * tt + 32 * w + l32;
     const uint16_t* vrow = Vb + (size_t)min(key_l, Sk - 1) * kvrs + 8 * hi;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ks++) vb[ks] = *reinterpret_cast<const bf16x8*>(vrow + 16 * ks);
+    for (int ks = 0; ks < NKS; ks++) vb[tt][ks] = *reinterpret_cast<const bf16x8*>(vrow + 16 * ks);
   }
   wait_vmem();
 
-  f32x16 dk[NDT], dv[NDT];
+  f32x16 dk[KT][NDT], dv[KT][NDT];
 #pragma unroll
-  for (int dt = 0; dt < NDT; dt++) {
-    dk[dt] = f32x16{};
-    dv[dt] = f32x16{};
-  }
+  for (int tt = 0; tt < KT; tt++)
+#pragma unroll
+    for (int dt = 0; dt < NDT; dt++) {
+      dk[tt][dt] = f32x16{};
+      dv[tt][dt] = f32x16{};
+    }
 
   // dQ tiles.  D = 128: waves 0-3 each compute 32 queries x d columns
   // 32w .. 32w+31 as one 32x32 tile (one such wave per SIMD, so the matrix
@@ -257,7 +266,7 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[i][j]), rs, dq_voff, so, 0);
   };
 
-  // dQ' (32 x D) = dS' (32 x 256 keys) K (256 keys x D) of one block as
+  // dQ' (32 x D) = dS' (32 x BN keys) K (BN keys x D) of one block as
   // 16x16 tiles, from the dS'^T tile `sdSt`.  Operands are read one key
   // slice ahead of the products.
   auto dq_block32 = [&](const uint16_t* sdSt, f32x4* dq) {
@@ -403,20 +412,28 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     const uint32_t offT0 = 2 * swz_off<D>(4 * lhi + (lL >> 2), tcol);    // transposing reads of Q / dO
     const uint32_t offT1 = 2 * swz_off<D>(4 * lhi + (lL >> 2) + 8, tcol);
 
-    // Keys n0 .. n0+n_vis-1 exist and see some query of this block.  A wave
-    // whose 32 keys lie past that has P = 0 throughout: it skips the four
-    // products, writes zeros as its rows of dS'^T and only takes part in dQ
-    // and the barriers.
-    const int n_vis = CAUSAL ? min(min(BN, Sk - n0), m0 + BM + off - n0) : min(BN, Sk - n0);
-    const bool active = 32 * w < n_vis;
+    // Keys n0 .. n0+n_vis-1 exist and see some query of this block.  A
+    // 32-key tile of a wave past that has P = 0 throughout: it skips the four
+    // products and writes zeros as its rows of dS'^T; the wave still takes
+    // part in dQ and the barriers.
+    // (Opaque per step: a loop-invariant value would let the compiler
+    // specialise the loop body per tile state and spill.)
+    const int n_vis = opaque(__builtin_amdgcn_readfirstlane(CAUSAL ? min(min(BN, Sk - n0), m0 + BM + off - n0)
+                                                                   : min(BN, Sk - n0)));
     f32x4 dq[DQF4];
-    if (active) {
-      // S = Q K^T and dP = dO V^T for the block's 32 queries x this wave's
+    // With two tiles the dQ product goes first, while only the accumulators
+    // and V are live (between a tile's S/dP and its softmax there is no room).
+    if (KT > 1 && st > 0) dq_block(pS, dq);
+#pragma unroll
+    for (int tt = 0; tt < KT; tt++) {
+    const int kt0 = 256 * tt + 32 * w;  // first key of this tile in the block
+    if (kt0 < n_vis) {
+      // S = Q K^T and dP = dO V^T for the block's 32 queries x this tile's
       // 32 keys.  Operands are read one k-step ahead of the products that
       // use them.
       f32x16 s = f32x16{}, dp = f32x16{};
       {
-        const uint16_t* kw_base = sK + 32 * w * D;
+        const uint16_t* kw_base = sK + kt0 * D;
         bf16x8 aq = lds_b128_at(cQ, offR), bk = lds_b128_at(kw_base, offR), ad = lds_b128_at(cdO, offR);
 #pragma unroll
         for (int ks = 0; ks < NKS; ks++) {
@@ -428,17 +445,17 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
             ad1 = lds_b128_at(cdO, oq);
           }
           s = mfma32(aq, bk, s);
-          dp = mfma32(ad, vb[ks], dp);
+          dp = mfma32(ad, vb[tt][ks], dp);
           aq = aq1;
           bk = bk1;
           ad = ad1;
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      if (st > 0) dq_block(pS, dq);
+      if (KT == 1 && st > 0) dq_block(pS, dq);
 
       // P' = scale P and dS' = scale dS.  Element j of lane l is query
-      // 8(j/4) + 4hi + j%4 of the block, key 32w + l32.
+      // 8(j/4) + 4hi + j%4 of the block, key kt0 + l32.
       const uint32_t orow = 16 * lhi;  // byte offset of query 4hi in the LSE / Delta rows
       uint32_t pp[8], dd[8];
       auto softmax_grad = [&](auto mask_tag, int qlim, int qend) {
@@ -463,14 +480,14 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
           dd[2 * jg + 1] = pack_bf16x2(dv4[2], dv4[3]);
         }
       };
-      // Blocks on the causal diagonal or at either end of the sequence are
+      // Tiles on the causal diagonal or at either end of the sequence are
       // masked.  This lane's key is hidden from block queries below qlim (all
       // of them for keys past the end, the earlier ones under causal masking)
       // and from queries at or past qend (rows past the end of the sequence);
       // both limits are taken relative to 4hi, so that the per-element query
       // index is a constant.
-      if ((n0 + BN > Sk) || (m0 + BM > S) || (CAUSAL && m0 + off < n0 + BN)) {
-        const int key_e = n0 + 32 * w + ll32;
+      if ((n0 + kt0 + 32 > Sk) || (m0 + BM > S) || (CAUSAL && m0 + off < n0 + kt0 + 32)) {
+        const int key_e = n0 + kt0 + ll32;
         const int qlim = (key_e >= Sk ? BM : (CAUSAL ? key_e - off - m0 : -1)) - 4 * lhi;
         softmax_grad(std::true_type{}, qlim, S - m0 - 4 * lhi);
       } else {
@@ -479,7 +496,7 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
       // dS'^T to LDS as [key][query]: four consecutive queries per 8-byte
       // write.
       {
-        const uint32_t aW = lds_addr(wS) + 2 * dst_off(32 * w + ll32, 4 * lhi);
+        const uint32_t aW = lds_addr(wS) + 2 * dst_off(kt0 + ll32, 4 * lhi);
 #pragma unroll
         for (int jg = 0; jg < 4; jg++) lds_store_b64_addr(aW ^ (16u * jg), u32x2{dd[2 * jg], dd[2 * jg + 1]});
       }
@@ -503,19 +520,22 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
           const int o4 = 4 * (it / NDT), dt = it % NDT;
           const bf16x8 pa = __builtin_bit_cast(bf16x8, u32x4{pp[o4], pp[o4 + 1], pp[o4 + 2], pp[o4 + 3]});
           const bf16x8 da = __builtin_bit_cast(bf16x8, u32x4{dd[o4], dd[o4 + 1], dd[o4 + 2], dd[o4 + 3]});
-          dv[dt] = mfma32(pa, bo, dv[dt]);
-          dk[dt] = mfma32(da, bq, dk[dt]);
+          dv[tt][dt] = mfma32(pa, bo, dv[tt][dt]);
+          dk[tt][dt] = mfma32(da, bq, dk[tt][dt]);
           bo = bo1;
           bq = bq1;
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     } else {
-      if (st > 0) dq_block(pS, dq);
+      if (KT == 1 && st > 0) dq_block(pS, dq);
       // Zero rows of dS'^T, so that the dQ product can run over all keys.
-      const uint32_t aW = lds_addr(wS) + 2 * dst_off(32 * w + ll32, 4 * lhi);
+      const uint32_t aW = lds_addr(wS) + 2 * dst_off(kt0 + ll32, 4 * lhi);
 #pragma unroll
       for (int jg = 0; jg < 4; jg++) lds_store_b64_addr(aW ^ (16u * jg), u32x2{0u, 0u});
+    }
+    // (Tiles one after the other: their live ranges must not overlap.)
+    __builtin_amdgcn_sched_barrier(0);
     }
     if (st > 0) dq_store(m0 - BM, dq);
   };
@@ -531,35 +551,38 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     dq_block(((n_steps - 1) & 1) ? sdSt1 : sdSt0, dq);
     dq_store(m_begin + (n_steps - 1) * BM, dq);
   }
-  // Each wave holds the complete dK/dV of its 32 keys.  Element j of lane l
-  // of tile dt is key 32w + 8(j/4) + 4hi + j%4, d = 32dt + l32.
+  // Each wave holds the complete dK/dV of its KT tiles of 32 keys.  Element
+  // j of lane l of tile (tt, dt) is key 256tt + 32w + 8(j/4) + 4hi + j%4,
+  // d = 32dt + l32.
   const float inv_scale = 1.f / p.scale;
   const int le = opaque_v(lane);  // output addresses derived here, not kept live
   const int ehi = le >> 5, el32 = le & 31;
 #pragma unroll
-  for (int dt = 0; dt < NDT; dt++) {
-    const int d = 32 * dt + el32;
+  for (int tt = 0; tt < KT; tt++)
 #pragma unroll
-    for (int j = 0; j < 16; j++) {
-      const int key = n0 + 32 * w + 8 * (j >> 2) + 4 * ehi + (j & 3);
-      if (key < Sk) {
-        if (PARTIAL) {
-          const size_t o = ((size_t)(krow0 + key) * Hq + h) * D + d;
-          p.dk_part[o] = dk[dt][j];
-          p.dv_part[o] = dv[dt][j] * inv_scale;
-        } else {
-          const size_t o = ((size_t)(krow0 + key) * Hkv + kvh) * D + d;
-          p.dk[o] = to_bf16(dk[dt][j]);
-          p.dv[o] = to_bf16(dv[dt][j] * inv_scale);
+    for (int dt = 0; dt < NDT; dt++) {
+      const int d = 32 * dt + el32;
+#pragma unroll
+      for (int j = 0; j < 16; j++) {
+        const int key = n0 + 256 * tt + 32 * w + 8 * (j >> 2) + 4 * ehi + (j & 3);
+        if (key < Sk) {
+          if (PARTIAL) {
+            const size_t o = ((size_t)(krow0 + key) * Hq + h) * D + d;
+            p.dk_part[o] = dk[tt][dt][j];
+            p.dv_part[o] = dv[tt][dt][j] * inv_scale;
+          } else {
+            const size_t o = ((size_t)(krow0 + key) * Hkv + kvh) * D + d;
+            p.dk[o] = to_bf16(dk[tt][dt][j]);
+            p.dv[o] = to_bf16(dv[tt][dt][j] * inv_scale);
+          }
         }
       }
     }
-  }
 }
 
 template <int D, bool CAUSAL, bool ATOMIC, bool PARTIAL>
 hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
-  const int n_nblk = (p.Sk + kBN - 1) / kBN;
+  const int n_nblk = (p.Sk + bwd_block_n(D) - 1) / bwd_block_n(D);
   const long long nwg = (long long)p.B * p.Hq * n_nblk;
   hipLaunchKernelGGL((bwd_kernel<D, CAUSAL, ATOMIC, PARTIAL>), dim3((unsigned)nwg), dim3(kNW * 64), 0, stream, p);
   return hipGetLastError();

@@ -7,9 +7,11 @@
 
 namespace mi355 {
 
-// Key-block height of the backward kernel; the split dQ path keeps one fp32
+// Key-block height of the backward kernel for head dim D: 32-key tiles, one
+// per wave of its 8 waves at D = 128 and two at D = 64 (whose dK/dV
+// accumulators take half the registers).  The split dQ path keeps one fp32
 // dQ partial per block of this many keys.
-constexpr int kBwdBlockN = 256;
+__host__ __device__ constexpr int bwd_block_n(int D) { return D == 64 ? 512 : 256; }
 
 // Packed variable-length sequences: when `cu` is set, "batch" b is sequence
 // b of the packed rows: queries cu[b] .. cu[b+1]-1 of T query rows and keys

@@ -696,9 +696,10 @@ def main():
         out[other] = time_other_path(args, w, bd, torch, inp, o, lse, causal, 1 - use_atomic, stream)
     if use_atomic:
         # The atomic path's other bound: every query row receives one fp32 add
-        # per element from each key block (256 keys) it sees.
-        n_blk = -(-w.seqlen // 256)
-        blocks_seen = sum(s // 256 + 1 for s in range(w.seqlen)) if causal else w.seqlen * n_blk
+        # per element from each key block (256 keys at head_dim 128, 512 at 64) it sees.
+        bn = 512 if w.head_dim == 64 else 256
+        n_blk = -(-w.seqlen // bn)
+        blocks_seen = sum(s // bn + 1 for s in range(w.seqlen)) if causal else w.seqlen * n_blk
         n_atomics = blocks_seen * w.batch * w.heads_q * w.head_dim
         out["dq_atomics"] = {"count": n_atomics, "per_s": round(n_atomics / (bwd_ms * 1e-3) / 1e9, 1), "unit": "G/s"}
     if not args.no_cpu_baseline:

@@ -97,7 +97,8 @@ int attn_bwd_preprocess(const uint16_t* o, const uint16_t* dout, float* delta, f
  * problem (0 when none is needed).  Layout, for reference only:
  *   groups > 1: fp32 per-query-head dK and dV partials, [B,S,Hq,D] each;
  *   use_atomic == 0: fp32 per-KV-block dQ partials, [n_kv_blocks,B,Hq,S,D],
- *     n_kv_blocks = ceil(S / 256) (the backward kernel's key-block height).
+ *     n_kv_blocks = ceil(S / bn), bn = 256 for head_dim 128 and 512 for
+ *     head_dim 64 (the backward kernel's key-block height).
  * Returns 0 for an invalid shape.
  */
 size_t attn_bwd_workspace_bytes(attn_shape shape, int causal, int use_atomic);
@@ -154,7 +155,8 @@ int attn_bwd_dq_sum(const void* workspace, size_t workspace_bytes, float* dq_acc
  *   attn_bwd_postprocess(dq_accum, NULL, 0, dq, NULL, NULL, shape with
  *   groups = 1, stream) afterwards for the bf16 dQ.
  *   Scratch needed: (groups > 1 ? 2 : 0) * B*S*Hq*D * 4 bytes plus
- *   ceil(S / 256) * B*S*Hq*D * 4 bytes; beyond 64 MiB the call returns
+ *   ceil(S / bn) * B*S*Hq*D * 4 bytes (bn as in attn_bwd_workspace_bytes);
+ *   beyond 64 MiB the call returns
  *   ATTN_ERR_SCRATCH and launches nothing.
  *   The scratch of a GPU is shared by every call on it and holds what the
  *   last call left: calls that may overlap on one GPU (on different streams
@@ -256,7 +258,8 @@ int attn_fwd_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v, uin
  * Workspace bytes of attn_bwd_varlen and attn_bwd_varlen_postprocess (0 when
  * none is needed):
  *   groups > 1: fp32 dK and dV partials, [Tk,Hq,D] each;
- *   use_atomic == 0: fp32 dQ partials, [ceil(max_seqlen_k / 256),Hq,Tq,D].
+ *   use_atomic == 0: fp32 dQ partials, [ceil(max_seqlen_k / bn),Hq,Tq,D],
+ *     bn as in attn_bwd_workspace_bytes.
  * Returns 0 for an invalid shape.
  */
 size_t attn_bwd_varlen_workspace_bytes(attn_varlen_shape shape, int causal, int use_atomic);

@@ -64,11 +64,18 @@ def test_strerror_covers_every_code():
 def test_workspace_bytes(g, s):
     sh = shp(b=2, s=s, hq=8, g=g, d=64)
     nq = 2 * s * 8 * 64
-    nblk = math.ceil(s / 256)  # key blocks of 256
+    nblk = math.ceil(s / 512)  # key blocks of 512 at head_dim 64
     gqa = 2 * nq * 4 if g > 1 else 0
     for causal in (0, 1):
         assert lib().attn_bwd_workspace_bytes(sh, causal, 1) == gqa
         assert lib().attn_bwd_workspace_bytes(sh, causal, 0) == gqa + nblk * nq * 4
+
+
+def test_workspace_bytes_block_height_follows_head_dim():
+    # 256-key blocks at head_dim 128: S = 300 needs 2 slots, S = 256 one.
+    for s_, nblk in ((256, 1), (257, 2), (300, 2), (4096, 16)):
+        nq = 2 * s_ * 8 * 128
+        assert lib().attn_bwd_workspace_bytes(shp(b=2, s=s_, hq=8, g=1, d=128), 1, 0) == nblk * nq * 4
 
 
 def test_workspace_bytes_invalid_is_zero():
@@ -200,7 +207,7 @@ def test_varlen_workspace_bytes(g, mk):
     gqa = 2 * nk * 4 if g > 1 else 0
     for causal in (0, 1):
         assert lib().attn_bwd_varlen_workspace_bytes(sh, causal, 1) == gqa
-        assert lib().attn_bwd_varlen_workspace_bytes(sh, causal, 0) == gqa + math.ceil(mk / 256) * nq * 4
+        assert lib().attn_bwd_varlen_workspace_bytes(sh, causal, 0) == gqa + math.ceil(mk / 512) * nq * 4
     assert lib().attn_bwd_varlen_workspace_bytes(vshp(hq=6, g=4), 0, 0) == 0
     assert lib().attn_bwd_varlen_workspace_bytes(vshp(), 0, 7) == 0
 
@@ -382,15 +389,16 @@ def test_sparse_mla_pre_post_errors():
     assert g(A, MIS, mshp(), None) == E["align"]
 
 
-# Scratch of attn_bwd_noalloc: 64 MiB; need = (2 if groups > 1) * nq * 4 + ceil(S/256) * nq * 4.
+# Scratch of attn_bwd_noalloc: 64 MiB; need = (2 if groups > 1) * nq * 4 + ceil(S/bn) * nq * 4, with key
+# blocks of bn = 256 keys at head_dim 128 and 512 at head_dim 64.
 @pytest.mark.parametrize("kw,code", [
     ({"dk": None, "shape": shp(g=1)}, "null"), ({"dv": None}, "null"), ({"delta": None}, "null"),
     ({"shape": shp(hq=6, g=4)}, "shape"), ({"shape": shp(d=96)}, "hd"), ({"causal": 2}, "flag"),
     ({"scale": 0.0}, "range"),
     # B1 S4096 Hq8 D128, MHA: 16 blocks * 4 Mi floats * 4 B = 256 MiB.
     ({"shape": shp(b=1, s=4096, hq=8, g=1, d=128)}, "scratch"),
-    # B2 S1024 Hq16 D64, GQA: (2 + 4) * 2 Mi floats * 4 B = 48 MiB fits; Hq32 (96 MiB) does not.
-    ({"shape": shp(b=2, s=1024, hq=32, g=4, d=64)}, "scratch"),
+    # B2 S1024 Hq16 D64, GQA: (2 + 2) * 2 Mi floats * 4 B = 32 MiB fits; Hq48 (96 MiB) does not.
+    ({"shape": shp(b=2, s=1024, hq=48, g=4, d=64)}, "scratch"),
     ({"shape": shp(b=2, s=1024, hq=16, g=4, d=64), "dq": MIS}, "align"),
     ({"q": MIS}, "align"),
 ])

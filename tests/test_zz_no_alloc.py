@@ -26,7 +26,8 @@ SCRATCH_BYTES = 64 << 20
 
 def _scratch_need(b, s, hq, g, d):
     nq = b * s * hq * d
-    return ((2 * nq * 4) if g > 1 else 0) + math.ceil(s / 256) * nq * 4
+    bn = 512 if d == 64 else 256  # key-block height of the backward kernel
+    return ((2 * nq * 4) if g > 1 else 0) + math.ceil(s / bn) * nq * 4
 
 
 def _noalloc(d, causal, scale):
@@ -80,8 +81,8 @@ def _check_one(case, b, s, hq, hkv, d, causal, seed, with_oracle):
 
 
 def test_noalloc_mha_largest_then_small():
-    # B1 S2048 Hq16 D64: 8 key blocks x 2 Mi floats x 4 B = exactly 64 MiB.
-    _check_one("mha max", 1, 2048, 16, 16, 64, True, seed=5, with_oracle=False)
+    # B1 S2048 Hq32 D64: 4 key blocks of 512 x 4 Mi floats x 4 B = exactly 64 MiB.
+    _check_one("mha max", 1, 2048, 32, 32, 64, True, seed=5, with_oracle=False)
     _check_one("mha small", 2, 300, 4, 4, 128, False, seed=6, with_oracle=True)
 
 
