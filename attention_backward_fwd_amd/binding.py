@@ -117,6 +117,11 @@ def library():
         lib.attn_sparse_mla_bwd.argtypes = [P, P, P, P, P, P, P, P, smla_shape, ctypes.c_float, P]
         lib.attn_sparse_mla_bwd_postprocess.restype = ctypes.c_int
         lib.attn_sparse_mla_bwd_postprocess.argtypes = [P, P, smla_shape, P]
+        lib.attn_sparse_mla_bwd_split_workspace_bytes.restype = ctypes.c_size_t
+        lib.attn_sparse_mla_bwd_split_workspace_bytes.argtypes = [smla_shape]
+        lib.attn_sparse_mla_bwd_split.restype = ctypes.c_int
+        lib.attn_sparse_mla_bwd_split.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.c_size_t, smla_shape,
+                                                  ctypes.c_float, P]
         _lib = lib
     return _lib
 
@@ -255,6 +260,19 @@ def attn_sparse_mla_bwd(q, kv, dout, indices, lse, delta, dq, dkv_accum, shape, 
 def attn_sparse_mla_bwd_postprocess(dkv_accum, dkv, shape, stream=None):
     _check(library().attn_sparse_mla_bwd_postprocess(_ptr(dkv_accum), _ptr(dkv), shape, _stream(stream)),
            "attn_sparse_mla_bwd_postprocess")
+
+
+def attn_sparse_mla_bwd_split_workspace_bytes(shape):
+    return int(library().attn_sparse_mla_bwd_split_workspace_bytes(shape))
+
+
+def attn_sparse_mla_bwd_split(q, kv, dout, indices, lse, delta, dq, dkv, workspace, shape, softmax_scale,
+                              stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().attn_sparse_mla_bwd_split(_ptr(q), _ptr(kv), _ptr(dout), _ptr(indices), _ptr(lse), _ptr(delta),
+                                               _ptr(dq), _ptr(dkv), _ptr(workspace), ws_bytes, shape,
+                                               float(softmax_scale), _stream(stream)),
+           "attn_sparse_mla_bwd_split")
 
 
 def gla_chunk_bwd_workspace_bytes(shape):
@@ -439,22 +457,42 @@ def sparse_mla_forward(q, kv, indices, scale, stream=None):
 
 
 class SmlaBwdBuffers:
-    """Outputs and scratch of one sparse MLA backward problem."""
+    """Outputs and scratch of one sparse MLA backward problem: the fp32 dKV
+    accumulator of the atomic path, or (use_atomic=False, given the index
+    tensor) the deterministic path's workspace."""
 
-    def __init__(self, q, kv):
+    def __init__(self, q, kv, use_atomic=True, indices=None):
         t, h, _ = q.shape
+        self.use_atomic = bool(use_atomic)
         self.delta = torch.empty((t, h), dtype=torch.float32, device=q.device)
         self.dq = torch.empty_like(q)
-        self.dkv_accum = torch.empty((kv.shape[0], 576), dtype=torch.float32, device=q.device)
         self.dkv = torch.empty_like(kv)
+        if self.use_atomic:
+            self.dkv_accum = torch.empty((kv.shape[0], 576), dtype=torch.float32, device=q.device)
+            self.workspace = None
+        else:
+            if indices is None:
+                raise ValueError("the deterministic path sizes its workspace from the index tensor")
+            n = attn_sparse_mla_bwd_split_workspace_bytes(smla_shape_of(q, kv, indices))
+            if n == 0:
+                raise ValueError("invalid sparse MLA shape")
+            self.dkv_accum = None
+            self.workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
 
 
-def sparse_mla_backward(q, kv, indices, o, lse, do, scale, buffers=None, stream=None):
-    """dq [T,H,576], dkv [Tk,576] via preprocess -> backward -> postprocess."""
+def sparse_mla_backward(q, kv, indices, o, lse, do, scale, buffers=None, stream=None, use_atomic=True):
+    """dq [T,H,576], dkv [Tk,576] via preprocess -> backward -> postprocess
+    (fp32 atomic dKV), or with use_atomic=False via preprocess -> the
+    deterministic backward (per-entry partial rows, fixed-order sum)."""
     _require_gpu_inputs(q, kv, o, do)
     shape = smla_shape_of(q, kv, indices)
-    bb = buffers or SmlaBwdBuffers(q, kv)
-    attn_sparse_mla_bwd_preprocess(o, do, bb.delta, bb.dkv_accum, shape, stream)
-    attn_sparse_mla_bwd(q, kv, do, indices, lse, bb.delta, bb.dq, bb.dkv_accum, shape, scale, stream)
-    attn_sparse_mla_bwd_postprocess(bb.dkv_accum, bb.dkv, shape, stream)
+    bb = buffers or SmlaBwdBuffers(q, kv, use_atomic, indices)
+    if bb.use_atomic:
+        attn_sparse_mla_bwd_preprocess(o, do, bb.delta, bb.dkv_accum, shape, stream)
+        attn_sparse_mla_bwd(q, kv, do, indices, lse, bb.delta, bb.dq, bb.dkv_accum, shape, scale, stream)
+        attn_sparse_mla_bwd_postprocess(bb.dkv_accum, bb.dkv, shape, stream)
+    else:
+        attn_sparse_mla_bwd_preprocess(o, do, bb.delta, None, shape, stream)
+        attn_sparse_mla_bwd_split(q, kv, do, indices, lse, bb.delta, bb.dq, bb.dkv, bb.workspace, shape, scale,
+                                  stream)
     return bb.dq, bb.dkv

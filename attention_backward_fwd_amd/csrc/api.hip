@@ -7,6 +7,7 @@
 
 #include "kernels.h"
 #include "mi355_attn.h"
+#include "smla_split.h"
 
 using namespace mi355;
 
@@ -506,6 +507,29 @@ int attn_sparse_mla_bwd(const uint16_t* q, const uint16_t* kv, const uint16_t* d
     return ATTN_ERR_ALIGN;
   return hip_status(launch_smla_bwd(q, kv, dout, indices, lse, delta, dq, dkv_accum, shape.tokens, shape.kv_tokens,
                                     shape.heads, shape.topk, softmax_scale, (hipStream_t)stream));
+}
+
+size_t attn_sparse_mla_bwd_split_workspace_bytes(smla_shape shape) {
+  if (check_smla(shape)) return 0;
+  return smla_split_workspace_bytes(shape.tokens, shape.kv_tokens, shape.heads, shape.topk);
+}
+
+int attn_sparse_mla_bwd_split(const uint16_t* q, const uint16_t* kv, const uint16_t* dout, const int32_t* indices,
+                              const float* lse, const float* delta, uint16_t* dq, uint16_t* dkv, void* workspace,
+                              size_t workspace_bytes, smla_shape shape, float softmax_scale, void* stream) {
+  if (!q || !kv || !dout || !indices || !lse || !delta || !dq || !dkv) return ATTN_ERR_NULL_PTR;
+  const int st = check_smla(shape);
+  if (st) return st;
+  if (!good_scale(softmax_scale)) return ATTN_ERR_RANGE;
+  if (!workspace ||
+      workspace_bytes < smla_split_workspace_bytes(shape.tokens, shape.kv_tokens, shape.heads, shape.topk))
+    return ATTN_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(kv) || !aligned16(dout) || !aligned16(dq) || !aligned16(dkv) ||
+      !aligned16(workspace) || !aligned4(indices) || !aligned4(lse) || !aligned4(delta))
+    return ATTN_ERR_ALIGN;
+  return hip_status(launch_smla_bwd_split(q, kv, dout, indices, lse, delta, dq, dkv, workspace, shape.tokens,
+                                          shape.kv_tokens, shape.heads, shape.topk, softmax_scale,
+                                          (hipStream_t)stream));
 }
 
 int attn_sparse_mla_bwd_postprocess(const float* dkv_accum, uint16_t* dkv, smla_shape shape, void* stream) {

@@ -20,6 +20,7 @@
 // to the XCDs round-robin, longest lists first.
 #include "common.h"
 #include "kernels.h"
+#include "smla_split.h"
 
 namespace mi355 {
 
@@ -32,6 +33,9 @@ constexpr int kSub = kKT * 128;  // elements of a 128-channel sub-tile of 32 row
 // Backward: the dKV atomics of a tile that may still be in flight when the
 // next tile starts (each wave issues 64 or 80 per tile; the counter holds 63).
 constexpr int kAtomSlack = 48;
+// The same for the split backward's 16-byte partial-row stores (16 or 20 per
+// wave and tile).
+constexpr int kStoreSlack = 16;
 // Byte offset past the end of any dKV accumulator (at most kSmlaMaxKvTokens
 // rows of 576 fp32): atomics sent there are dropped.
 constexpr uint32_t kDropOffset = 0x7FFFFFF0u;
@@ -78,6 +82,13 @@ __device__ __forceinline__ bf16x8 sop_tr_ch(const uint16_t* t, int dt, int k0, i
 // LDS-DMA; an entry is used iff it lies inside the list and 0 <= j < Tk.
 __device__ __forceinline__ void load_entries_async(const int* idx_t, int it, int K, int* slot, int w, int lane) {
   if (w == 0 && lane < kKT) dma_b32_asm(idx_t + min(it * kKT + lane, K - 1), lds_addr(slot));
+}
+// The same for a second per-entry list (the split backward's partial-row
+// positions), issued right after the index list.
+__device__ __forceinline__ void load_entries2_async(const int* idx_t, const int* pos_t, int it, int K, int* slot,
+                                                    int* pslot, int w, int lane) {
+  load_entries_async(idx_t, it, K, slot, w, lane);
+  if (pos_t) load_entries_async(pos_t, it, K, pslot, w, lane);
 }
 __device__ __forceinline__ bool entry_ok(const int* slot, int r, int e0, int K, int Tk) {
   const int j = slot[r];
@@ -350,10 +361,19 @@ __global__ __launch_bounds__(256) void smla_post_kernel(const float* __restrict_
 // the XCDs round-robin and tiles past the last valid entry are skipped.  The
 // atomic rate of the memory system (~340 G fp32 adds/s), not the matrix
 // work, bounds this kernel: 576 adds per (token, valid entry).
+// SPLIT: instead of the atomics, each valid entry's dKV row (this head
+// tile's share) is stored whole, with plain 16-byte stores, as row
+// pos[t, i] * n_ht + head tile of `part` (pos: the entry's place among the
+// entries ordered by key row, then token, then slot); unused entries write
+// row `dummy_row`, which nothing reads, so that every wave issues the same
+// number of stores per tile.  A fixed-order sum over each key row's
+// consecutive partial rows then gives dKV.
+template <bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void smla_bwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const uint16_t* __restrict__ dout,
     const int* __restrict__ idx, const float* __restrict__ lse, const float* __restrict__ delta,
-    uint16_t* __restrict__ dq, float* __restrict__ dkv_acc, int T, int Tk, int H, int K, float scale) {
+    uint16_t* __restrict__ dq, float* __restrict__ dkv_acc, float* __restrict__ part, const int* __restrict__ pos,
+    long long dummy_row, int T, int Tk, int H, int K, float scale) {
   __shared__ __attribute__((aligned(16))) uint16_t sQ[4 * kSub + kKT * 64];
   __shared__ __attribute__((aligned(16))) uint16_t sKV0[4 * kSub + kKT * 64];
   __shared__ __attribute__((aligned(16))) uint16_t sKV1[4 * kSub + kKT * 64];
@@ -361,6 +381,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void s
   __shared__ __attribute__((aligned(16))) uint16_t sDS[kKT * kHT];  // scale dS as [entry][head]
   __shared__ __attribute__((aligned(16))) uint16_t sPT[kKT * kHT];  // P as [entry][head]
   __shared__ __attribute__((aligned(16))) int sIdx[3][kKT];  // raw entry lists, as in the forward
+  __shared__ __attribute__((aligned(16))) int sPos[SPLIT ? 3 : 1][kKT];  // SPLIT: partial-row positions
   __shared__ int sRed[4];
 
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), hi = lane >> 5;
@@ -373,6 +394,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void s
   const int id = blockIdx.x;
   const int t = __builtin_amdgcn_readfirstlane(T - 1 - id / n_ht), h0 = __builtin_amdgcn_readfirstlane((id % n_ht) * kHT);
   const int* idx_t = idx + (size_t)t * K;
+  const int* pos_t = SPLIT ? pos + (size_t)t * K : nullptr;
   const int head = h0 + l32;                   // this lane's head (S^T columns)
   const bool head_ok = head < H;
   const int hc = min(head, H - 1);
@@ -417,8 +439,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void s
   const GatherCols gcols = gather_cols(w, lane);
   // Entry lists and gathers as in the forward kernel.
   if (n_tiles > 0) {
-    load_entries_async(idx_t, 0, K, sIdx[0], w, lane);
-    if (n_tiles > 1) load_entries_async(idx_t, 1, K, sIdx[1], w, lane);
+    load_entries2_async(idx_t, pos_t, 0, K, sIdx[0], sPos[0], w, lane);
+    if (n_tiles > 1) load_entries2_async(idx_t, pos_t, 1, K, sIdx[1], sPos[SPLIT ? 1 : 0], w, lane);
     wait_vmem();
     lds_barrier();
     gather_rows_async(kv, sIdx[0], 0, K, Tk, sKV0, gcols, w, lane);
@@ -443,11 +465,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void s
     // atomics (at least 64 per wave, issued after the gather), which may
     // stay in flight: the counter retires in issue order.
     if (it > 0)
-      wait_vmem_but<kAtomSlack>();
+      wait_vmem_but<SPLIT ? kStoreSlack : kAtomSlack>();
     else
       wait_vmem();
     lds_barrier();  // tile it and the list of tile it+1 resident; every wave is done with tile it-1
-    if (it + 2 < n_tiles) load_entries_async(idx_t, it + 2, K, sIdx[(it + 2) % 3], w, lane);
+    if (it + 2 < n_tiles)
+      load_entries2_async(idx_t, pos_t, it + 2, K, sIdx[(it + 2) % 3], sPos[SPLIT ? (it + 2) % 3 : 0], w, lane);
     if (it + 1 < n_tiles) gather_rows_async(kv, sIdx[(it + 1) % 3], (it + 1) * kKT, K, Tk, nKV, gcols, w, lane);
     const int* cIdx = sIdx[slot];
     const int e0 = it * kKT;
@@ -511,6 +534,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void s
       ads[kk] = __builtin_bit_cast(bf16x8, u32x4{a0[0], a0[1], a1[0], a1[1]});
       apt[kk] = __builtin_bit_cast(bf16x8, u32x4{b0[0], b0[1], b1[0], b1[1]});
     }
+    if constexpr (SPLIT) {
+      // Transposed: dKV^T[channel][entry] = Q^T dS^T + dO^T P^T (the same
+      // operands, swapped), so that lane l32 holds entry l32's channels
+      // 32 blk + c_row(j): four 16-byte pieces of its partial row per block.
+      const long long r =
+          entry_ok(cIdx, l32, e0, K, Tk) ? (long long)sPos[slot][l32] * n_ht + h0 / kHT : dummy_row;
+      // Positions lie in [0, T K): the clamp only keeps the stores inside the buffer.
+      float* prow = part + ((unsigned long long)r <= (unsigned long long)dummy_row ? r : dummy_row) * kQK + 4 * hi;
+#pragma unroll
+      for (int bi = 0; bi < 5; bi++) {
+        if (bi >= nblk) continue;
+        const int blk = w + 4 * bi;
+        f32x16 acc = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < 2; kk++) {
+          acc = mfma32(sop_tr_ch(sQ, blk, 16 * kk, lane), ads[kk], acc);
+          if (blk < 16) acc = mfma32(vdo[bi][kk], apt[kk], acc);
+        }
+#pragma unroll
+        for (int g = 0; g < 4; g++)
+          *reinterpret_cast<f32x4*>(prow + 32 * blk + 8 * g) =
+              f32x4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+      }
+      return;
+    }
 #pragma unroll
     for (int bi = 0; bi < 5; bi++) {
       if (bi >= nblk) continue;
@@ -571,8 +619,18 @@ hipError_t launch_smla_bwd(const uint16_t* q, const uint16_t* kv, const uint16_t
                            const float* lse, const float* delta, uint16_t* dq, float* dkv_acc, int T, int Tk, int H,
                            int K, float scale, hipStream_t stream) {
   const int n_ht = (H + kHT - 1) / kHT;
-  hipLaunchKernelGGL(smla_bwd_kernel, dim3((unsigned)((long long)T * n_ht)), dim3(256), 0, stream, q, kv, dout, idx,
-                     lse, delta, dq, dkv_acc, T, Tk, H, K, scale);
+  hipLaunchKernelGGL(smla_bwd_kernel<false>, dim3((unsigned)((long long)T * n_ht)), dim3(256), 0, stream, q, kv, dout,
+                     idx, lse, delta, dq, dkv_acc, nullptr, nullptr, 0LL, T, Tk, H, K, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_smla_bwd_partial(const uint16_t* q, const uint16_t* kv, const uint16_t* dout, const int* idx,
+                                   const float* lse, const float* delta, uint16_t* dq, float* part, const int* pos,
+                                   int T, int Tk, int H, int K, float scale, hipStream_t stream) {
+  const int n_ht = (H + kHT - 1) / kHT;
+  const long long dummy_row = (long long)T * K * n_ht;
+  hipLaunchKernelGGL(smla_bwd_kernel<true>, dim3((unsigned)((long long)T * n_ht)), dim3(256), 0, stream, q, kv, dout,
+                     idx, lse, delta, dq, nullptr, part, pos, dummy_row, T, Tk, H, K, scale);
   return hipGetLastError();
 }
 

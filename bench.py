@@ -38,7 +38,7 @@ def flops(w, causal):
 
 BWD_SOURCES = ("bwd.hip", "common.h", "kernels.h")  # what the backward kernel is built from
 GLA_SOURCES = ("gla.hip", "common.h", "kernels.h")  # what the GLA chunk backward is built from
-SMLA_SOURCES = ("smla.hip", "common.h", "kernels.h")  # ... the sparse MLA kernels
+SMLA_SOURCES = ("smla.hip", "smla_split.hip", "smla_split.h", "common.h", "kernels.h")  # ... the sparse MLA kernels
 MERGE_SOURCES = ("merge.hip", "common.h", "kernels.h")  # ... the partial-merge kernel
 
 
@@ -328,12 +328,14 @@ def bench_gla(args, bd, torch):
 
 
 def bench_smla(args, bd, torch):
-    """Sparse MLA forward + backward (preprocess, backward, postprocess) on
-    the sparse MLA workload.  FLOPs: per (token, head, valid entry)
-    2*(576 + 512) forward and 2*(576 + 512 + 576 + 576 + 512) backward (S, dP,
-    dQ, dK, dV).  The backward kernel's dKV goes out as fp32 atomic adds,
-    576 per (token, valid entry) and 32-head tile; ``atomics`` reports their
-    rate."""
+    """Sparse MLA forward + backward on the sparse MLA workload.  FLOPs: per
+    (token, head, valid entry) 2*(576 + 512) forward and
+    2*(576 + 512 + 576 + 576 + 512) backward (S, dP, dQ, dK, dV).  Two dKV
+    paths: fp32 atomic adds (576 per token, valid entry and 32-head tile;
+    ``atomics`` reports their rate), then a postprocess cast; or the
+    deterministic path (--use-atomic 0): index sort, per-entry partial rows,
+    fixed-order sum, all inside one call.  The path not chosen is timed after
+    it on the same inputs (``other_path``) unless --no-other-path."""
     from attention_backward_fwd_amd.synthetic import SMLA_WORKLOAD, smla_indices, smla_inputs
 
     w = SMLA_WORKLOAD
@@ -347,39 +349,73 @@ def bench_smla(args, bd, torch):
     shape = bd.smla_shape_of(q, kv, idx)
     o = torch.empty((t, h, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((t, h), dtype=torch.float32, device=dev)
-    bb = bd.SmlaBwdBuffers(q, kv)
     stream = torch.cuda.current_stream()
-    ev = {n: [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)] for n in ("fwd", "bwd")}
-
-    def step(i=None):
-        if i is not None:
-            ev["fwd"][2 * i].record(stream)
-        bd.attn_sparse_mla_fwd(q, kv, idx, o, lse, shape, scale, stream)
-        if i is not None:
-            ev["fwd"][2 * i + 1].record(stream)
-        bd.attn_sparse_mla_bwd_preprocess(o, do, bb.delta, bb.dkv_accum, shape, stream)
-        if i is not None:
-            ev["bwd"][2 * i].record(stream)
-        bd.attn_sparse_mla_bwd(q, kv, do, idx, lse, bb.delta, bb.dq, bb.dkv_accum, shape, scale, stream)
-        if i is not None:
-            ev["bwd"][2 * i + 1].record(stream)
-        bd.attn_sparse_mla_bwd_postprocess(bb.dkv_accum, bb.dkv, shape, stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
     n_valid = int((idx_cpu >= 0).sum())
     fwd_f = 2.0 * n_valid * h * (576 + 512)
     bwd_f = 2.0 * n_valid * h * (576 + 512 + 576 + 576 + 512)
-    fwd_ms = sum(ev["fwd"][2 * i].elapsed_time(ev["fwd"][2 * i + 1]) for i in range(args.steps)) / args.steps
-    bwd_ms = sum(ev["bwd"][2 * i].elapsed_time(ev["bwd"][2 * i + 1]) for i in range(args.steps)) / args.steps
+
+    def run(use_atomic, steps, warmup):
+        bb = bd.SmlaBwdBuffers(q, kv, use_atomic, idx)
+        names = ("fwd", "pre", "call", "post")
+        ev = {n: [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)] for n in names}
+
+        def mark(n, i, end):
+            if i is not None:
+                ev[n][2 * i + end].record(stream)
+
+        def step(i=None):
+            mark("fwd", i, 0)
+            bd.attn_sparse_mla_fwd(q, kv, idx, o, lse, shape, scale, stream)
+            mark("fwd", i, 1)
+            mark("pre", i, 0)
+            bd.attn_sparse_mla_bwd_preprocess(o, do, bb.delta, bb.dkv_accum, shape, stream)
+            mark("pre", i, 1)
+            mark("call", i, 0)
+            if use_atomic:
+                bd.attn_sparse_mla_bwd(q, kv, do, idx, lse, bb.delta, bb.dq, bb.dkv_accum, shape, scale, stream)
+            else:
+                bd.attn_sparse_mla_bwd_split(q, kv, do, idx, lse, bb.delta, bb.dq, bb.dkv, bb.workspace, shape, scale,
+                                             stream)
+            mark("call", i, 1)
+            mark("post", i, 0)
+            if use_atomic:
+                bd.attn_sparse_mla_bwd_postprocess(bb.dkv_accum, bb.dkv, shape, stream)
+            mark("post", i, 1)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(i)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        ms = {n: sum(ev[n][2 * i].elapsed_time(ev[n][2 * i + 1]) for i in range(steps)) / steps for n in names}
+        ms["backward"] = ms["pre"] + ms["call"] + ms["post"]
+        ws = 0 if bb.workspace is None else bb.workspace.numel()
+        del bb
+        return ms, elapsed, ws
+
+    use_atomic = bool(args.use_atomic)
+    ms, elapsed, ws = run(use_atomic, args.steps, args.warmup)
     value = (fwd_f + bwd_f) * args.steps / elapsed / 1e12
     n_atomics = n_valid * 576 * ((h + 31) // 32)
+
+    def path_record(m, atomic, ws_bytes):
+        rec = {"dkv_path": "atomic" if atomic else "split", "bwd_call_ms": round(m["call"], 4),
+               "preprocess_ms": round(m["pre"], 4), "postprocess_ms": round(m["post"], 4),
+               "whole_backward_ms": round(m["backward"], 4),
+               "whole_backward_tflops": round(bwd_f / (m["backward"] * 1e-3) / 1e12, 3),
+               "frac_whole_backward": round(bwd_f / (m["backward"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        if not atomic:
+            rec["deterministic"] = True
+            rec["workspace_gb"] = round(ws_bytes / 1e9, 3)
+        return rec
+
+    other = None
+    if not args.no_other_path:
+        m2, _, ws2 = run(not use_atomic, max(3, min(args.steps, 10)), 2)
+        other = path_record(m2, not use_atomic, ws2)
     cpu = None
     if not args.no_cpu_baseline:
         from oracle import sparse_mla as sm
@@ -397,19 +433,32 @@ def bench_smla(args, bd, torch):
         cpu = {"value": round(flop_done / t_cpu / 1e12, 6), "unit": "TFLOP/s", "cores": int(_blas_threads()),
                "kind": "oracle", "sample": f"{done} of {t} tokens (every 4th from the last), fwd+bwd in fp64, "
                                            f"{t_cpu:.1f} s; the same per-entry FLOP count"}
+    call_tf = bwd_f / (ms["call"] * 1e-3) / 1e12
+    if use_atomic:
+        roof = {"kernel": "smla_bwd_kernel", "bound": "mfma", "achieved": round(call_tf, 3),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(call_tf / PEAK_BF16_TFLOPS, 4),
+                "traffic": recorded_traffic(w["name"], "bwd", SMLA_SOURCES)}
+    else:
+        # The deterministic call launches the sort, the backward kernel and the
+        # sum together: its time (all three) prices the backward's FLOPs.
+        roof = {"kernel": "attn_sparse_mla_bwd_split (sort + smla_bwd_kernel + dkv_sum)", "bound": "mfma",
+                "achieved": round(call_tf, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(call_tf / PEAK_BF16_TFLOPS, 4),
+                "traffic": recorded_traffic(w["name"], "bwd_split", SMLA_SOURCES)}
     print(json.dumps({
         "metric": "sparse MLA fwd+bwd TFLOP/s (bf16)", "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(elapsed / args.steps * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w["name"], "tokens": t, "kv_tokens": t, "heads": h, "topk": k,
-                   "valid_entries": n_valid, "dim_qk": 576, "dim_v": 512},
-        "fwd_kernel_ms": round(fwd_ms, 4), "fwd_tflops": round(fwd_f / (fwd_ms * 1e-3) / 1e12, 3),
-        "bwd_kernel_ms": round(bwd_ms, 4), "bwd_tflops": round(bwd_f / (bwd_ms * 1e-3) / 1e12, 3),
-        "atomics": {"count": n_atomics, "per_s": round(n_atomics / (bwd_ms * 1e-3) / 1e9, 1), "unit": "G/s"},
-        "roofline": {"kernel": "smla_bwd_kernel", "bound": "mfma", "achieved": round(bwd_f / (bwd_ms * 1e-3) / 1e12, 3),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(bwd_f / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                     "traffic": recorded_traffic(w["name"], "bwd", SMLA_SOURCES)},
+                   "valid_entries": n_valid, "dim_qk": 576, "dim_v": 512,
+                   "dkv_path": "atomic" if use_atomic else "split"},
+        "fwd_kernel_ms": round(ms["fwd"], 4), "fwd_tflops": round(fwd_f / (ms["fwd"] * 1e-3) / 1e12, 3),
+        "bwd_kernel_ms": round(ms["call"], 4), "bwd_tflops": round(call_tf, 3),
+        **path_record(ms, use_atomic, ws),
+        **({"atomics": {"count": n_atomics, "per_s": round(n_atomics / (ms["call"] * 1e-3) / 1e9, 1), "unit": "G/s"}}
+           if use_atomic else {}),
+        **({"other_path": other} if other else {}),
+        "roofline": roof,
         **({"cpu_baseline": cpu} if cpu else {}),
     }), flush=True)
 

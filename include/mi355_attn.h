@@ -388,6 +388,34 @@ int attn_sparse_mla_bwd(const uint16_t* q, const uint16_t* kv, const uint16_t* d
                         float softmax_scale, void* stream);
 int attn_sparse_mla_bwd_postprocess(const float* dkv_accum, uint16_t* dkv, smla_shape shape, void* stream);
 
+/*
+ * Sparse MLA backward with a deterministic dKV (bitwise reproducible run to
+ * run), the alternative to fp32 atomics that the cuDNN frontend pull request
+ * "CSA: add fused Compressor forward+backward CuTe-DSL kernels (ported from
+ * Megatron-LM)" (NVIDIA cudnn-frontend #427, numerics and determinism
+ * section) names: partials reduced in a fixed order.  Takes the place of
+ * attn_sparse_mla_bwd + attn_sparse_mla_bwd_postprocess (run
+ * attn_sparse_mla_bwd_preprocess first, dkv_accum may be NULL there):
+ *   dq  [tokens, heads, 576] bf16, written, as attn_sparse_mla_bwd;
+ *   dkv [kv_tokens, 576] bf16, written whole: row j is the bf16 (RNE) of
+ *       the sum, over the valid entries (t, i) with indices[t, i] = j and
+ *       over the 32-head tiles of t, of scale * sum_h dS q[t,h] (+ sum_h
+ *       P dout[t,h] in channels 0..511), each entry's fp32 row formed
+ *       whole and the rows added in one fixed order (by token, slot, head
+ *       tile); 0 for a row no valid entry names.
+ * workspace: device memory of at least
+ * attn_sparse_mla_bwd_split_workspace_bytes(shape) bytes, 16-byte aligned,
+ * owned by the caller, no initial contents needed; its size is dominated by
+ * one fp32 row of 576 per entry slot and 32-head tile
+ * (tokens * topk * ceil(heads / 32) * 2304 bytes).  Errors as
+ * attn_sparse_mla_bwd, plus ATTN_ERR_WORKSPACE (NULL or too small).
+ * attn_sparse_mla_bwd_split_workspace_bytes returns 0 for an invalid shape.
+ */
+size_t attn_sparse_mla_bwd_split_workspace_bytes(smla_shape shape);
+int attn_sparse_mla_bwd_split(const uint16_t* q, const uint16_t* kv, const uint16_t* dout, const int32_t* indices,
+                              const float* lse, const float* delta, uint16_t* dq, uint16_t* dkv, void* workspace,
+                              size_t workspace_bytes, smla_shape shape, float softmax_scale, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

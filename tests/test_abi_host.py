@@ -32,7 +32,8 @@ def test_library_exports_every_header_symbol():
                             "attn_bwd_varlen_workspace_bytes", "attn_bwd_varlen",
                             "attn_bwd_varlen_postprocess", "gla_chunk_bwd_workspace_bytes", "gla_chunk_bwd",
                             "attn_sparse_mla_fwd", "attn_sparse_mla_bwd_preprocess", "attn_sparse_mla_bwd",
-                            "attn_sparse_mla_bwd_postprocess"])
+                            "attn_sparse_mla_bwd_postprocess", "attn_sparse_mla_bwd_split_workspace_bytes",
+                            "attn_sparse_mla_bwd_split"])
     for n in names:
         assert hasattr(lib(), n), n
 
@@ -387,6 +388,58 @@ def test_sparse_mla_pre_post_errors():
     g = lib().attn_sparse_mla_bwd_postprocess
     assert g(None, A, mshp(), None) == E["null"]
     assert g(A, MIS, mshp(), None) == E["align"]
+
+
+def _a256(x):
+    return (x + 255) // 256 * 256
+
+
+def smla_split_ws(t, tk, h, k):
+    """Workspace of the deterministic sparse MLA backward, region by region:
+    one fp32 row of 576 per entry slot and 32-head tile plus a sink row;
+    entry positions; key-row offsets (tk + 1); two (key, entry) buffer pairs
+    of the radix sort; the digit counts of its widest pass (passes of at most
+    10 bits over keys 0 .. tk, tiles of 4096 entries); one scan partial per
+    4096 counts."""
+    n, n_ht = t * k, -(-h // 32)
+    bits = tk.bit_length()
+    passes = 1 if bits <= 10 else 2
+    hist = (1 << -(-bits // passes)) * -(-n // 4096)
+    return (_a256((n * n_ht + 1) * 2304) + _a256(4 * n) + _a256(4 * (tk + 1)) + 4 * _a256(4 * n) + _a256(4 * hist)
+            + _a256(4 * -(-hist // 4096)))
+
+
+@pytest.mark.parametrize("t,tk,h,k", [(8, 100, 16, 64), (8, 100, 40, 64), (3, 1023, 1, 1), (5, 1024, 33, 9),
+                                      (4096, 4096, 32, 2048), (7, (1 << 19), 128, 8192)])
+def test_sparse_mla_split_workspace_bytes(t, tk, h, k):
+    assert bd.attn_sparse_mla_bwd_split_workspace_bytes(mshp(t=t, tk=tk, h=h, k=k)) == smla_split_ws(t, tk, h, k)
+
+
+def test_sparse_mla_split_workspace_bytes_small_case_by_hand():
+    # T8 K64 H16 Tk100: 513 rows * 2304 B + 2048 + 512 + 4 * 2048 + 512 (128 digits) + 256.
+    assert bd.attn_sparse_mla_bwd_split_workspace_bytes(mshp()) == 1193472
+    assert bd.attn_sparse_mla_bwd_split_workspace_bytes(mshp(h=0)) == 0
+    assert bd.attn_sparse_mla_bwd_split_workspace_bytes(mshp(dqk=128)) == 0
+
+
+def msplit(**kw):
+    need = bd.attn_sparse_mla_bwd_split_workspace_bytes(mshp())
+    args = dict(q=A, kv=A, do=A, idx=A, lse=A, delta=A, dq=A, dkv=A, ws=A, wsb=need, shape=mshp(), scale=0.05,
+                stream=None)
+    args.update(kw)
+    return lib().attn_sparse_mla_bwd_split(args["q"], args["kv"], args["do"], args["idx"], args["lse"],
+                                           args["delta"], args["dq"], args["dkv"], args["ws"], args["wsb"],
+                                           args["shape"], args["scale"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"dkv": None}, "null"), ({"idx": None}, "null"), ({"shape": mshp(k=0)}, "shape"),
+    ({"shape": mshp(dv=256)}, "hd"), ({"scale": float("nan")}, "range"), ({"shape": mshp(k=8193)}, "range"),
+    ({"ws": None}, "ws"), ({"wsb": 1193471}, "ws"), ({"dkv": MIS}, "align"), ({"ws": MIS}, "align"),
+    ({"lse": P(0x10002)}, "align"),
+])
+def test_sparse_mla_split_errors(kw, code):
+    assert msplit(**kw) == E[code]
 
 
 # Scratch of attn_bwd_noalloc: 64 MiB; need = (2 if groups > 1) * nq * 4 + ceil(S/bn) * nq * 4, with key

@@ -73,13 +73,20 @@ def test_smla_fwd_full_size_sampled():
     _check(o[rows], lse[rows], ro, rl, f"[smla full] {w['name']} tokens {rows}")
 
 
-def _run_bwd(inp, idx):
+def _run_bwd(inp, idx, use_atomic=True, fill=float("nan")):
+    """Forward, then the backward on the atomic (use_atomic) or the
+    deterministic path, with every output poisoned (NaN) and the
+    deterministic path's workspace filled with the fp32 value `fill` (which
+    its integer regions then read as garbage)."""
     q, kv, do = inp["q"].cuda(), inp["kv"].cuda(), inp["do"].cuda()
     ix = idx.cuda() if isinstance(idx, torch.Tensor) else torch.from_numpy(idx).cuda()
     o, lse = bd.sparse_mla_forward(q, kv, ix, SCALE)
-    bb = bd.SmlaBwdBuffers(q, kv)
+    bb = bd.SmlaBwdBuffers(q, kv, use_atomic, ix)
     for x in (bb.delta, bb.dq, bb.dkv_accum, bb.dkv):
-        x.fill_(float("nan"))
+        if x is not None:
+            x.fill_(float("nan"))
+    if bb.workspace is not None:
+        bb.workspace.view(torch.float32)[: bb.workspace.numel() // 4].fill_(fill)
     dq, dkv = bd.sparse_mla_backward(q, kv, ix, o, lse, do, SCALE, buffers=bb)
     torch.cuda.synchronize()
     return {"dq": dq, "dkv": dkv, "delta": bb.delta, "o": o}
@@ -174,3 +181,91 @@ def test_smla_gaps_and_scattered_sentinels():
         assert r <= TOL, (n, r)
     unused = np.all(ref["dkv"] == 0.0, axis=1)
     assert np.all(np64(gpu["dkv"])[unused] == 0.0)
+
+
+# ------------------------------------------------------------ deterministic dKV path
+
+SPLIT_CASES = CASES + [(64, 3000, 32, 256), (40, 5000, 8, 700)]   # the last two: two sort passes, several tiles
+
+
+@pytest.mark.parametrize("t,tk,h,k", SPLIT_CASES)
+def test_smla_bwd_split_against_oracle(t, tk, h, k):
+    """use_atomic=False: dq and dkv against the oracle element by element;
+    dq identical to the atomic path's (the same kernel code computes it);
+    dkv bitwise identical over two runs with different workspace garbage."""
+    inp = smla_inputs(t, tk, h, seed=t + k)
+    idx = _indices(t, tk, k, seed=h)
+    f = {n: x.double().numpy() for n, x in inp.items()}
+    ref = sm.sparse_mla_bwd(f["q"], f["kv"], idx, f["do"], SCALE)
+    gpu = _run_bwd(inp, idx, use_atomic=False)
+    case = f"smla bwd split T{t} Tk{tk} H{h} K{k}"
+    ratios = {n: err_ratio(np64(gpu[n]), ref[n]) for n in ("dq", "dkv", "delta")}
+    say(f"{case}: " + " ".join(f"{n}={r:.2e}" for n, r in ratios.items()))
+    for n, r in ratios.items():
+        assert r <= TOL, (case, n, r)
+    unused = np.all(ref["dkv"] == 0.0, axis=1)
+    assert np.all(np64(gpu["dkv"])[unused] == 0.0), case
+    atomic = _run_bwd(inp, idx, use_atomic=True)
+    assert torch.equal(gpu["dq"], atomic["dq"]), case
+    again = _run_bwd(inp, idx, use_atomic=False, fill=-7.5)
+    assert torch.equal(gpu["dkv"], again["dkv"]) and torch.equal(gpu["dq"], again["dq"]), case
+
+
+def test_smla_bwd_split_gaps_and_scattered_sentinels():
+    t, tk, h, k = 6, 400, 40, 130
+    inp = smla_inputs(t, tk, h, seed=21)
+    idx = _gappy_indices(t, tk, k, seed=22)
+    f = {n: x.double().numpy() for n, x in inp.items()}
+    ref = sm.sparse_mla_bwd(f["q"], f["kv"], idx, f["do"], SCALE)
+    gpu = _run_bwd(inp, idx, use_atomic=False)
+    ratios = {n: err_ratio(np64(gpu[n]), ref[n]) for n in ("dq", "dkv")}
+    say("smla bwd split gaps: " + " ".join(f"{n}={r:.2e}" for n, r in ratios.items()))
+    for n, r in ratios.items():
+        assert r <= TOL, (n, r)
+    unused = np.all(ref["dkv"] == 0.0, axis=1)
+    assert np.all(np64(gpu["dkv"])[unused] == 0.0)
+
+
+def test_smla_bwd_split_mid_size_elementwise():
+    """As test_smla_bwd_mid_size_elementwise, on the deterministic path
+    (1024 tokens x 512 entries: 128 sort tiles, two radix passes)."""
+    t, h, k = 1024, 32, 512
+    inp = smla_inputs(t, t, h, seed=4)
+    idx = smla_indices(t, t, k, seed=4)
+    f = {n: x.double().numpy() for n, x in inp.items()}
+    ref = sm.sparse_mla_bwd(f["q"], f["kv"], idx.numpy(), f["do"], SCALE)
+    gpu = _run_bwd(inp, idx, use_atomic=False)
+    ratios = {n: err_ratio(np64(gpu[n]), ref[n]) for n in ("dq", "dkv", "delta")}
+    say(f"smla bwd split T{t} H{h} K{k}: " + " ".join(f"{n}={r:.2e}" for n, r in ratios.items()))
+    for n, r in ratios.items():
+        assert r <= TOL, (n, r)
+
+
+def test_smla_bwd_split_full_size():
+    """The benchmark workload on the deterministic path: dq of sampled tokens
+    against the oracle, dkv of sampled keys against the oracle (each key's
+    gradient summed over the tokens that select it), the whole dkv against
+    the atomic path's element by element, and bitwise repeatability."""
+    w = SMLA_WORKLOAD
+    t, h, k = w["tokens"], w["heads"], w["topk"]
+    inp = smla_inputs(t, t, h, seed=0)
+    idx = smla_indices(t, t, k, seed=0)
+    say(f"[smla full bwd split] {w['name']}: gpu")
+    gpu = _run_bwd(inp, idx, use_atomic=False)
+    atomic = _run_bwd(inp, idx, use_atomic=True)
+    assert torch.equal(gpu["dq"], atomic["dq"])
+    r_atomic = err_ratio(np64(gpu["dkv"]), np64(atomic["dkv"]))
+    again = _run_bwd(inp, idx, use_atomic=False, fill=3.25)
+    assert torch.equal(gpu["dkv"], again["dkv"])
+    # Keys 3800, 4000, 4095 (selected by ~150, ~50 and 1 of the later tokens):
+    # the oracle over those tokens, whole (all their entries).
+    keys = [3800, 4000, 4095]
+    idx_np = idx.numpy()
+    toks = sorted(set(np.nonzero(np.isin(idx_np, keys))[0].tolist()))
+    sub = sm.sparse_mla_bwd(inp["q"][toks].double().numpy(), inp["kv"].double().numpy(), idx_np[toks],
+                            inp["do"][toks].double().numpy(), SCALE)
+    r_keys = err_ratio(np64(gpu["dkv"][keys]), sub["dkv"][keys])
+    r_dq = err_ratio(np64(gpu["dq"][toks[:8]]), sub["dq"][:8])
+    say(f"[smla full bwd split] dkv vs atomic={r_atomic:.2e} dkv(keys {keys}, {len(toks)} tokens)={r_keys:.2e} "
+        f"dq(sampled)={r_dq:.2e}")
+    assert r_atomic <= TOL and r_keys <= TOL and r_dq <= TOL
