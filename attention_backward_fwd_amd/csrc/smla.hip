@@ -131,33 +131,6 @@ __device__ __forceinline__ void gather_rows_async(const uint16_t* g, const int* 
   dma_b128_asm_off<0>(p2, tb + 2 * (4 * kSub + w * 512));
 }
 
-// Partial results of the four waves (16 fp32 per lane, one 32x32 result
-// each) are summed through LDS in a fixed order: each wave stores its
-// partial (store_partial), a barrier follows, and every wave adds the four
-// (sum_partials).  Layout [wave][j / 4][lane][j % 4], 16-byte accesses.  The
-// accesses are inline assembly: compiler-visible LDS accesses to this buffer
-// were made to wait for the gathers in flight to the other buffers.
-__device__ __forceinline__ void store_partial(uint32_t base, int w, int lane, const f32x16& v) {
-  const uint32_t a = base + (uint32_t)(w * 4096 + lane * 16);
-#pragma unroll
-  for (int jg = 0; jg < 4; jg++)
-    lds_store_b128_addr(a + 1024u * jg, f32x4{v[4 * jg], v[4 * jg + 1], v[4 * jg + 2], v[4 * jg + 3]});
-}
-__device__ __forceinline__ f32x16 sum_partials(uint32_t base, int lane) {
-  const uint32_t a = base + (uint32_t)(lane * 16);
-  f32x16 out;
-#pragma unroll
-  for (int jg = 0; jg < 4; jg++) {
-    f32x4 p0 = lds_load_b128_addr(a + 1024u * jg), p1 = lds_load_b128_addr(a + 4096u + 1024u * jg);
-    f32x4 p2 = lds_load_b128_addr(a + 8192u + 1024u * jg), p3 = lds_load_b128_addr(a + 12288u + 1024u * jg);
-    lds_wait4(p0, p1, p2, p3);
-    const f32x4 r = (p0 + p1) + (p2 + p3);
-#pragma unroll
-    for (int i = 0; i < 4; i++) out[4 * jg + i] = r[i];
-  }
-  return out;
-}
-
 // Number of 32-entry tiles up to and including the last valid entry of the
 // list idx_t[0 .. K) (0 when it has none): tiles past it hold only unused
 // slots and are skipped.  All 256 threads take part; `red` is 4 ints of LDS.
@@ -347,16 +320,20 @@ __global__ __launch_bounds__(256) void smla_post_kernel(const float* __restrict_
 }
 
 // Backward kernel: one workgroup (4 waves) per (token, 32-head tile).  Per
-// tile of 32 entries (gathered as in the forward): S^T (partials over the
-// 576 channels, summed through LDS), P = exp(S - LSE); dP^T = V dO^T
-// (partials over wave w's 128 value channels; dO operands in registers);
-// dS = P (dP - Delta); padded heads and unused entries get P = dS = 0.  Then
-//   dQ^T += KV^T dS^T   (in registers across all tiles; wave w owns channel
-//                        blocks w, w+4, .. of the 18 blocks of 32)
-//   dKV   = scale dS^T Q + P^T dO   for the tile's 32 entries (dS^T, P^T
-//                        through LDS as [entry][head]), added to the fp32
-//                        accumulator row of each valid entry with buffer
-//                        atomics that stay in flight into the next tile.
+// tile of 32 entries (gathered as in the forward), wave w owns the block of
+// entries 16(w >> 1) .. +15 and heads h0 + 16(w & 1) .. +15, as in the
+// forward, and computes its scores S^T and dP^T = V dO^T over all channels
+// with 16x16x32 products (the entries' rows from LDS, read once for both;
+// query and dO operands in registers): no partial sums cross waves.  Then
+// P = exp(S - LSE), dS = P (dP - Delta) (padded heads and unused entries: 0),
+// and the waves hand scale dS and P over through LDS as [entry][head] tiles
+// (one barrier) for the two products that contract over entries or heads:
+//   dQ^T += KV^T (scale dS)^T   (in registers across all tiles; wave w owns
+//                                channel blocks w, w+4, .. of the 18 blocks of 32)
+//   dKV   = (scale dS)^T Q + P^T dO   for the tile's 32 entries, same channel
+//                                blocks, added to the fp32 accumulator row of
+//                                each valid entry with buffer atomics that stay
+//                                in flight into the next tile.
 // dQ (bf16) is written at the end.  As in the forward, tokens are dealt to
 // the XCDs round-robin and tiles past the last valid entry are skipped.  The
 // atomic rate of the memory system (~340 G fp32 adds/s), not the matrix
@@ -375,9 +352,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void s
     uint16_t* __restrict__ dq, float* __restrict__ dkv_acc, float* __restrict__ part, const int* __restrict__ pos,
     long long dummy_row, int T, int Tk, int H, int K, float scale) {
   __shared__ __attribute__((aligned(16))) uint16_t sQ[4 * kSub + kKT * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t sDO[4 * kSub];  // dout rows of the 32 heads
   __shared__ __attribute__((aligned(16))) uint16_t sKV0[4 * kSub + kKT * 64];
   __shared__ __attribute__((aligned(16))) uint16_t sKV1[4 * kSub + kKT * 64];
-  __shared__ __attribute__((aligned(16))) float sSp[4 * 16 * 64];  // partials (S^T, then dP^T)
   __shared__ __attribute__((aligned(16))) uint16_t sDS[kKT * kHT];  // scale dS as [entry][head]
   __shared__ __attribute__((aligned(16))) uint16_t sPT[kKT * kHT];  // P as [entry][head]
   __shared__ __attribute__((aligned(16))) int sIdx[3][kKT];  // raw entry lists, as in the forward
@@ -385,7 +362,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void s
   __shared__ int sRed[4];
 
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), hi = lane >> 5;
-  const int l32 = lane & 31;
+  const int l32 = lane & 31, g = lane >> 4, r = lane & 15;
+  const int hh = w & 1, eh = w >> 1;
   const int n_ht = (H + kHT - 1) / kHT;
   // Workgroups go to the XCDs round-robin, so consecutive ids spread a run
   // of tokens over all of them (list lengths, and so costs, change slowly
@@ -395,11 +373,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void s
   const int t = __builtin_amdgcn_readfirstlane(T - 1 - id / n_ht), h0 = __builtin_amdgcn_readfirstlane((id % n_ht) * kHT);
   const int* idx_t = idx + (size_t)t * K;
   const int* pos_t = SPLIT ? pos + (size_t)t * K : nullptr;
-  const int head = h0 + l32;                   // this lane's head (S^T columns)
-  const bool head_ok = head < H;
-  const int hc = min(head, H - 1);
-  const float lse_l2 = lse[(size_t)t * H + hc] * kLog2e;  // -inf for a token without entries: P = 0 below
-  const float dl = delta[(size_t)t * H + hc];
+  // This lane's head in the score block (result column r).
+  const int hs = h0 + 16 * hh + r;
+  const bool hs_ok = hs < H;
+  const int hsc = min(hs, H - 1);
+  const float lse_l2 = lse[(size_t)t * H + hsc] * kLog2e;  // -inf for a token without entries: P = 0 below
+  const float dl = delta[(size_t)t * H + hsc];
   const float c = scale * kLog2e;
 
   {
@@ -408,19 +387,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void s
     for (int st = 0; st < 4; st++) tile_load_async<128, kHT, 4>(qb + 128 * st, kQK, h0, H, sQ + st * kSub, w, lane);
     tile_load_async<64, kHT, 4>(qb + 512, kQK, h0, H, sQ + 4 * kSub, w, lane);
   }
-  // dO operands, fixed for the whole workgroup:
-  //   dP^T B operand (k = value channel 128w + 16kk .., n = head): dO[head][..]
-  //   dKV  B operand (k = head 16kk' .., n = channel 32 blk + l32): dO[head'][ch]
   const uint16_t* dob = dout + ((size_t)t * H) * kVD;
-  bf16x8 bdo[8];
 #pragma unroll
-  for (int kk = 0; kk < 8; kk++) {
-    const uint16_t* r = dob + (size_t)hc * kVD + 128 * w + 16 * kk;
-    const u32x2 a = *reinterpret_cast<const u32x2*>(r + 4 * hi);
-    const u32x2 b = *reinterpret_cast<const u32x2*>(r + 8 + 4 * hi);
-    bdo[kk] = __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
-  }
-  bf16x8 vdo[4][2];  // channel blocks w, w+4, w+8, w+12 (< 16): dO[head 16kk + op_k(i)][32 blk + l32]
+  for (int st = 0; st < 4; st++) tile_load_async<128, kHT, 4>(dob + 128 * st, kVD, h0, H, sDO + st * kSub, w, lane);
+  // Score operands (B of the 16x16x32 product, k = channel, n = head hs):
+  // lane (r, g) reads channels 32ks + 8g .. +7 of q[hs] from sQ and of
+  // dout[hs] from sDO.
+  // dKV's dO operand (A, k = head 16kk + op_k(i), m = channel 32 blk + l32)
+  // for channel blocks w, w+4, w+8, w+12 (< 16).
+  bf16x8 vdo[4][2];
 #pragma unroll
   for (int bi = 0; bi < 4; bi++)
 #pragma unroll
@@ -429,11 +404,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void s
       float x[8];
 #pragma unroll
       for (int i = 0; i < 8; i++) {
-        const int hh = min(h0 + 16 * kk + (i < 4 ? 4 * hi + i : 8 + 4 * hi + (i - 4)), H - 1);
-        x[i] = from_bf16(dob[(size_t)hh * kVD + ch]);
+        const int h = min(h0 + 16 * kk + (i < 4 ? 4 * hi + i : 8 + 4 * hi + (i - 4)), H - 1);
+        x[i] = from_bf16(dob[(size_t)h * kVD + ch]);
       }
       vdo[bi][kk] = pack8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
     }
+  // Complete these loads here, once: waits the compiler would otherwise put
+  // at their first use inside the tile loop would drain the gathers in flight.
+  asm volatile("s_waitcnt vmcnt(0)"
+               : "+v"(vdo[0][0]), "+v"(vdo[0][1]), "+v"(vdo[1][0]), "+v"(vdo[1][1]), "+v"(vdo[2][0]),
+                 "+v"(vdo[2][1]), "+v"(vdo[3][0]), "+v"(vdo[3][1]));
 
   const int n_tiles = live_tiles(idx_t, K, Tk, sRed, w, lane);
   const GatherCols gcols = gather_cols(w, lane);
@@ -450,20 +430,43 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void s
   // the same number of atomics per tile whatever the entries (the wait at the
   // start of the next tile counts on that).
   const __amdgpu_buffer_rsrc_t acc_rs = buffer_rsrc(dkv_acc, (uint32_t)Tk * (uint32_t)(kQK * 4));
+  // Byte offsets of the score block's operands, channels 32ks + 8g .. +7:
+  // row 16eh + r of a gathered tile (A), row 16hh + r of sQ and sDO (B).
+  // Inside a 128-channel sub-tile only ks % 4 changes the swizzled slot; the
+  // sub-tile adds a constant.
+  uint32_t offK[6], offH[6];
+#pragma unroll
+  for (int m = 0; m < 4; m++) {
+    offK[m] = 2u * (uint32_t)swz_off<128>(16 * eh + r, 32 * m + 8 * g);
+    offH[m] = 2u * (uint32_t)swz_off<128>(16 * hh + r, 32 * m + 8 * g);
+  }
+#pragma unroll
+  for (int m = 0; m < 2; m++) {
+    offK[4 + m] = 2u * (uint32_t)(4 * kSub + swz_off<64>(16 * eh + r, 32 * m + 8 * g));
+    offH[4 + m] = 2u * (uint32_t)(4 * kSub + swz_off<64>(16 * hh + r, 32 * m + 8 * g));
+  }
+  auto sub_op = [&](const uint16_t* tl, const uint32_t(&o)[6], int ks) {
+    return lds_b128_at(tl, ks < 16 ? o[ks & 3] + 2u * kSub * (ks >> 2) : o[ks - 12]);
+  };
+  // dQ's (scale dS)^T operand (B, k = entry, n = head l32), transposing reads
+  // of the [entry][head] tile in the k order of sop_tr.
+  const int gp = (lane >> 4) & 1, L = lane & 15;
+  const uint32_t offD0 = 2u * (uint32_t)((4 * hi + (L >> 2)) * kHT + 16 * gp + 4 * (L & 3));
 
   const int nblk = w < 2 ? 5 : 4;  // channel blocks of this wave: w, w+4, w+8, w+12, (w+16)
   f32x16 dqa[5];
 #pragma unroll
   for (int bi = 0; bi < 5; bi++) dqa[bi] = f32x16{};
 
-  auto tile = [&](auto buf_tag, int it) {
+  auto tile = [&](auto buf_tag, auto nb_tag, int it) {
     constexpr int BUF = decltype(buf_tag)::value;
+    constexpr int NB = decltype(nb_tag)::value;  // channel blocks of this wave
     const uint16_t* cKV = BUF ? sKV1 : sKV0;
     uint16_t* nKV = BUF ? sKV0 : sKV1;
     const int slot = it % 3;
     // Tile it resident.  It was gathered before the previous tile's dKV
-    // atomics (at least 64 per wave, issued after the gather), which may
-    // stay in flight: the counter retires in issue order.
+    // atomics or stores (at least 16 per wave, issued after the gather),
+    // which may stay in flight: the counter retires in issue order.
     if (it > 0)
       wait_vmem_but<SPLIT ? kStoreSlack : kAtomSlack>();
     else
@@ -474,59 +477,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void s
     if (it + 1 < n_tiles) gather_rows_async(kv, sIdx[(it + 1) % 3], (it + 1) * kKT, K, Tk, nKV, gcols, w, lane);
     const int* cIdx = sIdx[slot];
     const int e0 = it * kKT;
-    // S^T partial over channels 144w .. 144w+143.
-    f32x16 sp = f32x16{};
+    const uint32_t vmask =
+        (uint32_t)__builtin_amdgcn_ballot_w64(lane < kKT ? entry_ok(cIdx, lane, e0, K, Tk) : false);
+    // S^T and dP^T of the block: entries 16eh + 4g + j, head hs.
+    f32x4 s = f32x4{}, dp = f32x4{};
 #pragma unroll
-    for (int kk = 0; kk < 9; kk++) {
-      const int d0 = 144 * w + 16 * kk;
-      sp = mfma32(sop_row(cKV, l32, d0, hi), sop_row(sQ, l32, d0, hi), sp);
+    for (int ks = 0; ks < 18; ks++) {
+      const bf16x8 a = sub_op(cKV, offK, ks);
+      s = mfma16(a, sub_op(sQ, offH, ks), s);
+      if (ks < 16) dp = mfma16(a, sub_op(sDO, offH, ks), dp);
     }
-    // dP^T partial over value channels 128w .. 128w+127.
-    f32x16 dpp = f32x16{};
+    const uint32_t ml = vmask >> (16 * eh + 4 * g);
+    float p[4], ds[4];
 #pragma unroll
-    for (int kk = 0; kk < 8; kk++) dpp = mfma32(sop_row(cKV, l32, 128 * w + 16 * kk, hi), bdo[kk], dpp);
-    const uint32_t sp_base = lds_addr(sSp);
-    store_partial(sp_base, w, lane, sp);
-    lds_barrier();
-    const f32x16 ssum = sum_partials(sp_base, lane);
-    f32x16 p;
-#pragma unroll
-    for (int j = 0; j < 16; j++) {
-      const bool ok = head_ok && entry_ok(cIdx, c_row(j, hi), e0, K, Tk);
-      p[j] = ok ? __builtin_amdgcn_exp2f(fmaf(ssum[j], c, -lse_l2)) : 0.f;
+    for (int j = 0; j < 4; j++) {
+      const bool ok = hs_ok && ((ml >> j) & 1u);
+      p[j] = ok ? __builtin_amdgcn_exp2f(fmaf(s[j], c, -lse_l2)) : 0.f;
+      ds[j] = p[j] * (dp[j] - dl);
     }
-    lds_barrier();  // S sums read by every wave: the buffer takes the dP partials
-    store_partial(sp_base, w, lane, dpp);
-    lds_barrier();
-    const f32x16 dpsum = sum_partials(sp_base, lane);
-    f32x16 ds;
 #pragma unroll
-    for (int j = 0; j < 16; j++) ds[j] = p[j] * (dpsum[j] - dl);
-    // dS^T and P^T to LDS as [entry][head] (wave 0 writes; all read below).
-    if (w == 0) {
-#pragma unroll
-      for (int j = 0; j < 16; j++) {
-        const int e = c_row(j, hi);
-        sDS[e * kHT + l32] = to_bf16(scale * ds[j]);
-        sPT[e * kHT + l32] = to_bf16(p[j]);
-      }
+    for (int j = 0; j < 4; j++) {
+      const int e = 16 * eh + 4 * g + j;
+      sDS[e * kHT + 16 * hh + r] = to_bf16(scale * ds[j]);
+      sPT[e * kHT + 16 * hh + r] = to_bf16(p[j]);
     }
-    // dQ^T += KV^T dS^T (dS^T from registers, entries in operand k order).
-    bf16x8 bds[2];
-#pragma unroll
-    for (int kk = 0; kk < 2; kk++)
-      bds[kk] = pack8(ds[8 * kk + 0], ds[8 * kk + 1], ds[8 * kk + 2], ds[8 * kk + 3], ds[8 * kk + 4], ds[8 * kk + 5],
-                      ds[8 * kk + 6], ds[8 * kk + 7]);
-#pragma unroll
-    for (int bi = 0; bi < 5; bi++)
-      if (bi < nblk)
-#pragma unroll
-        for (int kk = 0; kk < 2; kk++) dqa[bi] = mfma32(sop_tr_ch(cKV, w + 4 * bi, 16 * kk, lane), bds[kk], dqa[bi]);
     lds_barrier();  // sDS / sPT complete
-    // dKV rows of the tile's entries: C[entry][channel], channel blocks of this wave.
-    bf16x8 ads[2], apt[2];
+    // Per channel block of this wave: dQ^T += KV^T (scale dS)^T, and the
+    // block's dKV (operands of the next block read while this one's products
+    // run; the result leaves after the next block's products are issued).
+    bf16x8 bds[2], ads[2], apt[2];
 #pragma unroll
     for (int kk = 0; kk < 2; kk++) {
+      bds[kk] = lds_tr8_at(sDS, offD0 + 2u * (16 * kk) * kHT, offD0 + 2u * (16 * kk + 8) * kHT);
+      // (scale dS)^T and P^T rows of entry l32, heads in op_k order.
       const uint16_t* rd = sDS + l32 * kHT + 16 * kk;
       const uint16_t* rp = sPT + l32 * kHT + 16 * kk;
       const u32x2 a0 = *reinterpret_cast<const u32x2*>(rd + 4 * hi), a1 = *reinterpret_cast<const u32x2*>(rd + 8 + 4 * hi);
@@ -534,60 +517,88 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void s
       ads[kk] = __builtin_bit_cast(bf16x8, u32x4{a0[0], a0[1], a1[0], a1[1]});
       apt[kk] = __builtin_bit_cast(bf16x8, u32x4{b0[0], b0[1], b1[0], b1[1]});
     }
+    // SPLIT: entry l32's partial row (this lane's four channels of each 8).
+    float* prow = nullptr;
     if constexpr (SPLIT) {
-      // Transposed: dKV^T[channel][entry] = Q^T dS^T + dO^T P^T (the same
-      // operands, swapped), so that lane l32 holds entry l32's channels
-      // 32 blk + c_row(j): four 16-byte pieces of its partial row per block.
-      const long long r =
-          entry_ok(cIdx, l32, e0, K, Tk) ? (long long)sPos[slot][l32] * n_ht + h0 / kHT : dummy_row;
+      const long long rr = ((vmask >> l32) & 1u) ? (long long)sPos[slot][l32] * n_ht + h0 / kHT : dummy_row;
       // Positions lie in [0, T K): the clamp only keeps the stores inside the buffer.
-      float* prow = part + ((unsigned long long)r <= (unsigned long long)dummy_row ? r : dummy_row) * kQK + 4 * hi;
-#pragma unroll
-      for (int bi = 0; bi < 5; bi++) {
-        if (bi >= nblk) continue;
-        const int blk = w + 4 * bi;
-        f32x16 acc = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < 2; kk++) {
-          acc = mfma32(sop_tr_ch(sQ, blk, 16 * kk, lane), ads[kk], acc);
-          if (blk < 16) acc = mfma32(vdo[bi][kk], apt[kk], acc);
-        }
-#pragma unroll
-        for (int g = 0; g < 4; g++)
-          *reinterpret_cast<f32x4*>(prow + 32 * blk + 8 * g) =
-              f32x4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
-      }
-      return;
+      prow = part + ((unsigned long long)rr <= (unsigned long long)dummy_row ? rr : dummy_row) * kQK + 4 * hi;
     }
+    auto blk_ops = [&](int blk, bf16x8(&o)[4]) {
+      o[0] = sop_tr_ch(cKV, blk, 0, lane);
+      o[1] = sop_tr_ch(cKV, blk, 16, lane);
+      o[2] = sop_tr_ch(sQ, blk, 0, lane);
+      o[3] = sop_tr_ch(sQ, blk, 16, lane);
+    };
+    // SPLIT: dKV^T[channel][entry] (operands swapped), lane l32 holds entry
+    // l32's channels 32 blk + c_row(j): four 16-byte pieces per block.
+    // Atomic: dKV[entry][channel], lane l32 holds channel 32 blk + l32 of
+    // entries c_row(j).
+    auto emit = [&](int blk, const f32x16& acc) {
+      if constexpr (SPLIT) {
 #pragma unroll
-    for (int bi = 0; bi < 5; bi++) {
-      if (bi >= nblk) continue;
-      const int blk = w + 4 * bi;
-      f32x16 acc = f32x16{};
+        for (int gg = 0; gg < 4; gg++)
+          *reinterpret_cast<f32x4*>(prow + 32 * blk + 8 * gg) =
+              f32x4{acc[4 * gg], acc[4 * gg + 1], acc[4 * gg + 2], acc[4 * gg + 3]};
+      } else {
 #pragma unroll
-      for (int kk = 0; kk < 2; kk++) {
-        acc = mfma32(ads[kk], sop_tr_ch(sQ, blk, 16 * kk, lane), acc);
-        if (blk < 16) acc = mfma32(apt[kk], vdo[bi][kk], acc);
+        for (int j = 0; j < 16; j++) {
+          const int e = c_row(j, hi);
+          const uint32_t off = ((vmask >> e) & 1u)
+                                   ? (uint32_t)cIdx[e] * (uint32_t)(kQK * 4) + (uint32_t)(32 * blk + l32) * 4u
+                                   : kDropOffset;
+          __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[j], acc_rs, off, 0, 0);
+        }
       }
+    };
+    bf16x8 op[2][4];
+    f32x16 acc[2];
+    blk_ops(w, op[0]);
 #pragma unroll
-      for (int j = 0; j < 16; j++) {
-        const int e = c_row(j, hi);
-        const uint32_t off = entry_ok(cIdx, e, e0, K, Tk)
-                                 ? (uint32_t)cIdx[e] * (uint32_t)(kQK * 4) + (uint32_t)(32 * blk + l32) * 4u
-                                 : kDropOffset;
-        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[j], acc_rs, off, 0, 0);
+    for (int bi = 0; bi < NB; bi++) {
+      // Blocks w, w+4, w+8, w+12 (all with value channels), and w+16 for waves 0, 1.
+      if (bi + 1 < NB) blk_ops(w + 4 * (bi + 1), op[(bi + 1) & 1]);
+      const bf16x8(&o)[4] = op[bi & 1];
+      dqa[bi] = mfma32(o[0], bds[0], dqa[bi]);
+      dqa[bi] = mfma32(o[1], bds[1], dqa[bi]);
+      f32x16& a = acc[bi & 1];
+      if constexpr (SPLIT) {
+        a = mfma32(o[2], ads[0], f32x16{});
+        a = mfma32(o[3], ads[1], a);
+        if (bi < 4) {
+          a = mfma32(vdo[bi][0], apt[0], a);
+          a = mfma32(vdo[bi][1], apt[1], a);
+        }
+      } else {
+        a = mfma32(ads[0], o[2], f32x16{});
+        a = mfma32(ads[1], o[3], a);
+        if (bi < 4) {
+          a = mfma32(apt[0], vdo[bi][0], a);
+          a = mfma32(apt[1], vdo[bi][1], a);
+        }
       }
+      if (bi > 0) emit(w + 4 * (bi - 1), acc[(bi - 1) & 1]);
+    }
+    emit(w + 4 * (NB - 1), acc[(NB - 1) & 1]);
+  };
+  // Waves 0, 1 own five channel blocks, waves 2, 3 four: one copy of the
+  // loop each, so that block counts are constants inside it.
+  auto run = [&](auto nb_tag) {
+    for (int it = 0; it < n_tiles; it += 2) {
+      tile(std::integral_constant<int, 0>{}, nb_tag, it);
+      if (it + 1 < n_tiles) tile(std::integral_constant<int, 1>{}, nb_tag, it + 1);
     }
   };
-  for (int it = 0; it < n_tiles; it += 2) {
-    tile(std::integral_constant<int, 0>{}, it);
-    if (it + 1 < n_tiles) tile(std::integral_constant<int, 1>{}, it + 1);
-  }
+  if (w < 2)
+    run(std::integral_constant<int, 5>{});
+  else
+    run(std::integral_constant<int, 4>{});
   if (n_tiles == 0) wait_vmem();  // the query tile's loads
 
   // dq[t, head, channel]: dQ^T element j of block blk is channel
-  // 32 blk + c_row(j), head l32; four consecutive channels per store.
-  if (head_ok) {
+  // 32 blk + c_row(j), head h0 + l32; four consecutive channels per store.
+  const int head = h0 + l32;
+  if (head < H) {
     uint16_t* dqr = dq + ((size_t)t * H + head) * kQK;
 #pragma unroll
     for (int bi = 0; bi < 5; bi++) {
@@ -596,8 +607,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void s
 #pragma unroll
       for (int jg = 0; jg < 4; jg++)
         *reinterpret_cast<u32x2*>(dqr + 32 * blk + c_row(4 * jg, hi)) =
-            u32x2{pack_bf16x2(scale * dqa[bi][4 * jg], scale * dqa[bi][4 * jg + 1]),
-                  pack_bf16x2(scale * dqa[bi][4 * jg + 2], scale * dqa[bi][4 * jg + 3])};
+            u32x2{pack_bf16x2(dqa[bi][4 * jg], dqa[bi][4 * jg + 1]), pack_bf16x2(dqa[bi][4 * jg + 2], dqa[bi][4 * jg + 3])};
     }
   }
 }
