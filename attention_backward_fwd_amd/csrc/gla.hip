@@ -439,19 +439,21 @@ __global__ __launch_bounds__(512) void gla_sweep_kernel(const uint16_t* __restri
 }
 
 // dg[b, t, h] = sum_{t' >= t} dG_{t'} with dG_t = q_t.dq_t - k_t.dk_t.  One
-// workgroup per (b, 4 consecutive heads), 256 threads per head; segments of
-// 4096 tokens from the end, 16 consecutive tokens per thread: in-thread
-// suffix sums, an exclusive suffix over the 256 thread totals of a head (one
-// wave per head, four totals per lane, shuffles), the running total carried
-// to the next segment.  The threads of a head group are interleaved so that
-// each store covers 4 heads of a token (16 contiguous bytes of dg).
-constexpr int kDgHeads = 4, kDgThreads = 256, kDgPer = 16;
+// workgroup per (b, 4 consecutive heads, segment of 1024 tokens counted from
+// the end), 256 threads per head, 4 consecutive tokens per thread: the sum
+// of all tokens after the segment (each thread a fixed strided share, then
+// a fixed reduction tree), in-thread suffix sums, and an exclusive suffix
+// over the 256 thread totals of a head (one wave per head, four totals per
+// lane, shuffles).  The threads of a head group are interleaved so that each
+// store covers 4 heads of a token (16 contiguous bytes of dg).
+constexpr int kDgHeads = 4, kDgThreads = 256, kDgPer = 4, kDgSeg = kDgThreads * kDgPer;
 __global__ __launch_bounds__(kDgHeads * kDgThreads) void gla_dg_kernel(const float* __restrict__ dGp,
                                                                         float* __restrict__ dg, int T, int H,
                                                                         int BH) {
-  constexpr int SEG = kDgThreads * kDgPer, NPL = kDgThreads / 64;  // totals per lane in the head scan
+  constexpr int NPL = kDgThreads / 64;                 // totals per lane in the head scan
+  constexpr int NWV = kDgHeads * kDgThreads / 64;     // waves of the workgroup
   __shared__ float sT[kDgHeads][kDgThreads];
-  __shared__ float sTot[kDgHeads];
+  __shared__ float sTot[kDgHeads][NWV];
   const int tid = threadIdx.x, hl = tid % kDgHeads, tq = tid / kDgHeads;
   const int lane = tid & 63, w = tid >> 6;
   const int b = blockIdx.x, h = blockIdx.y * kDgHeads + hl;
@@ -460,51 +462,75 @@ __global__ __launch_bounds__(kDgHeads * kDgThreads) void gla_dg_kernel(const flo
   const float* pq = dGp + (size_t)bh * T;
   const float* pk = dGp + ((size_t)BH + bh) * T;
   float* dst = dg + (size_t)b * T * H + h;
-  float carry = 0.f;
-  for (int seg_end = T; seg_end > 0; seg_end -= SEG) {
-    const int t0 = seg_end - SEG + kDgPer * tq;  // this thread's first token (may be negative)
-    float x[kDgPer];
-    float tot = 0.f;
+  const int seg_end = T - (int)blockIdx.z * kDgSeg;
+  const bool vec = (T & 3) == 0;
+  auto load4 = [&](int t0, float (&x)[kDgPer]) {
+    if (vec && t0 >= 0 && t0 + 4 <= T) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(pq + t0);
+      const f32x4 c = *reinterpret_cast<const f32x4*>(pk + t0);
 #pragma unroll
-    for (int i = kDgPer - 1; i >= 0; i--) {
-      const int t = t0 + i;
-      tot += (t >= 0 ? pq[t] - pk[t] : 0.f);
-      x[i] = tot;  // sum of this thread's tokens t0+i .. t0+kDgPer-1
-    }
-    sT[hl][tq] = tot;
-    __syncthreads();
-    if (w < kDgHeads) {  // wave w: exclusive suffix over the totals of head w
-      float a[NPL], part = 0.f;
+      for (int i = 0; i < 4; i++) x[i] = a[i] - c[i];
+    } else {
 #pragma unroll
-      for (int i = NPL - 1; i >= 0; i--) {
-        a[i] = sT[w][NPL * lane + i];
-        part += a[i];
-      }
-      float suf = part;  // inclusive suffix over the lanes
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const float y = __shfl_down(suf, o, 64);
-        if (lane + o < 64) suf += y;
-      }
-      float run = suf - part;
-#pragma unroll
-      for (int i = NPL - 1; i >= 0; i--) {
-        sT[w][NPL * lane + i] = run;
-        run += a[i];
-      }
-      if (lane == 0) sTot[w] = suf;
-    }
-    __syncthreads();
-    const float after = sT[hl][tq] + carry;  // tokens of this head after this thread's block
-    if (on) {
-#pragma unroll
-      for (int i = 0; i < kDgPer; i++) {
+      for (int i = 0; i < 4; i++) {
         const int t = t0 + i;
-        if (t >= 0) dst[(size_t)t * H] = x[i] + after;
+        x[i] = (t >= 0 && t < T) ? pq[t] - pk[t] : 0.f;
       }
     }
-    carry += sTot[hl];
-    __syncthreads();  // sT and sTot reused by the next segment
+  };
+  // Tokens after the segment: this thread's share, then the head's sum.
+  float after_seg = 0.f;
+  for (int t0 = seg_end + kDgPer * tq; t0 < T; t0 += kDgSeg) {
+    float y[kDgPer];
+    load4(t0, y);
+    after_seg += (y[0] + y[1]) + (y[2] + y[3]);
+  }
+#pragma unroll
+  for (int o = kDgHeads; o < 64; o <<= 1) after_seg += __shfl_xor(after_seg, o, 64);
+  if (lane < kDgHeads) sTot[lane][w] = after_seg;  // lane == hl here; w < NWV
+  // This segment.
+  const int t0 = seg_end - kDgSeg + kDgPer * tq;  // this thread's first token (may be negative)
+  float x[kDgPer];
+  load4(t0, x);
+  float tot = 0.f;
+#pragma unroll
+  for (int i = kDgPer - 1; i >= 0; i--) {
+    tot += x[i];
+    x[i] = tot;  // sum of this thread's tokens t0+i .. t0+kDgPer-1
+  }
+  sT[hl][tq] = tot;
+  __syncthreads();
+  float carry = 0.f;
+#pragma unroll
+  for (int i = 0; i < NWV; i++) carry += sTot[hl][i];
+  if (w < kDgHeads) {  // wave w: exclusive suffix over the totals of head w
+    float a[NPL], part = 0.f;
+#pragma unroll
+    for (int i = NPL - 1; i >= 0; i--) {
+      a[i] = sT[w][NPL * lane + i];
+      part += a[i];
+    }
+    float suf = part;  // inclusive suffix over the lanes
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float y = __shfl_down(suf, o, 64);
+      if (lane + o < 64) suf += y;
+    }
+    float run = suf - part;
+#pragma unroll
+    for (int i = NPL - 1; i >= 0; i--) {
+      sT[w][NPL * lane + i] = run;
+      run += a[i];
+    }
+  }
+  __syncthreads();
+  const float after = sT[hl][tq] + carry;  // tokens of this head after this thread's block
+  if (on) {
+#pragma unroll
+    for (int i = 0; i < kDgPer; i++) {
+      const int t = t0 + i;
+      if (t >= 0) dst[(size_t)t * H] = x[i] + after;
+    }
   }
 }
 
@@ -516,8 +542,8 @@ hipError_t launch_gla_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* 
   float* dGp = (float*)workspace;
   hipLaunchKernelGGL(gla_sweep_kernel, dim3(B * H, 2), dim3(512), 0, stream, q, k, v, dout, g, dq, dk, dv, dGp, T,
                      H, scale);
-  hipLaunchKernelGGL(gla_dg_kernel, dim3(B, (H + kDgHeads - 1) / kDgHeads), dim3(kDgHeads * kDgThreads), 0, stream,
-                     dGp, dg, T, H, B * H);
+  hipLaunchKernelGGL(gla_dg_kernel, dim3(B, (H + kDgHeads - 1) / kDgHeads, (T + kDgSeg - 1) / kDgSeg),
+                     dim3(kDgHeads * kDgThreads), 0, stream, dGp, dg, T, H, B * H);
   return hipGetLastError();
 }
 

@@ -64,7 +64,10 @@ def _compare(gpu, ref, case, heads=None, inp=None):
         assert r <= TOL, (case, n, r)
 
 
-CASES = [(1, 64, 1), (2, 100, 3), (1, 1, 2), (1, 200, 2), (2, 333, 1), (1, 129, 2)]
+# The last two span several 1024-token segments of the gate's running sum
+# (T % 4 == 0: vector loads; T % 4 == 2: element loads) and a partial group of
+# four heads.
+CASES = [(1, 64, 1), (2, 100, 3), (1, 1, 2), (1, 200, 2), (2, 333, 1), (1, 129, 2), (1, 2500, 5), (1, 1030, 2)]
 
 
 @pytest.mark.parametrize("b,t,h", CASES)
