@@ -34,7 +34,8 @@ constexpr int kSub = kKT * 128;  // elements of a 128-channel sub-tile of 32 row
 // next tile starts (each wave issues 64 or 80 per tile; the counter holds 63).
 constexpr int kAtomSlack = 48;
 // The same for the split backward's 16-byte partial-row stores (16 or 20 per
-// wave and tile).
+// wave and tile: four per channel block, each a distinct 16-byte piece, so no
+// compilation can issue fewer; more would only make the wait stricter).
 constexpr int kStoreSlack = 16;
 // Byte offset past the end of any dKV accumulator (at most kSmlaMaxKvTokens
 // rows of 576 fp32): atomics sent there are dropped.
