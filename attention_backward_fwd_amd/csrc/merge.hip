@@ -48,7 +48,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const uint16_t* __restrict__
 #pragma unroll
         for (int u = 0; u < 4; u++) {
           const int k = min(k0 + u, n_parts - 1);  // past the end: reread the last part, weight 0
-          ov[u] = *reinterpret_cast<const u32x4*>(o_parts + (size_t)k * part_elems + off);
+          // Streaming load: each partial is read once.
+          ov[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(o_parts + (size_t)k * part_elems + off));
           wk[u] = k0 + u < n_parts ? __builtin_amdgcn_exp2f((lse_parts[(size_t)k * rows + lrow] - m) * kLog2e) : 0.f;
         }
 #pragma unroll

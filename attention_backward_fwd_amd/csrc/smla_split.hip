@@ -232,15 +232,16 @@ __global__ __launch_bounds__(kSumGroups * kSumCols) void dkv_sum_kernel(const fl
   const f32x4* p = reinterpret_cast<const f32x4*>(part) + c4;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   long long r = r0 + g;
+  // Streaming loads: each partial row is read once.
+  auto ld = [&](long long rr) { return __builtin_nontemporal_load(p + rr * kSumCols); };
   for (; r + 3 * kSumGroups < r1; r += 4 * kSumGroups) {
-    const f32x4 a0 = p[r * kSumCols], a1 = p[(r + kSumGroups) * kSumCols];
-    const f32x4 a2 = p[(r + 2 * kSumGroups) * kSumCols], a3 = p[(r + 3 * kSumGroups) * kSumCols];
+    const f32x4 a0 = ld(r), a1 = ld(r + kSumGroups), a2 = ld(r + 2 * kSumGroups), a3 = ld(r + 3 * kSumGroups);
     acc += a0;
     acc += a1;
     acc += a2;
     acc += a3;
   }
-  for (; r < r1; r += kSumGroups) acc += p[r * kSumCols];
+  for (; r < r1; r += kSumGroups) acc += ld(r);
   if (g > 0) red[g - 1][c4] = acc;
   __syncthreads();
   if (g == 0) {
