@@ -60,6 +60,11 @@ namespace mi355 {
 
 namespace {
 
+// Cache policy of the split path's dQ partial stores: nontemporal (each
+// 128-byte row piece of a store is whole, and the dQ sum reads it once).
+constexpr int kStreamStore = 2;
+
+
 constexpr int kBM = 32;  // queries per step
 constexpr int kNW = 8;   // waves per workgroup
 
@@ -263,7 +268,7 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     if (ATOMIC)
       __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v[i][j], rs, dq_voff, so, 0);
     else
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[i][j]), rs, dq_voff, so, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[i][j]), rs, dq_voff, so, kStreamStore);
   };
 
   // dQ' (32 x D) = dS' (32 x BN keys) K (BN keys x D) of one block as
@@ -567,9 +572,10 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
         const int key = n0 + 256 * tt + 32 * w + 8 * (j >> 2) + 4 * ehi + (j & 3);
         if (key < Sk) {
           if (PARTIAL) {
+            // Streaming stores: the group sum reads each partial once.
             const size_t o = ((size_t)(krow0 + key) * Hq + h) * D + d;
-            p.dk_part[o] = dk[tt][dt][j];
-            p.dv_part[o] = dv[tt][dt][j] * inv_scale;
+            __builtin_nontemporal_store(dk[tt][dt][j], p.dk_part + o);
+            __builtin_nontemporal_store(dv[tt][dt][j] * inv_scale, p.dv_part + o);
           } else {
             const size_t o = ((size_t)(krow0 + key) * Hkv + kvh) * D + d;
             p.dk[o] = to_bf16(dk[tt][dt][j]);
