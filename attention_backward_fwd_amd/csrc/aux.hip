@@ -58,9 +58,9 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const uint16_t* __restr
 // apart), added one at a time in ascending order, so the bits do not depend on
 // how the loads are grouped; the loads are issued up to eight at a time so
 // that they are in flight together instead of one memory latency apart.
-// fp32 partials and accumulators are read once, right after they were
-// written: streaming loads keep them from displacing other data in the
-// caches (17% faster for the split path's sum at 4 x 32 x 4096 x 128).
+// fp32 partials written with streaming stores and read once: streaming
+// loads keep them from displacing other data in the caches (17% faster for
+// the split path's sum at 4 x 32 x 4096 x 128).
 __device__ __forceinline__ f32x4 ld_stream(const float* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
 }
@@ -219,8 +219,10 @@ __global__ __launch_bounds__(256) void postprocess_kernel(const float* __restric
       const long long bs = row / Hq;
       const int s = (int)(bs % S);
       const long long b = bs / S;
-      const float* src = dq_accum + ((b * Hq + h) * S + s) * D + d0;
-      *reinterpret_cast<u32x4*>(dq + i * 8) = cvt8(ld_stream(src), ld_stream(src + 4));
+      // Plain loads: the accumulator was just written (atomics, or the
+      // split path's sum) and is usually still in the last-level cache.
+      const f32x4* src = reinterpret_cast<const f32x4*>(dq_accum + ((b * Hq + h) * S + s) * D + d0);
+      *reinterpret_cast<u32x4*>(dq + i * 8) = cvt8(src[0], src[1]);
     } else {
       const long long c = i - nq8;          // chunk of the [B,S,Hkv,D] output
       const long long rowkv = c / dchunks;  // (b, s, kv) flattened
