@@ -113,13 +113,22 @@ __device__ __forceinline__ float lane_value(float x, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
 }
 
-// Inclusive running sum over the 64 lanes of one wave.
-__device__ __forceinline__ float wave_scan(float x, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const float y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+// Inclusive running sum over the 64 lanes of one wave, in DPP moves (no LDS
+// round trips): running sums inside each row of 16 lanes (row_shr 1, 2, 4,
+// 8; lanes shifted in from outside the row read 0), then the last lane of
+// rows 0 and 2 added to rows 1 and 3 (row_bcast:15), then lane 31 to rows 2
+// and 3 (row_bcast:31).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xf, true));
+}
+__device__ __forceinline__ float wave_scan(float x, int) {
+  x += dpp_move<0x111, 0xf>(x);  // row_shr:1
+  x += dpp_move<0x112, 0xf>(x);  // row_shr:2
+  x += dpp_move<0x114, 0xf>(x);  // row_shr:4
+  x += dpp_move<0x118, 0xf>(x);  // row_shr:8
+  x += dpp_move<0x142, 0xa>(x);  // row_bcast:15 into rows 1, 3
+  x += dpp_move<0x143, 0xc>(x);  // row_bcast:31 into rows 2, 3
   return x;
 }
 
