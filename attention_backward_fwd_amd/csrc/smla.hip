@@ -132,6 +132,19 @@ __device__ __forceinline__ void gather_rows_async(const uint16_t* g, const int* 
   dma_b128_asm_off<0>(p2, tb + 2 * (4 * kSub + w * 512));
 }
 
+// Combine a per-lane value with the one held 16 lanes away (the other row of
+// its pair of 16-lane rows): permlane16_swap(x, x) returns {own, other} in
+// rows 0, 2 and {other, own} in rows 1, 3, so a symmetric operation of the
+// pair is the result in every lane (VALU only, no LDS round trip).
+__device__ __forceinline__ float x16_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float x16_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Number of 32-entry tiles up to and including the last valid entry of the
 // list idx_t[0 .. K) (0 when it has none): tiles past it hold only unused
 // slots and are skipped.  All 256 threads take part; `red` is 4 ints of LDS.
@@ -236,8 +249,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
         if (!((ml >> j) & 1u)) s[j] = -INFINITY;
     }
     float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = xhalf_max(x16_max(mx));
     sMx[w][lane] = mx;
     lds_barrier();
     const float mxc = fmaxf(mx, sMx[partner][lane]) * c;
@@ -268,8 +280,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
 
   // Row sums: this wave's 16 entries (the four lane groups), then the
   // partner's (same reference).
-  l_i += __shfl_xor(l_i, 16, 64);
-  l_i += __shfl_xor(l_i, 32, 64);
+  l_i = xhalf_sum(x16_sum(l_i));
   sL[w][lane] = l_i;
   lds_barrier();
   const float l_tot = eh ? sL[partner][lane] + l_i : l_i + sL[partner][lane];
