@@ -211,6 +211,30 @@ def test_smla_bwd_split_against_oracle(t, tk, h, k):
     assert torch.equal(gpu["dkv"], again["dkv"]) and torch.equal(gpu["dq"], again["dq"]), case
 
 
+def test_smla_bwd_split_wide_key_range():
+    """Key rows 0 .. 299999 (19-bit keys: two radix passes of 10 and 9 bits,
+    1024-digit counts), most of them selected by no token (their dkv rows
+    must be exact zeros), and 128 heads (four 32-head tiles per token, so
+    four partial rows per entry)."""
+    t, tk, h, k = 6, 300000, 128, 300
+    rng = np.random.default_rng(31)
+    idx = np.stack([rng.choice(tk, size=k, replace=False) for _ in range(t)]).astype(np.int32)
+    idx[0, :5] = [0, 1, tk - 1, tk - 2, 150000]                 # both ends of the key range
+    idx[1, 7] = idx[1, 8]                                       # a key listed twice
+    idx[2, 100:] = -1
+    inp = smla_inputs(t, tk, h, seed=32)
+    f = {n: x.double().numpy() for n, x in inp.items()}
+    ref = sm.sparse_mla_bwd(f["q"], f["kv"], idx, f["do"], SCALE)
+    gpu = _run_bwd(inp, idx, use_atomic=False)
+    ratios = {n: err_ratio(np64(gpu[n]), ref[n]) for n in ("dq", "dkv")}
+    say("smla bwd split wide keys: " + " ".join(f"{n}={r:.2e}" for n, r in ratios.items()))
+    for n, r in ratios.items():
+        assert r <= TOL, (n, r)
+    unused = np.all(ref["dkv"] == 0.0, axis=1)
+    assert unused.sum() > tk - t * k
+    assert np.all(np64(gpu["dkv"])[unused] == 0.0)
+
+
 def test_smla_bwd_split_gaps_and_scattered_sentinels():
     t, tk, h, k = 6, 400, 40, 130
     inp = smla_inputs(t, tk, h, seed=21)
