@@ -617,8 +617,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the problem shards over (batch, KV head) with no exchange; see the design notes)",
+        print("bench.py measures one GPU only: the library has no multi-GPU path (attention shards over "
+              "(batch, KV head) with no exchange between GPUs, so each GPU would run this same one-GPU problem)",
               file=sys.stderr)
         sys.exit(2)
 
