@@ -401,8 +401,10 @@ int attn_sparse_mla_bwd_postprocess(const float* dkv_accum, uint16_t* dkv, smla_
  *       the sum, over the valid entries (t, i) with indices[t, i] = j and
  *       over the 32-head tiles of t, of scale * sum_h dS q[t,h] (+ sum_h
  *       P dout[t,h] in channels 0..511), each entry's fp32 row formed
- *       whole and the rows added in one fixed order (by token, slot, head
- *       tile); 0 for a row no valid entry names.
+ *       whole and the rows added in one fixed order that depends on the
+ *       index lists alone (rows ordered by token, slot and head tile, summed
+ *       in four interleaved running sums that are then added in a fixed
+ *       order); 0 for a row no valid entry names.
  * workspace: device memory of at least
  * attn_sparse_mla_bwd_split_workspace_bytes(shape) bytes, 16-byte aligned,
  * owned by the caller, no initial contents needed; its size is dominated by
