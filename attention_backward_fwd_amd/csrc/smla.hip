@@ -72,12 +72,6 @@ __device__ __forceinline__ bf16x8 sop_tr64(const uint16_t* t, int k0, int x0, in
   const uint16_t* s = t + 4 * kSub;
   return lds_read_tr8(s + swz_off<64>(k0 + 4 * hi + (L >> 2), col), s + swz_off<64>(k0 + 8 + 4 * hi + (L >> 2), col));
 }
-// Transposing operand for channel block `dt` (32 channels: 0..15 in the
-// 128-channel sub-tiles, 16 and 17 in the 64-channel one).
-__device__ __forceinline__ bf16x8 sop_tr_ch(const uint16_t* t, int dt, int k0, int lane) {
-  return dt < 16 ? sop_tr(t, dt >> 2, k0, 32 * (dt & 3), lane) : sop_tr64(t, k0, 32 * (dt - 16), lane);
-}
-
 // Entry lists.  Wave 0 copies the raw indices of tile it (entries
 // 32it .. 32it+31, addresses clamped to the list) into an LDS slot by
 // LDS-DMA; an entry is used iff it lies inside the list and 0 <= j < Tk.
@@ -497,13 +491,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void s
     const int e0 = it * kKT;
     const uint32_t vmask =
         (uint32_t)__builtin_amdgcn_ballot_w64(lane < kKT ? entry_ok(cIdx, lane, e0, K, Tk) : false);
+    // SPLIT: the partial rows this lane stores: entry 16R + 8j + lane/8 for
+    // round R and half j, 16 bytes (chunk lane % 8) of its 128-byte line per
+    // channel block.
+    float* trow[2][2] = {{nullptr, nullptr}, {nullptr, nullptr}};
+    if constexpr (SPLIT) {
+      // The four positions are read together (unconditionally: every slot
+      // holds a value), then each row is chosen without branches; a
+      // position outside [0, dummy_row) (none are) would store to the sink row.
+      int pe[4];
+#pragma unroll
+      for (int q = 0; q < 4; q++) pe[q] = sPos[slot][8 * q + (lane >> 3)];
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const int et = 8 * q + (lane >> 3);
+        const unsigned long long rv = (unsigned long long)(long long)pe[q] * (unsigned)n_ht + (unsigned)(h0 / kHT);
+        const bool use = ((vmask >> et) & 1u) && rv < (unsigned long long)dummy_row;
+        const unsigned long long rr = use ? rv : (unsigned long long)dummy_row;
+        trow[q >> 1][q & 1] = part + rr * kQK + 4 * (lane & 7);
+      }
+    }
     // S^T and dP^T of the block: entries 16eh + 4g + j, head hs.
     f32x4 s = f32x4{}, dp = f32x4{};
+    {
+      // Operands fetched PF - 1 k-steps ahead of their products.
+      constexpr int PF = 4;
+      bf16x8 ka[18], qa[18], da[16];
+      auto fetch = [&](int i) {
+        ka[i] = sub_op(cKV, offK, i);
+        qa[i] = sub_op(sQ, offH, i);
+        if (i < 16) da[i] = sub_op(sDO, offH, i);
+      };
 #pragma unroll
-    for (int ks = 0; ks < 18; ks++) {
-      const bf16x8 a = sub_op(cKV, offK, ks);
-      s = mfma16(a, sub_op(sQ, offH, ks), s);
-      if (ks < 16) dp = mfma16(a, sub_op(sDO, offH, ks), dp);
+      for (int i = 0; i < PF - 1; i++) fetch(i);
+#pragma unroll
+      for (int ks = 0; ks < 18; ks++) {
+        if (ks + PF - 1 < 18) fetch(ks + PF - 1);
+        s = mfma16(ka[ks], qa[ks], s);
+        if (ks < 16) dp = mfma16(ka[ks], da[ks], dp);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     const uint32_t ml = vmask >> (16 * eh + 4 * g);
     float p[4], ds[4];
@@ -535,27 +562,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void s
       ads[kk] = __builtin_bit_cast(bf16x8, u32x4{a0[0], a0[1], a1[0], a1[1]});
       apt[kk] = __builtin_bit_cast(bf16x8, u32x4{b0[0], b0[1], b1[0], b1[1]});
     }
-    // SPLIT: the partial rows this lane stores: entry 16R + 8j + lane/8 for
-    // round R and half j, 16 bytes (chunk lane % 8) of its 128-byte line per
-    // channel block.
-    float* trow[2][2] = {{nullptr, nullptr}, {nullptr, nullptr}};
-    if constexpr (SPLIT) {
-#pragma unroll
-      for (int R = 0; R < 2; R++)
-#pragma unroll
-        for (int j = 0; j < 2; j++) {
-          const int et = 16 * R + 8 * j + (lane >> 3);
-          const long long rr = ((vmask >> et) & 1u) ? (long long)sPos[slot][et] * n_ht + h0 / kHT : dummy_row;
-          // Positions lie in [0, T K): the clamp only keeps the stores inside the buffer.
-          trow[R][j] = part + ((unsigned long long)rr <= (unsigned long long)dummy_row ? rr : dummy_row) * kQK +
-                       4 * (lane & 7);
-        }
-    }
-    auto blk_ops = [&](int blk, bf16x8(&o)[4]) {
-      o[0] = sop_tr_ch(cKV, blk, 0, lane);
-      o[1] = sop_tr_ch(cKV, blk, 16, lane);
-      o[2] = sop_tr_ch(sQ, blk, 0, lane);
-      o[3] = sop_tr_ch(sQ, blk, 16, lane);
+    // Operands of this wave's block bi (channel block w + 4 bi): in the
+    // 128-channel sub-tile bi for bi < 4, else the 64-channel one (w < 2).
+    // bi is a constant after unrolling, so no path is chosen at run time.
+    auto blk_ops = [&](int bi, bf16x8(&o)[4]) {
+      if (bi < 4) {
+        o[0] = sop_tr(cKV, bi, 0, 32 * w, lane);
+        o[1] = sop_tr(cKV, bi, 16, 32 * w, lane);
+        o[2] = sop_tr(sQ, bi, 0, 32 * w, lane);
+        o[3] = sop_tr(sQ, bi, 16, 32 * w, lane);
+      } else {
+        o[0] = sop_tr64(cKV, 0, 32 * w, lane);
+        o[1] = sop_tr64(cKV, 16, 32 * w, lane);
+        o[2] = sop_tr64(sQ, 0, 32 * w, lane);
+        o[3] = sop_tr64(sQ, 16, 32 * w, lane);
+      }
     };
     // SPLIT: dKV^T[channel][entry] (operands swapped), lane l32 holds entry
     // l32's channels 32 blk + c_row(j): four 16-byte pieces per block.
@@ -605,11 +626,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void s
     };
     bf16x8 op[2][4];
     f32x16 acc[2];
-    blk_ops(w, op[0]);
+    blk_ops(0, op[0]);
 #pragma unroll
     for (int bi = 0; bi < NB; bi++) {
       // Blocks w, w+4, w+8, w+12 (all with value channels), and w+16 for waves 0, 1.
-      if (bi + 1 < NB) blk_ops(w + 4 * (bi + 1), op[(bi + 1) & 1]);
+      if (bi + 1 < NB) blk_ops(bi + 1, op[(bi + 1) & 1]);
       const bf16x8(&o)[4] = op[bi & 1];
       dqa[bi] = mfma32(o[0], bds[0], dqa[bi]);
       dqa[bi] = mfma32(o[1], bds[1], dqa[bi]);
