@@ -233,9 +233,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     const int* cl = sIdx[it % 3];
     const uint32_t vmask =
         (uint32_t)__builtin_amdgcn_ballot_w64(lane < kKT ? entry_ok(cl, lane, it * kKT, K, Tk) : false);
-    f32x4 s = f32x4{};
+    f32x4 s;
+    {
+      // Operands fetched three k-steps ahead; two accumulation chains (even
+      // and odd k-steps) added at the end.
+      constexpr int PF = 4;
+      bf16x8 ka[18];
+      f32x4 s0 = f32x4{}, s1 = f32x4{};
 #pragma unroll
-    for (int ks = 0; ks < 18; ks++) s = mfma16(lds_b128_at(cKV, offA[ks]), bq[ks], s);
+      for (int i = 0; i < PF - 1; i++) ka[i] = lds_b128_at(cKV, offA[i]);
+#pragma unroll
+      for (int ks = 0; ks < 18; ks++) {
+        if (ks + PF - 1 < 18) ka[ks + PF - 1] = lds_b128_at(cKV, offA[ks + PF - 1]);
+        if (ks & 1)
+          s1 = mfma16(ka[ks], bq[ks], s1);
+        else
+          s0 = mfma16(ka[ks], bq[ks], s0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      s = s0 + s1;
+    }
     if (vmask != 0xFFFFFFFFu) {
       const uint32_t ml = vmask >> (16 * eh + 4 * g);
 #pragma unroll
