@@ -74,6 +74,34 @@ __device__ __forceinline__ bf16x8 op_trc(const uint16_t* t, const Lofs<DT>& o, i
 // The k index (0..15 within a 16-step) of element i of a lane's operand.
 __device__ __forceinline__ int op_k(int i, int hi) { return (i < 4 ? 4 * hi + i : 8 + 4 * hi + (i - 4)); }
 
+// A chain of N products whose LDS operands are fetched PF - 1 steps ahead of
+// the products that use them (fetch(k) returns step k's operands; use(k, ops)
+// issues its products), one scheduling region per step.  Everything unrolls,
+// so the operand array is registers.  One step ahead measured best here
+// (deeper prefetch and split accumulation chains were no faster).
+constexpr int kOpAhead = 2;  // PF of the chains below
+template <int N, int PF, typename Fetch, typename Use>
+__device__ __forceinline__ void pipelined(Fetch&& fetch, Use&& use) {
+  decltype(fetch(0)) ops[N];
+#pragma unroll
+  for (int i = 0; i < PF - 1 && i < N; i++) ops[i] = fetch(i);
+#pragma unroll
+  for (int k = 0; k < N; k++) {
+    if (k + PF - 1 < N) ops[k + PF - 1] = fetch(k + PF - 1);
+    use(k, ops[k]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+struct Ops2 {
+  bf16x8 a, b;
+};
+struct Ops3 {
+  bf16x8 a, b, c;
+};
+struct Ops4 {
+  bf16x8 a, b, c, d;
+};
+
 
 // ------------------------------------------------------------ chunk sweeps
 // One workgroup of 8 waves per (b*H + h, dir) walks the chunks of its
@@ -237,9 +265,9 @@ __device__ __forceinline__ void gla_sweep(const uint16_t* __restrict__ q, const 
     auto score = [&](const uint16_t* ta, int ra, const uint16_t* tb_, int rb) {
       const Lofs<kD> oD = phase_lofs(lofs);
       f32x16 acc = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < kD / 16; ks++)
-        acc = mfma32(op_row16<kD>(ta, oD, 32 * ra, 16 * ks), op_row16<kD>(tb_, oD, 32 * rb, 16 * ks), acc);
+      pipelined<kD / 16, kOpAhead>(
+          [&](int ks) { return Ops2{op_row16<kD>(ta, oD, 32 * ra, 16 * ks), op_row16<kD>(tb_, oD, 32 * rb, 16 * ks)}; },
+          [&](int, const Ops2& o) { acc = mfma32(o.a, o.b, acc); });
       return acc;
     };
     // Mask and scale of a score tile whose lanes are the tokens 32 lb.. and
@@ -280,12 +308,15 @@ __device__ __forceinline__ void gla_sweep(const uint16_t* __restrict__ q, const 
       const Lofs<kD> oD = phase_lofs(lofs);
 #pragma unroll
       for (int nb = 0; nb < 2; nb++) st[nb] *= decay;
-#pragma unroll
-      for (int ks = 0; ks < kC / 16; ks++) {
-        const bf16x8 a = scale_by(op_tr<kD>(ty, oD, 16 * ks, vb), ks);
-#pragma unroll
-        for (int nb = 0; nb < 2; nb++) st[nb] = mfma32(a, op_tr<kD>(tx, oD, 16 * ks, kb + 32 * nb), st[nb]);
-      }
+      pipelined<kC / 16, kOpAhead>(
+          [&](int ks) {
+            return Ops3{op_tr<kD>(ty, oD, 16 * ks, vb), op_tr<kD>(tx, oD, 16 * ks, kb), op_tr<kD>(tx, oD, 16 * ks, kb + 32)};
+          },
+          [&](int ks, const Ops3& o) {
+            const bf16x8 a = scale_by(o.a, ks);
+            st[0] = mfma32(a, o.b, st[0]);
+            st[1] = mfma32(a, o.c, st[1]);
+          });
     };
 
     // Outputs leave as whole rows: a wave puts its 32 tokens x 32 features
@@ -348,9 +379,9 @@ __device__ __forceinline__ void gla_sweep(const uint16_t* __restrict__ q, const 
       f32x16 aq = f32x16{};
       {
         const Lofs<kD> oD = phase_lofs(lofs);
-#pragma unroll
-        for (int ks = 0; ks < kD / 16; ks++)
-          aq = mfma32(op_row16<kD>(sS, oD, 32 * fb, 16 * ks), op_row16<kD>(cO, oD, 32 * tb, 16 * ks), aq);
+        pipelined<kD / 16, kOpAhead>(
+            [&](int ks) { return Ops2{op_row16<kD>(sS, oD, 32 * fb, 16 * ks), op_row16<kD>(cO, oD, 32 * tb, 16 * ks)}; },
+            [&](int, const Ops2& o) { aq = mfma32(o.a, o.b, aq); });
       }
       aq *= scale * __expf(G_tok);
       // h_{n+1} = e^{gl} h_n + sum_s e^{gl - G_s} k_s^T v_s (s < nv)
@@ -364,9 +395,11 @@ __device__ __forceinline__ void gla_sweep(const uint16_t* __restrict__ q, const 
       lds_barrier();  // score tiles complete
       {
         const Lofs<kD> oD = phase_lofs(lofs);
-#pragma unroll
-        for (int ks = 0; ks < kC / 16; ks++)
-          aq = mfma32(op_tr<kD>(cK, oD, 16 * ks, 32 * fb), sM[(2 * ((ks >> 1) * 2 + tb) + (ks & 1)) * 64 + lane], aq);
+        pipelined<kC / 16, kOpAhead>(
+            [&](int ks) {
+              return Ops2{op_tr<kD>(cK, oD, 16 * ks, 32 * fb), sM[(2 * ((ks >> 1) * 2 + tb) + (ks & 1)) * 64 + lane]};
+            },
+            [&](int, const Ops2& o) { aq = mfma32(o.a, o.b, aq); });
       }
       dot_partial(cQ, aq);
       // dq is staged where this wave's lanes just read q (no other wave reads
@@ -382,11 +415,15 @@ __device__ __forceinline__ void gla_sweep(const uint16_t* __restrict__ q, const 
       f32x16 ak = f32x16{}, av = f32x16{};
       {
         const Lofs<kD> oD = phase_lofs(lofs);
-#pragma unroll
-        for (int ks = 0; ks < kD / 16; ks++) {
-          ak = mfma32(op_row16<kD>(sS, oD, 32 * fb, 16 * ks), op_row16<kD>(cV, oD, 32 * tb, 16 * ks), ak);
-          av = mfma32(op_trc<kD>(sS, oD, 16 * ks, 32 * fb), op_row16<kD>(cK, oD, 32 * tb, 16 * ks), av);
-        }
+        pipelined<kD / 16, kOpAhead>(
+            [&](int ks) {
+              return Ops4{op_row16<kD>(sS, oD, 32 * fb, 16 * ks), op_row16<kD>(cV, oD, 32 * tb, 16 * ks),
+                          op_trc<kD>(sS, oD, 16 * ks, 32 * fb), op_row16<kD>(cK, oD, 32 * tb, 16 * ks)};
+            },
+            [&](int, const Ops4& o) {
+              ak = mfma32(o.a, o.b, ak);
+              av = mfma32(o.c, o.d, av);
+            });
       }
       const float fkv = __expf(gl - G_tok);
       ak *= fkv;
@@ -399,12 +436,16 @@ __device__ __forceinline__ void gla_sweep(const uint16_t* __restrict__ q, const 
       lds_barrier();  // score tiles complete
       {
         const Lofs<kD> oD = phase_lofs(lofs);
-#pragma unroll
-        for (int ks = 0; ks < kC / 16; ks++) {
-          const int id = (ks >> 1) * 2 + tb;
-          ak = mfma32(op_tr<kD>(cQ, oD, 16 * ks, 32 * fb), sM[(2 * id + (ks & 1)) * 64 + lane], ak);
-          av = mfma32(op_tr<kD>(cO, oD, 16 * ks, 32 * fb), sM[(2 * (4 + id) + (ks & 1)) * 64 + lane], av);
-        }
+        pipelined<kC / 16, kOpAhead>(
+            [&](int ks) {
+              const int id = (ks >> 1) * 2 + tb;
+              return Ops4{op_tr<kD>(cQ, oD, 16 * ks, 32 * fb), sM[(2 * id + (ks & 1)) * 64 + lane],
+                          op_tr<kD>(cO, oD, 16 * ks, 32 * fb), sM[(2 * (4 + id) + (ks & 1)) * 64 + lane]};
+            },
+            [&](int, const Ops4& o) {
+              ak = mfma32(o.a, o.b, ak);
+              av = mfma32(o.c, o.d, av);
+            });
       }
       dot_partial(cK, ak);
       // dk is staged where this wave's lanes just read k (no other wave reads
