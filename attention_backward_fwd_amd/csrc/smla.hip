@@ -347,7 +347,9 @@ __global__ __launch_bounds__(256) void smla_post_kernel(const float* __restrict_
 // entries 16(w >> 1) .. +15 and heads h0 + 16(w & 1) .. +15, as in the
 // forward, and computes its scores S^T and dP^T = V dO^T over all channels
 // with 16x16x32 products (the entries' rows from LDS, read once for both;
-// query and dO operands in registers): no partial sums cross waves.  Then
+// the token's query and dO rows sit in LDS for the whole list, and every
+// operand is read three k-steps ahead of its product): no partial sums
+// cross waves.  Then
 // P = exp(S - LSE), dS = P (dP - Delta) (padded heads and unused entries: 0),
 // and the waves hand scale dS and P over through LDS as [entry][head] tiles
 // (one barrier) for the two products that contract over entries or heads:
