@@ -51,12 +51,6 @@ __device__ __forceinline__ int sub_off(int row, int col) {
 
 // 32x32x16 operands (k order: lane half hi gets k = 4hi..4hi+3, 8+4hi..8+4hi+3
 // of each 16-step, the row order of a 32x32 result's elements 0..7).
-// Row-style: tile [x][k] in the sub-tile layout, k0 a multiple of 16.
-__device__ __forceinline__ bf16x8 sop_row(const uint16_t* t, int x, int k0, int hi) {
-  const u32x2 a = *reinterpret_cast<const u32x2*>(t + sub_off(x, k0 + 4 * hi));
-  const u32x2 b = *reinterpret_cast<const u32x2*>(t + sub_off(x, k0 + 8 + 4 * hi));
-  return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
-}
 // Transposing: tile [k][x] with x inside one 128-channel sub-tile `st`.
 __device__ __forceinline__ bf16x8 sop_tr(const uint16_t* t, int st, int k0, int x0, int lane) {
   const int hi = lane >> 5, L = lane & 15, gp = (lane >> 4) & 1;
