@@ -44,9 +44,12 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const uint16_t* __restr
     for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
     if (sub == 0) delta[row] = acc;
     if (dq_accum) {  // head-major [B][Hq][S][D]: row `row` starts at row * D
+      // Streaming stores: the zeros go straight out in whole lines (the
+      // accumulator is far larger than the caches, so the backward's
+      // atomics fetch it back from memory either way).
       f32x4* z = reinterpret_cast<f32x4*>(dq_accum + (size_t)row * D + 8 * sub);
-      z[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-      z[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      __builtin_nontemporal_store(f32x4{0.f, 0.f, 0.f, 0.f}, z);
+      __builtin_nontemporal_store(f32x4{0.f, 0.f, 0.f, 0.f}, z + 1);
     }
   }
 }
@@ -245,7 +248,9 @@ __global__ __launch_bounds__(256) void postprocess_kernel(const float* __restric
 
 unsigned grid_for(long long work, long long per_block) {
   long long g = (work + per_block - 1) / per_block;
-  const long long cap = 256LL * 64;  // enough resident workgroups for the whole chip
+  // One work item per thread (the kernels still loop, for grids past the
+  // cap): every thread's loads are in flight at once.
+  const long long cap = 1LL << 30;
   if (g > cap) g = cap;
   if (g < 1) g = 1;
   return (unsigned)g;
