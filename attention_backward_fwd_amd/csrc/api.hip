@@ -34,9 +34,16 @@ int n_key_blocks(const attn_shape& s) {
   return (s.seqlen + bn - 1) / bn;
 }
 
+// Grouped queries: fp32 dK/dV partials per (key row, KV head).
+int gqa_parts(const attn_shape& s) {
+  return bwd_gqa_parts(s.batch, s.heads_q / s.groups, s.groups, s.seqlen, s.head_dim);
+}
 // Workspace layout: [dK partials | dV partials] when groups > 1, then the
 // split path's dQ partials.  Every region is a multiple of 256 bytes.
-size_t ws_gqa_bytes(const attn_shape& s) { return s.groups > 1 ? 2 * elems_q(s) * sizeof(float) : 0; }
+size_t ws_gqa_half_bytes(const attn_shape& s) {
+  return s.groups > 1 ? elems_q(s) / s.groups * gqa_parts(s) * sizeof(float) : 0;
+}
+size_t ws_gqa_bytes(const attn_shape& s) { return 2 * ws_gqa_half_bytes(s); }
 size_t ws_split_bytes(const attn_shape& s, int use_atomic) {
   return use_atomic ? 0 : (size_t)n_key_blocks(s) * elems_q(s) * sizeof(float);
 }
@@ -212,9 +219,9 @@ int attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint
   p.dk = dk;
   p.dv = dv;
   char* ws = (char*)workspace;
-  const size_t nq_bytes = elems_q(shape) * sizeof(float);
   p.dk_part = shape.groups > 1 ? (float*)ws : nullptr;
-  p.dv_part = shape.groups > 1 ? (float*)(ws + nq_bytes) : nullptr;
+  p.dv_part = shape.groups > 1 ? (float*)(ws + ws_gqa_half_bytes(shape)) : nullptr;
+  p.hpw = shape.groups / gqa_parts(shape);
   p.dq_part = use_atomic ? nullptr : (float*)(ws + ws_gqa_bytes(shape));
   p.B = shape.batch;
   p.S = shape.seqlen;
@@ -272,10 +279,9 @@ int attn_bwd_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v, co
   const int bst = attn_bwd(q, k, v, dout, lse, delta, dq_accum, dk, dv, ws, kScratchBytes, shape, softmax_scale,
                            causal, 0, stream);
   if (bst || shape.groups == 1) return bst;
-  const size_t nq_bytes = elems_q(shape) * sizeof(float);
-  return hip_status(launch_gqa_reduce((const float*)ws, (const float*)(ws + nq_bytes), dk, dv, shape.seqlen,
-                                      shape.heads_q, shape.groups, shape.head_dim,
-                                      (long long)shape.batch * shape.seqlen, (hipStream_t)stream));
+  return hip_status(launch_gqa_reduce((const float*)ws, (const float*)(ws + ws_gqa_half_bytes(shape)), dk, dv,
+                                      shape.seqlen, shape.heads_q, shape.heads_q / shape.groups, gqa_parts(shape),
+                                      shape.head_dim, (long long)shape.batch * shape.seqlen, (hipStream_t)stream));
 }
 
 int attn_bwd_postprocess(const float* dq_accum, const void* workspace, size_t workspace_bytes, uint16_t* dq,
@@ -289,12 +295,11 @@ int attn_bwd_postprocess(const float* dq_accum, const void* workspace, size_t wo
   if (!aligned16(dq_accum) || !aligned16(dq) || (gqa && (!aligned16(dk) || !aligned16(dv) || !aligned16(workspace))))
     return ATTN_ERR_ALIGN;
   const char* ws = (const char*)workspace;
-  const size_t nq_bytes = elems_q(shape) * sizeof(float);
   return hip_status(launch_postprocess(dq_accum, gqa ? (const float*)ws : nullptr,
-                                       gqa ? (const float*)(ws + nq_bytes) : nullptr, dq, gqa ? dk : nullptr,
-                                       gqa ? dv : nullptr, shape.batch, shape.seqlen, shape.heads_q,
-                                       shape.groups, shape.head_dim, (long long)shape.batch * shape.seqlen,
-                                       (hipStream_t)stream));
+                                       gqa ? (const float*)(ws + ws_gqa_half_bytes(shape)) : nullptr, dq,
+                                       gqa ? dk : nullptr, gqa ? dv : nullptr, shape.batch, shape.seqlen,
+                                       shape.heads_q, shape.heads_q / shape.groups, gqa ? gqa_parts(shape) : 1,
+                                       shape.head_dim, (long long)shape.batch * shape.seqlen, (hipStream_t)stream));
 }
 
 int attn_merge(const uint16_t* o_parts, const float* lse_parts, int n_parts, uint16_t* o, float* lse,
@@ -395,6 +400,7 @@ int attn_bwd_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v, con
   p.dk_part = gqa ? (float*)ws : nullptr;
   p.dv_part = gqa ? (float*)(ws + nkv_bytes) : nullptr;
   p.dq_part = use_atomic ? nullptr : (float*)(ws + ws_varlen_gqa_bytes(shape));
+  p.hpw = 1;  // one query head per workgroup: each leaves its own partial
   p.cu = cu_seqlens_q;
   p.cu_k = cu_seqlens_k;
   p.T = shape.total_q;
@@ -448,8 +454,9 @@ int attn_bwd_varlen_postprocess(const float* dq_accum, const void* workspace, si
   const size_t nkv_bytes = (size_t)shape.total_k * shape.heads_q * shape.head_dim * sizeof(float);
   return hip_status(launch_postprocess(dq_accum, gqa ? (const float*)ws : nullptr,
                                        gqa ? (const float*)(ws + nkv_bytes) : nullptr, dq, gqa ? dk : nullptr,
-                                       gqa ? dv : nullptr, 1, shape.total_q, shape.heads_q, gqa ? shape.groups : 1,
-                                       shape.head_dim, shape.total_k, (hipStream_t)stream));
+                                       gqa ? dv : nullptr, 1, shape.total_q, shape.heads_q,
+                                       shape.heads_q / shape.groups, gqa ? shape.groups : 1, shape.head_dim,
+                                       shape.total_k, (hipStream_t)stream));
 }
 
 size_t gla_chunk_bwd_workspace_bytes(gla_shape shape) {

@@ -205,7 +205,8 @@ __device__ __forceinline__ u32x4 cvt8(f32x4 a, f32x4 b) {
 // Part 1 (chunks [0, nq8)): dq[b,s,h,:] = bf16(dq_accum[b,h,s,:]), 8 elements
 // per chunk (chunks numbered in the BSHD output order).
 // Part 2 (chunks [nq8, nq8 + nkv8), grouped queries only): dk/dv chunk of
-// (b, s, kv) = bf16(sum_r partial[b, s, kv*G + r]), ascending r.
+// (b, s, kv) = bf16(sum_r partial[b, s, kv, r]), ascending r < G (here G is
+// the number of partials per key row and KV head).
 __global__ __launch_bounds__(256) void postprocess_kernel(const float* __restrict__ dq_accum,
                                                           const float* __restrict__ dk_part,
                                                           const float* __restrict__ dv_part,
@@ -297,22 +298,22 @@ hipError_t launch_pad_fill(void* x0, void* x1, int fp32, int heads, float* lse, 
 }
 
 hipError_t launch_postprocess(const float* dq_accum, const float* dk_part, const float* dv_part, uint16_t* dq,
-                              uint16_t* dk, uint16_t* dv, int B, int S, int Hq, int G, int D,
+                              uint16_t* dk, uint16_t* dv, int B, int S, int Hq, int Hkv, int P, int D,
                               long long kv_rows, hipStream_t stream) {
   const long long nq8 = (long long)B * S * Hq * D / 8;
-  const long long nkv8 = G > 1 ? kv_rows * (Hq / G) * D / 8 : 0;
+  const long long nkv8 = dk_part ? kv_rows * Hkv * D / 8 : 0;
   hipLaunchKernelGGL(postprocess_kernel, dim3(grid_for(nq8 + nkv8, 256)), dim3(256), 0, stream, dq_accum,
-                     dk_part, dv_part, dq, dk, dv, nq8, nkv8, G, D, S, Hq);
+                     dk_part, dv_part, dq, dk, dv, nq8, nkv8, P, D, S, Hq);
   return hipGetLastError();
 }
 
 // The dK/dV half of the postprocess alone: dk/dv[b,s,kv,:] = bf16(sum over
-// r < G, ascending, of the per-query-head partials).
+// r < P, ascending, of the partials).
 hipError_t launch_gqa_reduce(const float* dk_part, const float* dv_part, uint16_t* dk, uint16_t* dv, int S, int Hq,
-                             int G, int D, long long kv_rows, hipStream_t stream) {
-  const long long nkv8 = kv_rows * (Hq / G) * D / 8;
+                             int Hkv, int P, int D, long long kv_rows, hipStream_t stream) {
+  const long long nkv8 = kv_rows * Hkv * D / 8;
   hipLaunchKernelGGL(postprocess_kernel, dim3(grid_for(nkv8, 256)), dim3(256), 0, stream, nullptr, dk_part,
-                     dv_part, nullptr, dk, dv, 0LL, nkv8, G, D, S, Hq);
+                     dv_part, nullptr, dk, dv, 0LL, nkv8, P, D, S, Hq);
   return hipGetLastError();
 }
 

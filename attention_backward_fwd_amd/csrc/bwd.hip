@@ -49,8 +49,10 @@
 // has exactly one writer, which makes that path bitwise deterministic.
 //
 // dK/dV never use atomics.  With one query head per KV head they are written
-// as bf16 here; with grouped-query attention each query head writes an fp32
-// partial and the postprocess sums a group's partials in a fixed order.
+// as bf16 here.  With grouped-query attention a workgroup sweeps G / P query
+// heads of its group one after the other (their dK/dV contributions add up
+// in its accumulators) and writes one fp32 partial; the postprocess sums a
+// group's P partials in a fixed order (P: bwd_gqa_parts()).
 #include <type_traits>
 
 #include "common.h"
@@ -123,13 +125,16 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
   const int hi = lane >> 5, l32 = lane & 31;
   const int Hq = p.Hq, G = p.G, Hkv = p.Hkv;
   const int n_nblk = (p.Sk + BN - 1) / BN;
+  // The workgroup sweeps HPW query heads of its group, one after the other;
+  // the group's NP = G / HPW head chunks each leave one dK/dV partial.
+  const int HPW = p.hpw, NP = G / HPW;
 
   // Tile order: each XCD gets a contiguous range of (batch, KV head) groups
   // (packed sequences: every eighth group, so that sequences of unequal
   // length load the XCDs evenly) and works through them a few at a time
   // (their Q/dO rows stay in its L2); key
   // blocks run heaviest-first (block 0 sees every query under causal
-  // masking) with a group's query heads side by side.
+  // masking) with a group's head chunks side by side.
   const int nwg = gridDim.x, NG = p.B * Hkv;
   int t = blockIdx.x, x = 0, nx = 1, NGx = NG;
   if (NG % 8 == 0) {
@@ -142,7 +147,7 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
   }
   // (Integer division runs on the vector unit; readfirstlane returns the
   // results to scalar registers, where everything derived from them stays.)
-  const int per_group = n_nblk * G;
+  const int per_group = n_nblk * NP;
   int grp, jbv, r;
   // Each XCD takes CH groups at a time: as many as keep about 8 MB of
   // shared rows in flight (Q and dO rows of one group's query heads (bf16)), at least 2, a power of two dividing
@@ -151,23 +156,30 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
   int CH = 2;
   while (2 * CH <= NGx && 2LL * CH * gbytes <= (8LL << 20)) CH *= 2;
   while (CH > 1 && NGx % CH) CH >>= 1;
+  // Workgroups that sweep several heads are few and long: then all of the
+  // XCD's groups go side by side, so that its key blocks run heaviest-first
+  // over all of them (longest-first list scheduling evens out the CUs; with
+  // a few groups at a time the last ones' heavy blocks start late and run
+  // alone).
+  if (HPW > 1) CH = NGx;
   if (nx == 8 && CH > 1) {
     // Their key blocks interleaved heaviest-first: group after group, the
     // last group's heaviest block would start near the end and run alone
     // while the XCD's other CUs idle.
     const int chunk = t / (CH * per_group), u = t % (CH * per_group);
-    jbv = u / (CH * G);
-    const int gl = CH * chunk + (u / G) % CH;  // group within this XCD's share
+    jbv = u / (CH * NP);
+    const int gl = CH * chunk + (u / NP) % CH;  // group within this XCD's share
     grp = p.cu ? gl * nx + x : x * NGx + gl;
-    r = u % G;
+    r = u % NP;
   } else {
     grp = p.cu ? (t / per_group) * nx + x : x * NGx + t / per_group;
-    jbv = (t % per_group) / G;
-    r = t % G;
+    jbv = (t % per_group) / NP;
+    r = t % NP;
   }
   const int jb = __builtin_amdgcn_readfirstlane(jbv);
   const int b = __builtin_amdgcn_readfirstlane(grp / Hkv), kvh = __builtin_amdgcn_readfirstlane(grp % Hkv);
-  const int h = __builtin_amdgcn_readfirstlane(kvh * G + r);
+  const int hc = __builtin_amdgcn_readfirstlane(r);                  // head chunk
+  const int h = __builtin_amdgcn_readfirstlane(kvh * G + hc * HPW);  // its first query head
   const int n0 = jb * BN;
   // This sequence's query and key rows (packed sequences: their own
   // lengths; key blocks past the end have nothing to do).  Query i sees key
@@ -178,8 +190,10 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
   const int Sk = __builtin_amdgcn_readfirstlane(sk.len), krow0 = __builtin_amdgcn_readfirstlane(sk.base);
   const int off = Sk - S;
   if (n0 >= Sk) return;
-  // Row-indexed tensors: [B][Hq][S], or [Hq][T] for packed sequences.
+  // Row-indexed tensors: [B][Hq][S], or [Hq][T] for packed sequences; head
+  // h + hh starts hh * hstr rows after head h.
   const size_t hrow0 = p.cu ? (size_t)h * p.T + row0 : (size_t)(b * Hq + h) * S;
+  const size_t hstr = p.cu ? (size_t)p.T : (size_t)S;
 
   const size_t qrs = (size_t)Hq * D, kvrs = (size_t)Hkv * D;
   const uint16_t* Qb = p.q + ((size_t)row0 * Hq + h) * D;
@@ -195,20 +209,21 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
   // n0 - off on (causal); none when that is past the end (dK = dV = 0).
   const int m_begin = CAUSAL ? max(n0 - off, 0) / BM * BM : 0;
   const int n_steps = S > m_begin ? (S - m_begin + BM - 1) / BM : 0;
+  const int n_tot = HPW * n_steps;  // steps over all the workgroup's heads
 
   // LSE and Delta of a query block land in LDS as raw fp32 rows (waves 0
   // and 1 each issue one 4-byte LDS-DMA load); rows past the end repeat the
   // last row and are masked below.
-  auto load_rows = [&](int m0, float* l_dst, float* d_dst) {
-    if (w == 0) row_load_async(lse_b + m0, S - m0, l_dst, lane);
-    if (w == 1) row_load_async(dl_b + m0, S - m0, d_dst, lane);
+  auto load_rows = [&](int hh, int m0, float* l_dst, float* d_dst) {
+    if (w == 0) row_load_async(lse_b + hh * hstr + m0, S - m0, l_dst, lane);
+    if (w == 1) row_load_async(dl_b + hh * hstr + m0, S - m0, d_dst, lane);
   };
   // Key block (resident for the whole sweep) and the first Q/dO block.
   tile_load_async<D, BN, NW>(Kb, kvrs, n0, Sk, sK, w, lane);
   if (n_steps > 0) {
     tile_load_async<D, BM, NW>(Qb, qrs, m_begin, S, sQ0, w, lane);
     tile_load_async<D, BM, NW>(dOb, qrs, m_begin, S, sdO0, w, lane);
-    load_rows(m_begin, sL0, sD0);
+    load_rows(0, m_begin, sL0, sD0);
   }
   // This wave's keys: n0 + 32w + l32.  Its V rows are the B operand of dP
   // (lane l: V[key][16ks + 8hi .. +7]) and stay in registers; keys past the
@@ -253,8 +268,8 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
   const size_t nq = (size_t)(p.cu ? p.T : p.B * p.S) * Hq * D;  // elements of one split partial slot
   constexpr int NEMIT = 4 * DQF4;  // atomics / stores per dQ wave per block
 
-  auto dq_rsrc = [&](int m0) {
-    const size_t blk_off = (hrow0 + m0) * D;
+  auto dq_rsrc = [&](int hh, int m0) {
+    const size_t blk_off = (hrow0 + hh * hstr + m0) * D;
     float* dst_base = ATOMIC ? p.dq_accum + blk_off : p.dq_part + (size_t)jb * nq + blk_off;
     return buffer_rsrc(dst_base, (uint32_t)BM * row_bytes);
   };
@@ -344,17 +359,17 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // dQ of the block at m0 leaves the workgroup: a full block as buffer
-  // atomics/stores, the last, partial one row by row (addresses derived
-  // here, not kept live).
-  auto dq_store = [&](int m0, const f32x4* dq) {
+  // dQ of the block at m0 of head h + hh leaves the workgroup: a full block
+  // as buffer atomics/stores, the last, partial one row by row (addresses
+  // derived here, not kept live).
+  auto dq_store = [&](int hh, int m0, const f32x4* dq) {
     if (!dq_wave) return;
     if (m0 + BM <= S) {
-      const __amdgpu_buffer_rsrc_t rs = dq_rsrc(m0);
+      const __amdgpu_buffer_rsrc_t rs = dq_rsrc(hh, m0);
 #pragma unroll
       for (int e = 0; e < NEMIT; e++) dq_emit(rs, dq, e);
     } else {
-      const size_t blk_off = (hrow0 + m0) * D;
+      const size_t blk_off = (hrow0 + hh * hstr + m0) * D;
       float* dst_base = ATOMIC ? p.dq_accum + blk_off : p.dq_part + (size_t)jb * nq + blk_off;
       const int lt = opaque_v(lane);
       const int tg = DQ32 ? lt >> 5 : lt >> 4;
@@ -378,7 +393,10 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
   // One query block; BUF selects the LDS buffers it reads (the other pair
   // receives the next block meanwhile) and the dS'^T tile it writes.  It
   // also computes and writes the dQ of the previous block from the other
-  // dS'^T tile, completed by the barrier that starts this step.
+  // dS'^T tile, completed by the barrier that starts this step.  Steps run
+  // over the query blocks of head h, then those of h + 1, ...; cur_h and
+  // cur_i name the head (from h) and query block of the current step.
+  int cur_h = 0, cur_i = 0;
   auto step = [&](auto buf_tag, int st) {
     constexpr int BUF = decltype(buf_tag)::value;
     uint16_t* cQ = BUF ? sQ1 : sQ0;
@@ -391,7 +409,12 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     float* nD = BUF ? sD0 : sD1;
     uint16_t* wS = BUF ? sdSt1 : sdSt0;        // this block's dS'^T
     const uint16_t* pS = BUF ? sdSt0 : sdSt1;  // the previous block's
-    const int m0 = m_begin + st * BM;
+    const int hh = cur_h, m0 = m_begin + cur_i * BM;
+    // The next block (loaded during this step) and the previous one (its dQ
+    // leaves at the end of this step), across a change of head.
+    const bool last_of_head = cur_i + 1 == n_steps;
+    const int nh = last_of_head ? hh + 1 : hh, nm0 = last_of_head ? m_begin : m0 + BM;
+    const int ph = cur_i == 0 ? hh - 1 : hh, pm0 = cur_i == 0 ? m_begin + (n_steps - 1) * BM : m0 - BM;
     // Block st resident.  From step 2 on, the dQ atomics/stores that ended
     // step st-1 (those of block st-2) came after those loads and may stay in
     // flight; step 0 wrote no dQ, so step 1 waits for everything.
@@ -400,10 +423,10 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     else
       wait_vmem();
     lds_barrier();  // block st resident, dS'^T of block st-1 complete; every wave is done with step st-1
-    if (st + 1 < n_steps) {
-      tile_load_async<D, BM, NW>(Qb, qrs, m0 + BM, S, nQ, w, lane);
-      tile_load_async<D, BM, NW>(dOb, qrs, m0 + BM, S, ndO, w, lane);
-      load_rows(m0 + BM, nL, nD);
+    if (st + 1 < n_tot) {
+      tile_load_async<D, BM, NW>(Qb + nh * D, qrs, nm0, S, nQ, w, lane);
+      tile_load_async<D, BM, NW>(dOb + nh * D, qrs, nm0, S, ndO, w, lane);
+      load_rows(nh, nm0, nL, nD);
     }
     // These loads stay ahead of this step's dQ atomics/stores in the
     // instruction stream: the next step's wait counts on that order.
@@ -542,19 +565,21 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     // (Tiles one after the other: their live ranges must not overlap.)
     __builtin_amdgcn_sched_barrier(0);
     }
-    if (st > 0) dq_store(m0 - BM, dq);
+    if (st > 0) dq_store(ph, pm0, dq);
+    cur_h = nh;
+    cur_i = last_of_head ? 0 : cur_i + 1;
   };
 
-  for (int st = 0; st < n_steps; st += 2) {
+  for (int st = 0; st < n_tot; st += 2) {
     step(std::integral_constant<int, 0>{}, st);
-    if (st + 1 < n_steps) step(std::integral_constant<int, 1>{}, st + 1);
+    if (st + 1 < n_tot) step(std::integral_constant<int, 1>{}, st + 1);
   }
   // dQ of the last block.
-  if (n_steps > 0) {
+  if (n_tot > 0) {
     lds_barrier();  // its dS'^T complete
     f32x4 dq[DQF4];
-    dq_block(((n_steps - 1) & 1) ? sdSt1 : sdSt0, dq);
-    dq_store(m_begin + (n_steps - 1) * BM, dq);
+    dq_block(((n_tot - 1) & 1) ? sdSt1 : sdSt0, dq);
+    dq_store(HPW - 1, m_begin + (n_steps - 1) * BM, dq);
   }
   // Each wave holds the complete dK/dV of its KT tiles of 32 keys.  Element
   // j of lane l of tile (tt, dt) is key 256tt + 32w + 8(j/4) + 4hi + j%4,
@@ -573,7 +598,7 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
         if (key < Sk) {
           if (PARTIAL) {
             // Streaming stores: the group sum reads each partial once.
-            const size_t o = ((size_t)(krow0 + key) * Hq + h) * D + d;
+            const size_t o = ((size_t)(krow0 + key) * (Hkv * NP) + kvh * NP + hc) * D + d;
             __builtin_nontemporal_store(dk[tt][dt][j], p.dk_part + o);
             __builtin_nontemporal_store(dv[tt][dt][j] * inv_scale, p.dv_part + o);
           } else {
@@ -589,7 +614,7 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2))) v
 template <int D, bool CAUSAL, bool ATOMIC, bool PARTIAL>
 hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   const int n_nblk = (p.Sk + bwd_block_n(D) - 1) / bwd_block_n(D);
-  const long long nwg = (long long)p.B * p.Hq * n_nblk;
+  const long long nwg = (long long)p.B * p.Hkv * (p.G / p.hpw) * n_nblk;
   hipLaunchKernelGGL((bwd_kernel<D, CAUSAL, ATOMIC, PARTIAL>), dim3((unsigned)nwg), dim3(kNW * 64), 0, stream, p);
   return hipGetLastError();
 }

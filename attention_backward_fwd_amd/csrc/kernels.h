@@ -13,6 +13,21 @@ namespace mi355 {
 // dQ partial per block of this many keys.
 __host__ __device__ constexpr int bwd_block_n(int D) { return D == 64 ? 512 : 256; }
 
+// Grouped-query attention: the number P of fp32 dK/dV partials the backward
+// leaves per (key row, KV head).  One workgroup sweeps the query blocks of
+// G / P query heads of a group one head after the other, so their dK/dV
+// contributions add up in its accumulators and only P partials per group
+// leave the kernel.  P is the smallest divisor of G that still gives the
+// grid (B x Hkv x P x key blocks workgroups) two workgroups per CU; with
+// fewer the causal key blocks, whose work differs up to n_blk-fold, would
+// not even out over the CUs.
+inline int bwd_gqa_parts(long long B, int Hkv, int G, int S, int D) {
+  const long long blocks = B * Hkv * ((S + bwd_block_n(D) - 1) / bwd_block_n(D));
+  for (int P = 1; P < G; P++)
+    if (G % P == 0 && blocks * P >= 512) return P;
+  return G;
+}
+
 // Packed variable-length sequences: when `cu` is set, "batch" b is sequence
 // b of the packed rows: queries cu[b] .. cu[b+1]-1 of T query rows and keys
 // cu_k[b] .. cu_k[b+1]-1 of Tk key rows (each range clamped to its tensor and
@@ -56,8 +71,9 @@ struct BwdParams {
   float* dq_part;   // split path: [n_kv_blocks][B][S][Hq][D] fp32
   uint16_t* dk;     // groups == 1 outputs, [B][S][Hkv][D] bf16
   uint16_t* dv;
-  float* dk_part;   // groups > 1: per-query-head partials, [B][Sk][Hq][D] fp32
+  float* dk_part;   // groups > 1: fp32 partials, [B][Sk][Hkv][G / hpw][D]
   float* dv_part;
+  int hpw;          // query heads of a group per workgroup (divides G)
   const int* cu;    // packed sequences: query offsets, or nullptr
   const int* cu_k;  // packed sequences: key offsets
   int T, Tk;        // query / key rows of the packed tensors (with cu)
@@ -83,13 +99,14 @@ hipError_t launch_dq_sum_varlen(const float* dq_part, float* dq_accum, const int
 // and those rows of an [Hq][T] LSE set to lse_value; null tensors skipped.
 hipError_t launch_pad_fill(void* x0, void* x1, int fp32, int heads, float* lse, int Hq, float lse_value,
                            const int* cu, int n_seqs, int T, int S, int D, hipStream_t stream);
-// dq = bf16(dq_accum) over B*S query rows; groups > 1: dk/dv = bf16(sum of
-// the group's partials) over kv_rows key rows.
+// dq = bf16(dq_accum) over B*S query rows; with partials (dk_part set):
+// dk/dv[row, kv] = bf16(sum of the P partials [row][kv][0 .. P-1]) over
+// kv_rows key rows of Hkv heads.
 hipError_t launch_postprocess(const float* dq_accum, const float* dk_part, const float* dv_part,
-                              uint16_t* dq, uint16_t* dk, uint16_t* dv, int B, int S, int Hq, int G,
+                              uint16_t* dq, uint16_t* dk, uint16_t* dv, int B, int S, int Hq, int Hkv, int P,
                               int D, long long kv_rows, hipStream_t stream);
 hipError_t launch_gqa_reduce(const float* dk_part, const float* dv_part, uint16_t* dk, uint16_t* dv, int S, int Hq,
-                             int G, int D, long long kv_rows, hipStream_t stream);
+                             int Hkv, int P, int D, long long kv_rows, hipStream_t stream);
 
 // Simple gated linear attention, chunked backward (head dim 128, chunks of
 // 64): a forward sweep (state h, dq) and a backward sweep (state dH, dk, dv)

@@ -510,7 +510,8 @@ def bench_sweep(args, bd, torch):
                                                                stream))
                 fwd_f, bwd_f = flops(w, causal)
                 pre_bytes = 4 * nq + 4 * rows + (4 * nq if ua else 0)
-                post_bytes = 6 * nq + ((8 * nq + 4 * nkv) if w.groups > 1 else 0)
+                # grouped heads: the fp32 dK/dV partials (the atomic path's whole workspace) read, bf16 dK/dV written
+                post_bytes = 6 * nq + ((bd.attn_bwd_workspace_bytes(sh, causal, 1) + 4 * nkv) if w.groups > 1 else 0)
                 t_back = t_pre + t_bwd + t_post
                 print(json.dumps({
                     "mode": "sweep", "workload": w.name, "causal": causal, "dq_path": path,

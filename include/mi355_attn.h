@@ -95,7 +95,12 @@ int attn_bwd_preprocess(const uint16_t* o, const uint16_t* dout, float* delta, f
 /*
  * Bytes of device workspace attn_bwd and attn_bwd_postprocess need for this
  * problem (0 when none is needed).  Layout, for reference only:
- *   groups > 1: fp32 per-query-head dK and dV partials, [B,S,Hq,D] each;
+ *   groups > 1: fp32 dK and dV partials, [B,S,Hkv,P,D] each, partial p
+ *     the sum over query heads kv*groups + p*groups/P .. of the next
+ *     groups/P (one backward workgroup sweeps those heads one after the
+ *     other).  P is the smallest divisor of groups with
+ *     B * Hkv * P * n_kv_blocks >= 512 (two workgroups per CU of the
+ *     256), else groups; n_kv_blocks as below;
  *   use_atomic == 0: fp32 per-KV-block dQ partials, [n_kv_blocks,B,Hq,S,D],
  *     n_kv_blocks = ceil(S / bn), bn = 256 for head_dim 128 and 512 for
  *     head_dim 64 (the backward kernel's key-block height).
@@ -115,8 +120,9 @@ size_t attn_bwd_workspace_bytes(attn_shape shape, int causal, int use_atomic);
  *     workspace slot; a second kernel sums the slots in ascending block order
  *     into dq_accum (fully overwritten).  Bitwise deterministic.
  *   groups == 1: dk, dv [B,S,Hkv,D] bf16 are written here.
- *   groups  > 1: per-query-head fp32 dK/dV partials go to the workspace and
- *     attn_bwd_postprocess reduces them; dk and dv are not touched (may be NULL).
+ *   groups  > 1: fp32 dK/dV partials (each over groups/P query heads, see
+ *     attn_bwd_workspace_bytes) go to the workspace and attn_bwd_postprocess
+ *     reduces them; dk and dv are not touched (may be NULL).
  *   workspace/workspace_bytes: at least attn_bwd_workspace_bytes(shape,
  *     causal, use_atomic) bytes; may be NULL when that is 0.
  */
@@ -154,8 +160,9 @@ int attn_bwd_dq_sum(const void* workspace, size_t workspace_bytes, float* dq_acc
  *   attn_bwd_postprocess applies to attn_bwd's partials happens here.  Run
  *   attn_bwd_postprocess(dq_accum, NULL, 0, dq, NULL, NULL, shape with
  *   groups = 1, stream) afterwards for the bf16 dQ.
- *   Scratch needed: (groups > 1 ? 2 : 0) * B*S*Hq*D * 4 bytes plus
- *   ceil(S / bn) * B*S*Hq*D * 4 bytes (bn as in attn_bwd_workspace_bytes);
+ *   Scratch needed: (groups > 1 ? 2P/groups : 0) * B*S*Hq*D * 4 bytes plus
+ *   ceil(S / bn) * B*S*Hq*D * 4 bytes (P and bn as in
+ *   attn_bwd_workspace_bytes);
  *   beyond 64 MiB the call returns
  *   ATTN_ERR_SCRATCH and launches nothing.
  *   The scratch of a GPU is shared by every call on it and holds what the
@@ -171,8 +178,8 @@ int attn_bwd_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v, co
 /*
  * Backward postprocess (flashattn_bwd_postprocess of the TileLang #940
  * examples): dq = bf16(dq_accum) with round-to-nearest-even; for groups > 1
- * also dk/dv[b,s,kv,:] = bf16(sum over r < groups, ascending, of the
- * workspace partials of query head kv*groups + r).
+ * also dk/dv[b,s,kv,:] = bf16(sum over p < P, ascending, of the workspace
+ * partials [b,s,kv,p]; P as in attn_bwd_workspace_bytes).
  *   dq_accum fp32 [B,Hq,S,D] (input); dq [B,S,Hq,D] bf16 (output);
  *   dk, dv [B,S,Hkv,D] bf16 (outputs, required only when groups > 1);
  *   workspace: the buffer attn_bwd used (required only when groups > 1).

@@ -1,5 +1,6 @@
 """Shared helpers of the GPU tests: run the HIP path through the C ABI."""
 
+import math
 import sys
 
 import numpy as np
@@ -8,6 +9,14 @@ import torch
 from attention_backward_fwd_amd import binding as bd
 
 TOL = 2e-2  # max|gpu - oracle| <= TOL * max|oracle|, per tensor
+
+
+def gqa_parts(b, s, hq, g, d):
+    """dK/dV partials per (key row, KV head) of the backward's workspace, by
+    the rule the header states: the smallest divisor P of the group size with
+    b * Hkv * P * key blocks >= 512, else the group size."""
+    blocks = b * (hq // g) * math.ceil(s / (512 if d == 64 else 256))
+    return next((p for p in range(1, g) if g % p == 0 and blocks * p >= 512), g)
 
 
 def say(msg):

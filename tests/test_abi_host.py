@@ -11,6 +11,7 @@ import math
 import pytest
 
 from attention_backward_fwd_amd import binding as bd
+from tests.gpu_helpers import gqa_parts
 
 P = ctypes.c_void_p
 A = P(0x10000)      # 16-byte aligned fake device address
@@ -70,6 +71,22 @@ def test_workspace_bytes(g, s):
     for causal in (0, 1):
         assert lib().attn_bwd_workspace_bytes(sh, causal, 1) == gqa
         assert lib().attn_bwd_workspace_bytes(sh, causal, 0) == gqa + nblk * nq * 4
+
+
+@pytest.mark.parametrize("b,s,hq,g,d,parts", [
+    (8, 2048, 32, 4, 128, 1),   # 8*8*8 = 512 workgroups with one partial per KV head
+    (1, 8192, 64, 8, 128, 2),   # 8*32 = 256: two partials of four heads each
+    (2, 1024, 48, 4, 64, 4),    # 2*12*2 = 48: one partial per query head
+    (6, 300, 96, 6, 128, 3),    # 6*16*2 = 192: P = 2 gives 384, P = 3 gives 576
+    (4, 300, 96, 6, 128, 6),    # 4*16*2 = 128: 1, 2, 3 give 128, 256, 384 -> the group size
+])
+def test_workspace_bytes_gqa_partials(b, s, hq, g, d, parts):
+    assert gqa_parts(b, s, hq, g, d) == parts
+    nkv = b * s * (hq // g) * d
+    nblk = math.ceil(s / (512 if d == 64 else 256))
+    sh = shp(b=b, s=s, hq=hq, g=g, d=d)
+    assert lib().attn_bwd_workspace_bytes(sh, 1, 1) == 2 * nkv * parts * 4
+    assert lib().attn_bwd_workspace_bytes(sh, 0, 0) == 2 * nkv * parts * 4 + nblk * b * s * hq * d * 4
 
 
 def test_workspace_bytes_block_height_follows_head_dim():
@@ -442,8 +459,8 @@ def test_sparse_mla_split_errors(kw, code):
     assert msplit(**kw) == E[code]
 
 
-# Scratch of attn_bwd_noalloc: 64 MiB; need = (2 if groups > 1) * nq * 4 + ceil(S/bn) * nq * 4, with key
-# blocks of bn = 256 keys at head_dim 128 and 512 at head_dim 64.
+# Scratch of attn_bwd_noalloc: 64 MiB; need = (2P/groups if groups > 1) * nq * 4 + ceil(S/bn) * nq * 4, with
+# key blocks of bn = 256 keys at head_dim 128 and 512 at head_dim 64 (P = groups at these sizes).
 @pytest.mark.parametrize("kw,code", [
     ({"dk": None, "shape": shp(g=1)}, "null"), ({"dv": None}, "null"), ({"delta": None}, "null"),
     ({"shape": shp(hq=6, g=4)}, "shape"), ({"shape": shp(d=96)}, "hd"), ({"causal": 2}, "flag"),

@@ -13,7 +13,7 @@ import torch
 
 from attention_backward_fwd_amd.synthetic import WORKLOADS, make_inputs, workload_inputs
 from oracle import attention as orc
-from tests.gpu_helpers import TOL, err_ratio, np64, run_path, say, to_dev
+from tests.gpu_helpers import TOL, err_ratio, gqa_parts, np64, run_path, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -105,6 +105,30 @@ def test_interleaved_group_order(b, hq, hkv, s, d, causal):
     for use_atomic in (1, 0):
         gpu = run_path(to_dev(inp), causal, scale, use_atomic)
         _compare(f"b{b} hq{hq} hkv{hkv} s{s} d{d} causal={causal} atomic={use_atomic}", gpu, ref)
+
+
+# (batch, heads_q, heads_kv, seqlen, head_dim, partials per KV head): grids
+# large enough that one workgroup sweeps several query heads of its group
+# (groups / partials of them), the dK/dV of those heads adding up in its
+# accumulators; the steps cross from one head to the next mid-pipeline.
+HEAD_CHUNKS = [
+    (32, 16, 8, 300, 128, 1),   # groups of 2, both heads in one workgroup, ragged second key block
+    (32, 16, 4, 600, 64, 2),    # groups of 4 as two chunks of 2, two 512-key blocks
+    (22, 32, 4, 520, 128, 2),   # groups of 8 as two chunks of 4, 11 groups per XCD
+    (6, 96, 16, 300, 128, 3),   # groups of 6 as three chunks of 2
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("b,hq,hkv,s,d,parts", HEAD_CHUNKS)
+def test_head_chunks(b, hq, hkv, s, d, parts, causal):
+    assert gqa_parts(b, s, hq, hq // hkv, d) == parts
+    inp = make_inputs(b, s, hq, hkv, d, seed=b * 1000 + s + d)
+    scale = 1.0 / math.sqrt(d)
+    ref = _oracle(inp, causal, scale, hq // hkv)
+    for use_atomic in (1, 0):
+        gpu = run_path(to_dev(inp), causal, scale, use_atomic)
+        _compare(f"b{b} hq{hq} hkv{hkv} s{s} d{d} parts={parts} causal={causal} atomic={use_atomic}", gpu, ref)
 
 
 def test_group_of_eight_odd_length():

@@ -17,7 +17,7 @@ import torch
 from attention_backward_fwd_amd import binding as bd
 from attention_backward_fwd_amd.synthetic import make_inputs
 from oracle import attention as orc
-from tests.gpu_helpers import TOL, err_ratio, np64, run_path, say, to_dev
+from tests.gpu_helpers import TOL, err_ratio, gqa_parts, np64, run_path, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -27,7 +27,7 @@ SCRATCH_BYTES = 64 << 20
 def _scratch_need(b, s, hq, g, d):
     nq = b * s * hq * d
     bn = 512 if d == 64 else 256  # key-block height of the backward kernel
-    return ((2 * nq * 4) if g > 1 else 0) + math.ceil(s / bn) * nq * 4
+    return ((2 * nq // g * gqa_parts(b, s, hq, g, d) * 4) if g > 1 else 0) + math.ceil(s / bn) * nq * 4
 
 
 def _noalloc(d, causal, scale):
