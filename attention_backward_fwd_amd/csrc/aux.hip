@@ -44,12 +44,11 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const uint16_t* __restr
     for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
     if (sub == 0) delta[row] = acc;
     if (dq_accum) {  // head-major [B][Hq][S][D]: row `row` starts at row * D
-      // Streaming stores: the zeros go straight out in whole lines (the
-      // accumulator is far larger than the caches, so the backward's
-      // atomics fetch it back from memory either way).
+      // (Plain stores: streaming ones measured faster only when the caches
+      // hold nothing dirty, and slower after other work.)
       f32x4* z = reinterpret_cast<f32x4*>(dq_accum + (size_t)row * D + 8 * sub);
-      __builtin_nontemporal_store(f32x4{0.f, 0.f, 0.f, 0.f}, z);
-      __builtin_nontemporal_store(f32x4{0.f, 0.f, 0.f, 0.f}, z + 1);
+      z[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      z[1] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
 }
