@@ -116,14 +116,19 @@ def test_full_size_whole_group_slice(name, use_atomic):
         assert ratios[n] <= TOL, (n, ratios[n])
 
 
-def test_split_bitwise_deterministic_full_size():
-    w = WORKLOADS["mha_causal_b4_h32_s4096_d128"]
+# MHA; grouped heads with one dK/dV partial per KV head (GQA-4: each backward
+# workgroup sweeps the group's four query heads) and with two (GQA-8).
+@pytest.mark.parametrize("name,causal", [("mha_causal_b4_h32_s4096_d128", True),
+                                         ("gqa4_causal_b8_h32_s2048_d128", True),
+                                         ("gqa8_b1_h64_s8192_d128", True)])
+def test_split_bitwise_deterministic_full_size(name, causal):
+    w = WORKLOADS[name]
     dev = to_dev(workload_inputs(w))
-    a = run_path(dev, True, w.scale, 0, poison=False)
+    a = run_path(dev, causal, w.scale, 0, poison=False)
     a = {n: a[n].clone() for n in ("dq", "dk", "dv", "dq_accum")}
-    b = run_path(dev, True, w.scale, 0, poison=True)
+    b = run_path(dev, causal, w.scale, 0, poison=True)
     for n in a:
         va = a[n].view(torch.int16) if a[n].dtype == torch.bfloat16 else a[n].view(torch.int32)
         vb = b[n].view(torch.int16) if b[n].dtype == torch.bfloat16 else b[n].view(torch.int32)
-        assert torch.equal(va, vb), n
-    say("[full] split path bitwise identical across runs at B4 H32 S4096 D128")
+        assert torch.equal(va, vb), (name, n)
+    say(f"[full] split path bitwise identical across runs: {name}")
