@@ -89,6 +89,26 @@ def test_workspace_bytes_gqa_partials(b, s, hq, g, d, parts):
     assert lib().attn_bwd_workspace_bytes(sh, 0, 0) == 2 * nkv * parts * 4 + nblk * b * s * hq * d * 4
 
 
+def test_workspace_bytes_follow_the_stated_partial_rule():
+    """attn_bwd_workspace_bytes against the rule the header states, over a
+    spread of grouped shapes (grids on both sides of 512 workgroups)."""
+    n = 0
+    for b in (1, 2, 3, 8, 22, 64):
+        for hq, g in ((8, 2), (16, 4), (24, 3), (32, 8), (48, 6), (64, 8), (96, 16)):
+            for s in (1, 255, 256, 513, 2048):
+                for d in (64, 128):
+                    if b * s * hq * d >= (1 << 31):
+                        continue
+                    sh = shp(b=b, s=s, hq=hq, g=g, d=d)
+                    nkv = b * s * (hq // g) * d
+                    nblk = math.ceil(s / (512 if d == 64 else 256))
+                    gqa = 2 * nkv * gqa_parts(b, s, hq, g, d) * 4
+                    assert lib().attn_bwd_workspace_bytes(sh, 1, 1) == gqa, (b, hq, g, s, d)
+                    assert lib().attn_bwd_workspace_bytes(sh, 1, 0) == gqa + nblk * b * s * hq * d * 4
+                    n += 1
+    assert n > 300
+
+
 def test_workspace_bytes_block_height_follows_head_dim():
     # 256-key blocks at head_dim 128: S = 300 needs 2 slots, S = 256 one.
     for s_, nblk in ((256, 1), (257, 2), (300, 2), (4096, 16)):
