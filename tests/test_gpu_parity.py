@@ -116,6 +116,7 @@ HEAD_CHUNKS = [
     (32, 16, 4, 600, 64, 2),    # groups of 4 as two chunks of 2, two 512-key blocks
     (22, 32, 4, 520, 128, 2),   # groups of 8 as two chunks of 4, 11 groups per XCD
     (6, 96, 16, 300, 128, 3),   # groups of 6 as three chunks of 2
+    (37, 14, 7, 300, 128, 1),   # 259 (batch, KV head) groups: not a multiple of 8, grid in plain order
 ]
 
 
