@@ -117,6 +117,8 @@ HEAD_CHUNKS = [
     (22, 32, 4, 520, 128, 2),   # groups of 8 as two chunks of 4, 11 groups per XCD
     (6, 96, 16, 300, 128, 3),   # groups of 6 as three chunks of 2
     (37, 14, 7, 300, 128, 1),   # 259 (batch, KV head) groups: not a multiple of 8, grid in plain order
+    (256, 4, 2, 17, 128, 1),    # one ragged query block per head: the sweep changes head at every step
+    (512, 2, 1, 1, 64, 1),      # a single query and key per sequence
 ]
 
 
