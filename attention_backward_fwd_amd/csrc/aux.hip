@@ -44,11 +44,13 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const uint16_t* __restr
     for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
     if (sub == 0) delta[row] = acc;
     if (dq_accum) {  // head-major [B][Hq][S][D]: row `row` starts at row * D
-      // (Plain stores: streaming ones measured faster only when the caches
-      // hold nothing dirty, and slower after other work.)
-      f32x4* z = reinterpret_cast<f32x4*>(dq_accum + (size_t)row * D + 8 * sub);
+      // Each store instruction covers whole lines (a row's first half, then
+      // its second half: 16 bytes per lane, consecutive lanes adjacent), not
+      // every other 16 bytes.  (Plain stores: streaming ones measured faster
+      // only when the caches hold nothing dirty, and slower after other work.)
+      f32x4* z = reinterpret_cast<f32x4*>(dq_accum + (size_t)row * D + 4 * sub);
       z[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-      z[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      z[TPR] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
 }
