@@ -198,13 +198,11 @@ __global__ __launch_bounds__(256) void pad_fill_kernel(void* __restrict__ x0, vo
   }
 }
 
-__device__ __forceinline__ u32x4 cvt8(f32x4 a, f32x4 b) {
-  return u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
-               pack_bf16x2(b[2], b[3])};
-}
+__device__ __forceinline__ u32x2 cvt4(f32x4 a) { return u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])}; }
 
 // Part 1 (chunks [0, nq8)): dq[b,s,h,:] = bf16(dq_accum[b,h,s,:]), 8 elements
-// per chunk (chunks numbered in the BSHD output order).
+// per chunk (chunks numbered in the BSHD output order; chunk c of a row takes
+// elements 4c.. of each half of the row).
 // Part 2 (chunks [nq8, nq8 + nkv8), grouped queries only): dk/dv chunk of
 // (b, s, kv) = bf16(sum_r partial[b, s, kv, r]), ascending r < G (here G is
 // the number of partials per key row and KV head).
@@ -226,24 +224,36 @@ __global__ __launch_bounds__(256) void postprocess_kernel(const float* __restric
       const long long b = bs / S;
       // Plain loads: the accumulator was just written (atomics, or the
       // split path's sum) and is usually still in the last-level cache.
-      const f32x4* src = reinterpret_cast<const f32x4*>(dq_accum + ((b * Hq + h) * S + s) * D + d0);
-      *reinterpret_cast<u32x4*>(dq + i * 8) = cvt8(src[0], src[1]);
+      // Chunk c of a row takes elements 4c.. of each half of the row, so
+      // that each load and store instruction covers whole lines.
+      const int c4 = d0 / 2;
+      const float* src = dq_accum + ((b * Hq + h) * S + s) * D + c4;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+      const f32x4 a2 = *reinterpret_cast<const f32x4*>(src + D / 2);
+      uint16_t* dst = dq + row * D + c4;
+      *reinterpret_cast<u32x2*>(dst) = cvt4(a);
+      *reinterpret_cast<u32x2*>(dst + D / 2) = cvt4(a2);
     } else {
       const long long c = i - nq8;          // chunk of the [B,S,Hkv,D] output
       const long long rowkv = c / dchunks;  // (b, s, kv) flattened
       const int d0 = (int)(c % dchunks) * 8;
-      const size_t base = (size_t)rowkv * G * D + d0;  // partial row (b, s, kv*G) at d0
+      const int c4 = d0 / 2;  // elements 4c.. of each half of the row, as for dQ
+      const size_t base = (size_t)rowkv * G * D + c4;  // partial row (b, s, kv, 0)
       f32x4 k0 = {0, 0, 0, 0}, k1 = {0, 0, 0, 0}, v0 = {0, 0, 0, 0}, v1 = {0, 0, 0, 0};
       for (int r = 0; r < G; r++) {
         const float* pk = dk_part + base + (size_t)r * D;
         const float* pv = dv_part + base + (size_t)r * D;
         k0 += ld_stream(pk);
-        k1 += ld_stream(pk + 4);
+        k1 += ld_stream(pk + D / 2);
         v0 += ld_stream(pv);
-        v1 += ld_stream(pv + 4);
+        v1 += ld_stream(pv + D / 2);
       }
-      *reinterpret_cast<u32x4*>(dk + c * 8) = cvt8(k0, k1);
-      *reinterpret_cast<u32x4*>(dv + c * 8) = cvt8(v0, v1);
+      uint16_t* dkr = dk + rowkv * D + c4;
+      uint16_t* dvr = dv + rowkv * D + c4;
+      *reinterpret_cast<u32x2*>(dkr) = cvt4(k0);
+      *reinterpret_cast<u32x2*>(dkr + D / 2) = cvt4(k1);
+      *reinterpret_cast<u32x2*>(dvr) = cvt4(v0);
+      *reinterpret_cast<u32x2*>(dvr + D / 2) = cvt4(v1);
     }
   }
 }
